@@ -1,0 +1,258 @@
+"""Plain, slow CPU oracle of the Qwen Sparse Attention (QSA) hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.  It shares no code
+with the HIP library.
+
+Arithmetic is float64 / int64.  Every step follows the method as described on
+the page "Qwen's million-token window has a 2,048-token keyhole" (cronfeed.work,
+English edition; its Chinese twin "Qwen 的百万 token 窗口，只有一道 2,048 token
+的锁孔" states the same facts):
+
+  * the opening section: each sparse-attention query picks up to 2,048
+    earlier tokens, grouped in at most 512 micro-blocks of four tokens, and
+    also takes the unfinished block at the sequence tail;
+  * section "A million-token window with a selective view": the indexer has
+    four query heads and one shared key head, compresses keys four at a time,
+    ranks the micro-blocks, expands the winners back to token positions and
+    runs core attention only there; the 2,048-token budget does not grow
+    with the context;
+  * section "Three speed claims, three different experiments": the baseline
+    is grouped-query attention, so core attention is GQA.
+
+The pages give no formula for the compression, the block score, the tie
+rule or the softmax scale.  The readings used here (each one listed with its
+reason in the design notes of this repository) are:
+
+  compress   kc[j] = sum_{r<4} k_idx[4j + r], exact, then one
+             round-to-nearest-even to bf16;
+  score      s[i][j] = sum_{h<4} max(0, q_idx[i,h] . kc[j]), no scale;
+  candidates completed blocks strictly before the query's own block,
+             j < bt = floor(t / 4);
+  select     keep all candidates when bt <= 512, else the 512 best under
+             (score descending, block index ascending);
+  tail       the query's own block, tokens 4*bt .. t (1 to 4 tokens);
+  attend     softmax(scale * q . k) over the gathered tokens, query head h
+             reading KV head floor(h / (Hq / Hkv)), scale = 1/sqrt(128).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 4          # tokens per micro-block
+TOPK = 512         # micro-blocks kept per query (2,048-token budget)
+IDX_HEADS = 4      # indexer query heads (one shared key head)
+IDX_DIM = 64       # indexer head dimension
+HEAD_DIM = 128     # core attention head dimension
+
+
+# --------------------------------------------------------------------------
+# bf16 <-> float64
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Value of bf16 bit patterns: the bf16 pattern is the top half of the
+    float32 pattern of the same number."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even); uint16 bits.
+
+    bf16 keeps 8 significant bits and float32's exponent range.  A finite
+    x = m * 2**e with 0.5 <= |m| < 1 is rounded to a multiple of its quantum
+    2**(e - 8), or of 2**-133 (the subnormal quantum) when x is that small;
+    np.rint rounds halves to even.  Results above the largest bf16 become inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x) & (x != 0.0)
+    v = np.where(finite, x, 1.0)
+    _, e = np.frexp(v)                           # |v| = m * 2**e, m in [0.5, 1)
+    q_exp = np.maximum(e - 8, -133)              # exponent of the bf16 quantum
+    r = np.ldexp(np.rint(np.ldexp(v, -q_exp)), q_exp)
+    max_bf16 = math.ldexp(255.0, 120)            # (2 - 2**-7) * 2**127
+    r = np.where(np.abs(r) > max_bf16, np.copysign(np.inf, v), r)
+    out = np.where(finite, r, x)
+    f32 = out.astype(np.float32)                 # exact: every result is a bf16 value
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# The four method steps
+# --------------------------------------------------------------------------
+
+def compress_keys(k_idx_bits: np.ndarray, n_tokens: int, first_block: int = 0) -> np.ndarray:
+    """Compressed indexer keys of blocks first_block .. floor(n_tokens/4) - 1.
+
+    The indexer "compresses keys four at a time" (section "A million-token
+    window with a selective view").  Reading: the micro-block key is the sum of
+    its four token keys, formed exactly and rounded once to bf16.
+    Returns uint16 bf16 bits, shape [n_blocks - first_block][64].
+    """
+    n_blocks = n_tokens // BLOCK
+    rows = bf16_bits_to_f64(k_idx_bits[first_block * BLOCK:n_blocks * BLOCK])
+    sums = np.zeros((n_blocks - first_block, rows.shape[-1]), dtype=np.float64)
+    for r in range(BLOCK):
+        sums += rows[r::BLOCK]
+    return f64_to_bf16_bits(sums)
+
+
+def block_scores(q_idx: np.ndarray, kc: np.ndarray) -> np.ndarray:
+    """Indexer score of every compressed block for one query.
+
+    q_idx: float64 [4][64] (the four indexer query heads); kc: float64
+    [n_blocks][64] (compressed keys of the shared key head).
+    s[j] = sum over heads of max(0, q_h . kc[j]).  The pages say only that the
+    indexer scores and ranks the blocks; the sum of per-head ReLU scores is the
+    reading adopted.  Exact for the small-integer inputs used here (every
+    partial sum is an integer far below 2**53).
+    """
+    per_head = kc @ q_idx.T                      # [n_blocks][4]
+    return np.maximum(per_head, 0.0).sum(axis=1)
+
+
+def select_blocks(scores: np.ndarray, k: int = TOPK) -> np.ndarray:
+    """Top-k micro-blocks of one query, ascending block ids (int64).
+
+    Up to 512 blocks are kept (opening section of the page: a 2,048-token
+    budget in at most 512 four-token micro-blocks).  With no more than k
+    candidates all are kept.  Otherwise v is the k-th largest score; every
+    block scoring above v is kept and the rest of the budget goes to the
+    lowest-numbered blocks scoring exactly v (the tie rule is a reading: the
+    pages state none).
+    """
+    n = scores.shape[0]
+    if n <= k:
+        return np.arange(n, dtype=np.int64)
+    v = np.partition(scores, n - k)[n - k]       # k-th largest value
+    above = np.nonzero(scores > v)[0]
+    ties = np.nonzero(scores == v)[0]            # ascending block ids
+    chosen = np.concatenate([above, ties[:k - above.shape[0]]])
+    return np.sort(chosen).astype(np.int64)
+
+
+def expand_tokens(sel: np.ndarray, t: int) -> np.ndarray:
+    """Token positions attended by the query at position t.
+
+    The winners are expanded "back to token positions", and the unfinished
+    block at the tail is added (opening section and section "A million-token
+    window with a selective view").  Reading: the tail is the query's own
+    block, tokens 4*floor(t/4) .. t, which holds 1 to 4 tokens.
+    """
+    bt = t // BLOCK
+    parts = [np.arange(BLOCK * int(j), BLOCK * int(j) + BLOCK, dtype=np.int64) for j in sel]
+    parts.append(np.arange(BLOCK * bt, t + 1, dtype=np.int64))
+    return np.sort(np.concatenate(parts))
+
+
+def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float):
+    """Grouped-query softmax attention of one query token over gathered rows.
+
+    q: float64 [Hq][D]; k_rows, v_rows: float64 [n][Hkv][D].  Query head h
+    reads KV head floor(h / (Hq / Hkv)).  Returns (o [Hq][D], lse [Hq]) with
+    lse = ln sum_s exp(scale * q_h . k_s).  Core attention over the selected
+    positions is GQA because the pages' dense baseline is grouped-query
+    attention (section "Three speed claims, three different experiments").
+    """
+    hq = q.shape[0]
+    hkv = k_rows.shape[1]
+    group = hq // hkv
+    o = np.zeros((hq, q.shape[1]), dtype=np.float64)
+    lse = np.full(hq, -np.inf, dtype=np.float64)
+    if k_rows.shape[0] == 0:
+        return o, lse
+    for h in range(hq):
+        g = h // group
+        z = scale * (k_rows[:, g, :] @ q[h])
+        m = z.max()
+        p = np.exp(z - m)
+        denom = p.sum()
+        o[h] = (p @ v_rows[:, g, :]) / denom
+        lse[h] = m + math.log(denom)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# Whole path
+# --------------------------------------------------------------------------
+
+def query_positions(length: int, n_query: int) -> np.ndarray:
+    """Positions of the n_query query tokens: the last n_query of the sequence."""
+    return np.arange(length - n_query, length, dtype=np.int64)
+
+
+def qsa_query(q_idx_i, kc_all, q_i, k_seq, v_seq, t: int, scale: float, k: int = TOPK):
+    """All steps for the query at position t.  Inputs are float64 arrays:
+    q_idx_i [4][64], kc_all [>= t//4][64], q_i [Hq][128], k_seq/v_seq [L][Hkv][128]."""
+    bt = t // BLOCK
+    s = block_scores(q_idx_i, kc_all[:bt])
+    sel = select_blocks(s, k)
+    tok = expand_tokens(sel, t)
+    o, lse = attend(q_i, k_seq[tok], v_seq[tok], scale)
+    return sel, tok, o, lse
+
+
+def qsa_forward(q_idx_bits, k_idx_bits, q_bits, k_bits, v_bits, lens, n_query: int,
+                scale: float | None = None, queries=None, k: int = TOPK):
+    """Run the oracle over a batch.
+
+    Arrays are uint16 bf16 bits in the layouts of the synthetic workloads.
+    ``queries`` optionally restricts the work to a list of (b, i) pairs.
+    Returns a dict with, per computed (b, i): sel, tok, out (float64 [Hq][128]),
+    lse, and per sequence the compressed keys kc (uint16 bits).
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    B = len(lens)
+    if queries is None:
+        queries = [(b, i) for b in range(B) for i in range(n_query)]
+    res = {"sel": {}, "tok": {}, "out": {}, "lse": {}, "kc": {}}
+    by_seq = {}
+    for b, i in queries:
+        by_seq.setdefault(b, []).append(i)
+    for b, idxs in by_seq.items():
+        length = int(lens[b])
+        kc_bits = compress_keys(k_idx_bits[b], length)
+        res["kc"][b] = kc_bits
+        kc = bf16_bits_to_f64(kc_bits)
+        pos = query_positions(length, n_query)
+        for i in idxs:
+            t = int(pos[i])
+            qi = bf16_bits_to_f64(q_idx_bits[b, i])
+            bt = t // BLOCK
+            s = block_scores(qi, kc[:bt])
+            sel = select_blocks(s, k)
+            tok = expand_tokens(sel, t)
+            o = lse = None
+            if q_bits is not None:
+                kr = bf16_bits_to_f64(k_bits[b, tok])
+                vr = bf16_bits_to_f64(v_bits[b, tok])
+                o, lse = attend(bf16_bits_to_f64(q_bits[b, i]), kr, vr, scale)
+            res["sel"][(b, i)] = sel
+            res["tok"][(b, i)] = tok
+            res["out"][(b, i)] = o
+            res["lse"][(b, i)] = lse
+    return res
+
+
+def dense_decode(q_bits, k_bits, v_bits, lens, n_query: int, scale: float | None = None,
+                 queries=None):
+    """Dense causal GQA over every earlier position (the comparator of the
+    speed experiment: grouped-query attention over the full context).
+    Returns {(b, i): (out, lse)}."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    B = len(lens)
+    if queries is None:
+        queries = [(b, i) for b in range(B) for i in range(n_query)]
+    out = {}
+    for b, i in queries:
+        t = int(lens[b]) - n_query + i
+        kr = bf16_bits_to_f64(k_bits[b, :t + 1])
+        vr = bf16_bits_to_f64(v_bits[b, :t + 1])
+        out[(b, i)] = attend(bf16_bits_to_f64(q_bits[b, i]), kr, vr, scale)
+    return out

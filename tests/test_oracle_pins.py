@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+values printed on the pages, a hand-worked example, closed forms, brute force,
+invariants and library routines.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+
+def bf16(vals):
+    """Exact bf16 bit patterns of small integers / simple floats (test input helper)."""
+    f = np.asarray(vals, dtype=np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- fixtures
+
+def test_page_constants(golden_dir):
+    with open(os.path.join(golden_dir, "page_constants.json")) as f:
+        c = json.load(f)
+    assert O.IDX_HEADS == c["index_query_heads"]["value"]
+    assert c["shared_key_heads"]["value"] == 1
+    assert O.BLOCK == c["block_tokens"]["value"]
+    assert O.TOPK == c["max_blocks"]["value"]
+    assert O.TOPK * O.BLOCK == c["token_budget"]["value"]
+    # the decode shape of the speed experiment: batch 4, 1 + 3 query positions
+    assert W.CONFIGS[4]["n_query"] == c["decode_queries_per_sequence"]["value"]
+    assert len(W.CONFIGS[4]["lens"]) == c["decode_batch"]["value"]
+    assert len(W.CONFIGS[3]["lens"]) == c["prefill_batch"]["value"]
+
+
+def test_worked_example(golden_dir):
+    with open(os.path.join(golden_dir, "worked_example.json")) as f:
+        ex = json.load(f)
+    k_idx = bf16(ex["k_idx"])
+    t = ex["t"]
+    kc = O.compress_keys(k_idx, t + 1)
+    assert kc.shape == (4, 2)
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(kc), np.array(ex["compressed"], float))
+    s = O.block_scores(np.array(ex["q_idx"], float), O.bf16_bits_to_f64(kc))
+    np.testing.assert_array_equal(s, ex["scores"])
+    sel = O.select_blocks(s, ex["k"])
+    np.testing.assert_array_equal(sel, ex["sel"])
+    tok = O.expand_tokens(sel, t)
+    np.testing.assert_array_equal(tok, ex["tok"])
+
+
+# ---------------------------------------------------------------- bf16
+
+def test_bf16_rounding_closed_forms():
+    cases = {
+        1.0: 0x3F80,
+        1.0 + 2.0 ** -8: 0x3F80,          # halfway, ties to even (down)
+        1.0 + 3 * 2.0 ** -8: 0x3F82,      # halfway, ties to even (up)
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,  # just above halfway
+        -2.5: 0xC020,
+        2.0 ** -133: 0x0001,              # smallest subnormal
+        2.5 * 2.0 ** -133: 0x0002,        # subnormal tie to even
+        3.5e38: 0x7F80,                   # above the largest bf16: inf
+        0.0: 0x0000,
+        256.0: 0x4380,
+        257.0: 0x4380,                    # 257 is halfway between 256 and 258: even
+        259.0: 0x4382,
+    }
+    got = O.f64_to_bf16_bits(np.array(list(cases.keys())))
+    assert [int(g) for g in got] == list(cases.values())
+
+
+def test_bf16_rounding_matches_torch_on_float32_inputs():
+    # For float32-representable inputs the definition reduces to torch's
+    # float32 -> bfloat16 conversion (round to nearest, ties to even).
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(200000).astype(np.float32)
+    x *= np.float32(2.0) ** rng.integers(-130, 120, x.shape[0]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.f64_to_bf16_bits(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_decode_roundtrip():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = O.bf16_bits_to_f64(bits)
+    fin = np.isfinite(vals)
+    back = O.f64_to_bf16_bits(vals[fin])
+    # +0/-0 and every finite pattern map back to themselves
+    np.testing.assert_array_equal(back, bits[fin])
+
+
+# ---------------------------------------------------------------- compress
+
+def test_compress_checksum_and_blocks():
+    w = W.make_custom(11, [1003], 5, 8, 1, parts=("index",))
+    n = int(w.lens[0])
+    kc = O.compress_keys(w.k_idx[0], n)
+    assert kc.shape == (n // 4, 64)
+    vals = O.bf16_bits_to_f64(w.k_idx[0])
+    # invariant: total of compressed keys = total of keys of completed blocks
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(kc).sum(0), vals[:4 * (n // 4)].sum(0))
+    # block-by-block with plain Python ints
+    for j in (0, 17, n // 4 - 1):
+        rows = [[int(v) for v in vals[4 * j + r]] for r in range(4)]
+        want = [sum(col) for col in zip(*rows)]
+        assert [int(x) for x in O.bf16_bits_to_f64(kc[j])] == want
+
+
+def test_compress_first_block_and_rounding():
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((64, 64)).astype(np.float32)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    full = O.compress_keys(kb, 64)
+    part = O.compress_keys(kb, 64, first_block=5)
+    np.testing.assert_array_equal(full[5:], part)
+    # non-integer inputs: one rounding of the exact sum (check with Fractions)
+    from fractions import Fraction
+    vals = O.bf16_bits_to_f64(kb)
+    for j in range(16):
+        for d in range(0, 64, 9):
+            exact = sum(Fraction(vals[4 * j + r, d]) for r in range(4))
+            got = Fraction(O.bf16_bits_to_f64(full[j:j + 1, d:d + 1])[0, 0])
+            # nearest bf16: no other bf16 value is strictly closer
+            f = float(got)
+            m, e = math.frexp(f) if f != 0 else (0.0, -200)
+            ulp = Fraction(2) ** (max(e - 8, -133)) if f != 0 else Fraction(2) ** -133
+            assert abs(got - exact) <= ulp / 2
+
+
+def test_compress_ignores_partial_block():
+    kb = bf16(np.ones((7, 3)))
+    kc = O.compress_keys(kb, 7)
+    assert kc.shape == (1, 3)
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(kc), [[4, 4, 4]])
+
+
+# ---------------------------------------------------------------- scores
+
+def test_scores_brute_force_python_ints():
+    rng = np.random.default_rng(5)
+    q = rng.integers(-8, 9, (4, 64))
+    kc = rng.integers(-32, 33, (37, 64))
+    s = O.block_scores(q.astype(float), kc.astype(float))
+    for j in range(37):
+        want = 0
+        for h in range(4):
+            dot = 0
+            for d in range(64):
+                dot += int(q[h, d]) * int(kc[j, d])
+            want += max(0, dot)
+        assert s[j] == want
+
+
+def test_scores_l1_closed_form():
+    # heads +e_a, +e_b, -e_a, -e_b turn the score into |kc_a| + |kc_b|
+    rng = np.random.default_rng(9)
+    kc = rng.integers(-100, 101, (200, 64)).astype(float)
+    a, b = 3, 41
+    q = np.zeros((4, 64))
+    q[0, a] = 1
+    q[1, b] = 1
+    q[2, a] = -1
+    q[3, b] = -1
+    np.testing.assert_array_equal(O.block_scores(q, kc), np.abs(kc[:, a]) + np.abs(kc[:, b]))
+
+
+def test_scores_relu_per_head_not_after_sum():
+    # two heads with opposite dots: per-head ReLU keeps the positive one
+    q = np.zeros((4, 2))
+    q[0] = [1, 0]
+    q[1] = [-1, 0]
+    kc = np.array([[5.0, 0.0]])
+    assert O.block_scores(q, kc)[0] == 5.0
+
+
+# ---------------------------------------------------------------- select
+
+def brute_topk(s, k):
+    if s.shape[0] <= k:
+        return np.arange(s.shape[0])
+    order = np.lexsort((np.arange(s.shape[0]), -s))  # score desc, index asc
+    return np.sort(order[:k])
+
+
+def test_select_vs_full_sort_tie_heavy():
+    rng = np.random.default_rng(21)
+    for trial in range(3000):
+        n = int(rng.integers(1, 300))
+        k = int(rng.integers(1, 40))
+        levels = int(rng.integers(1, 5))
+        s = rng.integers(0, levels, n).astype(float)
+        np.testing.assert_array_equal(O.select_blocks(s, k), brute_topk(s, k))
+
+
+def test_select_vs_full_sort_k512():
+    rng = np.random.default_rng(22)
+    for trial in range(60):
+        n = int(rng.integers(400, 2000))
+        s = rng.integers(0, int(rng.integers(2, 3000)), n).astype(float)
+        np.testing.assert_array_equal(O.select_blocks(s, 512), brute_topk(s, 512))
+
+
+def test_select_special_cases():
+    z = np.zeros(5000)
+    np.testing.assert_array_equal(O.select_blocks(z), np.arange(512))
+    c = np.full(3000, 7.0)
+    np.testing.assert_array_equal(O.select_blocks(c), np.arange(512))
+    small = np.arange(100, 0, -1).astype(float)
+    np.testing.assert_array_equal(O.select_blocks(small), np.arange(100))
+    rng = np.random.default_rng(4)
+    s = rng.integers(0, 50, 10000).astype(float)
+    s[7777] = 1000
+    assert 7777 in O.select_blocks(s)
+    # exactly 512 candidates: all kept; 513: one dropped (the lowest, last index on ties)
+    np.testing.assert_array_equal(O.select_blocks(np.ones(512)), np.arange(512))
+    np.testing.assert_array_equal(O.select_blocks(np.ones(513)), np.arange(512))
+
+
+def test_select_invariant_under_key_scaling():
+    # multiplying every indexer key by 4 scales all scores by 4: same selection
+    w = W.make_custom(12, [6000], 3, 8, 1, parts=("index",))
+    kc1 = O.bf16_bits_to_f64(O.compress_keys(w.k_idx[0], 6000))
+    q = O.bf16_bits_to_f64(w.q_idx[0, 0])
+    s1 = O.block_scores(q, kc1)
+    s4 = O.block_scores(q, 4 * kc1)
+    np.testing.assert_array_equal(s4, 4 * s1)
+    np.testing.assert_array_equal(O.select_blocks(s1), O.select_blocks(s4))
+
+
+# ---------------------------------------------------------------- tail / expand
+
+@pytest.mark.parametrize("n", [4093, 4094, 4095, 4096, 1, 2, 3, 4, 5])
+def test_tail_by_length_mod4(n):
+    t = n - 1
+    bt = t // 4
+    rng = np.random.default_rng(n)
+    s = rng.integers(0, 100, bt).astype(float)
+    sel = O.select_blocks(s)
+    tok = O.expand_tokens(sel, t)
+    tail = t - 4 * bt + 1
+    assert tail == (n - 1) % 4 + 1
+    assert tok.shape[0] == 4 * min(512, bt) + tail
+    assert tok[-1] == t and tok.max() == t
+    np.testing.assert_array_equal(tok[-tail:], np.arange(4 * bt, t + 1))
+    assert np.all(np.diff(tok) > 0)
+    assert tok.shape[0] <= O.TOPK * O.BLOCK + O.BLOCK
+
+
+# ---------------------------------------------------------------- attention
+
+def sdpa_ref(q, k, v, scale, causal_pos=None):
+    """torch's SDPA (float64, CPU) as the textbook routine: q [Hq][D], k/v [n][Hkv][D]."""
+    hq, hkv = q.shape[0], k.shape[1]
+    kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+    qq = torch.from_numpy(q)[:, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+    return out[:, 0, :].numpy()
+
+
+def test_attend_matches_sdpa():
+    rng = np.random.default_rng(31)
+    for hq, hkv, n in [(8, 1, 37), (32, 4, 300), (4, 4, 1), (6, 2, 9)]:
+        q = rng.standard_normal((hq, 128))
+        k = rng.standard_normal((n, hkv, 128))
+        v = rng.standard_normal((n, hkv, 128))
+        o, lse = O.attend(q, k, v, 0.088)
+        np.testing.assert_allclose(o, sdpa_ref(q, k, v, 0.088), rtol=1e-12, atol=1e-12)
+        # lse against its closed form for head 0
+        z = 0.088 * (k[:, 0, :] @ q[0])
+        assert abs(lse[0] - math.log(np.exp(z).sum())) < 1e-10
+
+
+def test_attend_special_cases():
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((8, 128))
+    v = rng.standard_normal((20, 2, 128))
+    o, lse = O.attend(q, np.zeros((20, 2, 128)), v, 0.1)
+    np.testing.assert_allclose(o[:4], np.broadcast_to(v[:, 0].mean(0), (4, 128)), atol=1e-14)
+    np.testing.assert_allclose(o[4:], np.broadcast_to(v[:, 1].mean(0), (4, 128)), atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(20), atol=1e-14)
+    k = rng.standard_normal((20, 2, 128))
+    o, _ = O.attend(q, k, np.full((20, 2, 128), 3.25), 0.1)
+    np.testing.assert_allclose(o, 3.25, atol=1e-13)
+    k = np.zeros((20, 2, 128))
+    k[13, :, :] = 50 * q[0] / np.linalg.norm(q[0])
+    o, _ = O.attend(q[:1], k[:, :1], v[:, :1], 1.0)
+    np.testing.assert_allclose(o[0], v[13, 0], atol=1e-12)
+
+
+def test_qsa_equals_dense_for_short_context():
+    # every context of at most 2,052 tokens keeps all its blocks: QSA == dense causal
+    w = W.make_custom(41, [2052, 1500, 7], 6, 16, 2)
+    res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, 6)
+    dense = O.dense_decode(w.q, w.k, w.v, w.lens, 6)
+    for key, (o, lse) in dense.items():
+        b, i = key
+        t = int(w.lens[b]) - 6 + i
+        if t < 0:
+            continue
+        np.testing.assert_array_equal(res["tok"][key], np.arange(t + 1))
+        np.testing.assert_allclose(res["out"][key], o, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(res["lse"][key], lse, rtol=0, atol=1e-12)
+    # and the dense oracle against torch's causal SDPA
+    b, i = 0, 5
+    t = int(w.lens[b]) - 6 + i
+    q = O.bf16_bits_to_f64(w.q[b, i])
+    k = O.bf16_bits_to_f64(w.k[b, :t + 1])
+    v = O.bf16_bits_to_f64(w.v[b, :t + 1])
+    np.testing.assert_allclose(dense[(b, i)][0], sdpa_ref(q, k, v, 1 / math.sqrt(128)),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_qsa_differs_from_dense_beyond_2052():
+    w = W.make_custom(42, [2053], 1, 8, 1)
+    res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, 1)
+    tok = res["tok"][(0, 0)]
+    assert tok.shape[0] == 2049  # 512 blocks + a one-token tail (t = 2052)
+    assert 2052 in tok
