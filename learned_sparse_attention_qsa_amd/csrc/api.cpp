@@ -1,0 +1,291 @@
+// C ABI of libqsa: argument validation, workspace sizing and kernel dispatch.
+// Every entry point checks what the host can see before it launches anything,
+// returns a status code, and never throws, allocates, frees or synchronises
+// (except the opt-in QSA_CHECK validation of device `lens`).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/qsa.h"
+#include "internal.h"
+
+using qsa::Dims;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+qsa_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return QSA_ERR_DEVICE;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QSA_ERR_DEVICE;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? QSA_OK : QSA_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qsa_status check_shape(const qsa_shape* s, Dims* d) {
+  if (!s) return QSA_ERR_NULL;
+  if (s->batch < 0 || s->n_query < 0 || s->max_len <= 0 || (s->max_len % 4) != 0)
+    return QSA_ERR_SHAPE;
+  if (s->n_query > s->max_len) return QSA_ERR_SHAPE;
+  if (s->q_heads < 1 || s->kv_heads < 1 || (s->q_heads % s->kv_heads) != 0) return QSA_ERR_SHAPE;
+  if (s->q_heads / s->kv_heads > 64) return QSA_ERR_SHAPE;
+  if (s->batch > 65535 || s->n_query > (1 << 24) || s->q_heads > 65535) return QSA_ERR_SHAPE;
+  if ((s->flags & ~3u) != 0 || s->flags == 3u) return QSA_ERR_SHAPE;
+  d->B = s->batch;
+  d->Lmax = s->max_len;
+  d->Nq = s->n_query;
+  d->Hq = s->q_heads;
+  d->Hkv = s->kv_heads;
+  d->scale = s->scale > 0.f ? s->scale : 1.0f / std::sqrt((float)QSA_HEAD_DIM);
+  return QSA_OK;
+}
+
+// Opt-in synchronous validation of the device-side lens array.
+qsa_status check_lens(const Dims& d, const int32_t* lens, hipStream_t stream) {
+  const char* env = std::getenv("QSA_CHECK");
+  if (!env || env[0] != '1' || d.B == 0) return QSA_OK;
+  std::vector<int32_t> h(d.B);
+  if (hipMemcpyAsync(h.data(), lens, sizeof(int32_t) * d.B, hipMemcpyDeviceToHost, stream) !=
+      hipSuccess)
+    return QSA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return QSA_ERR_HIP;
+  for (int b = 0; b < d.B; ++b)
+    if (h[b] < d.Nq || h[b] > d.Lmax) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+size_t forward_ws(const Dims& d, uint32_t flags) {
+  // index_topk and attend run one after the other, so they share the space;
+  // sel / n_sel come first when the caller does not provide them.
+  qsa::Carve c{nullptr, 0};
+  const size_t rows = (size_t)d.B * d.Nq;
+  c.take<int32_t>(rows * QSA_TOPK);
+  c.take<int32_t>(rows);
+  const size_t a = qsa::topk_workspace_bytes(d, qsa::choose_topk_path(d, flags));
+  const size_t b = qsa::attend_workspace_bytes(d);
+  c.take<char>(a > b ? a : b);
+  return c.off;
+}
+
+size_t ws_bytes_for(const Dims& d, uint32_t flags, int32_t op) {
+  switch (op) {
+    case QSA_OP_COMPRESS:
+    case QSA_OP_EXPAND:
+      return 0;
+    case QSA_OP_INDEX_TOPK:
+      return qsa::topk_workspace_bytes(d, qsa::choose_topk_path(d, flags));
+    case QSA_OP_SPARSE_ATTEND:
+      return qsa::attend_workspace_bytes(d);
+    case QSA_OP_FORWARD:
+      return forward_ws(d, flags);
+    case QSA_OP_DENSE_DECODE:
+      return qsa::dense_workspace_bytes(d);
+    default:
+      return 0;
+  }
+}
+
+qsa_status check_ws(const Dims& d, uint32_t flags, int32_t op, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(d, flags, op);
+  if (need == 0) return QSA_OK;
+  if (!ws || ws_bytes < need) return QSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QSA_ERR_ALIGN;
+  return QSA_OK;
+}
+
+qsa_status hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
+
+#define QSA_TRY(expr)            \
+  do {                           \
+    qsa_status st_ = (expr);     \
+    if (st_ != QSA_OK) return st_; \
+  } while (0)
+
+qsa_status need(const void* p) {
+  if (!p) return QSA_ERR_NULL;
+  return aligned16(p) ? QSA_OK : QSA_ERR_ALIGN;
+}
+
+qsa_status need_i32(const void* p) {
+  if (!p) return QSA_ERR_NULL;
+  return (reinterpret_cast<uintptr_t>(p) & 3u) == 0 ? QSA_OK : QSA_ERR_ALIGN;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qsa_workspace_bytes(const qsa_shape* shape, int32_t op) {
+  Dims d;
+  if (check_shape(shape, &d) != QSA_OK) return 0;
+  return ws_bytes_for(d, shape->flags, op);
+}
+
+const char* qsa_status_string(qsa_status status) {
+  switch (status) {
+    case QSA_OK:
+      return "ok";
+    case QSA_ERR_NULL:
+      return "a required pointer is NULL";
+    case QSA_ERR_ALIGN:
+      return "a pointer is not 16-byte aligned";
+    case QSA_ERR_SHAPE:
+      return "unsupported or inconsistent shape";
+    case QSA_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case QSA_ERR_DEVICE:
+      return "current device is not an MI355X (gfx950)";
+    case QSA_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+qsa_status qsa_compress_keys(const qsa_shape* shape, const uint16_t* k_idx, const int32_t* lens,
+                             const int32_t* first_block, uint16_t* k_cmp, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0) return QSA_OK;
+  QSA_TRY(need(k_idx));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(k_cmp));
+  if (first_block) QSA_TRY(need_i32(first_block));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, s));
+}
+
+qsa_status qsa_index_topk(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_cmp,
+                          const int32_t* lens, int32_t* sel, int32_t* n_sel, void* ws,
+                          size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need(q_idx));
+  QSA_TRY(need(k_cmp));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(sel));
+  QSA_TRY(need_i32(n_sel));
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_INDEX_TOPK, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_index_topk(d, qsa::choose_topk_path(d, shape->flags), q_idx, k_cmp,
+                                           lens, sel, n_sel, ws, s));
+}
+
+qsa_status qsa_expand_blocks(const qsa_shape* shape, const int32_t* lens, const int32_t* sel,
+                             const int32_t* n_sel, int32_t* tok, int32_t* n_tok, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(sel));
+  QSA_TRY(need_i32(n_sel));
+  QSA_TRY(need(tok));
+  QSA_TRY(need_i32(n_tok));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_expand(d, lens, sel, n_sel, tok, n_tok, s));
+}
+
+qsa_status qsa_sparse_attend(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* lens, const int32_t* sel,
+                             const int32_t* n_sel, uint16_t* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(sel));
+  QSA_TRY(need_i32(n_sel));
+  QSA_TRY(need(out));
+  if (lse) QSA_TRY(need_i32(lse));
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_SPARSE_ATTEND, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, ws, s));
+}
+
+qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_idx,
+                       uint16_t* k_cmp, const int32_t* first_block, const uint16_t* q,
+                       const uint16_t* k, const uint16_t* v, const int32_t* lens, uint16_t* out,
+                       float* lse, int32_t* sel_out, int32_t* n_sel_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0) return QSA_OK;
+  QSA_TRY(need(q_idx));
+  QSA_TRY(need(k_idx));
+  QSA_TRY(need(k_cmp));
+  if (first_block) QSA_TRY(need_i32(first_block));
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(out));
+  if (lse) QSA_TRY(need_i32(lse));
+  if (sel_out) QSA_TRY(need(sel_out));
+  if (n_sel_out) QSA_TRY(need_i32(n_sel_out));
+  if ((sel_out == nullptr) != (n_sel_out == nullptr)) return QSA_ERR_NULL;
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_FORWARD, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  qsa::Carve c{static_cast<char*>(ws), 0};
+  const size_t rows = (size_t)d.B * d.Nq;
+  int32_t* sel = c.take<int32_t>(rows * QSA_TOPK);
+  int32_t* n_sel = c.take<int32_t>(rows);
+  void* rest = c.take<char>(0);
+  if (sel_out) {
+    sel = sel_out;
+    n_sel = n_sel_out;
+  }
+  QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, s)));
+  if (d.Nq == 0) return QSA_OK;
+  QSA_TRY(hip_status(qsa::launch_index_topk(d, qsa::choose_topk_path(d, shape->flags), q_idx,
+                                            k_cmp, lens, sel, n_sel, rest, s)));
+  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, rest, s));
+}
+
+qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const int32_t* lens, uint16_t* out, float* lse,
+                                void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(out));
+  if (lse) QSA_TRY(need_i32(lse));
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_DENSE_DECODE, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_dense_decode(d, q, k, v, lens, out, lse, ws, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side helpers shared by the QSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kIdxHeads = 4;
+constexpr int kIdxDim = 64;
+constexpr int kBlock = 4;
+constexpr int kTopK = 512;
+constexpr int kHeadDim = 128;
+constexpr int kMaxTok = kTopK * kBlock + kBlock;  // 2052
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// float64 -> bf16 with a single rounding to nearest even.  The double is first
+// narrowed to float with round-to-odd (truncate, then set the last bit when
+// inexact); with 16 spare bits that makes the second rounding exact.
+__device__ __forceinline__ uint32_t f64_to_bf16(double d) {
+  float f = (float)d;
+  double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  if (back != d && !__builtin_isnan(d)) {
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;  // undo rounding away from zero
+    u |= 1u;
+  }
+  return f32_to_bf16(__uint_as_float(u));
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// 64-bit selection key: larger is better.  Score bits (non-negative float, so
+// the unsigned order of the bits is the numeric order) in the high word, the
+// complement of the block id in the low word, so equal scores prefer the
+// lower block id and all keys of one query are distinct.
+__device__ __forceinline__ uint64_t make_key(uint32_t score_bits, uint32_t j) {
+  return ((uint64_t)score_bits << 32) | (uint64_t)(0xffffffffu - j);
+}
+__device__ __forceinline__ uint32_t key_block(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
+
+// Sum over the four indexer heads of max(0, x), with -0 folded to +0 so the
+// bit pattern is canonical.
+__device__ __forceinline__ uint32_t relu_sum_bits(float a, float b, float c, float d) {
+  float s = fmaxf(a, 0.f) + fmaxf(b, 0.f) + fmaxf(c, 0.f) + fmaxf(d, 0.f);
+  return __float_as_uint(s) & 0x7fffffffu;
+}
+
+}  // namespace qsa

@@ -1,0 +1,79 @@
+// Key compression: one micro-block key per four indexer keys.
+//
+// Method: the indexer compresses keys four at a time (page "Qwen's
+// million-token window has a 2,048-token keyhole", section "A million-token
+// window with a selective view").  The operator is not printed; the block key
+// is the sum of its four token keys, formed exactly and rounded once to bf16.
+//
+// HBM-bound streaming pass: each thread owns one 16-byte chunk (8 dims) of
+// one block and reads the four 128-byte rows of that block at that chunk, so
+// a wavefront reads 8 whole blocks (4 KiB) with every load fully coalesced and
+// writes 8 whole compressed rows (1 KiB).  Sums are taken in float64 in row
+// order, which is exact for any bf16 inputs of sane range, and narrowed with
+// one round-to-nearest-even.
+#include "common.h"
+#include "internal.h"
+
+namespace qsa {
+namespace {
+
+__device__ __forceinline__ void acc8(double* s, uint4 w) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[2 * i] += (double)bf16_lo(x[i]);
+    s[2 * i + 1] += (double)bf16_hi(x[i]);
+  }
+}
+
+__global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k_idx,
+                                                       const int32_t* __restrict__ lens,
+                                                       const int32_t* __restrict__ first_block,
+                                                       uint16_t* __restrict__ k_cmp, int Lmax) {
+  const int b = blockIdx.y;
+  const int len = clampi(lens[b], 0, Lmax);
+  const int nb = len >> 2;
+  const int fb = first_block ? clampi(first_block[b], 0, nb) : 0;
+  const size_t nbp = (size_t)(Lmax >> 2);
+  const uint4* src = reinterpret_cast<const uint4*>(k_idx + (size_t)b * Lmax * kIdxDim);
+  uint4* dst = reinterpret_cast<uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
+  const long long end = (long long)nb * 8;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long g = (long long)fb * 8 + (long long)blockIdx.x * blockDim.x + threadIdx.x;
+       g < end; g += stride) {
+    const long long j = g >> 3;
+    const int c = (int)(g & 7);
+    const uint4* rows = src + j * 32 + c;  // row 4j at chunk c; rows are 8 uint4 apart
+    const uint4 r0 = rows[0], r1 = rows[8], r2 = rows[16], r3 = rows[24];
+    double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    acc8(s, r0);
+    acc8(s, r1);
+    acc8(s, r2);
+    acc8(s, r3);
+    uint4 o;
+    o.x = f64_to_bf16(s[0]) | (f64_to_bf16(s[1]) << 16);
+    o.y = f64_to_bf16(s[2]) | (f64_to_bf16(s[3]) << 16);
+    o.z = f64_to_bf16(s[4]) | (f64_to_bf16(s[5]) << 16);
+    o.w = f64_to_bf16(s[6]) | (f64_to_bf16(s[7]) << 16);
+    dst[j * 8 + c] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* lens,
+                           const int32_t* first_block, uint16_t* k_cmp, hipStream_t s) {
+  if (d.B == 0) return hipSuccess;
+  // Grid-stride: enough workgroups to keep HBM busy on a full rebuild, few
+  // enough that an incremental call (one new block per sequence) is cheap.
+  const long long chunks = (long long)(d.Lmax / 4) * 8;
+  long long wg = (chunks + 255) / 256;
+  const long long cap = first_block ? 256 : 2048;
+  if (wg > cap) wg = cap;
+  if (wg < 1) wg = 1;
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)wg, (unsigned)d.B), dim3(256), 0, s, k_idx,
+                     lens, first_block, k_cmp, d.Lmax);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,57 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernel
+// translation units.  Every launcher enqueues on `stream`, never allocates or
+// synchronises, and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct Dims {
+  int B, Lmax, Nq, Hq, Hkv;
+  float scale;
+};
+
+// ---- compress.hip
+hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* lens,
+                           const int32_t* first_block, uint16_t* k_cmp, hipStream_t s);
+
+// ---- expand.hip
+hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
+                         const int32_t* n_sel, int32_t* tok, int32_t* n_tok, hipStream_t s);
+
+// ---- topk.hip
+enum class TopkPath { kTable, kStream };
+TopkPath choose_topk_path(const Dims& d, uint32_t flags);
+size_t topk_workspace_bytes(const Dims& d, TopkPath path);
+hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
+                             const uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
+                             int32_t* n_sel, void* ws, hipStream_t s);
+
+// ---- attend.hip
+size_t attend_workspace_bytes(const Dims& d);
+hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const int32_t* lens, const int32_t* sel,
+                                const int32_t* n_sel, uint16_t* out, float* lse, void* ws,
+                                hipStream_t s);
+size_t dense_workspace_bytes(const Dims& d);
+hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* lens, uint16_t* out,
+                               float* lse, void* ws, hipStream_t s);
+
+// Workspace carving: aligned bump allocation inside the caller's buffer.
+struct Carve {
+  char* base;
+  size_t off;
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+}  // namespace qsa
