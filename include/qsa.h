@@ -105,8 +105,9 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int32_t op);
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* qsa_status_string(qsa_status status);
 
-/* Step 1, key compression ("compresses keys four at a time", section "A
- * million-token window with a selective view").  For every sequence b writes
+/* Step 1, key compression: the indexer folds every four consecutive keys
+ * into one micro-block key (page section "A million-token window with a
+ * selective view").  For every sequence b writes
  *   k_cmp[b][j][:] = bf16( sum_{r<4} k_idx[b][4j+r][:] )
  * for j in [first_block[b], floor(lens[b]/4)): the sum is formed exactly (in
  * float64) and rounded once to nearest-even bf16.  Blocks outside that range
@@ -116,9 +117,10 @@ qsa_status qsa_compress_keys(const qsa_shape* shape, const uint16_t* k_idx,
                              const int32_t* lens, const int32_t* first_block,
                              uint16_t* k_cmp, void* stream);
 
-/* Steps 2 and 3, indexer scoring and top-k ("scores compressed blocks and
- * selects the most relevant regions", "ranks those micro-blocks"; opening
- * section: at most 512 micro-blocks).  For the query at position t with
+/* Steps 2 and 3, indexer scoring and top-k: every query scores the
+ * compressed blocks and keeps the best-ranked ones (section "A million-token
+ * window with a selective view"), at most 512 of them (opening section).
+ * For the query at position t with
  * bt = floor(t/4) the candidates are the completed blocks j < bt, scored
  *   s_j = sum_{h<4} max(0, q_idx[h] . k_cmp[j])
  * (fp32 accumulation: exact for integer-valued inputs whose products and
@@ -132,16 +134,17 @@ qsa_status qsa_index_topk(const qsa_shape* shape, const uint16_t* q_idx,
                           int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
                           void* stream);
 
-/* Step 4, expansion of the kept blocks to token positions ("expands the
- * winners back to token positions"; opening section: plus the unfinished
- * block at the tail).  tok = ascending( {4j..4j+3 : j in sel} U {4bt..t} ),
+/* Step 4, expansion: the kept blocks become the token positions they cover
+ * (section "A million-token window with a selective view"), and the
+ * unfinished tail block is added (opening section).  tok = ascending( {4j..4j+3 : j in sel} U {4bt..t} ),
  * padded with -1 to 2052; n_tok = 4*n_sel + (t mod 4) + 1.  sel must be
  * ascending with every id < bt (as qsa_index_topk writes it). */
 qsa_status qsa_expand_blocks(const qsa_shape* shape, const int32_t* lens,
                              const int32_t* sel, const int32_t* n_sel, int32_t* tok,
                              int32_t* n_tok, void* stream);
 
-/* Step 5, sparse core attention ("applies core attention only there").  The
+/* Step 5, sparse core attention: core attention reads only the expanded
+ * positions (section "A million-token window with a selective view").  The
  * token list of every query is rebuilt from (sel, n_sel) as in
  * qsa_expand_blocks; query head h reads KV head floor(h / (Hq/Hkv)):
  *   out[h] = softmax_s(scale * q[h] . k[s]) V[s],  lse[h] = ln sum_s exp(.)
@@ -169,6 +172,20 @@ qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q,
                                 const uint16_t* k, const uint16_t* v,
                                 const int32_t* lens, uint16_t* out, float* lse,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing hook, for benchmarks and profilers (not part of the method).
+ * qsa_profile_attach hands the library n_events caller-created hipEvent_t
+ * handles (created with timing enabled, owned by the caller).  From then on,
+ * on the calling thread, the i-th kernel the library enqueues is bracketed by
+ * events[2i] (recorded on its stream just before the launch) and events[2i+1]
+ * (just after), until n_events/2 launches have been recorded.
+ * qsa_profile_detach stops recording and returns the number of bracketed
+ * launches; qsa_profile_kernel_name(i) names the i-th one ("" when out of
+ * range; valid until the next attach on this thread).  Recording adds two
+ * event markers per launch and nothing else. */
+qsa_status qsa_profile_attach(void** events, int32_t n_events);
+int32_t qsa_profile_detach(void);
+const char* qsa_profile_kernel_name(int32_t i);
 
 #ifdef __cplusplus
 }

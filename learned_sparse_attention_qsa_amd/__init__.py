@@ -43,6 +43,9 @@ EXPORTS = (
     "qsa_sparse_attend",
     "qsa_forward",
     "qsa_dense_gqa_decode",
+    "qsa_profile_attach",
+    "qsa_profile_detach",
+    "qsa_profile_kernel_name",
 )
 
 
@@ -88,8 +91,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_sparse_attend.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_dense_gqa_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for name in EXPORTS[2:]:
+    for name in EXPORTS[2:8]:
         getattr(lib, name).restype = i32
+    lib.qsa_profile_attach.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.qsa_profile_attach.restype = i32
+    lib.qsa_profile_detach.argtypes = []
+    lib.qsa_profile_detach.restype = i32
+    lib.qsa_profile_kernel_name.argtypes = [i32]
+    lib.qsa_profile_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -277,6 +286,37 @@ def dense_gqa_decode(shp: QsaShape, q, k, v, lens, out=None, lse=None, ws=None,
                                              _p(out), _p(lse), _p(ws), nb, _stream(dev))
     _check(st, "qsa_dense_gqa_decode")
     return out, lse
+
+
+class KernelTimer:
+    """Brackets every kernel the library launches on this thread with HIP
+    events (qsa_profile_attach), for benchmarks.  Use as a context manager;
+    afterwards `records()` lists (kernel name, milliseconds) in launch order."""
+
+    def __init__(self, max_launches: int = 512):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+        for e in self.events:  # materialise the HIP events
+            e.record()
+        torch.cuda.synchronize()
+        self._handles = (ctypes.c_void_p * len(self.events))(
+            *[ctypes.c_void_p(e.cuda_event) for e in self.events])
+        self._names = []
+
+    def __enter__(self):
+        _check(load_library().qsa_profile_attach(self._handles, len(self.events)),
+               "qsa_profile_attach")
+        return self
+
+    def __exit__(self, *exc):
+        lib = load_library()
+        n = lib.qsa_profile_detach()
+        self._names = [lib.qsa_profile_kernel_name(i).decode() for i in range(n)]
+        return False
+
+    def records(self):
+        torch.cuda.synchronize()
+        return [(name, self.events[2 * i].elapsed_time(self.events[2 * i + 1]))
+                for i, name in enumerate(self._names)]
 
 
 def default_scale() -> float:

@@ -15,6 +15,32 @@
 
 using qsa::Dims;
 
+// ---------------------------------------------------------------- profiling
+namespace {
+constexpr int kMaxProfiled = 1024;
+thread_local void** t_events = nullptr;
+thread_local int t_cap = 0;
+thread_local int t_count = 0;
+thread_local bool t_open = false;
+thread_local const char* t_names[kMaxProfiled];
+}  // namespace
+
+namespace qsa {
+void profile_before(hipStream_t s, const char* name) {
+  t_open = false;
+  if (!t_events || t_count >= kMaxProfiled || 2 * t_count + 1 >= t_cap) return;
+  if (hipEventRecord(static_cast<hipEvent_t>(t_events[2 * t_count]), s) != hipSuccess) return;
+  t_names[t_count] = name;
+  t_open = true;
+}
+void profile_after(hipStream_t s) {
+  if (!t_open) return;
+  t_open = false;
+  if (hipEventRecord(static_cast<hipEvent_t>(t_events[2 * t_count + 1]), s) == hipSuccess)
+    ++t_count;
+}
+}  // namespace qsa
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -128,6 +154,27 @@ qsa_status need_i32(const void* p) {
 }  // namespace
 
 extern "C" {
+
+qsa_status qsa_profile_attach(void** events, int32_t n_events) {
+  if (!events || n_events < 2) return QSA_ERR_NULL;
+  t_events = events;
+  t_cap = n_events;
+  t_count = 0;
+  t_open = false;
+  return QSA_OK;
+}
+
+int32_t qsa_profile_detach(void) {
+  const int n = t_count;
+  t_events = nullptr;
+  t_cap = 0;
+  return n;
+}
+
+const char* qsa_profile_kernel_name(int32_t i) {
+  if (i < 0 || i >= t_count || i >= kMaxProfiled) return "";
+  return t_names[i];
+}
 
 size_t qsa_workspace_bytes(const qsa_shape* shape, int32_t op) {
   Dims d;

@@ -415,10 +415,10 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
     a.part_o = c.take<float>(rh * a.n_split * kHeadDim);
     a.part_lse = c.take<float>(rh * a.n_split);
   }
-  hipLaunchKernelGGL(sparse_attend_kernel, dim3((unsigned)a.n_split, (unsigned)d.Nq, (unsigned)d.B),
+  QSA_LAUNCH(sparse_attend_kernel, dim3((unsigned)a.n_split, (unsigned)d.Nq, (unsigned)d.B),
                      dim3(256), 0, s, a);
   if (a.n_split > 1)
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128),
+    QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128),
                        0, s, a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
   return hipGetLastError();
 }
@@ -457,10 +457,10 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
   a.part_o = c.take<float>(rh * a.n_split * kHeadDim);
   a.part_lse = c.take<float>(rh * a.n_split);
   const int cchunks = (d.Nq * a.G + 15) / 16;
-  hipLaunchKernelGGL(dense_decode_kernel,
+  QSA_LAUNCH(dense_decode_kernel,
                      dim3((unsigned)a.n_split, (unsigned)(d.Hkv * cchunks), (unsigned)d.B), dim3(64),
                      0, s, a);
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0,
+  QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0,
                      s, a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
   return hipGetLastError();
 }

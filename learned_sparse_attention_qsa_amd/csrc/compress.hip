@@ -71,7 +71,7 @@ hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* 
   const long long cap = first_block ? 256 : 2048;
   if (wg > cap) wg = cap;
   if (wg < 1) wg = 1;
-  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)wg, (unsigned)d.B), dim3(256), 0, s, k_idx,
+  QSA_LAUNCH(compress_kernel, dim3((unsigned)wg, (unsigned)d.B), dim3(256), 0, s, k_idx,
                      lens, first_block, k_cmp, d.Lmax);
   return hipGetLastError();
 }

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(128) void expand_kernel(const int32_t* __restrict__
 hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
                          const int32_t* n_sel, int32_t* tok, int32_t* n_tok, hipStream_t s) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s, lens,
+  QSA_LAUNCH(expand_kernel, dim3((unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s, lens,
                      sel, n_sel, tok, n_tok, d.Lmax, d.Nq);
   return hipGetLastError();
 }

@@ -41,6 +41,11 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
                                const uint16_t* v, const int32_t* lens, uint16_t* out,
                                float* lse, void* ws, hipStream_t s);
 
+// Profiling hook: when a caller has attached HIP events (qsa_profile_attach),
+// every launch records one event before and one after itself on its stream.
+void profile_before(hipStream_t s, const char* name);
+void profile_after(hipStream_t s);
+
 // Workspace carving: aligned bump allocation inside the caller's buffer.
 struct Carve {
   char* base;
@@ -55,3 +60,10 @@ struct Carve {
 };
 
 }  // namespace qsa
+
+#define QSA_LAUNCH(kernel, grid, block, shmem, stream, ...)                  \
+  do {                                                                       \
+    ::qsa::profile_before((stream), #kernel);                                \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);     \
+    ::qsa::profile_after((stream));                                          \
+  } while (0)

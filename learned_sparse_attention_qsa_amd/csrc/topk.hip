@@ -704,26 +704,26 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   if (path == TopkPath::kTable) {
     TableWs w = carve_table(d, ws, nullptr);
     const size_t nz = rows * kHistBins + rows;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 4096)),
+    QSA_LAUNCH(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 4096)),
                        dim3(256), 0, s, w.ghist, nz, 0u);
     const unsigned slices = (unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice);
     const dim3 grid(slices, (unsigned)((d.Nq + 3) / 4), (unsigned)d.B);
-    hipLaunchKernelGGL(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores,
+    QSA_LAUNCH(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores,
                        w.ghist, d.Lmax, d.Nq);
-    hipLaunchKernelGGL(table_filter_kernel, grid, dim3(256), 0, s, w.scores, w.ghist, lens,
+    QSA_LAUNCH(table_filter_kernel, grid, dim3(256), 0, s, w.scores, w.ghist, lens,
                        w.cand, w.cand_cnt, d.Lmax, d.Nq, kSelCap);
-    hipLaunchKernelGGL(select_kernel, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, lens, sel,
+    QSA_LAUNCH(select_kernel, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, lens, sel,
                        n_sel, w.overflow, d.Lmax, d.Nq, kSelCap);
-    hipLaunchKernelGGL(select_fallback_kernel<false>, grid_q, dim3(256), 0, s, w.scores, q_idx,
+    QSA_LAUNCH(select_fallback_kernel<false>, grid_q, dim3(256), 0, s, w.scores, q_idx,
                        k_cmp, lens, w.overflow, sel, n_sel, d.Lmax, d.Nq);
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
-    hipLaunchKernelGGL(score_stream_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.lists,
+    QSA_LAUNCH(score_stream_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.lists,
                        w.cnt, d.Lmax, d.Nq);
-    hipLaunchKernelGGL(select_kernel, grid_q, dim3(256), 0, s, w.lists, w.cnt, lens, sel, n_sel,
+    QSA_LAUNCH(select_kernel, grid_q, dim3(256), 0, s, w.lists, w.cnt, lens, sel, n_sel,
                        w.overflow, d.Lmax, d.Nq, kListCap);
-    hipLaunchKernelGGL(select_fallback_kernel<true>, grid_q, dim3(256), 0, s, nullptr, q_idx,
+    QSA_LAUNCH(select_fallback_kernel<true>, grid_q, dim3(256), 0, s, nullptr, q_idx,
                        k_cmp, lens, w.overflow, sel, n_sel, d.Lmax, d.Nq);
   }
   return hipGetLastError();

@@ -88,9 +88,10 @@ def f64_to_bf16_bits(x) -> np.ndarray:
 def compress_keys(k_idx_bits: np.ndarray, n_tokens: int, first_block: int = 0) -> np.ndarray:
     """Compressed indexer keys of blocks first_block .. floor(n_tokens/4) - 1.
 
-    The indexer "compresses keys four at a time" (section "A million-token
-    window with a selective view").  Reading: the micro-block key is the sum of
-    its four token keys, formed exactly and rounded once to bf16.
+    The indexer folds each run of four keys into one micro-block key (section
+    "A million-token window with a selective view").  Reading: the micro-block
+    key is the sum of its four token keys, formed exactly and rounded once to
+    bf16.
     Returns uint16 bf16 bits, shape [n_blocks - first_block][64].
     """
     n_blocks = n_tokens // BLOCK
@@ -138,9 +139,9 @@ def select_blocks(scores: np.ndarray, k: int = TOPK) -> np.ndarray:
 def expand_tokens(sel: np.ndarray, t: int) -> np.ndarray:
     """Token positions attended by the query at position t.
 
-    The winners are expanded "back to token positions", and the unfinished
-    block at the tail is added (opening section and section "A million-token
-    window with a selective view").  Reading: the tail is the query's own
+    The kept blocks are turned back into the token positions they cover, and
+    the unfinished block at the tail is added (opening section and section "A
+    million-token window with a selective view").  Reading: the tail is the query's own
     block, tokens 4*floor(t/4) .. t, which holds 1 to 4 tokens.
     """
     bt = t // BLOCK

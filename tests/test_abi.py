@@ -21,7 +21,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = Q.load_library()
     declared = header_symbols()
-    assert len(declared) == 8
+    assert len(declared) == 11
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
