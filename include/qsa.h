@@ -81,7 +81,7 @@ enum {
 
 typedef struct {
   int32_t batch;     /* B >= 0 */
-  int32_t max_len;   /* Lmax: cache capacity in tokens, > 0, multiple of 4 */
+  int32_t max_len;   /* Lmax: cache capacity in tokens, > 0, multiple of 4, <= 2^30 */
   int32_t n_query;   /* Nq >= 0 query positions per sequence, <= max_len */
   int32_t q_heads;   /* Hq: core query heads, >= 1 */
   int32_t kv_heads;  /* Hkv: core KV heads, >= 1, divides Hq, Hq/Hkv <= 64 */

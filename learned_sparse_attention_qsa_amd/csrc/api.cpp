@@ -66,7 +66,7 @@ qsa_status check_shape(const qsa_shape* s, Dims* d) {
   if (!s) return QSA_ERR_NULL;
   if (s->batch < 0 || s->n_query < 0 || s->max_len <= 0 || (s->max_len % 4) != 0)
     return QSA_ERR_SHAPE;
-  if (s->n_query > s->max_len) return QSA_ERR_SHAPE;
+  if (s->n_query > s->max_len || s->max_len > (1 << 30)) return QSA_ERR_SHAPE;
   if (s->q_heads < 1 || s->kv_heads < 1 || (s->q_heads % s->kv_heads) != 0) return QSA_ERR_SHAPE;
   if (s->q_heads / s->kv_heads > 64) return QSA_ERR_SHAPE;
   if (s->batch > 65535 || s->n_query > (1 << 24) || s->q_heads > 65535) return QSA_ERR_SHAPE;
@@ -94,16 +94,48 @@ qsa_status check_lens(const Dims& d, const int32_t* lens, hipStream_t stream) {
   return QSA_OK;
 }
 
-size_t forward_ws(const Dims& d, uint32_t flags) {
-  // index_topk and attend run one after the other, so they share the space;
-  // sel / n_sel come first when the caller does not provide them.
-  qsa::Carve c{nullptr, 0};
+// Workspace of qsa_sparse_attend: split counters, then partial outputs.
+struct AttendPtrs {
+  uint32_t* counters;
+  float* part_o;
+  float* part_lse;
+};
+size_t carve_attend_partials(const Dims& d, char* base, AttendPtrs* p) {
+  qsa::Carve c{base, 0};
+  const qsa::AttendLayout l = qsa::attend_layout(d);
+  p->part_o = l.partial_floats ? c.take<float>(l.partial_floats) : nullptr;
+  p->part_lse = l.lse_floats ? c.take<float>(l.lse_floats) : nullptr;
+  return c.off;
+}
+size_t carve_attend(const Dims& d, void* ws, AttendPtrs* p) {
+  qsa::Carve c{static_cast<char*>(ws), 0};
+  const qsa::AttendLayout l = qsa::attend_layout(d);
+  p->counters = l.counters ? c.take<uint32_t>(l.counters) : nullptr;
+  char* rest = c.take<char>(0);
+  c.off += carve_attend_partials(d, rest, p);
+  return c.off;
+}
+
+// Workspace of qsa_forward: selection, split counters, then one region shared
+// by the top-k engine and (afterwards) the attention partials.
+struct ForwardPtrs {
+  int32_t* sel;
+  int32_t* n_sel;
+  AttendPtrs att;
+  void* shared;
+};
+size_t carve_forward(const Dims& d, uint32_t flags, void* ws, ForwardPtrs* p) {
+  qsa::Carve c{static_cast<char*>(ws), 0};
   const size_t rows = (size_t)d.B * d.Nq;
-  c.take<int32_t>(rows * QSA_TOPK);
-  c.take<int32_t>(rows);
+  p->sel = c.take<int32_t>(rows * QSA_TOPK);
+  p->n_sel = c.take<int32_t>(rows);
+  const qsa::AttendLayout l = qsa::attend_layout(d);
+  p->att.counters = l.counters ? c.take<uint32_t>(l.counters) : nullptr;
+  char* shared = c.take<char>(0);
+  p->shared = shared;
   const size_t a = qsa::topk_workspace_bytes(d, qsa::choose_topk_path(d, flags));
-  const size_t b = qsa::attend_workspace_bytes(d);
-  c.take<char>(a > b ? a : b);
+  const size_t b = carve_attend_partials(d, shared, &p->att);
+  c.off += a > b ? a : b;
   return c.off;
 }
 
@@ -114,10 +146,14 @@ size_t ws_bytes_for(const Dims& d, uint32_t flags, int32_t op) {
       return 0;
     case QSA_OP_INDEX_TOPK:
       return qsa::topk_workspace_bytes(d, qsa::choose_topk_path(d, flags));
-    case QSA_OP_SPARSE_ATTEND:
-      return qsa::attend_workspace_bytes(d);
-    case QSA_OP_FORWARD:
-      return forward_ws(d, flags);
+    case QSA_OP_SPARSE_ATTEND: {
+      AttendPtrs p;
+      return qsa::attend_layout(d).counters ? carve_attend(d, nullptr, &p) : 0;
+    }
+    case QSA_OP_FORWARD: {
+      ForwardPtrs p;
+      return carve_forward(d, flags, nullptr, &p);
+    }
     case QSA_OP_DENSE_DECODE:
       return qsa::dense_workspace_bytes(d);
     default:
@@ -215,7 +251,8 @@ qsa_status qsa_compress_keys(const qsa_shape* shape, const uint16_t* k_idx, cons
   QSA_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
-  return hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, s));
+  return hip_status(
+      qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, {nullptr, 0}, {nullptr, 0}, s));
 }
 
 qsa_status qsa_index_topk(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_cmp,
@@ -234,7 +271,7 @@ qsa_status qsa_index_topk(const qsa_shape* shape, const uint16_t* q_idx, const u
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
   return hip_status(qsa::launch_index_topk(d, qsa::choose_topk_path(d, shape->flags), q_idx, k_cmp,
-                                           lens, sel, n_sel, ws, s));
+                                           lens, sel, n_sel, ws, false, s));
 }
 
 qsa_status qsa_expand_blocks(const qsa_shape* shape, const int32_t* lens, const int32_t* sel,
@@ -272,7 +309,10 @@ qsa_status qsa_sparse_attend(const qsa_shape* shape, const uint16_t* q, const ui
   QSA_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
-  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, ws, s));
+  AttendPtrs p;
+  carve_attend(d, ws, &p);
+  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.part_o,
+                                              p.part_lse, p.counters, false, s));
 }
 
 qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_idx,
@@ -300,20 +340,22 @@ qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint
   QSA_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
-  qsa::Carve c{static_cast<char*>(ws), 0};
-  const size_t rows = (size_t)d.B * d.Nq;
-  int32_t* sel = c.take<int32_t>(rows * QSA_TOPK);
-  int32_t* n_sel = c.take<int32_t>(rows);
-  void* rest = c.take<char>(0);
-  if (sel_out) {
-    sel = sel_out;
-    n_sel = n_sel_out;
+  ForwardPtrs p;
+  carve_forward(d, shape->flags, ws, &p);
+  int32_t* sel = sel_out ? sel_out : p.sel;
+  int32_t* n_sel = sel_out ? n_sel_out : p.n_sel;
+  const qsa::TopkPath path = qsa::choose_topk_path(d, shape->flags);
+  qsa::ZeroRange z0{nullptr, 0}, z1{nullptr, 0};
+  if (d.Nq > 0) {
+    qsa::topk_zero_range(d, path, p.shared, &z0.p, &z0.n);
+    if (p.att.counters) z1 = {p.att.counters, qsa::attend_layout(d).counters};
   }
-  QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, s)));
+  QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, z0, z1, s)));
   if (d.Nq == 0) return QSA_OK;
-  QSA_TRY(hip_status(qsa::launch_index_topk(d, qsa::choose_topk_path(d, shape->flags), q_idx,
-                                            k_cmp, lens, sel, n_sel, rest, s)));
-  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, rest, s));
+  QSA_TRY(hip_status(
+      qsa::launch_index_topk(d, path, q_idx, k_cmp, lens, sel, n_sel, p.shared, z0.p != nullptr, s)));
+  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.att.part_o,
+                                              p.att.part_lse, p.att.counters, true, s));
 }
 
 qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -61,6 +61,7 @@ struct AttnArgs {
   float* lse;
   float* part_o;    // [rows][Hq][n_split][128] when n_split > 1
   float* part_lse;  // [rows][Hq][n_split]
+  uint32_t* counters;  // [rows] split arrival counters (sparse, n_split > 1)
   int B, Lmax, Nq, Hq, Hkv, G;
   float scale_log2;
   int split_tokens, n_split;
@@ -121,16 +122,52 @@ __device__ __forceinline__ void softmax_pv(Run& r, float* z, const uint16_t* vt)
   }
 }
 
-// Stage the V rows of 32 tokens into LDS: lane -> token lane/2, half lane&1.
-__device__ __forceinline__ void stage_v(uint16_t* vt, const uint16_t* vrow, bool valid) {
+// A 32-token tile of one KV head, in registers: the K fragments of the two
+// 16-token halves (MFMA A-operand layout: lane -> token lane&15, 16 bytes at
+// dims ks*32 + (lane>>4)*8) and the V rows (lane -> token lane/2, half lane&1).
+struct KVTile {
+  uint4 k[2][4];
+  uint4 v[8];
+};
+
+// kv_row(kk) returns the element offset of token-list entry kk's row for this
+// KV head, or -1 when kk is past the end of the range.
+template <typename RowOf>
+__device__ __forceinline__ void load_tile(KVTile& t, const uint16_t* kbase, const uint16_t* vbase,
+                                          int k0, RowOf row_of) {
   const int lane = lane_id();
-  const uint4* src = reinterpret_cast<const uint4*>(vrow) + (lane & 1) * 8;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const long long off = row_of(k0 + s * 16 + (lane & 15));
+    const uint4* kp = reinterpret_cast<const uint4*>(kbase + (off < 0 ? 0 : off));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) t.k[s][ks] = off >= 0 ? kp[ks * 4 + (lane >> 4)] : zero_u4();
+  }
+  const long long off = row_of(k0 + (lane >> 1));
+  const uint4* vp = reinterpret_cast<const uint4*>(vbase + (off < 0 ? 0 : off)) + (lane & 1) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t.v[i] = off >= 0 ? vp[i] : zero_u4();
+}
+
+__device__ __forceinline__ void stash_v(uint16_t* vt, const KVTile& t) {
+  const int lane = lane_id();
   uint4* dst = reinterpret_cast<uint4*>(vt + (lane >> 1) * kVStride + (lane & 1) * 64);
-  uint4 buf[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) buf[i] = valid ? src[i] : zero_u4();
+  for (int i = 0; i < 8; ++i) dst[i] = t.v[i];
+}
+
+// Logits of this lane's 8 tokens (two 16-token halves x 4 rows of the MFMA
+// output), already scaled to the exp2 domain.
+__device__ __forceinline__ void qk_logits(const KVTile& t, const bf16x8* qf, float scale_log2,
+                                          float* z) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = buf[i];
+  for (int s = 0; s < 2; ++s) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma16(as_bf16x8(t.k[s][ks]), qf[ks], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[s * 4 + i] = acc[i] * scale_log2;
+  }
 }
 
 // Final per-column reduction and store.  Column c = lane & 15.
@@ -164,13 +201,23 @@ __device__ __forceinline__ void finish(const Run& r, bool col_valid, uint16_t* o
 }
 
 // ------------------------------------------------------------------ sparse
-// Grid (n_split, Nq, B); 4 wavefronts; wavefront w takes work items
-// w, w+4, ... where item = (kv head, chunk of 16 query heads).
+// Grid (Nq * Hkv * hchunks, n_split, B): one workgroup per (query row, KV
+// head g, chunk of <= 16 query heads of g's group, token split).  Its four
+// wavefronts take interleaved 32-token tiles of the split (tile i goes to
+// wavefront i mod 4), each with its own online softmax, and are merged in
+// LDS.  With one split the result is final; otherwise the workgroup writes a
+// partial (o, lse) and the last of the n_split workgroups of its unit
+// (per-unit arrival counter) merges them and resets the counter to zero.
 __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   __shared__ int32_t s_sel[kTopK];
-  __shared__ __align__(16) uint16_t s_v[4][kTile * kVStride];
-  const int split = blockIdx.x, q = blockIdx.y, b = blockIdx.z;
+  __shared__ __align__(16) uint16_t s_v[4][kTile * kVStride];  // V tiles; then merge scratch
+  __shared__ float s_m[4][16], s_l[4][16], s_f[4][16], s_inv[16];
+  __shared__ int s_last;
+  const int unit = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int hchunks = (a.G + 15) >> 4;
+  const int q = unit / (a.Hkv * hchunks);
+  const int g = (unit / hchunks) % a.Hkv, hc = unit % hchunks;
   const size_t row = (size_t)b * a.Nq + q;
   const int len = clampi(a.lens[b], 0, a.Lmax);
   const int t = len - a.Nq + q;
@@ -185,72 +232,135 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   __syncthreads();
   const int k_begin = split * a.split_tokens;
   const int k_end = min(ntok, k_begin + a.split_tokens);
-  const int hchunks = (a.G + 15) >> 4;
-  const int items = a.Hkv * hchunks;
-  uint16_t* vt = s_v[wave];
-  auto tok_at = [&](int kk) -> int {
-    return kk < 4 * ns ? 4 * s_sel[kk >> 2] + (kk & 3) : 4 * bt + (kk - 4 * ns);
-  };
+  const int h0 = g * a.G + hc * 16;
+  const int nh = min(16, a.G - hc * 16);
+  const int col = lane & 15;
   const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
-  for (int item = wave; item < items; item += 4) {
-    const int g = item / hchunks, hc = item % hchunks;
-    const int h0 = g * a.G + hc * 16;
-    const int nh = min(16, a.G - hc * 16);
-    const int col = lane & 15;
-    bf16x8 qf[4];
-    {
-      const uint4* qp = reinterpret_cast<const uint4*>(a.q + (row * a.Hq + h0 + min(col, nh - 1)) * kHeadDim);
+  bf16x8 qf[4];
+  {
+    const uint4* qp =
+        reinterpret_cast<const uint4*>(a.q + (row * a.Hq + h0 + min(col, nh - 1)) * kHeadDim);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(col < nh ? qp[ks * 4 + (lane >> 4)] : zero_u4());
-    }
-    Run r;
-    run_init(r);
-    for (int k0 = k_begin; k0 < k_end; k0 += kTile) {
-      uint4 kf[2][4];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kk = k0 + s * 16 + (lane & 15);
-        const bool valid = kk < k_end;
-        const uint4* kp = reinterpret_cast<const uint4*>(
-            a.k + ((kv_seq + (size_t)(valid ? tok_at(kk) : 0) * a.Hkv) + g) * kHeadDim);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[s][ks] = valid ? kp[ks * 4 + (lane >> 4)] : zero_u4();
-      }
-      {
-        const int kk = k0 + (lane >> 1);
-        const bool valid = kk < k_end;
-        stage_v(vt, a.v + ((kv_seq + (size_t)(valid ? tok_at(kk) : 0) * a.Hkv) + g) * kHeadDim,
-                valid);
-      }
-      float z[8];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16(as_bf16x8(kf[s][ks]), qf[ks], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = k0 + s * 16 + (lane >> 4) * 4 + i;
-          z[s * 4 + i] = kk < k_end ? acc[i] * a.scale_log2 : kNegInf;
-        }
-      }
-      wave_sync_lds();
-      softmax_pv(r, z, vt);
-      wave_sync_lds();
-    }
-    const int h = h0 + col;
-    const bool partial = a.n_split > 1;
-    float* po = partial ? a.part_o + (((row * a.Hq) + h) * a.n_split + split) * kHeadDim : nullptr;
-    float* pl = partial ? a.part_lse + ((row * a.Hq) + h) * a.n_split + split : nullptr;
-    finish(r, col < nh, a.out + (row * a.Hq + h) * kHeadDim, a.lse ? a.lse + row * a.Hq + h : nullptr,
-           po, pl, partial);
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(col < nh ? qp[ks * 4 + (lane >> 4)] : zero_u4());
   }
+  const uint16_t* kbase = a.k + g * kHeadDim;
+  const uint16_t* vbase = a.v + g * kHeadDim;
+  auto row_of = [&](int kk) -> long long {
+    if (kk >= k_end) return -1;
+    const int tok = kk < 4 * ns ? 4 * s_sel[kk >> 2] + (kk & 3) : 4 * bt + (kk - 4 * ns);
+    return (long long)(kv_seq + (size_t)tok * a.Hkv) * kHeadDim;
+  };
+  uint16_t* vt = s_v[wave];
+  Run r;
+  run_init(r);
+  KVTile cur, nxt;
+  const int first = k_begin + wave * kTile;
+  if (first < k_end) load_tile(cur, kbase, vbase, first, row_of);
+  for (int k0 = first; k0 < k_end; k0 += 4 * kTile) {
+    stash_v(vt, cur);
+    if (k0 + 4 * kTile < k_end) load_tile(nxt, kbase, vbase, k0 + 4 * kTile, row_of);
+    float z[8];
+    qk_logits(cur, qf, a.scale_log2, z);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + s * 16 + (lane >> 4) * 4 + i >= k_end) z[s * 4 + i] = kNegInf;
+    wave_sync_lds();
+    softmax_pv(r, z, vt);
+    wave_sync_lds();
+    cur = nxt;
+  }
+  // ---- merge the four wavefronts (LDS)
+  float l = r.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  __syncthreads();  // every wavefront is done with its V tile: reuse s_v
+  float* O = reinterpret_cast<float*>(&s_v[0][0]);  // [4][16][128]
+  {
+    const int gq = lane >> 4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(O + (wave * 16 + col) * kHeadDim + dt * 16 + gq * 4) =
+          make_float4(r.o[dt][0], r.o[dt][1], r.o[dt][2], r.o[dt][3]);
+    if (lane < 16) {
+      s_m[wave][lane] = r.m;
+      s_l[wave][lane] = l;
+    }
+  }
+  __syncthreads();
+  const bool partial = a.n_split > 1;
+  if (tid < 16) {
+    float M = kNegInf;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][tid]);
+    float L = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = (M == kNegInf || s_m[w][tid] == kNegInf) ? 0.f : exp2f(s_m[w][tid] - M);
+      s_f[w][tid] = f;
+      L += f * s_l[w][tid];
+    }
+    s_inv[tid] = L > 0.f ? 1.f / L : 0.f;
+    const float lse_v = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    if (tid < nh) {
+      const size_t rh = row * a.Hq + h0 + tid;
+      if (partial)
+        a.part_lse[rh * a.n_split + split] = lse_v;
+      else if (a.lse)
+        a.lse[rh] = lse_v;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * kHeadDim; i += blockDim.x) {
+    const int c = i >> 7, d = i & 127;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o += s_f[w][c] * O[(w * 16 + c) * kHeadDim + d];
+    o *= s_inv[c];
+    const size_t rh = row * a.Hq + h0 + c;
+    if (partial)
+      a.part_o[(rh * a.n_split + split) * kHeadDim + d] = o;
+    else
+      a.out[rh * kHeadDim + d] = (uint16_t)f32_to_bf16(o);
+  }
+  if (!partial) return;
+  // ---- merge the splits of this unit (last workgroup to arrive)
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[(size_t)b * (a.Nq * a.Hkv * hchunks) + unit], 1u) ==
+                         (unsigned)(a.n_split - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int nsp = a.n_split;
+  if (tid < nh) {
+    const float* pl = a.part_lse + (row * a.Hq + h0 + tid) * nsp;
+    float M = kNegInf;
+    for (int s2 = 0; s2 < nsp; ++s2) M = fmaxf(M, pl[s2]);
+    float sw = 0.f;
+    for (int s2 = 0; s2 < nsp; ++s2) sw += M == kNegInf ? 0.f : __expf(pl[s2] - M);
+    s_m[0][tid] = M;
+    s_inv[tid] = sw > 0.f ? 1.f / sw : 0.f;
+    if (a.lse) a.lse[row * a.Hq + h0 + tid] = sw > 0.f ? M + __logf(sw) : kNegInf;
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * kHeadDim; i += blockDim.x) {
+    const int c = i >> 7, d = i & 127;
+    const size_t rh = row * a.Hq + h0 + c;
+    const float* pl = a.part_lse + rh * nsp;
+    const float* po = a.part_o + rh * nsp * kHeadDim + d;
+    const float M = s_m[0][c];
+    float o = 0.f;
+    for (int s2 = 0; s2 < nsp; ++s2)
+      o += (M == kNegInf ? 0.f : __expf(pl[s2] - M)) * po[(size_t)s2 * kHeadDim];
+    a.out[rh * kHeadDim + d] = (uint16_t)f32_to_bf16(o * s_inv[c]);
+  }
+  if (tid == 0) a.counters[(size_t)b * (a.Nq * a.Hkv * hchunks) + unit] = 0u;
 }
 
 // ------------------------------------------------------------------ dense
 // Grid (n_split, Hkv * ceil(Nq*G/16), B); one wavefront per workgroup, 16
 // (query, head) columns, all tokens 0..len-1 of the split range, causal mask
-// per column.  Always writes partials.
+// per column.  Always writes partials (merged by merge_kernel).
 __global__ __launch_bounds__(64) void dense_decode_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t s_v[kTile * kVStride];
   const int split = blockIdx.x, b = blockIdx.z;
@@ -278,43 +388,41 @@ __global__ __launch_bounds__(64) void dense_decode_kernel(AttnArgs a) {
   const int k_begin = split * a.split_tokens;
   const int k_end = min(t_hi + 1, k_begin + a.split_tokens);
   const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
+  const uint16_t* kbase = a.k + g * kHeadDim;
+  const uint16_t* vbase = a.v + g * kHeadDim;
+  auto row_of = [&](int kk) -> long long {
+    return kk < k_end ? (long long)(kv_seq + (size_t)kk * a.Hkv) * kHeadDim : -1;
+  };
   Run r;
   run_init(r);
+  KVTile cur, nxt;
+  if (k_begin < k_end) load_tile(cur, kbase, vbase, k_begin, row_of);
   for (int k0 = k_begin; k0 < k_end; k0 += kTile) {
-    uint4 kf[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kk = k0 + s * 16 + (lane & 15);
-      const bool valid = kk < k_end;
-      const uint4* kp = reinterpret_cast<const uint4*>(
-          a.k + ((kv_seq + (size_t)(valid ? kk : 0) * a.Hkv) + g) * kHeadDim);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[s][ks] = valid ? kp[ks * 4 + (lane >> 4)] : zero_u4();
-    }
-    {
-      const int kk = k0 + (lane >> 1);
-      const bool valid = kk < k_end;
-      stage_v(s_v, a.v + ((kv_seq + (size_t)(valid ? kk : 0) * a.Hkv) + g) * kHeadDim, valid);
-    }
+    stash_v(s_v, cur);
+    if (k0 + kTile < k_end) load_tile(nxt, kbase, vbase, k0 + kTile, row_of);
     float z[8];
+    qk_logits(cur, qf, a.scale_log2, z);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma16(as_bf16x8(kf[s][ks]), qf[ks], acc);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kk = k0 + s * 16 + (lane >> 4) * 4 + i;
-        z[s * 4 + i] = (kk < k_end && kk <= tq) ? acc[i] * a.scale_log2 : kNegInf;
+        if (kk >= k_end || kk > tq) z[s * 4 + i] = kNegInf;
       }
-    }
     wave_sync_lds();
     softmax_pv(r, z, s_v);
     wave_sync_lds();
+    cur = nxt;
   }
   float* po = a.part_o + (((row * a.Hq) + h) * a.n_split + split) * kHeadDim;
   float* pl = a.part_lse + ((row * a.Hq) + h) * a.n_split + split;
   finish(r, col_valid, nullptr, nullptr, po, pl, true);
+}
+
+__global__ void fill_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
 }
 
 // ------------------------------------------------------------------ merge
@@ -343,15 +451,19 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   if (lse && d == 0) lse[rh] = sw > 0.f ? M + __logf(sw) : kNegInf;
 }
 
+int sparse_units(const Dims& d) {
+  const int G = d.Hq / d.Hkv;
+  return d.Nq * d.Hkv * ((G + 15) / 16);
+}
+
 int sparse_splits(const Dims& d, int* split_tokens) {
-  // Enough workgroups to cover the chip for decode-sized batches; one split
-  // (no merge) when there are already many query rows.
-  const long long rows = (long long)d.B * d.Nq;
+  // About 256 workgroups or more; split a query's tokens only when the batch
+  // of (query, KV head) units is too small to cover the chip.
+  const long long units = (long long)d.B * sparse_units(d);
   int n_split = 1;
-  if (rows < 1024) {
-    n_split = (int)((1024 + rows - 1) / rows);
-    const int max_split = (kMaxTok + kTile - 1) / kTile;
-    if (n_split > max_split) n_split = max_split;
+  if (units < 256) {
+    n_split = (int)((256 + units - 1) / units);
+    if (n_split > 16) n_split = 16;
   }
   int st = (kMaxTok + n_split - 1) / n_split;
   st = (st + kTile - 1) / kTile * kTile;
@@ -376,20 +488,23 @@ int dense_splits(const Dims& d, int* split_tokens) {
 
 }  // namespace
 
-size_t attend_workspace_bytes(const Dims& d) {
+AttendLayout attend_layout(const Dims& d) {
+  AttendLayout l{};
   int st;
   const int ns = sparse_splits(d, &st);
-  if (ns <= 1) return 0;
-  Carve c{nullptr, 0};
-  const size_t rh = (size_t)d.B * d.Nq * d.Hq;
-  c.take<float>(rh * ns * kHeadDim);
-  c.take<float>(rh * ns);
-  return c.off;
+  if (ns > 1) {
+    const size_t rh = (size_t)d.B * d.Nq * d.Hq;
+    l.partial_floats = rh * ns * kHeadDim;
+    l.lse_floats = rh * ns;
+    l.counters = (size_t)d.B * sparse_units(d);
+  }
+  return l;
 }
 
 hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, const int32_t* sel,
-                                const int32_t* n_sel, uint16_t* out, float* lse, void* ws,
+                                const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
+                                float* part_lse, uint32_t* counters, bool counters_zeroed,
                                 hipStream_t s) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   AttnArgs a{};
@@ -410,16 +525,17 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
   a.scale_log2 = d.scale * kLog2e;
   a.n_split = sparse_splits(d, &a.split_tokens);
   if (a.n_split > 1) {
-    Carve c{static_cast<char*>(ws), 0};
-    const size_t rh = (size_t)d.B * d.Nq * d.Hq;
-    a.part_o = c.take<float>(rh * a.n_split * kHeadDim);
-    a.part_lse = c.take<float>(rh * a.n_split);
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.counters = counters;
+    if (!counters_zeroed) {
+      const size_t n = (size_t)d.B * sparse_units(d);
+      QSA_LAUNCH(fill_words_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)),
+                 dim3(256), 0, s, counters, n);
+    }
   }
-  QSA_LAUNCH(sparse_attend_kernel, dim3((unsigned)a.n_split, (unsigned)d.Nq, (unsigned)d.B),
-                     dim3(256), 0, s, a);
-  if (a.n_split > 1)
-    QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128),
-                       0, s, a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
+  QSA_LAUNCH(sparse_attend_kernel,
+             dim3((unsigned)sparse_units(d), (unsigned)a.n_split, (unsigned)d.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -458,10 +574,10 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
   a.part_lse = c.take<float>(rh * a.n_split);
   const int cchunks = (d.Nq * a.G + 15) / 16;
   QSA_LAUNCH(dense_decode_kernel,
-                     dim3((unsigned)a.n_split, (unsigned)(d.Hkv * cchunks), (unsigned)d.B), dim3(64),
-                     0, s, a);
-  QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0,
-                     s, a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
+             dim3((unsigned)a.n_split, (unsigned)(d.Hkv * cchunks), (unsigned)d.B), dim3(64), 0, s,
+             a);
+  QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
+             a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
   return hipGetLastError();
 }
 

@@ -65,11 +65,18 @@ __device__ __forceinline__ uint64_t make_key(uint32_t score_bits, uint32_t j) {
 }
 __device__ __forceinline__ uint32_t key_block(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
 
-// Sum over the four indexer heads of max(0, x), with -0 folded to +0 so the
-// bit pattern is canonical.
+// max(0, x) for a non-NaN float as one integer max on its bit pattern: a
+// set sign bit reads as a negative int, so every negative value and -0
+// become +0.  (fmaxf would first quiet possible NaNs, doubling the cost.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sum over the four indexer heads of max(0, x); the result is +0 or positive,
+// so its bit pattern orders like its value.
+__device__ __forceinline__ float relu_sum(float a, float b, float c, float d) {
+  return (relu(a) + relu(b)) + (relu(c) + relu(d));
+}
 __device__ __forceinline__ uint32_t relu_sum_bits(float a, float b, float c, float d) {
-  float s = fmaxf(a, 0.f) + fmaxf(b, 0.f) + fmaxf(c, 0.f) + fmaxf(d, 0.f);
-  return __float_as_uint(s) & 0x7fffffffu;
+  return __float_as_uint(relu_sum(a, b, c, d)) & 0x7fffffffu;
 }
 
 }  // namespace qsa

@@ -15,8 +15,15 @@ struct Dims {
 };
 
 // ---- compress.hip
+// Up to two word ranges the same launch clears (counters of the later steps
+// when the whole path runs back to back).
+struct ZeroRange {
+  uint32_t* p;
+  size_t n;
+};
 hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* lens,
-                           const int32_t* first_block, uint16_t* k_cmp, hipStream_t s);
+                           const int32_t* first_block, uint16_t* k_cmp, ZeroRange z0,
+                           ZeroRange z1, hipStream_t s);
 
 // ---- expand.hip
 hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
@@ -26,15 +33,24 @@ hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
 enum class TopkPath { kTable, kStream };
 TopkPath choose_topk_path(const Dims& d, uint32_t flags);
 size_t topk_workspace_bytes(const Dims& d, TopkPath path);
+// Words of the workspace that must be zero before the scoring pass.
+void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n);
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
                              const uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
-                             int32_t* n_sel, void* ws, hipStream_t s);
+                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s);
 
 // ---- attend.hip
-size_t attend_workspace_bytes(const Dims& d);
+// Scratch of the sparse attention when a query row is split over several
+// workgroups: partial outputs and log-sum-exps, and per-row arrival counters
+// that must be zero before the launch (the kernel leaves them zero).
+struct AttendLayout {
+  size_t partial_floats, lse_floats, counters;
+};
+AttendLayout attend_layout(const Dims& d);
 hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, const int32_t* sel,
-                                const int32_t* n_sel, uint16_t* out, float* lse, void* ws,
+                                const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
+                                float* part_lse, uint32_t* counters, bool counters_zeroed,
                                 hipStream_t s);
 size_t dense_workspace_bytes(const Dims& d);
 hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k,

@@ -45,7 +45,8 @@ namespace {
 constexpr int kHistBins = 2048;    // table engine: bins of (score bits >> 20)
 constexpr int kTableSlice = 2048;  // blocks per table-engine workgroup
 constexpr int kSelCap = 8192;      // candidates a select workgroup holds in LDS
-constexpr int kListCap = 2048;     // stream engine: list capacity per query
+constexpr int kHistW = 256;        // stream engine: threshold-tracking bins per query
+constexpr int kHyst = 64;          // stream engine: new counts between threshold updates
 constexpr int kStreamTile = 64;    // blocks per key tile (stream engine)
 constexpr int kStreamQ = 64;       // queries per stream workgroup (16 per wavefront)
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -167,77 +168,90 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
     p[i] = v;
 }
 
-// ------------------------------------------------------------------ select
-// One workgroup per query: exact top-512 of the candidate list of the row.
-__global__ __launch_bounds__(256) void select_kernel(const uint64_t* __restrict__ cand,
-                                                     const uint32_t* __restrict__ cand_cnt,
-                                                     const int32_t* __restrict__ lens,
-                                                     int32_t* __restrict__ sel,
-                                                     int32_t* __restrict__ n_sel,
-                                                     uint32_t* __restrict__ overflow, int Lmax,
-                                                     int Nq, int cap) {
-  __shared__ uint64_t keys[kSelCap];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t bcast[2];
-  __shared__ int32_t outb[kTopK];
-  __shared__ uint32_t outn;
-  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const size_t row = (size_t)b * Nq + q;
-  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
-  int32_t* srow = sel + row * kTopK;
-  if (write_trivial(t, srow, n_sel + row)) {
-    if (tid == 0) overflow[row] = 0;
-    return;
+// One wavefront: per-lane counts c[0..3] of bins 4*lane .. 4*lane+3 (bin
+// order = value order); find the highest bin whose suffix count (that bin and
+// every bin above it) reaches k.  Returns the bin and its suffix count.  The
+// caller guarantees the total reaches k.
+__device__ __forceinline__ void wave_suffix_bin4(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k, int& bin,
+                                                 uint32_t& suffix) {
+  const int l = lane_id();
+  const uint32_t mine = c0 + c1 + c2 + c3;
+  uint32_t S = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(S, off);
+    if (l + off < 64) S += o;
   }
-  const uint32_t n = cand_cnt[row];
-  if (n > (uint32_t)cap || n > (uint32_t)kSelCap || n < (uint32_t)kTopK) {
-    if (tid == 0) overflow[row] = 1;
-    return;
+  const uint64_t m = __ballot(S >= k);
+  const int L = 63 - __clzll((long long)m);
+  uint32_t cum = __shfl(S, L) - __shfl(mine, L);
+  const uint32_t b3 = __shfl(c3, L), b2 = __shfl(c2, L), b1 = __shfl(c1, L), b0 = __shfl(c0, L);
+  int d;
+  if (cum + b3 >= k) {
+    d = 3;
+    cum += b3;
+  } else if (cum + b3 + b2 >= k) {
+    d = 2;
+    cum += b3 + b2;
+  } else if (cum + b3 + b2 + b1 >= k) {
+    d = 1;
+    cum += b3 + b2 + b1;
+  } else {
+    d = 0;
+    cum += b3 + b2 + b1 + b0;
   }
-  if (tid == 0) {
-    overflow[row] = 0;
-    outn = 0;
-  }
-  const uint64_t* src = cand + row * (size_t)cap;
-  for (uint32_t i = tid; i < n; i += blockDim.x) keys[i] = src[i];
-  __syncthreads();
-  const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
-  for (uint32_t i = tid; i < n; i += blockDim.x) {
-    const uint64_t key = keys[i];
-    if (key >= kth) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
-  }
-  __syncthreads();
-  bitonic_sort_512(outb);
-  for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
-  if (tid == 0) n_sel[row] = kTopK;
+  bin = 4 * L + d;
+  suffix = cum;
 }
 
-// ------------------------------------------------------------------ fallback
-// Exact top-512 straight from the whole row, for rows flagged by select_kernel.
-// kRecompute: recompute scores from q_idx / k_cmp (stream engine, no table);
-// otherwise read the score table.  Output comes out in ascending order because
-// the final pass walks the blocks in order.
+// One wavefront, a kHistBins-bin histogram h (LDS or global): the highest bin
+// whose suffix count reaches k, and that suffix count.
+__device__ __forceinline__ void wave_suffix_bin_2048(const uint32_t* h, uint32_t k, int& bin,
+                                                     uint32_t& suffix) {
+  const int lane = lane_id();
+  // lane holds bins [32*lane, 32*lane+32); rotated order keeps LDS reads
+  // conflict-free
+  uint32_t mine = 0;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) mine += h[32 * lane + ((i + lane) & 31)];
+  uint32_t S = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(S, off);
+    if (lane + off < 64) S += o;
+  }
+  const uint64_t m = __ballot(S >= k);
+  const int L = 63 - __clzll((long long)m);
+  const uint32_t above = __shfl(S, L) - __shfl(mine, L);
+  // lanes 0..31 take one bin of lane L's range each; suffix within it
+  const int i = lane & 31;
+  uint32_t c = lane < 32 ? h[32 * L + i] : 0u;
+  uint32_t T = c;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const uint32_t o = __shfl_down(T, off);
+    if (i + off < 32) T += o;
+  }
+  const uint64_t m2 = __ballot(lane < 32 && above + T >= k);
+  const int I = 63 - __clzll((long long)m2);
+  bin = 32 * L + I;
+  suffix = above + __shfl(T, I);
+}
+
+// ------------------------------------------------------------------ select
+// Exact top-512 of one query straight from its whole row, walking the blocks
+// in order (so the output comes out ascending).  Slow path for rows whose
+// candidate list does not fit the fast path.  kRecompute: no score table
+// exists (stream engine), scores are recomputed from q_idx and k_cmp.
 template <bool kRecompute>
-__global__ __launch_bounds__(256) void select_fallback_kernel(
-    const uint32_t* __restrict__ table, const uint16_t* __restrict__ q_idx,
-    const uint16_t* __restrict__ k_cmp, const int32_t* __restrict__ lens,
-    const uint32_t* __restrict__ overflow, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-    int Lmax, int Nq) {
-  __shared__ float qf[kIdxHeads * kIdxDim];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t bcast[2];
-  __shared__ uint32_t wsum[4];
-  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const size_t row = (size_t)b * Nq + q;
-  if (overflow[row] == 0) return;
-  const int nbp = Lmax >> 2;
-  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
-  const int bt = t >> 2;  // > 512, guaranteed by the flag
-  const uint32_t* trow = table + row * (size_t)nbp;
-  const uint16_t* kc = k_cmp + (size_t)b * nbp * kIdxDim;
+__device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, const uint16_t* kc,
+                                 int bt, int32_t* srow, float* qf, uint32_t* hist,
+                                 uint32_t* bcast, uint32_t* wsum) {
+  const int tid = threadIdx.x;
   if (kRecompute) {
     for (int i = tid; i < kIdxHeads * kIdxDim; i += blockDim.x)
-      qf[i] = __uint_as_float((uint32_t)q_idx[row * kIdxHeads * kIdxDim + i] << 16);
+      qf[i] = __uint_as_float((uint32_t)qrow[i] << 16);
     __syncthreads();
   }
   auto key_of = [&](int j) -> uint64_t {
@@ -281,7 +295,6 @@ __global__ __launch_bounds__(256) void select_fallback_kernel(
     __syncthreads();
   }
   const uint64_t kth = prefix;
-  int32_t* srow = sel + row * kTopK;
   const int lane = lane_id(), wave = tid >> 6;
   uint32_t written = 0;
   for (int base = 0; base < bt; base += blockDim.x) {
@@ -296,16 +309,109 @@ __global__ __launch_bounds__(256) void select_fallback_kernel(
     for (int w = 0; w < 4; ++w) written += wsum[w];
     __syncthreads();
   }
+}
+
+// One workgroup per query row.  Fast path: the row's candidates (nsub
+// segments of up to seg_cap keys, segment lengths in cand_cnt; only keys whose
+// score reaches the row's final threshold, when one is given) go to LDS, a
+// radix select finds the 512th key and the winners are sorted.  Rows with too
+// few or too many candidates take the exact whole-row path.
+template <bool kRecompute>
+__global__ __launch_bounds__(256) void select_kernel(
+    const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int nsub,
+    int seg_cap, const int32_t* __restrict__ tau_final, const uint32_t* __restrict__ table,
+    int tstride, const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp,
+    const int32_t* __restrict__ lens, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+    int Lmax, int Nq) {
+  __shared__ uint64_t keys[kSelCap];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bcast[2];
+  __shared__ int32_t outb[kTopK];
+  __shared__ uint32_t outn;
+  __shared__ uint32_t bad;
+  __shared__ float qf[kIdxHeads * kIdxDim];
+  __shared__ uint32_t wsum[4];
+  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t row = (size_t)b * Nq + q;
+  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
+  int32_t* srow = sel + row * kTopK;
+  if (write_trivial(t, srow, n_sel + row)) return;
+  const int bt = t >> 2;
+  const int tau = tau_final ? tau_final[row] : -1;
+  if (tid == 0) {
+    outn = 0;
+    bad = 0;
+  }
+  __syncthreads();
+  const int lane = lane_id();
+  // threads_per_seg threads walk each segment
+  const int tps = blockDim.x / nsub;
+  const int seg = tid / tps, sub = tid % tps;
+  uint32_t n_seg = 0;
+  if (seg < nsub) {
+    n_seg = cand_cnt[row * nsub + seg];
+    if (n_seg > (uint32_t)seg_cap) {
+      atomicOr(&bad, 1u);
+      n_seg = seg_cap;
+    }
+  }
+  const uint64_t* src = cand + (row * nsub + (seg < nsub ? seg : 0)) * (size_t)seg_cap;
+  uint32_t longest = n_seg;
+  for (int off = 32; off >= 1; off >>= 1) longest = max(longest, (uint32_t)__shfl_xor((int)longest, off));
+  for (uint32_t i0 = 0; i0 < longest; i0 += 8 * tps) {
+    uint64_t kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = i0 + u * tps + sub;
+      kv[u] = (seg < nsub && i < n_seg) ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = i0 + u * tps + sub;
+      const bool keep = seg < nsub && i < n_seg && (int)(uint32_t)(kv[u] >> 32) >= tau;
+      const uint64_t m = __ballot(keep);
+      if (m == 0) continue;
+      const int leader = __ffsll((long long)m) - 1;
+      uint32_t p0 = 0;
+      if (lane == leader) p0 = atomicAdd(&outn, (uint32_t)__popcll(m));
+      p0 = __shfl(p0, leader);
+      const uint32_t p = p0 + (uint32_t)__popcll(m & lanemask_lt());
+      if (keep && p < (uint32_t)kSelCap) keys[p] = kv[u];
+    }
+  }
+  __syncthreads();
+  const uint32_t n = outn;
+  const bool ok = bad == 0 && n >= (uint32_t)kTopK && n <= (uint32_t)kSelCap;
+  __syncthreads();
+  if (ok) {
+    const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
+    if (tid == 0) outn = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += blockDim.x) {
+      const uint64_t key = keys[i];
+      if (key >= kth) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
+    }
+    __syncthreads();
+    bitonic_sort_512(outb);
+    for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
+    if (tid == 0) n_sel[row] = kTopK;
+    return;
+  }
+  const int nbp = Lmax >> 2;
+  select_whole_row<kRecompute>(table + (kRecompute ? 0 : row * (size_t)tstride),
+                               q_idx + row * kIdxHeads * kIdxDim,
+                               k_cmp + (size_t)b * nbp * kIdxDim, bt, srow, qf, hist, bcast, wsum);
   if (tid == 0) n_sel[row] = kTopK;
 }
 
 // ------------------------------------------------------------------ TABLE
-// Grid (slices, ceil(Nq/4), B); 4 wavefronts; each wavefront scores 4
+// Grid (slices, ceil(Nq/4), B); 4 wavefronts; each wavefront scores U
 // consecutive 16-block column tiles per step.
 __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_cmp,
                                                           const int32_t* __restrict__ lens,
                                                           uint32_t* __restrict__ scores,
+                                                          int tstride,
                                                           uint32_t* __restrict__ ghist, int Lmax,
                                                           int Nq) {
   __shared__ uint32_t hist[4 * kHistBins];
@@ -335,12 +441,12 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
   const int t_o = query_t(len, Nq, qo);
   const int bt_o = (qo < Nq && t_o >= 0) ? (t_o >> 2) : 0;
   const int lim = min(bt_o, j_end);
-  uint32_t* srow = scores + ((size_t)b * Nq + min(qo, Nq - 1)) * nbp;
+  uint32_t* srow = scores + ((size_t)b * Nq + min(qo, Nq - 1)) * tstride;
   uint32_t* myhist = hist + kc * kHistBins;
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
   __syncthreads();
 
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int jt = j_begin + wave * 16 * U; jt < j_end; jt += 64 * U) {
     uint4 bv[U][2];
 #pragma unroll
@@ -368,94 +474,117 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 4 * kHistBins; i += blockDim.x) {
-    const int qq = i / kHistBins;
-    const uint32_t c = hist[i];
-    if (c != 0 && q0 + qq < Nq)
-      atomicAdd(&ghist[((size_t)b * Nq + q0 + qq) * kHistBins + (i % kHistBins)], c);
+  // Publish only the bins at or above this slice's own 512-suffix bin: the
+  // global threshold bin can never lie below it, so lower bins never matter.
+  const int qq = q0 + wave;
+  if (qq < Nq) {
+    const uint32_t* h = hist + wave * kHistBins;
+    uint32_t tot = 0;
+    for (int i = lane; i < kHistBins; i += 64) tot += h[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    int lo = 0;
+    if (tot >= (uint32_t)kTopK) {
+      uint32_t sfx;
+      wave_suffix_bin_2048(h, kTopK, lo, sfx);
+    }
+    uint32_t* g = ghist + ((size_t)b * Nq + qq) * kHistBins;
+    for (int i = lo + lane; i < kHistBins; i += 64) {
+      const uint32_t c = h[i];
+      if (c != 0) atomicAdd(&g[i], c);
+    }
   }
 }
 
 // Same grid as score_table_kernel.  Appends the keys at or above each
 // query's threshold bin to the query's candidate list.
 __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __restrict__ scores,
+                                                           int tstride,
                                                            const uint32_t* __restrict__ ghist,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ cand,
                                                            uint32_t* __restrict__ cand_cnt,
                                                            int Lmax, int Nq, int cap) {
-  __shared__ uint32_t bins[4][kHistBins];
   __shared__ int thr[4];
+  __shared__ uint32_t wcnt[4][4];
+  __shared__ uint32_t wbase[4];
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
   const int len = clampi(lens[b], 0, Lmax);
-  const int nbp = Lmax >> 2;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int j_begin = slice * kTableSlice;
   {
     const int qq = q0 + wave;
     int m = -1;  // -1: nothing to append for this query
     const int t = query_t(len, Nq, qq);
     if (qq < Nq && t >= 0 && (t >> 2) > kTopK && j_begin < (t >> 2)) {
-      const size_t row = (size_t)b * Nq + qq;
-      const uint4* h4 = reinterpret_cast<const uint4*>(ghist + row * kHistBins);
-      uint4* s4 = reinterpret_cast<uint4*>(bins[wave]);
-      for (int i = lane; i < kHistBins / 4; i += 64) s4[i] = h4[i];
-      wave_sync_lds();
-      const uint32_t* hb = bins[wave] + lane * 32;
-      uint32_t mine = 0;
-      for (int i = 0; i < 32; ++i) mine += hb[i];
-      uint32_t S = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(S, off);
-        if (lane + off < 64) S += o;
-      }
-      const uint64_t msk = __ballot(S >= (uint32_t)kTopK);
-      const int L = 63 - __clzll((long long)msk);
-      uint32_t cum = __shfl(S, L) - __shfl(mine, L);
-      int mb = 0;
-      uint32_t total = 0;
-      if (lane == L) {
-        for (int i = 31; i >= 0; --i) {
-          cum += hb[i];
-          if (cum >= (uint32_t)kTopK) {
-            mb = L * 32 + i;
-            total = cum;
-            break;
-          }
-        }
-      }
-      mb = __shfl(mb, L);
-      total = __shfl(total, L);
+      int mb;
+      uint32_t total;
+      wave_suffix_bin_2048(ghist + ((size_t)b * Nq + qq) * kHistBins, kTopK, mb, total);
       m = total <= (uint32_t)cap ? mb : -1;
     }
     if (lane == 0) thr[wave] = m;
   }
   __syncthreads();
+  // All loads first: 4 queries x 2 passes of 1024 blocks, 4 blocks per thread.
+  uint4 v[4][2];
+  int jend[4];
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    const int qq = min(q0 + qi, Nq - 1);
+    const int bt = query_t(len, Nq, qq) >> 2;
+    jend[qi] = thr[qi] >= 0 ? min(j_begin + kTableSlice, bt) : j_begin;
+    const uint32_t* srow = scores + ((size_t)b * Nq + qq) * tstride;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int j4 = j_begin + p * 1024 + tid * 4;
+      v[qi][p] = j4 < jend[qi] ? *reinterpret_cast<const uint4*>(srow + j4) : zero_u4();
+    }
+  }
+  // Count this workgroup's candidates per query, reserve space with one
+  // atomic per query, then write (no per-candidate global atomics).
+  uint32_t pm[4];  // bit (p*4+e): element passes
+#pragma unroll
   for (int qi = 0; qi < 4; ++qi) {
     const int m = thr[qi];
-    if (m < 0) continue;
-    const int qq = q0 + qi;
-    const size_t row = (size_t)b * Nq + qq;
-    const int bt = query_t(len, Nq, qq) >> 2;
-    const int j_end = min(j_begin + kTableSlice, bt);
-    const uint32_t* srow = scores + row * nbp;
-    uint64_t* crow = cand + row * (size_t)cap;
-    for (int base = j_begin + wave * 64; base < j_end; base += 256) {
-      const int j = base + lane;
-      uint32_t bits = 0;
-      bool pred = false;
-      if (j < j_end) {
-        bits = srow[j];
-        pred = (int)(bits >> 20) >= m;
+    pm[qi] = 0;
+    uint32_t n = 0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t e4[4] = {v[qi][p].x, v[qi][p].y, v[qi][p].z, v[qi][p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j_begin + p * 1024 + tid * 4 + e;
+        const bool pred = m >= 0 && j < jend[qi] && (int)(e4[e] >> 20) >= m;
+        pm[qi] |= (pred ? 1u : 0u) << (p * 4 + e);
+        n += (uint32_t)__popcll(__ballot(pred));
       }
-      const uint64_t mask = __ballot(pred);
-      if (mask != 0) {
-        const int leader = __ffsll((long long)mask) - 1;
-        uint32_t pos0 = 0;
-        if (lane == leader) pos0 = atomicAdd(&cand_cnt[row], (uint32_t)__popcll(mask));
-        pos0 = __shfl(pos0, leader);
-        if (pred) crow[pos0 + (uint32_t)__popcll(mask & lanemask_lt())] = make_key(bits, (uint32_t)j);
+    }
+    if (lane == 0) wcnt[qi][wave] = n;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    const uint32_t tot = wcnt[tid][0] + wcnt[tid][1] + wcnt[tid][2] + wcnt[tid][3];
+    wbase[tid] = tot ? atomicAdd(&cand_cnt[(size_t)b * Nq + q0 + tid], tot) : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    if (thr[qi] < 0) continue;
+    uint32_t off = wbase[qi];
+    for (int w = 0; w < wave; ++w) off += wcnt[qi][w];
+    uint64_t* crow = cand + ((size_t)b * Nq + q0 + qi) * (size_t)cap;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t e4[4] = {v[qi][p].x, v[qi][p].y, v[qi][p].z, v[qi][p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool pred = (pm[qi] >> (p * 4 + e)) & 1u;
+        const uint64_t mask = __ballot(pred);
+        if (pred) {
+          const int j = j_begin + p * 1024 + tid * 4 + e;
+          crow[off + (uint32_t)__popcll(mask & lanemask_lt())] = make_key(e4[e], (uint32_t)j);
+        }
+        off += (uint32_t)__popcll(mask);
       }
     }
   }
@@ -499,17 +628,321 @@ __device__ uint64_t wave_compact(uint64_t* list, uint32_t n, uint32_t* hist) {
   return prefix;
 }
 
-// Grid (ceil(Nq/64), B); 4 wavefronts x 16 queries.
-__global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
+// Stream engine, per query: threshold tau (a score; below 0 = accept all)
+// and a 256-bin histogram of the appended scores at bf16 resolution, bin i =
+// (score bits >> 16) - base (the last bin also holds everything above;
+// scores below the base go to a spare 257th bin that is never read).  Every
+// counted element has score bits >= base<<16 and was appended; so if the
+// bins from m up hold >= 512 counts, at least 512 blocks seen so far score
+// >= (base+m)<<16, and any later block scoring no more than that is beaten by
+// all of them (an equal score loses on the higher block id): tau can rise to
+// (base+m)<<16.
+//
+// Survivors are first queued in LDS (one 8-byte entry: score, local query,
+// block id) by the scoring lanes; once per tile the queue is drained with
+// all 64 lanes busy: list slot, list store, histogram update.  That keeps
+// the per-survivor work of the scoring pass to a handful of instructions.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kRing = 8;        // LDS tile slots of the stream engine
+constexpr int kListCap = 16384; // candidate list entries per query
+constexpr int kQueue = kStreamTile * 16;  // survivors one tile can produce per wavefront
+constexpr int kHistWords = kHistW / 2 + 1;  // 256 packed bins + the spare bin
+
+// Barriers of the stream engine: no wait on vector-memory stores, so list
+// appends stay in flight across tiles.
+__device__ __forceinline__ void stream_barrier_compute() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Loader: the tiles up to two past the one just consumed must have landed;
+// the (kRing - 3) later tiles (8 loads each) may still be in flight.
+__device__ __forceinline__ void stream_barrier_loader() {
+  asm volatile("s_waitcnt vmcnt(40) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+static_assert(8 * (kRing - 3) == 40, "loader wait count");
+
+// Loader wavefront: copy one 64-block tile of compressed keys straight from
+// HBM into ring slot `slot` (8 KiB, eight 16-byte-per-lane DMA loads).  The
+// slot is stored swizzled: block row r, 16-byte chunk c lives at r*8 + (c ^ (r&7)).
+// Rows past bt_wg load row 0 instead (their scores are masked by the consumer).
+__device__ __forceinline__ void dma_tile(uint4* slot, const uint4* kb, int tile, int bt_wg) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s16 = i * 64 + lane;
+    const int row = s16 >> 3;
+    const int ch = (s16 & 7) ^ (row & 7);
+    int j = tile * kStreamTile + row;
+    if (j >= bt_wg) j = 0;
+    __builtin_amdgcn_global_load_lds(kb + (size_t)j * 8 + ch, (lds_void_t*)(slot + i * 64), 16, 0, 0);
+  }
+}
+
+// B fragments (compressed keys) of one 32-block half (column tile ct) of a
+// 64-block tile, read from the LDS ring.
+__device__ __forceinline__ void load_b(const uint4* kt, int ct, bf16x8 (&bf)[4]) {
+  const int lane = lane_id();
+  const int row = ct * 32 + (lane & 31);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int ch = ks * 2 + (lane >> 5);
+    bf[ks] = as_bf16x8(kt[row * 8 + (ch ^ (row & 7))]);
+  }
+}
+
+// Scores of one 32-block half for the wavefront's 16 queries x 4 heads.
+__device__ __forceinline__ void mma_half(const bf16x8 (&bf)[4], const bf16x8 (&A)[2][4],
+                                         f32x16 (&acc)[2]) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[rt][i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) acc[rt] = mfma32(A[rt][ks], bf[ks], acc[rt]);
+}
+
+__device__ __forceinline__ int rdl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Per-wavefront state.  Slot (rt, c) of a lane scores local query
+// rt*8 + c*2 + (lane >> 5); the lane keeps a copy of that query's tau.
+struct Stream {
+  float tau_l[2][4];
+  int tau_v, base_v, trig_v;  // lane q < 16: query q's tau bits, base, next update point
+  int tq0;                    // position of local query (lane >> 5)
+  int nq_left;                // queries of the batch from local query (lane >> 5) on
+  uint64_t* lists;            // list of local query 0; query q at + q * kListCap
+  uint32_t (*h)[kHistWords];  // the wavefront's 16 histograms
+  uint32_t* hc;               // 16 counts currently in the histograms
+  uint32_t* cnt;              // 16 list lengths
+  uint32_t* mx;               // 16 best scores seen before the base is set
+  uint32_t* rs;               // 256-word radix scratch
+  uint64_t* queue;            // kQueue survivors of the current tile
+};
+
+__device__ __forceinline__ int slot_query(int rt, int c) { return rt * 8 + c * 2 + (lane_id() >> 5); }
+
+// Histogram base of local query q (any lane may ask for any q).
+__device__ __forceinline__ int rdl_dyn_base(const Stream& st, int q) { return __shfl(st.base_v, q); }
+
+// Filter one 32-block half against tau; queue the survivors behind the qn
+// already queued this tile.  kFull: every block of the tile is below every
+// query's own block.  Returns the new queue length.
+template <bool kFull>
+__device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2], int tile, int ct,
+                                               int qn) {
+  const int lane = lane_id();
+  const int j = tile * kStreamTile + ct * 32 + (lane & 31);
+  float sc[2][4];
+  bool pass[2][4];
+  bool any = false;
+  // scores and pass tests of all 8 slots first, without branches, so the
+  // compiler can interleave them
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sc[rt][c] = relu_sum(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
+                           acc[rt][4 * c + 3]);
+      bool p = sc[rt][c] > st.tau_l[rt][c];
+      if (!kFull) {
+        const int off = rt * 8 + c * 2;
+        const int tq = st.tq0 + off;
+        p = p && off < st.nq_left && tq >= 0 && j < (tq >> 2);
+      }
+      pass[rt][c] = p;
+      any = any || p;
+    }
+  if (__ballot(any) == 0) return qn;
+  const uint32_t tag = (uint32_t)j | ((uint32_t)(lane >> 5) << 28);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint64_t m = __ballot(pass[rt][c]);
+      if (pass[rt][c]) {
+        const uint32_t pos = (uint32_t)qn + (uint32_t)__popcll(m & lanemask_lt());
+        st.queue[pos] = ((uint64_t)__float_as_uint(sc[rt][c]) << 32) |
+                        (uint64_t)(tag + ((uint32_t)(rt * 8 + c * 2) << 28));
+      }
+      qn += __popcll(m);
+    }
+  return qn;
+}
+
+// Drain the tile's queue: append every survivor to its query's list and
+// count it in the histogram (first tile: only track the best score).
+template <bool kFirst>
+__device__ __forceinline__ void stream_drain(Stream& st, int qn) {
+  const int lane = lane_id();
+  wave_sync_lds();
+  for (int i0 = 0; i0 < qn; i0 += 64) {
+    const int i = i0 + lane;
+    if (i < qn) {
+      const uint64_t e = st.queue[i];
+      const uint32_t bits = (uint32_t)(e >> 32);
+      const uint32_t lo = (uint32_t)e;
+      const int q = (int)(lo >> 28);
+      const uint32_t j = lo & 0x0fffffffu;
+      const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
+      // (the upkeep compacts a list before it can fill: pos < kListCap)
+      st.lists[(size_t)q * kListCap + min(pos, (uint32_t)kListCap - 1)] = make_key(bits, j);
+      if (kFirst) {
+        atomicMax(&st.mx[q], bits);
+      } else {
+        const int bin = (int)(bits >> 16) - rdl_dyn_base(st, q);
+        const int bb = bin < 0 ? kHistW : min(bin, kHistW - 1);
+        atomicAdd(&st.h[q][bb >> 1], 1u << ((bb & 1) * 16));
+        atomicAdd(&st.hc[q], bin < 0 ? 0u : 1u);
+      }
+    }
+  }
+  wave_sync_lds();
+}
+
+// New tau / base of local query i: refresh the lanes' copies.
+__device__ __forceinline__ void stream_set_query(Stream& st, int i, int tau_bits, int base) {
+  const int lane = lane_id();
+  if (lane == i) {
+    st.tau_v = tau_bits;
+    st.base_v = base;
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (slot_query(rt, c) == i) st.tau_l[rt][c] = __uint_as_float((uint32_t)tau_bits);
+}
+
+// Raise tau of local query i from its histogram (one wavefront).
+__device__ __forceinline__ void stream_raise_tau(Stream& st, int i) {
+  const int lane = lane_id();
+  uint32_t* h = st.h[i];
+  const uint32_t w0 = h[2 * lane], w1 = h[2 * lane + 1];
+  int m;
+  uint32_t total;
+  wave_suffix_bin4(w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16, kTopK, m, total);
+  if (m > 0) {
+    uint32_t nw[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int src = 4 * lane + 2 * half + e + m;
+        uint32_t cc = 0;
+        if (src < kHistW) cc = (h[src >> 1] >> ((src & 1) * 16)) & 0xffffu;
+        packed |= cc << (16 * e);
+      }
+      nw[half] = packed;
+    }
+    wave_sync_lds();
+    h[2 * lane] = nw[0];
+    h[2 * lane + 1] = nw[1];
+  }
+  const int nb = rdl(st.base_v, i) + m;
+  const int nt = max(nb << 16, rdl(st.tau_v, i));
+  if (lane == 0) st.hc[i] = total;
+  if (lane == i) st.trig_v = (int)total + kHyst;
+  stream_set_query(st, i, nt, nb);
+  wave_sync_lds();
+}
+
+// Rare: the list of local query i is nearly full.  Keep its 512 best keys,
+// set tau to the exact 512th score and rebuild the histogram from them.
+__device__ __forceinline__ void stream_compact(Stream& st, int i) {
+  const int lane = lane_id();
+  uint64_t* list = st.lists + (size_t)i * kListCap;
+  const uint32_t n = st.cnt[i];
+  const uint64_t kth = wave_compact(list, n, st.rs);
+  const int tau_bits = (int)(uint32_t)(kth >> 32);
+  const int base = tau_bits >> 16;
+  st.h[i][2 * lane] = 0u;
+  st.h[i][2 * lane + 1] = 0u;
+  if (lane == 0) st.h[i][kHistW / 2] = 0u;
+  wave_sync_lds();
+  for (int k2 = lane; k2 < kTopK; k2 += 64) {
+    const uint32_t sb = (uint32_t)(list[k2] >> 32);
+    const int bin = min((int)(sb >> 16) - base, kHistW - 1);
+    atomicAdd(&st.h[i][bin >> 1], 1u << ((bin & 1) * 16));
+  }
+  if (lane == 0) {
+    st.hc[i] = kTopK;
+    st.cnt[i] = kTopK;
+  }
+  if (lane == i) st.trig_v = kTopK + kHyst;
+  stream_set_query(st, i, max(tau_bits, rdl(st.tau_v, i)), base);
+  wave_sync_lds();
+}
+
+// After a tile: raise tau where enough new counts arrived, compact nearly
+// full lists (rare).
+__device__ __forceinline__ void stream_upkeep(Stream& st) {
+  const int lane = lane_id();
+  const uint32_t hc = lane < 16 ? st.hc[lane] : 0u;
+  const uint32_t cnt = lane < 16 ? st.cnt[lane] : 0u;
+  uint64_t r = __ballot(lane < 16 && (int)hc >= st.trig_v);
+  while (r) {
+    const int i = __builtin_ctzll(r);
+    r &= r - 1;
+    stream_raise_tau(st, i);
+  }
+  // one tile adds at most 64 entries to a list
+  uint64_t f = __ballot(lane < 16 && cnt > (uint32_t)(kListCap - 2 * kStreamTile));
+  while (f) {
+    const int i = __builtin_ctzll(f);
+    f &= f - 1;
+    stream_compact(st, i);
+  }
+}
+
+// One tile k: MFMAs of its second half, filter of its first half (computed
+// in the previous step), MFMAs of the next tile's first half, filter of the
+// second half, queue drain, per-query upkeep, barrier.
+template <bool kFirst, bool kFull>
+__device__ __forceinline__ void stream_step(Stream& st, const bf16x8 (&A)[2][4],
+                                            uint4 (*ring)[kStreamTile * 8], f32x16 (&accA)[2],
+                                            f32x16 (&accB)[2], int k, int ntiles) {
+  const int lane = lane_id();
+  const bool more = k + 1 < ntiles;
+  bf16x8 bf[4], bn[4];
+  load_b(ring[k % kRing], 1, bf);
+  if (more) load_b(ring[(k + 1) % kRing], 0, bn);
+  mma_half(bf, A, accB);
+  int qn = stream_epilogue<kFull>(st, accA, k, 0, 0);
+  if (more) mma_half(bn, A, accA);
+  qn = stream_epilogue<kFull>(st, accB, k, 1, qn);
+  if (qn > 0) stream_drain<kFirst>(st, qn);
+  if (kFirst) {
+    // histogram base: one octave below the best score of the first tile
+    wave_sync_lds();
+    const int base = lane < 16 ? max(0, (int)(st.mx[lane] >> 16) - 128) : 0;
+    for (int i = 0; i < 16; ++i) stream_set_query(st, i, (int)0xbf800000u, rdl(base, i));
+  } else if (qn > 0) {
+    stream_upkeep(st);
+  }
+  stream_barrier_compute();
+}
+
+// Grid (ceil(Nq/64), B); 5 wavefronts: 4 compute wavefronts x 16 queries and
+// one loader wavefront feeding an 8-slot LDS ring of key tiles.  Compute
+// wavefronts run tile k+1's MFMAs before tile k's filtering (double-buffered
+// accumulators), so matrix and vector work overlap.
+__global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
                                                            const uint16_t* __restrict__ k_cmp,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ lists,
                                                            uint32_t* __restrict__ list_cnt,
-                                                           int Lmax, int Nq) {
-  __shared__ uint4 ktile[2][kStreamTile * 8];
-  __shared__ int32_t s_tau[kStreamQ];
+                                                           int32_t* __restrict__ tau_out, int Lmax,
+                                                           int Nq) {
+  __shared__ uint4 ring[kRing][kStreamTile * 8];
+  __shared__ uint32_t s_h[kStreamQ][kHistWords];
+  __shared__ uint32_t s_hc[kStreamQ];
+  __shared__ uint32_t s_mx[kStreamQ];
   __shared__ uint32_t s_cnt[kStreamQ];
-  __shared__ uint32_t s_hist[4][256];
+  __shared__ uint32_t s_rs[4][256];
+  __shared__ uint64_t s_queue[4][kQueue];
 
   const int qbase = blockIdx.x * kStreamQ, b = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -517,12 +950,36 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
   const int nbp = Lmax >> 2;
   const int t_last = query_t(len, Nq, min(qbase + kStreamQ - 1, Nq - 1));
   const int bt_wg = t_last >= 0 ? (t_last >> 2) : 0;
+  const int ntiles = (bt_wg + kStreamTile - 1) / kStreamTile;
+  const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
+  for (int i = tid; i < kStreamQ * kHistWords; i += blockDim.x) (&s_h[0][0])[i] = 0u;
   if (tid < kStreamQ) {
-    s_tau[tid] = -1;
-    s_cnt[tid] = 0;
+    s_hc[tid] = 0u;
+    s_mx[tid] = 0u;
+    s_cnt[tid] = 0u;
   }
-  const int wq0 = qbase + wave * 16;
 
+  if (wave == 4) {
+    // ---------------- loader
+    for (int t = 0; t < kRing - 1; ++t) dma_tile(ring[t], kb, t, bt_wg);
+    stream_barrier_loader();
+    for (int k = 0; k < ntiles; ++k) {
+      dma_tile(ring[(k + kRing - 1) % kRing], kb, k + kRing - 1, bt_wg);
+      stream_barrier_loader();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the workgroup
+    return;
+  }
+
+  // ---------------- compute wavefronts
+  const int wq0 = qbase + wave * 16;
+  Stream st;
+  st.h = &s_h[wave * 16];
+  st.hc = &s_hc[wave * 16];
+  st.mx = &s_mx[wave * 16];
+  st.cnt = &s_cnt[wave * 16];
+  st.rs = s_rs[wave];
+  st.queue = s_queue[wave];
   // Stationary A fragments: 2 row tiles x 4 k-steps.  Row (lane & 31) of row
   // tile rt is query wq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
   bf16x8 A[2][4];
@@ -535,106 +992,53 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
     for (int ks = 0; ks < 4; ++ks)
       A[rt][ks] = as_bf16x8(qa < Nq ? p[ks * 2 + (lane >> 5)] : zero_u4());
   }
-  // Output queries of this lane: (rt, c) -> local query rt*8 + c*2 + (lane >> 5).
-  int btq[2][4];
-  uint64_t* lrow[2][4];
+  int bt_min = 0x7fffffff;
+  st.tq0 = query_t(len, Nq, wq0 + (lane >> 5));
+  st.nq_left = Nq - wq0 - (lane >> 5);
+  // (lists of rows past the batch are never written: their slots never pass)
+  st.lists = lists + ((size_t)b * Nq + wq0) * kListCap;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int qq = wq0 + rt * 8 + c * 2 + (lane >> 5);
+      const int qq = wq0 + slot_query(rt, c);
       const int t = query_t(len, Nq, qq);
-      btq[rt][c] = (qq < Nq && t >= 0) ? (t >> 2) : 0;
-      lrow[rt][c] = lists + ((size_t)b * Nq + min(qq, Nq - 1)) * kListCap;
+      bt_min = min(bt_min, (qq < Nq && t >= 0) ? (t >> 2) : 0);
+      st.tau_l[rt][c] = -1.f;
     }
+  // tiles entirely below every query's own block need no causal mask
+  for (int off = 32; off >= 1; off >>= 1) bt_min = min(bt_min, __shfl_xor(bt_min, off));
+  st.tau_v = (int)0xbf800000u;  // bits of -1.0f (as int: negative, below every score)
+  st.base_v = 0;
+  st.trig_v = kTopK + kHyst;
+  // Settle the A-fragment loads now, so no wait on vector memory (which
+  // would also wait for the list appends) is needed inside the tile loop.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  stream_barrier_compute();
 
-  const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
-  const int ntiles = (bt_wg + kStreamTile - 1) / kStreamTile;
-  uint4 nxt[2];
-  auto fetch = [&](int tile) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + 256 * u;
-      const int j = tile * kStreamTile + (e >> 3);
-      nxt[u] = j < bt_wg ? kb[(size_t)j * 8 + (e & 7)] : zero_u4();
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + 256 * u;
-      const int row = e >> 3, ch = e & 7;
-      ktile[buf][row * 8 + (ch ^ (row & 7))] = nxt[u];
-    }
-  };
+  // Pipeline over 32-block halves: the MFMAs of the next half run, and its
+  // key fragments are read from LDS, while the current half is filtered.
+  // Three loops: the first tile, the tiles below every query's own block
+  // (no causal mask), and the last tiles (masked).
+  f32x16 accA[2], accB[2];
   if (ntiles > 0) {
-    fetch(0);
-    stash(0);
+    bf16x8 bf[4];
+    load_b(ring[0], 0, bf);
+    mma_half(bf, A, accA);
   }
-  __syncthreads();
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const bool has_next = tile + 1 < ntiles;
-    if (has_next) fetch(tile + 1);
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[rt][ct][i] = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int row = ct * 32 + (lane & 31);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ch = ks * 2 + (lane >> 5);
-        const bf16x8 bf = as_bf16x8(ktile[buf][row * 8 + (ch ^ (row & 7))]);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) acc[rt][ct] = mfma32(A[rt][ks], bf, acc[rt][ct]);
-      }
-    }
-
-    const int j0 = tile * kStreamTile;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int lq = wave * 16 + rt * 8 + c * 2 + (lane >> 5);
-        const int tau = s_tau[lq];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int j = j0 + ct * 32 + (lane & 31);
-          const uint32_t bits = relu_sum_bits(acc[rt][ct][4 * c], acc[rt][ct][4 * c + 1],
-                                              acc[rt][ct][4 * c + 2], acc[rt][ct][4 * c + 3]);
-          if (j < btq[rt][c] && (int)bits > tau) {
-            const uint32_t slot = atomicAdd(&s_cnt[lq], 1u);
-            lrow[rt][c][slot] = make_key(bits, (uint32_t)j);
-          }
-        }
-      }
-    wave_sync_lds();
-    // Lists close to capacity: select their top 512 and raise the threshold.
-    for (int i = 0; i < 16; ++i) {
-      const int lq = wave * 16 + i;
-      const uint32_t n = s_cnt[lq];
-      if (n > (uint32_t)(kListCap - 2 * kStreamTile)) {
-        const int qq = qbase + lq;
-        uint64_t* list = lists + ((size_t)b * Nq + qq) * kListCap;
-        const uint64_t kth = wave_compact(list, n, s_hist[wave]);
-        if (lane == 0) {
-          s_cnt[lq] = kTopK;
-          s_tau[lq] = (int)(uint32_t)(kth >> 32);
-        }
-        wave_sync_lds();
-      }
-    }
-    if (has_next) stash(buf ^ 1);
-    __syncthreads();
+  const int nfull = min(ntiles, bt_min / kStreamTile);
+  if (ntiles > 0) {
+    if (nfull > 0)
+      stream_step<true, true>(st, A, ring, accA, accB, 0, ntiles);
+    else
+      stream_step<true, false>(st, A, ring, accA, accB, 0, ntiles);
   }
-  if (tid < kStreamQ && qbase + tid < Nq) list_cnt[(size_t)b * Nq + qbase + tid] = s_cnt[tid];
+  for (int k = 1; k < nfull; ++k) stream_step<false, true>(st, A, ring, accA, accB, k, ntiles);
+  for (int k = max(1, nfull); k < ntiles; ++k)
+    stream_step<false, false>(st, A, ring, accA, accB, k, ntiles);
+  wave_sync_lds();
+  if (lane < 16 && wq0 + lane < Nq) list_cnt[(size_t)b * Nq + wq0 + lane] = st.cnt[lane];
+  if (lane < 16 && wq0 + lane < Nq) tau_out[(size_t)b * Nq + wq0 + lane] = st.tau_v;
 }
 
 }  // namespace
@@ -650,26 +1054,27 @@ TopkPath choose_topk_path(const Dims& d, uint32_t flags) {
 }
 
 namespace {
+int table_stride(const Dims& d) { return ((d.Lmax / 4) + 3) & ~3; }
 struct TableWs {
   uint32_t* scores;
-  uint32_t* ghist;
+  uint32_t* ghist;  // histograms, then candidate counts (zeroed together)
   uint32_t* cand_cnt;
-  uint32_t* overflow;
   uint64_t* cand;
+  size_t zero_n;
 };
 struct StreamWs {
   uint64_t* lists;
   uint32_t* cnt;
-  uint32_t* overflow;
+  int32_t* tau;
 };
 TableWs carve_table(const Dims& d, void* ws, size_t* total) {
   Carve c{static_cast<char*>(ws), 0};
   const size_t rows = (size_t)d.B * d.Nq;
   TableWs w;
-  w.scores = c.take<uint32_t>(rows * (size_t)(d.Lmax / 4));
-  w.ghist = c.take<uint32_t>(rows * kHistBins + rows);  // histogram, then counts
+  w.scores = c.take<uint32_t>(rows * (size_t)table_stride(d));
+  w.zero_n = rows * kHistBins + rows;
+  w.ghist = c.take<uint32_t>(w.zero_n);
   w.cand_cnt = w.ghist ? w.ghist + rows * kHistBins : nullptr;
-  w.overflow = c.take<uint32_t>(rows);
   w.cand = c.take<uint64_t>(rows * kSelCap);
   if (total) *total = c.off;
   return w;
@@ -680,7 +1085,7 @@ StreamWs carve_stream(const Dims& d, void* ws, size_t* total) {
   StreamWs w;
   w.lists = c.take<uint64_t>(rows * kListCap);
   w.cnt = c.take<uint32_t>(rows);
-  w.overflow = c.take<uint32_t>(rows);
+  w.tau = c.take<int32_t>(rows);
   if (total) *total = c.off;
   return w;
 }
@@ -695,36 +1100,46 @@ size_t topk_workspace_bytes(const Dims& d, TopkPath path) {
   return total;
 }
 
+void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n) {
+  if (path == TopkPath::kTable) {
+    TableWs w = carve_table(d, ws, nullptr);
+    *ptr = w.ghist;
+    *n = w.zero_n;
+  } else {
+    *ptr = nullptr;
+    *n = 0;
+  }
+}
+
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
                              const uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
-                             int32_t* n_sel, void* ws, hipStream_t s) {
+                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
-  const size_t rows = (size_t)d.B * d.Nq;
   const dim3 grid_q((unsigned)d.Nq, (unsigned)d.B);
   if (path == TopkPath::kTable) {
     TableWs w = carve_table(d, ws, nullptr);
-    const size_t nz = rows * kHistBins + rows;
-    QSA_LAUNCH(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 4096)),
-                       dim3(256), 0, s, w.ghist, nz, 0u);
+    const int ts = table_stride(d);
+    if (!ws_zeroed)
+      QSA_LAUNCH(fill_u32_kernel,
+                 dim3((unsigned)std::min<size_t>((w.zero_n + 255) / 256, 4096)), dim3(256), 0, s,
+                 w.ghist, w.zero_n, 0u);
     const unsigned slices = (unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice);
     const dim3 grid(slices, (unsigned)((d.Nq + 3) / 4), (unsigned)d.B);
-    QSA_LAUNCH(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores,
-                       w.ghist, d.Lmax, d.Nq);
-    QSA_LAUNCH(table_filter_kernel, grid, dim3(256), 0, s, w.scores, w.ghist, lens,
-                       w.cand, w.cand_cnt, d.Lmax, d.Nq, kSelCap);
-    QSA_LAUNCH(select_kernel, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, lens, sel,
-                       n_sel, w.overflow, d.Lmax, d.Nq, kSelCap);
-    QSA_LAUNCH(select_fallback_kernel<false>, grid_q, dim3(256), 0, s, w.scores, q_idx,
-                       k_cmp, lens, w.overflow, sel, n_sel, d.Lmax, d.Nq);
+    QSA_LAUNCH(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
+               w.ghist, d.Lmax, d.Nq);
+    QSA_LAUNCH(table_filter_kernel, grid, dim3(256), 0, s, w.scores, ts, w.ghist, lens, w.cand,
+               w.cand_cnt, d.Lmax, d.Nq, kSelCap);
+    QSA_LAUNCH(select_kernel<false>, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, 1, kSelCap,
+               (const int32_t*)nullptr, w.scores, ts, q_idx, k_cmp, lens, sel, n_sel, d.Lmax,
+               d.Nq);
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
-    QSA_LAUNCH(score_stream_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.lists,
-                       w.cnt, d.Lmax, d.Nq);
-    QSA_LAUNCH(select_kernel, grid_q, dim3(256), 0, s, w.lists, w.cnt, lens, sel, n_sel,
-                       w.overflow, d.Lmax, d.Nq, kListCap);
-    QSA_LAUNCH(select_fallback_kernel<true>, grid_q, dim3(256), 0, s, nullptr, q_idx,
-                       k_cmp, lens, w.overflow, sel, n_sel, d.Lmax, d.Nq);
+    QSA_LAUNCH(score_stream_kernel, grid, dim3(320), 0, s, q_idx, k_cmp, lens, w.lists, w.cnt,
+               w.tau, d.Lmax, d.Nq);
+    QSA_LAUNCH(select_kernel<true>, grid_q, dim3(256), 0, s, w.lists, w.cnt, 1, kListCap,
+               (const int32_t*)w.tau, (const uint32_t*)nullptr, 0, q_idx, k_cmp, lens, sel, n_sel,
+               d.Lmax, d.Nq);
   }
   return hipGetLastError();
 }

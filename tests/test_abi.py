@@ -45,7 +45,7 @@ def test_workspace_sizes():
     assert Q.workspace_bytes(dec, Q.OP_FORWARD) >= Q.workspace_bytes(dec, Q.OP_INDEX_TOPK)
     pre = Q.shape(1, 1 << 20, 16384, 32, 4)
     # prefill uses the streaming engine: no score table (would be 16 GiB)
-    assert Q.workspace_bytes(pre, Q.OP_INDEX_TOPK) < 1 << 30
+    assert Q.workspace_bytes(pre, Q.OP_INDEX_TOPK) < 3 << 30
     assert Q.workspace_bytes(pre, Q.OP_SPARSE_ATTEND) == 0
     forced = Q.shape(1, 1 << 16, 16384, 32, 4, flags=Q.FLAG_TOPK_TABLE)
     assert Q.workspace_bytes(forced, Q.OP_INDEX_TOPK) >= 16384 * 16384 * 4
@@ -62,6 +62,7 @@ BAD_SHAPES = [
     Q.shape(1, 8, 1, 130, 2),        # group of 65 heads
     Q.shape(1, 8, 1, 8, 1, flags=3),  # both engines forced
     Q.shape(1, 8, 1, 8, 1, flags=8),  # unknown flag
+    Q.shape(1, (1 << 30) + 4, 1, 8, 1),  # beyond 2^30 tokens
 ]
 
 FAKE = ctypes.c_void_p(1 << 20)       # aligned, never dereferenced: errors come first
