@@ -646,7 +646,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kRing = 8;        // LDS tile slots of the stream engine
 constexpr int kListCap = 16384; // candidate list entries per query
-constexpr int kQueue = kStreamTile * 16;  // survivors one tile can produce per wavefront
+// survivors one tile can add to a wavefront's queue, plus fewer than 64 held over
+constexpr int kQueue = kStreamTile * 16 + 64;
 constexpr int kHistWords = kHistW / 2 + 1;  // 256 packed bins + the spare bin
 
 // Barriers of the stream engine: no wait on vector-memory stores, so list
@@ -723,8 +724,6 @@ struct Stream {
 
 __device__ __forceinline__ int slot_query(int rt, int c) { return rt * 8 + c * 2 + (lane_id() >> 5); }
 
-// Histogram base of local query q (any lane may ask for any q).
-__device__ __forceinline__ int rdl_dyn_base(const Stream& st, int q) { return __shfl(st.base_v, q); }
 
 // Filter one 32-block half against tau; queue the survivors behind the qn
 // already queued this tile.  kFull: every block of the tile is below every
@@ -736,7 +735,7 @@ __device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2
   const int j = tile * kStreamTile + ct * 32 + (lane & 31);
   float sc[2][4];
   bool pass[2][4];
-  bool any = false;
+  uint64_t any = 0;
   // scores and pass tests of all 8 slots first, without branches, so the
   // compiler can interleave them
 #pragma unroll
@@ -752,9 +751,9 @@ __device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2
         p = p && off < st.nq_left && tq >= 0 && j < (tq >> 2);
       }
       pass[rt][c] = p;
-      any = any || p;
+      any |= __ballot(p);
     }
-  if (__ballot(any) == 0) return qn;
+  if (any == 0) return qn;
   const uint32_t tag = (uint32_t)j | ((uint32_t)(lane >> 5) << 28);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
@@ -762,7 +761,8 @@ __device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2
     for (int c = 0; c < 4; ++c) {
       const uint64_t m = __ballot(pass[rt][c]);
       if (pass[rt][c]) {
-        const uint32_t pos = (uint32_t)qn + (uint32_t)__popcll(m & lanemask_lt());
+        const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)qn));
         st.queue[pos] = ((uint64_t)__float_as_uint(sc[rt][c]) << 32) |
                         (uint64_t)(tag + ((uint32_t)(rt * 8 + c * 2) << 28));
       }
@@ -779,19 +779,22 @@ __device__ __forceinline__ void stream_drain(Stream& st, int qn) {
   wave_sync_lds();
   for (int i0 = 0; i0 < qn; i0 += 64) {
     const int i = i0 + lane;
+    const uint64_t e = st.queue[min(i, qn - 1)];
+    const uint32_t bits = (uint32_t)(e >> 32);
+    const uint32_t lo = (uint32_t)e;
+    const int q = (int)(lo >> 28);
+    const uint32_t j = lo & 0x0fffffffu;
+    // (a lane-crossing read takes its value only from active lanes: do it
+    // before the tail lanes drop out)
+    const int qbase = kFirst ? 0 : __shfl(st.base_v, q);
     if (i < qn) {
-      const uint64_t e = st.queue[i];
-      const uint32_t bits = (uint32_t)(e >> 32);
-      const uint32_t lo = (uint32_t)e;
-      const int q = (int)(lo >> 28);
-      const uint32_t j = lo & 0x0fffffffu;
       const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
       // (the upkeep compacts a list before it can fill: pos < kListCap)
       st.lists[(size_t)q * kListCap + min(pos, (uint32_t)kListCap - 1)] = make_key(bits, j);
       if (kFirst) {
         atomicMax(&st.mx[q], bits);
       } else {
-        const int bin = (int)(bits >> 16) - rdl_dyn_base(st, q);
+        const int bin = (int)(bits >> 16) - qbase;
         const int bb = bin < 0 ? kHistW : min(bin, kHistW - 1);
         atomicAdd(&st.h[q][bb >> 1], 1u << ((bb & 1) * 16));
         atomicAdd(&st.hc[q], bin < 0 ? 0u : 1u);
@@ -899,27 +902,33 @@ __device__ __forceinline__ void stream_upkeep(Stream& st) {
 
 // One tile k: MFMAs of its second half, filter of its first half (computed
 // in the previous step), MFMAs of the next tile's first half, filter of the
-// second half, queue drain, per-query upkeep, barrier.
+// second half; then, once a full wavefront's worth of survivors is queued
+// (or on the first tile), the queue drain and the per-query upkeep; barrier.
 template <bool kFirst, bool kFull>
 __device__ __forceinline__ void stream_step(Stream& st, const bf16x8 (&A)[2][4],
                                             uint4 (*ring)[kStreamTile * 8], f32x16 (&accA)[2],
-                                            f32x16 (&accB)[2], int k, int ntiles) {
+                                            f32x16 (&accB)[2], int k, int ntiles, int& qn) {
   const int lane = lane_id();
-  const bool more = k + 1 < ntiles;
   bf16x8 bf[4], bn[4];
   load_b(ring[k % kRing], 1, bf);
-  if (more) load_b(ring[(k + 1) % kRing], 0, bn);
+  // (the slot of tile k+1 is always LDS of the ring; unused past the end)
+  load_b(ring[(k + 1) % kRing], 0, bn);
   mma_half(bf, A, accB);
-  int qn = stream_epilogue<kFull>(st, accA, k, 0, 0);
-  if (more) mma_half(bn, A, accA);
+  qn = stream_epilogue<kFull>(st, accA, k, 0, qn);
+  // (unconditional, also past the last tile: a conditional update would make
+  // the compiler copy the accumulators, and the copies wait for the MFMAs)
+  mma_half(bn, A, accA);
   qn = stream_epilogue<kFull>(st, accB, k, 1, qn);
-  if (qn > 0) stream_drain<kFirst>(st, qn);
   if (kFirst) {
+    if (qn > 0) stream_drain<true>(st, qn);
+    qn = 0;
     // histogram base: one octave below the best score of the first tile
     wave_sync_lds();
     const int base = lane < 16 ? max(0, (int)(st.mx[lane] >> 16) - 128) : 0;
     for (int i = 0; i < 16; ++i) stream_set_query(st, i, (int)0xbf800000u, rdl(base, i));
-  } else if (qn > 0) {
+  } else if (qn >= 64) {
+    stream_drain<false>(st, qn);
+    qn = 0;
     stream_upkeep(st);
   }
   stream_barrier_compute();
@@ -1021,6 +1030,7 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
   // Three loops: the first tile, the tiles below every query's own block
   // (no causal mask), and the last tiles (masked).
   f32x16 accA[2], accB[2];
+  int qn = 0;  // survivors queued, not yet drained
   if (ntiles > 0) {
     bf16x8 bf[4];
     load_b(ring[0], 0, bf);
@@ -1029,13 +1039,14 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
   const int nfull = min(ntiles, bt_min / kStreamTile);
   if (ntiles > 0) {
     if (nfull > 0)
-      stream_step<true, true>(st, A, ring, accA, accB, 0, ntiles);
+      stream_step<true, true>(st, A, ring, accA, accB, 0, ntiles, qn);
     else
-      stream_step<true, false>(st, A, ring, accA, accB, 0, ntiles);
+      stream_step<true, false>(st, A, ring, accA, accB, 0, ntiles, qn);
   }
-  for (int k = 1; k < nfull; ++k) stream_step<false, true>(st, A, ring, accA, accB, k, ntiles);
+  for (int k = 1; k < nfull; ++k) stream_step<false, true>(st, A, ring, accA, accB, k, ntiles, qn);
   for (int k = max(1, nfull); k < ntiles; ++k)
-    stream_step<false, false>(st, A, ring, accA, accB, k, ntiles);
+    stream_step<false, false>(st, A, ring, accA, accB, k, ntiles, qn);
+  if (qn > 0) stream_drain<false>(st, qn);
   wave_sync_lds();
   if (lane < 16 && wq0 + lane < Nq) list_cnt[(size_t)b * Nq + wq0 + lane] = st.cnt[lane];
   if (lane < 16 && wq0 + lane < Nq) tau_out[(size_t)b * Nq + wq0 + lane] = st.tau_v;
