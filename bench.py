@@ -7,7 +7,8 @@ QSA decode step at a 1M-token context, batch 4 x 4 query positions (1 token +
 qsa_forward call: compression of the newly completed block, indexer scoring of
 every earlier micro-block, top-512 selection, expansion and sparse GQA
 attention.  Inputs are resident in HBM; the 256 MiB infinity cache and the L2s
-are flushed (untimed) before every step, as the other layers of a model would.
+are flushed (untimed, by reading a 1 GiB buffer) before every step, as the
+other layers of a model would.
 
 The same line carries
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch
@@ -81,23 +82,29 @@ def kernel_stats(records, n_steps):
 
 
 def timed_steps(step, n, flush, Q, torch):
-    """n steps, flush before each (untimed); per-step HIP events; per-kernel
-    events through the library's profiling hook."""
+    """n steps, flush before each (untimed), per-step HIP events; then up to
+    20 more steps with the library's per-launch events (kept out of the step
+    times: the extra event records add their own time to the stream)."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    timer = Q.KernelTimer(max_launches=16 * n + 16)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    with timer:
-        for i in range(n):
-            flush()
-            starts[i].record()
-            step()
-            ends[i].record()
+    for i in range(n):
+        flush()
+        starts[i].record()
+        step()
+        ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return step_ms, kernel_stats(timer.records(), n), wall
+    nk = min(n, 20)
+    timer = Q.KernelTimer(max_launches=16 * nk + 16)
+    with timer:
+        for i in range(nk):
+            flush()
+            step()
+    torch.cuda.synchronize()
+    return step_ms, kernel_stats(timer.records(), nk), wall
 
 
 def pct(xs, p):
@@ -306,10 +313,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     Q.load_library()
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # 1 GiB, four times the infinity cache.  The flush READS it: that evicts the
+    # step's inputs from the infinity cache and the L2s and leaves only clean
+    # lines behind.  (Writing it would leave ~0.25 GiB of dirty lines whose
+    # write-back then competes with the next step's reads, a cost of whatever
+    # wrote them, not of this layer.)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush():
-        flush_buf.fill_(1)
+        torch.sum(flush_buf, dim=0, out=flush_sink)
 
     d = decode_leg(args, Q, W, torch, np, flush)
     step_ms = d["step_ms"]

@@ -37,7 +37,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [_hipcc(), "-O2", "-fPIC", "-std=c++17", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc(), "-O2", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -94,9 +94,8 @@ qsa_status check_lens(const Dims& d, const int32_t* lens, hipStream_t stream) {
   return QSA_OK;
 }
 
-// Workspace of qsa_sparse_attend: split counters, then partial outputs.
+// Workspace of qsa_sparse_attend: partial outputs of split query rows.
 struct AttendPtrs {
-  uint32_t* counters;
   float* part_o;
   float* part_lse;
 };
@@ -108,16 +107,11 @@ size_t carve_attend_partials(const Dims& d, char* base, AttendPtrs* p) {
   return c.off;
 }
 size_t carve_attend(const Dims& d, void* ws, AttendPtrs* p) {
-  qsa::Carve c{static_cast<char*>(ws), 0};
-  const qsa::AttendLayout l = qsa::attend_layout(d);
-  p->counters = l.counters ? c.take<uint32_t>(l.counters) : nullptr;
-  char* rest = c.take<char>(0);
-  c.off += carve_attend_partials(d, rest, p);
-  return c.off;
+  return carve_attend_partials(d, static_cast<char*>(ws), p);
 }
 
-// Workspace of qsa_forward: selection, split counters, then one region shared
-// by the top-k engine and (afterwards) the attention partials.
+// Workspace of qsa_forward: selection, then one region shared by the top-k
+// engine and (afterwards) the attention partials.
 struct ForwardPtrs {
   int32_t* sel;
   int32_t* n_sel;
@@ -129,8 +123,6 @@ size_t carve_forward(const Dims& d, uint32_t flags, void* ws, ForwardPtrs* p) {
   const size_t rows = (size_t)d.B * d.Nq;
   p->sel = c.take<int32_t>(rows * QSA_TOPK);
   p->n_sel = c.take<int32_t>(rows);
-  const qsa::AttendLayout l = qsa::attend_layout(d);
-  p->att.counters = l.counters ? c.take<uint32_t>(l.counters) : nullptr;
   char* shared = c.take<char>(0);
   p->shared = shared;
   const size_t a = qsa::topk_workspace_bytes(d, qsa::choose_topk_path(d, flags));
@@ -148,7 +140,7 @@ size_t ws_bytes_for(const Dims& d, uint32_t flags, int32_t op) {
       return qsa::topk_workspace_bytes(d, qsa::choose_topk_path(d, flags));
     case QSA_OP_SPARSE_ATTEND: {
       AttendPtrs p;
-      return qsa::attend_layout(d).counters ? carve_attend(d, nullptr, &p) : 0;
+      return carve_attend(d, nullptr, &p);
     }
     case QSA_OP_FORWARD: {
       ForwardPtrs p;
@@ -252,7 +244,7 @@ qsa_status qsa_compress_keys(const qsa_shape* shape, const uint16_t* k_idx, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
   return hip_status(
-      qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, {nullptr, 0}, {nullptr, 0}, s));
+      qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, {nullptr, 0}, s));
 }
 
 qsa_status qsa_index_topk(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_cmp,
@@ -312,7 +304,7 @@ qsa_status qsa_sparse_attend(const qsa_shape* shape, const uint16_t* q, const ui
   AttendPtrs p;
   carve_attend(d, ws, &p);
   return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.part_o,
-                                              p.part_lse, p.counters, false, s));
+                                              p.part_lse, s));
 }
 
 qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_idx,
@@ -345,17 +337,14 @@ qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint
   int32_t* sel = sel_out ? sel_out : p.sel;
   int32_t* n_sel = sel_out ? n_sel_out : p.n_sel;
   const qsa::TopkPath path = qsa::choose_topk_path(d, shape->flags);
-  qsa::ZeroRange z0{nullptr, 0}, z1{nullptr, 0};
-  if (d.Nq > 0) {
-    qsa::topk_zero_range(d, path, p.shared, &z0.p, &z0.n);
-    if (p.att.counters) z1 = {p.att.counters, qsa::attend_layout(d).counters};
-  }
-  QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, z0, z1, s)));
+  qsa::ZeroRange z0{nullptr, 0};
+  if (d.Nq > 0) qsa::topk_zero_range(d, path, p.shared, &z0.p, &z0.n);
+  QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, z0, s)));
   if (d.Nq == 0) return QSA_OK;
   QSA_TRY(hip_status(
       qsa::launch_index_topk(d, path, q_idx, k_cmp, lens, sel, n_sel, p.shared, z0.p != nullptr, s)));
   return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.att.part_o,
-                                              p.att.part_lse, p.att.counters, true, s));
+                                              p.att.part_lse, s));
 }
 
 qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,

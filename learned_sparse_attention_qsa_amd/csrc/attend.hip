@@ -61,7 +61,6 @@ struct AttnArgs {
   float* lse;
   float* part_o;    // [rows][Hq][n_split][128] when n_split > 1
   float* part_lse;  // [rows][Hq][n_split]
-  uint32_t* counters;  // [rows] split arrival counters (sparse, n_split > 1)
   int B, Lmax, Nq, Hq, Hkv, G;
   float scale_log2;
   int split_tokens, n_split;
@@ -206,13 +205,13 @@ __device__ __forceinline__ void finish(const Run& r, bool col_valid, uint16_t* o
 // wavefronts take interleaved 32-token tiles of the split (tile i goes to
 // wavefront i mod 4), each with its own online softmax, and are merged in
 // LDS.  With one split the result is final; otherwise the workgroup writes a
-// partial (o, lse) and the last of the n_split workgroups of its unit
-// (per-unit arrival counter) merges them and resets the counter to zero.
+// partial (o, lse) that merge_kernel combines.  (A merge by the last
+// workgroup to arrive would need a device-scope fence per workgroup, and on
+// this chip such a fence writes back the whole L2 of its XCD.)
 __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   __shared__ int32_t s_sel[kTopK];
   __shared__ __align__(16) uint16_t s_v[4][kTile * kVStride];  // V tiles; then merge scratch
   __shared__ float s_m[4][16], s_l[4][16], s_f[4][16], s_inv[16];
-  __shared__ int s_last;
   const int unit = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int hchunks = (a.G + 15) >> 4;
@@ -322,39 +321,6 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     else
       a.out[rh * kHeadDim + d] = (uint16_t)f32_to_bf16(o);
   }
-  if (!partial) return;
-  // ---- merge the splits of this unit (last workgroup to arrive)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[(size_t)b * (a.Nq * a.Hkv * hchunks) + unit], 1u) ==
-                         (unsigned)(a.n_split - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int nsp = a.n_split;
-  if (tid < nh) {
-    const float* pl = a.part_lse + (row * a.Hq + h0 + tid) * nsp;
-    float M = kNegInf;
-    for (int s2 = 0; s2 < nsp; ++s2) M = fmaxf(M, pl[s2]);
-    float sw = 0.f;
-    for (int s2 = 0; s2 < nsp; ++s2) sw += M == kNegInf ? 0.f : __expf(pl[s2] - M);
-    s_m[0][tid] = M;
-    s_inv[tid] = sw > 0.f ? 1.f / sw : 0.f;
-    if (a.lse) a.lse[row * a.Hq + h0 + tid] = sw > 0.f ? M + __logf(sw) : kNegInf;
-  }
-  __syncthreads();
-  for (int i = tid; i < nh * kHeadDim; i += blockDim.x) {
-    const int c = i >> 7, d = i & 127;
-    const size_t rh = row * a.Hq + h0 + c;
-    const float* pl = a.part_lse + rh * nsp;
-    const float* po = a.part_o + rh * nsp * kHeadDim + d;
-    const float M = s_m[0][c];
-    float o = 0.f;
-    for (int s2 = 0; s2 < nsp; ++s2)
-      o += (M == kNegInf ? 0.f : __expf(pl[s2] - M)) * po[(size_t)s2 * kHeadDim];
-    a.out[rh * kHeadDim + d] = (uint16_t)f32_to_bf16(o * s_inv[c]);
-  }
-  if (tid == 0) a.counters[(size_t)b * (a.Nq * a.Hkv * hchunks) + unit] = 0u;
 }
 
 // ------------------------------------------------------------------ dense
@@ -426,24 +392,42 @@ __global__ void fill_words_kernel(uint32_t* p, size_t n) {
 }
 
 // ------------------------------------------------------------------ merge
-// Grid (Hq, Nq, B), 128 threads (one per output dim).
+// Grid (Hq, Nq, B), 128 threads (one per output dim).  Combines the n_split
+// partial (o, lse) pairs of one (query, head): o = sum_s e^(lse_s - M) o_s /
+// sum_s e^(lse_s - M).  Loads go out 32 splits at a time so that their
+// latencies overlap.
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse, int Nq, int Hq,
                                                     int n_split) {
+  constexpr int kChunk = 32;
   const int h = blockIdx.x, q = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const size_t rh = ((size_t)b * Nq + q) * Hq + h;
   const float* pl = part_lse + rh * n_split;
-  const float* po = part_o + rh * n_split * kHeadDim;
+  const float* po = part_o + rh * n_split * kHeadDim + d;
   float M = kNegInf;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pl[s]);
+  for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s)
+      if (s0 + s < n_split) M = fmaxf(M, pl[s0 + s]);
+  }
   float acc = 0.f, sw = 0.f;
   if (M != kNegInf) {
-    for (int s = 0; s < n_split; ++s) {
-      const float w = __expf(pl[s] - M);
-      sw += w;
-      acc += w * po[(size_t)s * kHeadDim + d];
+    for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+      float w[kChunk], v[kChunk];
+#pragma unroll
+      for (int s = 0; s < kChunk; ++s) {
+        const bool ok = s0 + s < n_split;
+        w[s] = ok ? pl[s0 + s] : kNegInf;
+        v[s] = ok ? po[(size_t)(s0 + s) * kHeadDim] : 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < kChunk; ++s) {
+        const float e = w[s] == kNegInf ? 0.f : __expf(w[s] - M);
+        sw += e;
+        acc += e * v[s];
+      }
     }
   }
   const float o = sw > 0.f ? acc / sw : 0.f;
@@ -457,19 +441,18 @@ int sparse_units(const Dims& d) {
 }
 
 int sparse_splits(const Dims& d, int* split_tokens) {
-  // About 256 workgroups or more; split a query's tokens only when the batch
-  // of (query, KV head) units is too small to cover the chip.
+  // Decode-sized batches have few (query, KV head) units: split their token
+  // lists so that about 1,024 workgroups each gather one 32-token tile per
+  // wavefront (128 tokens), with all of a workgroup's loads in flight at once.
   const long long units = (long long)d.B * sparse_units(d);
-  int n_split = 1;
-  if (units < 256) {
-    n_split = (int)((256 + units - 1) / units);
-    if (n_split > 16) n_split = 16;
+  int st = kMaxTok;
+  if (units < 1024) {
+    const long long want = (1024 + units - 1) / units;
+    st = (int)((kMaxTok + want - 1) / want);
+    st = (st + 4 * kTile - 1) / (4 * kTile) * (4 * kTile);
   }
-  int st = (kMaxTok + n_split - 1) / n_split;
-  st = (st + kTile - 1) / kTile * kTile;
-  n_split = (kMaxTok + st - 1) / st;
   *split_tokens = st;
-  return n_split;
+  return (kMaxTok + st - 1) / st;
 }
 
 int dense_splits(const Dims& d, int* split_tokens) {
@@ -496,7 +479,6 @@ AttendLayout attend_layout(const Dims& d) {
     const size_t rh = (size_t)d.B * d.Nq * d.Hq;
     l.partial_floats = rh * ns * kHeadDim;
     l.lse_floats = rh * ns;
-    l.counters = (size_t)d.B * sparse_units(d);
   }
   return l;
 }
@@ -504,8 +486,7 @@ AttendLayout attend_layout(const Dims& d) {
 hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, const int32_t* sel,
                                 const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
-                                float* part_lse, uint32_t* counters, bool counters_zeroed,
-                                hipStream_t s) {
+                                float* part_lse, hipStream_t s) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   AttnArgs a{};
   a.q = q;
@@ -527,15 +508,12 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
   if (a.n_split > 1) {
     a.part_o = part_o;
     a.part_lse = part_lse;
-    a.counters = counters;
-    if (!counters_zeroed) {
-      const size_t n = (size_t)d.B * sparse_units(d);
-      QSA_LAUNCH(fill_words_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)),
-                 dim3(256), 0, s, counters, n);
-    }
   }
   QSA_LAUNCH(sparse_attend_kernel,
              dim3((unsigned)sparse_units(d), (unsigned)a.n_split, (unsigned)d.B), dim3(256), 0, s, a);
+  if (a.n_split > 1)
+    QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
+               part_o, part_lse, out, lse, d.Nq, d.Hq, a.n_split);
   return hipGetLastError();
 }
 

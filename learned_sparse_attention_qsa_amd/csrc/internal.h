@@ -15,15 +15,15 @@ struct Dims {
 };
 
 // ---- compress.hip
-// Up to two word ranges the same launch clears (counters of the later steps
-// when the whole path runs back to back).
+// A word range the same launch clears (the top-k engine's histograms and
+// counters when the whole path runs back to back).
 struct ZeroRange {
   uint32_t* p;
   size_t n;
 };
 hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* lens,
-                           const int32_t* first_block, uint16_t* k_cmp, ZeroRange z0,
-                           ZeroRange z1, hipStream_t s);
+                           const int32_t* first_block, uint16_t* k_cmp, ZeroRange z,
+                           hipStream_t s);
 
 // ---- expand.hip
 hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
@@ -41,17 +41,15 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
 
 // ---- attend.hip
 // Scratch of the sparse attention when a query row is split over several
-// workgroups: partial outputs and log-sum-exps, and per-row arrival counters
-// that must be zero before the launch (the kernel leaves them zero).
+// workgroups: partial outputs and log-sum-exps.
 struct AttendLayout {
-  size_t partial_floats, lse_floats, counters;
+  size_t partial_floats, lse_floats;
 };
 AttendLayout attend_layout(const Dims& d);
 hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, const int32_t* sel,
                                 const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
-                                float* part_lse, uint32_t* counters, bool counters_zeroed,
-                                hipStream_t s);
+                                float* part_lse, hipStream_t s);
 size_t dense_workspace_bytes(const Dims& d);
 hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* lens, uint16_t* out,

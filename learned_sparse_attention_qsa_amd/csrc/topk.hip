@@ -15,13 +15,16 @@
 // Two engines, with bit-identical results:
 //
 //  TABLE (few queries, decode-shaped): one streaming pass scores every block
-//  with MFMA (16x16x32, 4 queries x 4 heads per tile), writes the fp32 score
-//  table and a per-query 2048-bin histogram of the score's top bits.  A
-//  second pass picks, from the histogram, the highest bin whose cumulative
-//  count from the top reaches 512 and appends every key in or above it to a
-//  candidate list (its size is known from the histogram).  A select kernel
-//  then finds the exact 512th key in LDS.  Cost over the bare k_cmp scan: the
-//  score table (4 B per query per block) written once and read once.
+//  with MFMA (16x16x32, 4 queries x 4 heads per tile) and writes the fp32
+//  score table plus, for every 16-block group, the group's best score.  The
+//  512 largest group maxima belong to 512 distinct blocks, so the 512th
+//  largest group maximum is a lower bound of the row's 512th best score; a
+//  small per-row radix pass finds it (rounded down to 22 significant bits)
+//  from the group maxima alone.  A filter pass appends every key whose score
+//  reaches that bound (typically a few percent more than 512 keys) to a
+//  candidate list, and a select kernel sorts them in LDS.  Cost over the
+//  bare k_cmp scan: the score table (4 B per query per block) written once
+//  and read once.
 //
 //  STREAM (many queries, prefill-shaped): a workgroup holds 64 queries x 4
 //  heads stationary in registers and streams the compressed keys through LDS
@@ -42,8 +45,10 @@
 namespace qsa {
 namespace {
 
-constexpr int kHistBins = 2048;    // table engine: bins of (score bits >> 20)
-constexpr int kTableSlice = 2048;  // blocks per table-engine workgroup
+constexpr int kHistBins = 2048;    // radix bins of 11 bits (table threshold)
+constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine)
+constexpr int kFilterSlice = 2048; // blocks per filter workgroup (table engine)
+constexpr int kGroup = 16;         // blocks per group maximum (table engine)
 constexpr int kSelCap = 8192;      // candidates a select workgroup holds in LDS
 constexpr int kHistW = 256;        // stream engine: threshold-tracking bins per query
 constexpr int kHyst = 64;          // stream engine: new counts between threshold updates
@@ -149,6 +154,91 @@ __device__ void bitonic_sort_512(int32_t* a) {
       __syncthreads();
     }
   }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort, descending, of N = 256 * NPT 64-bit values; thread t holds
+// elements t*NPT .. t*NPT + NPT - 1 in v.  Exchanges within a thread use
+// registers, within a wavefront lane shuffles, across wavefronts the LDS
+// buffer xch (N values); only those last stages need barriers.  256 threads.
+template <int NPT>
+__device__ __forceinline__ void block_sort_desc(uint64_t (&v)[NPT], uint64_t* xch) {
+  constexpr int N = 256 * NPT;
+  const int t = threadIdx.x;
+  // fully unrolled: j must be a compile-time constant for the register cases
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < NPT) {
+#pragma unroll
+        for (int s = 0; s < NPT; ++s) {
+          if (s & j) continue;
+          const int i = t * NPT + s;
+          const bool desc = (i & k) == 0;
+          const uint64_t a = v[s], b = v[s | j];
+          const bool sw = (a < b) == desc;
+          v[s] = sw ? b : a;
+          v[s | j] = sw ? a : b;
+        }
+      } else {
+        uint64_t o[NPT];
+        if (j < 64 * NPT) {
+#pragma unroll
+          for (int s = 0; s < NPT; ++s) o[s] = shfl_xor_u64(v[s], j / NPT);
+        } else {
+          __syncthreads();
+#pragma unroll
+          for (int s = 0; s < NPT; ++s) xch[t * NPT + s] = v[s];
+          __syncthreads();
+#pragma unroll
+          for (int s = 0; s < NPT; ++s) o[s] = xch[(t * NPT + s) ^ j];
+        }
+#pragma unroll
+        for (int s = 0; s < NPT; ++s) {
+          const int i = t * NPT + s;
+          const bool desc = (i & k) == 0;
+          const bool keep_max = ((i & j) == 0) == desc;
+          v[s] = keep_max ? (v[s] > o[s] ? v[s] : o[s]) : (v[s] < o[s] ? v[s] : o[s]);
+        }
+      }
+    }
+  }
+}
+
+// Select's finish for n <= N candidates in keys[0..n): sort them (descending),
+// then sort the block ids of the first 512 ascending into outb.
+template <int NPT>
+__device__ __forceinline__ void finish_small(uint64_t* keys, uint32_t n, int32_t* outb) {
+  const int t = threadIdx.x;
+  uint64_t v[NPT];
+#pragma unroll
+  for (int s = 0; s < NPT; ++s) {
+    const uint32_t i = (uint32_t)(t * NPT + s);
+    v[s] = i < n ? keys[i] : 0ull;  // 0 is below every key
+  }
+  block_sort_desc<NPT>(v, keys);
+  __syncthreads();
+  // the 512 best keys sit at positions 0..511: pass their ids through LDS
+  // and sort them ascending (as complemented ids, descending)
+#pragma unroll
+  for (int s = 0; s < NPT; ++s) {
+    const int i = t * NPT + s;
+    if (i < kTopK) outb[i] = (int32_t)key_block(v[s]);
+  }
+  __syncthreads();
+  uint64_t w[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) w[s] = 0xffffffffull - (uint32_t)outb[2 * t + s];
+  block_sort_desc<2>(w, keys);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) outb[2 * t + s] = (int32_t)(0xffffffffu - (uint32_t)w[s]);
+  __syncthreads();
 }
 
 __device__ __forceinline__ int query_t(int len, int Nq, int q) { return len - Nq + q; }
@@ -384,14 +474,25 @@ __global__ __launch_bounds__(256) void select_kernel(
   const bool ok = bad == 0 && n >= (uint32_t)kTopK && n <= (uint32_t)kSelCap;
   __syncthreads();
   if (ok) {
-    const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
-    if (tid == 0) outn = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < n; i += blockDim.x) {
-      const uint64_t key = keys[i];
-      if (key >= kth) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
+    if (n <= 2048u) {
+      // few candidates: sort them all, keep the first 512, sort their ids
+      if (n <= 1024u)
+        finish_small<4>(keys, n, outb);
+      else
+        finish_small<8>(keys, n, outb);
+      for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
+      if (tid == 0) n_sel[row] = kTopK;
+      return;
+    } else {
+      const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
+      if (tid == 0) outn = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < n; i += blockDim.x) {
+        const uint64_t key = keys[i];
+        if (key >= kth) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     bitonic_sort_512(outb);
     for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
     if (tid == 0) n_sel[row] = kTopK;
@@ -405,29 +506,29 @@ __global__ __launch_bounds__(256) void select_kernel(
 }
 
 // ------------------------------------------------------------------ TABLE
-// Grid (slices, ceil(Nq/4), B); 4 wavefronts; each wavefront scores U
-// consecutive 16-block column tiles per step.
+// Grid (ceil(Lmax/4 / kTableSlice), ceil(Nq/4), B), 256 threads.  Wavefront w
+// scores blocks [j_begin + 256 w, + 256) in two batches of eight 16-block
+// tiles.  MFMA 16x16x32: A = 16 rows (query r/4, head r%4), B = 16 blocks;
+// the lane (r, kc) receives block r of the tile for query q0 + kc, all four
+// heads.  A tile is also one group: its maximum over the 16 lanes of a query
+// goes to gmax.
 __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __restrict__ q_idx,
                                                           const uint16_t* __restrict__ k_cmp,
                                                           const int32_t* __restrict__ lens,
                                                           uint32_t* __restrict__ scores,
                                                           int tstride,
-                                                          uint32_t* __restrict__ ghist, int Lmax,
-                                                          int Nq) {
-  __shared__ uint32_t hist[4 * kHistBins];
+                                                          uint32_t* __restrict__ gmax,
+                                                          int gstride, int Lmax, int Nq) {
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
   const int len = clampi(lens[b], 0, Lmax);
   const int nbp = Lmax >> 2;
   const int t_last = query_t(len, Nq, min(q0 + 3, Nq - 1));
-  if (t_last < 4) return;
   const int j_begin = slice * kTableSlice;
-  const int j_end = min(j_begin + kTableSlice, t_last >> 2);
+  const int j_end = min(j_begin + kTableSlice, t_last >= 0 ? (t_last >> 2) : 0);
   if (j_begin >= j_end) return;
-  for (int i = threadIdx.x; i < 4 * kHistBins; i += blockDim.x) hist[i] = 0;
 
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int r = lane & 15, kc = lane >> 4;
-  // A operand: row r = (query r/4, head r%4); k chunk kc (dims kc*8.., 32+kc*8..)
   bf16x8 a0 = as_bf16x8(zero_u4()), a1 = a0;
   const int qa = q0 + (r >> 2);
   if (qa < Nq) {
@@ -436,18 +537,20 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
     a0 = as_bf16x8(p[kc]);
     a1 = as_bf16x8(p[4 + kc]);
   }
-  // Output of the 16x16 tile: lane holds block column r for query q0+kc, all heads.
   const int qo = q0 + kc;
   const int t_o = query_t(len, Nq, qo);
   const int bt_o = (qo < Nq && t_o >= 0) ? (t_o >> 2) : 0;
   const int lim = min(bt_o, j_end);
-  uint32_t* srow = scores + ((size_t)b * Nq + min(qo, Nq - 1)) * tstride;
-  uint32_t* myhist = hist + kc * kHistBins;
+  const size_t orow = (size_t)b * Nq + min(qo, Nq - 1);
+  uint32_t* srow = scores + orow * tstride;
+  uint32_t* grow = gmax + orow * gstride;
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
-  __syncthreads();
 
   constexpr int U = 8;
-  for (int jt = j_begin + wave * 16 * U; jt < j_end; jt += 64 * U) {
+#pragma unroll 1
+  for (int batch = 0; batch < 2; ++batch) {
+    const int jt = j_begin + wave * (2 * U * 16) + batch * (U * 16);
+    if (jt >= j_end) break;
     uint4 bv[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -465,74 +568,174 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mfma16(a0, as_bf16x8(bv[u][0]), acc);
       acc = mfma16(a1, as_bf16x8(bv[u][1]), acc);
-      const int jo = jt + u * 16 + r;
-      if (jo < lim) {
-        const uint32_t bits = relu_sum_bits(acc[0], acc[1], acc[2], acc[3]);
-        srow[jo] = bits;
-        atomicAdd(&myhist[bits >> 20], 1u);
-      }
-    }
-  }
-  __syncthreads();
-  // Publish only the bins at or above this slice's own 512-suffix bin: the
-  // global threshold bin can never lie below it, so lower bins never matter.
-  const int qq = q0 + wave;
-  if (qq < Nq) {
-    const uint32_t* h = hist + wave * kHistBins;
-    uint32_t tot = 0;
-    for (int i = lane; i < kHistBins; i += 64) tot += h[i];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-    int lo = 0;
-    if (tot >= (uint32_t)kTopK) {
-      uint32_t sfx;
-      wave_suffix_bin_2048(h, kTopK, lo, sfx);
-    }
-    uint32_t* g = ghist + ((size_t)b * Nq + qq) * kHistBins;
-    for (int i = lo + lane; i < kHistBins; i += 64) {
-      const uint32_t c = h[i];
-      if (c != 0) atomicAdd(&g[i], c);
+      const int j0 = jt + u * 16;
+      const int jo = j0 + r;
+      // masked blocks count as score +0 in the group maximum: they can only
+      // lower the bound, which stays valid
+      const uint32_t bits = jo < lim ? relu_sum_bits(acc[0], acc[1], acc[2], acc[3]) : 0u;
+      if (jo < lim) srow[jo] = bits;
+      uint32_t gm = bits;
+      gm = max(gm, (uint32_t)__shfl_xor((int)gm, 8));
+      gm = max(gm, (uint32_t)__shfl_xor((int)gm, 4));
+      gm = max(gm, (uint32_t)__shfl_xor((int)gm, 2));
+      gm = max(gm, (uint32_t)__shfl_xor((int)gm, 1));
+      if (r == 0 && j0 < lim && qo < Nq) grow[j0 / kGroup] = gm;
     }
   }
 }
 
-// Same grid as score_table_kernel.  Appends the keys at or above each
-// query's threshold bin to the query's candidate list.
+// The group maxima a thread visits: chunk c of 16 x 4 values starting at
+// 4 * (c * 16 * blockDim.x + threadIdx.x), 16 loads of 16 bytes in flight.
+// Values at or past G read as 0 (below or equal to every real maximum, so
+// the callers' counts and bounds are unaffected: they only count values that
+// reach a positive cut, or take maxima).
+__device__ __forceinline__ void load_group_chunk(const uint32_t* g, int G, int c, uint4 (&v)[16]) {
+  const uint4* g4 = reinterpret_cast<const uint4*>(g);
+  const int n4 = (G + 3) >> 2;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int i = c * 16 * (int)blockDim.x + u * (int)blockDim.x + (int)threadIdx.x;
+    v[u] = i < n4 ? g4[i] : zero_u4();
+    const int e = 4 * i;
+    if (e + 3 >= G) {
+      if (e >= G) v[u].x = 0u;
+      if (e + 1 >= G) v[u].y = 0u;
+      if (e + 2 >= G) v[u].z = 0u;
+      v[u].w = 0u;
+    }
+  }
+}
+
+// One workgroup per query row: a lower bound tau of the row's 512th best score
+// from its group maxima.  With G >= 512 groups the 512th largest group
+// maximum is such a bound (512 distinct blocks reach it); this kernel finds it
+// by two 11-bit radix passes and keeps 22 bits (rounding down keeps it a lower
+// bound).  Each thread first keeps its two largest maxima: the smallest of
+// those 512 numbers is itself a valid bound, so only maxima at or above it are
+// counted.  Rows with fewer than 512 groups keep every candidate (tau = 0).
+__global__ __launch_bounds__(256) void table_threshold_kernel(const uint32_t* __restrict__ gmax,
+                                                              int gstride,
+                                                              const int32_t* __restrict__ lens,
+                                                              uint32_t* __restrict__ thr,
+                                                              int Lmax, int Nq) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t s_cut;
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const int row = blockIdx.x, b = row / Nq, q = row % Nq, tid = threadIdx.x;
+  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
+  const int bt = t >= 0 ? (t >> 2) : 0;
+  const int G = (bt + kGroup - 1) / kGroup;
+  if (bt <= kTopK || G < kTopK) {
+    if (tid == 0) thr[row] = 0u;
+    return;
+  }
+  const uint32_t* g = gmax + (size_t)row * gstride;
+  const int nchunks = (((G + 3) >> 2) + 16 * (int)blockDim.x - 1) / (16 * (int)blockDim.x);
+  uint32_t m1 = 0, m2 = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 v[16];
+    load_group_chunk(g, G, c, v);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = e4[e];
+        m2 = x >= m1 ? m1 : max(m2, x);
+        m1 = max(m1, x);
+      }
+    }
+  }
+  if (tid == 0) s_cut = 0xffffffffu;
+  for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  // Padding zeros and threads with fewer than two maxima can only lower the
+  // cut (0 is always valid); otherwise 256 threads x 2 maxima reach it.
+  atomicMin(&s_cut, m2);
+  __syncthreads();
+  const uint32_t cut = max(s_cut, 1u);  // (padding zeros never counted)
+  const bool cut_zero = s_cut == 0u;
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 v[16];
+    load_group_chunk(g, G, c, v);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * (c * 16 * (int)blockDim.x + u * (int)blockDim.x + tid) + e;
+        if (idx < G && (cut_zero || e4[e] >= cut)) atomicAdd(&hist[e4[e] >> 20], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int bin;
+    uint32_t sfx;
+    wave_suffix_bin_2048(hist, kTopK, bin, sfx);
+    if (tid == 0) {
+      s_bin = bin;
+      s_above = sfx - hist[bin];
+    }
+  }
+  __syncthreads();
+  const uint32_t bin1 = (uint32_t)s_bin;
+  const uint32_t k2 = (uint32_t)kTopK - s_above;
+  for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 v[16];
+    load_group_chunk(g, G, c, v);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * (c * 16 * (int)blockDim.x + u * (int)blockDim.x + tid) + e;
+        if (idx < G && (e4[e] >> 20) == bin1) atomicAdd(&hist[(e4[e] >> 9) & (kHistBins - 1)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int bin2;
+    uint32_t sfx;
+    wave_suffix_bin_2048(hist, k2, bin2, sfx);
+    if (tid == 0) thr[row] = (bin1 << 20) | ((uint32_t)bin2 << 9);
+  }
+}
+
+// Grid (ceil(Lmax/4 / kFilterSlice), ceil(Nq/4), B).  Appends the keys whose
+// score reaches the row's bound to the row's candidate list (one atomic per
+// workgroup and row reserves the space; keys past the list capacity are
+// dropped, and the select kernel sees the overflow in the count).
 __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __restrict__ scores,
                                                            int tstride,
-                                                           const uint32_t* __restrict__ ghist,
+                                                           const uint32_t* __restrict__ thr,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ cand,
                                                            uint32_t* __restrict__ cand_cnt,
                                                            int Lmax, int Nq, int cap) {
-  __shared__ int thr[4];
   __shared__ uint32_t wcnt[4][4];
   __shared__ uint32_t wbase[4];
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
   const int len = clampi(lens[b], 0, Lmax);
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
-  const int j_begin = slice * kTableSlice;
-  {
-    const int qq = q0 + wave;
-    int m = -1;  // -1: nothing to append for this query
-    const int t = query_t(len, Nq, qq);
-    if (qq < Nq && t >= 0 && (t >> 2) > kTopK && j_begin < (t >> 2)) {
-      int mb;
-      uint32_t total;
-      wave_suffix_bin_2048(ghist + ((size_t)b * Nq + qq) * kHistBins, kTopK, mb, total);
-      m = total <= (uint32_t)cap ? mb : -1;
-    }
-    if (lane == 0) thr[wave] = m;
-  }
-  __syncthreads();
+  const int j_begin = slice * kFilterSlice;
   // All loads first: 4 queries x 2 passes of 1024 blocks, 4 blocks per thread.
   uint4 v[4][2];
   int jend[4];
+  uint32_t tau[4];
 #pragma unroll
   for (int qi = 0; qi < 4; ++qi) {
     const int qq = min(q0 + qi, Nq - 1);
-    const int bt = query_t(len, Nq, qq) >> 2;
-    jend[qi] = thr[qi] >= 0 ? min(j_begin + kTableSlice, bt) : j_begin;
+    const int t = query_t(len, Nq, qq);
+    const int bt = t >= 0 ? (t >> 2) : 0;
+    // rows with at most 512 candidates are finished by the select kernel alone
+    const bool live = q0 + qi < Nq && bt > kTopK;
+    jend[qi] = live ? min(j_begin + kFilterSlice, bt) : j_begin;
+    tau[qi] = live ? thr[(size_t)b * Nq + qq] : 0u;
     const uint32_t* srow = scores + ((size_t)b * Nq + qq) * tstride;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -540,12 +743,9 @@ __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __res
       v[qi][p] = j4 < jend[qi] ? *reinterpret_cast<const uint4*>(srow + j4) : zero_u4();
     }
   }
-  // Count this workgroup's candidates per query, reserve space with one
-  // atomic per query, then write (no per-candidate global atomics).
   uint32_t pm[4];  // bit (p*4+e): element passes
 #pragma unroll
   for (int qi = 0; qi < 4; ++qi) {
-    const int m = thr[qi];
     pm[qi] = 0;
     uint32_t n = 0;
 #pragma unroll
@@ -554,7 +754,7 @@ __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __res
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = j_begin + p * 1024 + tid * 4 + e;
-        const bool pred = m >= 0 && j < jend[qi] && (int)(e4[e] >> 20) >= m;
+        const bool pred = j < jend[qi] && e4[e] >= tau[qi];
         pm[qi] |= (pred ? 1u : 0u) << (p * 4 + e);
         n += (uint32_t)__popcll(__ballot(pred));
       }
@@ -564,12 +764,12 @@ __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __res
   __syncthreads();
   if (tid < 4) {
     const uint32_t tot = wcnt[tid][0] + wcnt[tid][1] + wcnt[tid][2] + wcnt[tid][3];
-    wbase[tid] = tot ? atomicAdd(&cand_cnt[(size_t)b * Nq + q0 + tid], tot) : 0u;
+    wbase[tid] = (tot && q0 + tid < Nq) ? atomicAdd(&cand_cnt[(size_t)b * Nq + q0 + tid], tot) : 0u;
   }
   __syncthreads();
 #pragma unroll
   for (int qi = 0; qi < 4; ++qi) {
-    if (thr[qi] < 0) continue;
+    if (q0 + qi >= Nq) break;
     uint32_t off = wbase[qi];
     for (int w = 0; w < wave; ++w) off += wcnt[qi][w];
     uint64_t* crow = cand + ((size_t)b * Nq + q0 + qi) * (size_t)cap;
@@ -582,7 +782,8 @@ __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __res
         const uint64_t mask = __ballot(pred);
         if (pred) {
           const int j = j_begin + p * 1024 + tid * 4 + e;
-          crow[off + (uint32_t)__popcll(mask & lanemask_lt())] = make_key(e4[e], (uint32_t)j);
+          const uint32_t pos = off + (uint32_t)__popcll(mask & lanemask_lt());
+          if (pos < (uint32_t)cap) crow[pos] = make_key(e4[e], (uint32_t)j);
         }
         off += (uint32_t)__popcll(mask);
       }
@@ -1066,12 +1267,13 @@ TopkPath choose_topk_path(const Dims& d, uint32_t flags) {
 
 namespace {
 int table_stride(const Dims& d) { return ((d.Lmax / 4) + 3) & ~3; }
+int group_stride(const Dims& d) { return (((d.Lmax / 4) + kGroup - 1) / kGroup + 3) & ~3; }
 struct TableWs {
   uint32_t* scores;
-  uint32_t* ghist;  // histograms, then candidate counts (zeroed together)
-  uint32_t* cand_cnt;
+  uint32_t* gmax;
+  uint32_t* thr;
+  uint32_t* cand_cnt;  // zeroed before the filter
   uint64_t* cand;
-  size_t zero_n;
 };
 struct StreamWs {
   uint64_t* lists;
@@ -1083,9 +1285,9 @@ TableWs carve_table(const Dims& d, void* ws, size_t* total) {
   const size_t rows = (size_t)d.B * d.Nq;
   TableWs w;
   w.scores = c.take<uint32_t>(rows * (size_t)table_stride(d));
-  w.zero_n = rows * kHistBins + rows;
-  w.ghist = c.take<uint32_t>(w.zero_n);
-  w.cand_cnt = w.ghist ? w.ghist + rows * kHistBins : nullptr;
+  w.gmax = c.take<uint32_t>(rows * (size_t)group_stride(d));
+  w.thr = c.take<uint32_t>(rows);
+  w.cand_cnt = c.take<uint32_t>(rows);
   w.cand = c.take<uint64_t>(rows * kSelCap);
   if (total) *total = c.off;
   return w;
@@ -1114,8 +1316,8 @@ size_t topk_workspace_bytes(const Dims& d, TopkPath path) {
 void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n) {
   if (path == TopkPath::kTable) {
     TableWs w = carve_table(d, ws, nullptr);
-    *ptr = w.ghist;
-    *n = w.zero_n;
+    *ptr = w.cand_cnt;
+    *n = (size_t)d.B * d.Nq;
   } else {
     *ptr = nullptr;
     *n = 0;
@@ -1129,16 +1331,19 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   const dim3 grid_q((unsigned)d.Nq, (unsigned)d.B);
   if (path == TopkPath::kTable) {
     TableWs w = carve_table(d, ws, nullptr);
-    const int ts = table_stride(d);
+    const int ts = table_stride(d), gs = group_stride(d);
+    const size_t rows = (size_t)d.B * d.Nq;
     if (!ws_zeroed)
-      QSA_LAUNCH(fill_u32_kernel,
-                 dim3((unsigned)std::min<size_t>((w.zero_n + 255) / 256, 4096)), dim3(256), 0, s,
-                 w.ghist, w.zero_n, 0u);
-    const unsigned slices = (unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice);
-    const dim3 grid(slices, (unsigned)((d.Nq + 3) / 4), (unsigned)d.B);
-    QSA_LAUNCH(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
-               w.ghist, d.Lmax, d.Nq);
-    QSA_LAUNCH(table_filter_kernel, grid, dim3(256), 0, s, w.scores, ts, w.ghist, lens, w.cand,
+      QSA_LAUNCH(fill_u32_kernel, dim3((unsigned)std::min<size_t>((rows + 255) / 256, 4096)),
+                 dim3(256), 0, s, w.cand_cnt, rows, 0u);
+    const unsigned qg = (unsigned)((d.Nq + 3) / 4);
+    const dim3 grid_s((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
+    const dim3 grid_f((unsigned)((d.Lmax / 4 + kFilterSlice - 1) / kFilterSlice), qg, (unsigned)d.B);
+    QSA_LAUNCH(score_table_kernel, grid_s, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
+               w.gmax, gs, d.Lmax, d.Nq);
+    QSA_LAUNCH(table_threshold_kernel, dim3((unsigned)rows), dim3(256), 0, s, w.gmax, gs, lens,
+               w.thr, d.Lmax, d.Nq);
+    QSA_LAUNCH(table_filter_kernel, grid_f, dim3(256), 0, s, w.scores, ts, w.thr, lens, w.cand,
                w.cand_cnt, d.Lmax, d.Nq, kSelCap);
     QSA_LAUNCH(select_kernel<false>, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, 1, kSelCap,
                (const int32_t*)nullptr, w.scores, ts, q_idx, k_cmp, lens, sel, n_sel, d.Lmax,
