@@ -208,6 +208,7 @@ __device__ __forceinline__ void finish(const Run& r, bool col_valid, uint16_t* o
 // partial (o, lse) that merge_kernel combines.  (A merge by the last
 // workgroup to arrive would need a device-scope fence per workgroup, and on
 // this chip such a fence writes back the whole L2 of its XCD.)
+template <bool kMulti>  // false: every wavefront has at most one 32-token tile
 __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   __shared__ int32_t s_sel[kTopK];
   __shared__ __align__(16) uint16_t s_v[4][kTile * kVStride];  // V tiles; then merge scratch
@@ -220,21 +221,18 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   const size_t row = (size_t)b * a.Nq + q;
   const int len = clampi(a.lens[b], 0, a.Lmax);
   const int t = len - a.Nq + q;
-  int ns = 0, ntok = 0, bt = 0;
-  if (t >= 0) {
-    bt = t >> 2;
-    ns = clampi(a.n_sel[row], 0, bt < kTopK ? bt : kTopK);
-    ntok = 4 * ns + (t - 4 * bt) + 1;
-  }
-  for (int i = tid; i < ns; i += blockDim.x)
-    s_sel[i] = clampi(a.sel[row * kTopK + i], 0, bt - 1);  // ids outside [0, bt) are a caller bug
-  __syncthreads();
   const int k_begin = split * a.split_tokens;
-  const int k_end = min(ntok, k_begin + a.split_tokens);
+  // This split's slice of the selection, loaded before n_sel is known (the
+  // loads do not wait on each other): blocks [kb0, kb0 + split_tokens / 4).
+  const int kb0 = k_begin >> 2;
+  const int nsb = min(a.split_tokens >> 2, kTopK - kb0);  // <= 512 = 2 per thread
+  int32_t my_sel[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (tid + 256 * i < nsb) my_sel[i] = a.sel[row * kTopK + kb0 + tid + 256 * i];
   const int h0 = g * a.G + hc * 16;
   const int nh = min(16, a.G - hc * 16);
   const int col = lane & 15;
-  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
   bf16x8 qf[4];
   {
     const uint4* qp =
@@ -242,22 +240,38 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(col < nh ? qp[ks * 4 + (lane >> 4)] : zero_u4());
   }
+  int ns = 0, ntok = 0, bt = 0;
+  if (t >= 0) {
+    bt = t >> 2;
+    ns = clampi(a.n_sel[row], 0, bt < kTopK ? bt : kTopK);
+    ntok = 4 * ns + (t - 4 * bt) + 1;
+  }
+  // ids outside [0, bt) are a caller bug: clamped so no access leaves the row
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i;
+    if (e < nsb && kb0 + e < ns) s_sel[e] = clampi(my_sel[i], 0, bt - 1);
+  }
+  __syncthreads();
+  const int k_end = min(ntok, k_begin + a.split_tokens);
+  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
   const uint16_t* kbase = a.k + g * kHeadDim;
   const uint16_t* vbase = a.v + g * kHeadDim;
   auto row_of = [&](int kk) -> long long {
     if (kk >= k_end) return -1;
-    const int tok = kk < 4 * ns ? 4 * s_sel[kk >> 2] + (kk & 3) : 4 * bt + (kk - 4 * ns);
+    const int tok = kk < 4 * ns ? 4 * s_sel[(kk >> 2) - kb0] + (kk & 3) : 4 * bt + (kk - 4 * ns);
     return (long long)(kv_seq + (size_t)tok * a.Hkv) * kHeadDim;
   };
   uint16_t* vt = s_v[wave];
   Run r;
   run_init(r);
-  KVTile cur, nxt;
+  KVTile cur;
   const int first = k_begin + wave * kTile;
   if (first < k_end) load_tile(cur, kbase, vbase, first, row_of);
   for (int k0 = first; k0 < k_end; k0 += 4 * kTile) {
     stash_v(vt, cur);
-    if (k0 + 4 * kTile < k_end) load_tile(nxt, kbase, vbase, k0 + 4 * kTile, row_of);
+    KVTile nxt;
+    if (kMulti && k0 + 4 * kTile < k_end) load_tile(nxt, kbase, vbase, k0 + 4 * kTile, row_of);
     float z[8];
     qk_logits(cur, qf, a.scale_log2, z);
 #pragma unroll
@@ -268,6 +282,7 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     wave_sync_lds();
     softmax_pv(r, z, vt);
     wave_sync_lds();
+    if (!kMulti) break;
     cur = nxt;
   }
   // ---- merge the four wavefronts (LDS)
@@ -448,8 +463,8 @@ int sparse_splits(const Dims& d, int* split_tokens) {
   int st = kMaxTok;
   if (units < 1024) {
     const long long want = (1024 + units - 1) / units;
-    st = (int)((kMaxTok + want - 1) / want);
-    st = (st + 4 * kTile - 1) / (4 * kTile) * (4 * kTile);
+    st = (int)(kMaxTok / want) / (4 * kTile) * (4 * kTile);
+    if (st < 4 * kTile) st = 4 * kTile;
   }
   *split_tokens = st;
   return (kMaxTok + st - 1) / st;
@@ -509,8 +524,11 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
     a.part_o = part_o;
     a.part_lse = part_lse;
   }
-  QSA_LAUNCH(sparse_attend_kernel,
-             dim3((unsigned)sparse_units(d), (unsigned)a.n_split, (unsigned)d.B), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)sparse_units(d), (unsigned)a.n_split, (unsigned)d.B);
+  if (a.split_tokens <= 4 * kTile)
+    QSA_LAUNCH(sparse_attend_kernel<false>, grid, dim3(256), 0, s, a);
+  else
+    QSA_LAUNCH(sparse_attend_kernel<true>, grid, dim3(256), 0, s, a);
   if (a.n_split > 1)
     QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
                part_o, part_lse, out, lse, d.Nq, d.Hq, a.n_split);

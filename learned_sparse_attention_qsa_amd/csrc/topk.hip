@@ -211,18 +211,13 @@ __device__ __forceinline__ void block_sort_desc(uint64_t (&v)[NPT], uint64_t* xc
   }
 }
 
-// Select's finish for n <= N candidates in keys[0..n): sort them (descending),
-// then sort the block ids of the first 512 ascending into outb.
+// Select's finish for at most 256 * NPT candidates held in v (0 = empty, below
+// every key): sort them (descending), then sort the block ids of the first 512
+// ascending into outb.  xch: LDS scratch of 256 * NPT keys.
 template <int NPT>
-__device__ __forceinline__ void finish_small(uint64_t* keys, uint32_t n, int32_t* outb) {
+__device__ __forceinline__ void finish_sorted(uint64_t (&v)[NPT], uint64_t* xch, int32_t* outb) {
   const int t = threadIdx.x;
-  uint64_t v[NPT];
-#pragma unroll
-  for (int s = 0; s < NPT; ++s) {
-    const uint32_t i = (uint32_t)(t * NPT + s);
-    v[s] = i < n ? keys[i] : 0ull;  // 0 is below every key
-  }
-  block_sort_desc<NPT>(v, keys);
+  block_sort_desc<NPT>(v, xch);
   __syncthreads();
   // the 512 best keys sit at positions 0..511: pass their ids through LDS
   // and sort them ascending (as complemented ids, descending)
@@ -235,10 +230,23 @@ __device__ __forceinline__ void finish_small(uint64_t* keys, uint32_t n, int32_t
   uint64_t w[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) w[s] = 0xffffffffull - (uint32_t)outb[2 * t + s];
-  block_sort_desc<2>(w, keys);
+  block_sort_desc<2>(w, xch);
 #pragma unroll
   for (int s = 0; s < 2; ++s) outb[2 * t + s] = (int32_t)(0xffffffffu - (uint32_t)w[s]);
   __syncthreads();
+}
+
+// The same for n <= 256 * NPT candidates in keys[0..n) (LDS, also the scratch).
+template <int NPT>
+__device__ __forceinline__ void finish_small(uint64_t* keys, uint32_t n, int32_t* outb) {
+  const int t = threadIdx.x;
+  uint64_t v[NPT];
+#pragma unroll
+  for (int s = 0; s < NPT; ++s) {
+    const uint32_t i = (uint32_t)(t * NPT + s);
+    v[s] = i < n ? keys[i] : 0ull;
+  }
+  finish_sorted<NPT>(v, keys, outb);
 }
 
 __device__ __forceinline__ int query_t(int len, int Nq, int q) { return len - Nq + q; }
@@ -250,12 +258,6 @@ __device__ __forceinline__ bool write_trivial(int t, int32_t* srow, int32_t* n_s
   for (int i = threadIdx.x; i < kTopK; i += blockDim.x) srow[i] = i < bt ? i : -1;
   if (threadIdx.x == 0) *n_sel_row = bt;
   return true;
-}
-
-__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = v;
 }
 
 // One wavefront: per-lane counts c[0..3] of bins 4*lane .. 4*lane+3 (bin
@@ -423,6 +425,11 @@ __global__ __launch_bounds__(256) void select_kernel(
   __shared__ uint32_t wsum[4];
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const size_t row = (size_t)b * Nq + q;
+  // threads_per_seg threads walk each segment; the segment length is read
+  // before (and independently of) lens
+  const int tps = blockDim.x / nsub;
+  const int seg = tid / tps, sub = tid % tps;
+  const uint32_t n_seg_raw = seg < nsub ? cand_cnt[row * nsub + seg] : 0u;
   const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
   int32_t* srow = sel + row * kTopK;
   if (write_trivial(t, srow, n_sel + row)) return;
@@ -434,18 +441,43 @@ __global__ __launch_bounds__(256) void select_kernel(
   }
   __syncthreads();
   const int lane = lane_id();
-  // threads_per_seg threads walk each segment
-  const int tps = blockDim.x / nsub;
-  const int seg = tid / tps, sub = tid % tps;
   uint32_t n_seg = 0;
   if (seg < nsub) {
-    n_seg = cand_cnt[row * nsub + seg];
+    n_seg = n_seg_raw;
     if (n_seg > (uint32_t)seg_cap) {
       atomicOr(&bad, 1u);
       n_seg = seg_cap;
     }
   }
   const uint64_t* src = cand + (row * nsub + (seg < nsub ? seg : 0)) * (size_t)seg_cap;
+  if (nsub == 1 && n_seg <= 1024u && cand_cnt[row] <= (uint32_t)seg_cap) {
+    // short list: straight into registers, 4 keys per thread, then sort
+    uint64_t v[4];
+    int mine = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const uint32_t i = (uint32_t)(tid * 4 + s2);
+      const uint64_t key = i < n_seg ? src[i] : 0ull;
+      const bool keep = i < n_seg && (int)(uint32_t)(key >> 32) >= tau;
+      v[s2] = keep ? key : 0ull;
+      mine += keep ? 1 : 0;
+    }
+    atomicAdd(&outn, (uint32_t)mine);
+    __syncthreads();
+    if (outn >= (uint32_t)kTopK) {
+      finish_sorted<4>(v, keys, outb);
+      for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
+      if (tid == 0) n_sel[row] = kTopK;
+      return;
+    }
+    // too few: the exact whole-row path below
+    __syncthreads();
+    if (tid == 0) {
+      outn = 0;
+      bad = 1;
+    }
+    __syncthreads();
+  }
   uint32_t longest = n_seg;
   for (int off = 32; off >= 1; off >>= 1) longest = max(longest, (uint32_t)__shfl_xor((int)longest, off));
   for (uint32_t i0 = 0; i0 < longest; i0 += 8 * tps) {
@@ -584,40 +616,43 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
   }
 }
 
-// The group maxima a thread visits: chunk c of 16 x 4 values starting at
-// 4 * (c * 16 * blockDim.x + threadIdx.x), 16 loads of 16 bytes in flight.
-// Values at or past G read as 0 (below or equal to every real maximum, so
-// the callers' counts and bounds are unaffected: they only count values that
-// reach a positive cut, or take maxima).
-__device__ __forceinline__ void load_group_chunk(const uint32_t* g, int G, int c, uint4 (&v)[16]) {
+// One workgroup (1,024 threads) per query row: a lower bound tau of the
+// row's 512th best score from its group maxima.  With G >= 512 groups the
+// 512th largest group maximum is such a bound (512 distinct blocks reach it);
+// two 11-bit radix passes find it to 22 bits, rounded down (still a lower
+// bound).  First every thread keeps its two largest maxima: when every thread
+// has two, the smallest of those 2,048 numbers is itself a valid bound, so
+// only maxima at or above it need counting.  Rows with fewer than 512 groups
+// keep every candidate (tau = 0).  Each thread reads 16 maxima per chunk
+// (four 16-byte loads in flight); later passes re-read them from the L2.
+constexpr int kThrThreads = 1024;
+
+__device__ __forceinline__ void load_group_chunk(const uint32_t* g, int G, int c, uint32_t (&x)[16]) {
   const uint4* g4 = reinterpret_cast<const uint4*>(g);
   const int n4 = (G + 3) >> 2;
+  uint4 v[4];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int i = c * 16 * (int)blockDim.x + u * (int)blockDim.x + (int)threadIdx.x;
+  for (int u = 0; u < 4; ++u) {
+    const int i = (c * 4 + u) * kThrThreads + (int)threadIdx.x;
     v[u] = i < n4 ? g4[i] : zero_u4();
-    const int e = 4 * i;
-    if (e + 3 >= G) {
-      if (e >= G) v[u].x = 0u;
-      if (e + 1 >= G) v[u].y = 0u;
-      if (e + 2 >= G) v[u].z = 0u;
-      v[u].w = 0u;
-    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * ((c * 4 + u) * kThrThreads + (int)threadIdx.x);
+    x[4 * u + 0] = v[u].x;
+    x[4 * u + 1] = e + 1 < G ? v[u].y : 0u;
+    x[4 * u + 2] = e + 2 < G ? v[u].z : 0u;
+    x[4 * u + 3] = e + 3 < G ? v[u].w : 0u;
   }
 }
+__device__ __forceinline__ bool group_valid(int G, int c, int k) {
+  const int u = k >> 2, e = k & 3;
+  return 4 * ((c * 4 + u) * kThrThreads + (int)threadIdx.x) + e < G;
+}
 
-// One workgroup per query row: a lower bound tau of the row's 512th best score
-// from its group maxima.  With G >= 512 groups the 512th largest group
-// maximum is such a bound (512 distinct blocks reach it); this kernel finds it
-// by two 11-bit radix passes and keeps 22 bits (rounding down keeps it a lower
-// bound).  Each thread first keeps its two largest maxima: the smallest of
-// those 512 numbers is itself a valid bound, so only maxima at or above it are
-// counted.  Rows with fewer than 512 groups keep every candidate (tau = 0).
-__global__ __launch_bounds__(256) void table_threshold_kernel(const uint32_t* __restrict__ gmax,
-                                                              int gstride,
-                                                              const int32_t* __restrict__ lens,
-                                                              uint32_t* __restrict__ thr,
-                                                              int Lmax, int Nq) {
+__global__ __launch_bounds__(kThrThreads) void table_threshold_kernel(
+    const uint32_t* __restrict__ gmax, int gstride, const int32_t* __restrict__ lens,
+    uint32_t* __restrict__ thr, int Lmax, int Nq) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t s_cut;
   __shared__ int s_bin;
@@ -631,43 +666,35 @@ __global__ __launch_bounds__(256) void table_threshold_kernel(const uint32_t* __
     return;
   }
   const uint32_t* g = gmax + (size_t)row * gstride;
-  const int nchunks = (((G + 3) >> 2) + 16 * (int)blockDim.x - 1) / (16 * (int)blockDim.x);
+  const int nchunks = (G + 16 * kThrThreads - 1) / (16 * kThrThreads);
   uint32_t m1 = 0, m2 = 0;
   for (int c = 0; c < nchunks; ++c) {
-    uint4 v[16];
-    load_group_chunk(g, G, c, v);
+    uint32_t x[16];
+    load_group_chunk(g, G, c, x);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = e4[e];
-        m2 = x >= m1 ? m1 : max(m2, x);
-        m1 = max(m1, x);
-      }
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t v = group_valid(G, c, k) ? x[k] : 0u;
+      m2 = v >= m1 ? m1 : max(m2, v);
+      m1 = max(m1, v);
     }
   }
   if (tid == 0) s_cut = 0xffffffffu;
   for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0u;
   __syncthreads();
-  // Padding zeros and threads with fewer than two maxima can only lower the
-  // cut (0 is always valid); otherwise 256 threads x 2 maxima reach it.
-  atomicMin(&s_cut, m2);
+  // A thread with fewer than two maxima reports 0, which makes the cut 0: then
+  // every maximum is counted (always valid).
+  uint32_t wm = m2;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wm = min(wm, (uint32_t)__shfl_xor((int)wm, off));
+  if ((tid & 63) == 0) atomicMin(&s_cut, wm);
   __syncthreads();
-  const uint32_t cut = max(s_cut, 1u);  // (padding zeros never counted)
-  const bool cut_zero = s_cut == 0u;
+  const uint32_t cut = s_cut;
   for (int c = 0; c < nchunks; ++c) {
-    uint4 v[16];
-    load_group_chunk(g, G, c, v);
+    uint32_t x[16];
+    load_group_chunk(g, G, c, x);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = 4 * (c * 16 * (int)blockDim.x + u * (int)blockDim.x + tid) + e;
-        if (idx < G && (cut_zero || e4[e] >= cut)) atomicAdd(&hist[e4[e] >> 20], 1u);
-      }
-    }
+    for (int k = 0; k < 16; ++k)
+      if (group_valid(G, c, k) && x[k] >= cut) atomicAdd(&hist[x[k] >> 20], 1u);
   }
   __syncthreads();
   if (tid < 64) {
@@ -685,17 +712,12 @@ __global__ __launch_bounds__(256) void table_threshold_kernel(const uint32_t* __
   for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0u;
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
-    uint4 v[16];
-    load_group_chunk(g, G, c, v);
+    uint32_t x[16];
+    load_group_chunk(g, G, c, x);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = 4 * (c * 16 * (int)blockDim.x + u * (int)blockDim.x + tid) + e;
-        if (idx < G && (e4[e] >> 20) == bin1) atomicAdd(&hist[(e4[e] >> 9) & (kHistBins - 1)], 1u);
-      }
-    }
+    for (int k = 0; k < 16; ++k)
+      if (group_valid(G, c, k) && (x[k] >> 20) == bin1)
+        atomicAdd(&hist[(x[k] >> 9) & (kHistBins - 1)], 1u);
   }
   __syncthreads();
   if (tid < 64) {
@@ -706,25 +728,25 @@ __global__ __launch_bounds__(256) void table_threshold_kernel(const uint32_t* __
   }
 }
 
-// Grid (ceil(Lmax/4 / kFilterSlice), ceil(Nq/4), B).  Appends the keys whose
-// score reaches the row's bound to the row's candidate list (one atomic per
-// workgroup and row reserves the space; keys past the list capacity are
-// dropped, and the select kernel sees the overflow in the count).
+// Grid (nslices, ceil(Nq/4), B); workgroup w reads blocks [w * fslice, +
+// fslice) of 4 rows (fslice a multiple of kFilterSlice) and writes the keys
+// whose score reaches the row's bound to its own segment of the row's
+// candidate list (segment w, fslice keys: it cannot overflow), and the count
+// to cand_cnt[row][w].  No global atomics: candidates are rare (about 512 of
+// a row's blocks) and contended counters would serialize them.
 __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __restrict__ scores,
                                                            int tstride,
                                                            const uint32_t* __restrict__ thr,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ cand,
                                                            uint32_t* __restrict__ cand_cnt,
-                                                           int Lmax, int Nq, int cap) {
-  __shared__ uint32_t wcnt[4][4];
-  __shared__ uint32_t wbase[4];
+                                                           int Lmax, int Nq, int fslice) {
+  __shared__ uint32_t s_cnt[4];
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
+  const int nslices = gridDim.x;
   const int len = clampi(lens[b], 0, Lmax);
-  const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
-  const int j_begin = slice * kFilterSlice;
-  // All loads first: 4 queries x 2 passes of 1024 blocks, 4 blocks per thread.
-  uint4 v[4][2];
+  const int tid = threadIdx.x;
+  if (tid < 4) s_cnt[tid] = 0u;
   int jend[4];
   uint32_t tau[4];
 #pragma unroll
@@ -734,61 +756,50 @@ __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __res
     const int bt = t >= 0 ? (t >> 2) : 0;
     // rows with at most 512 candidates are finished by the select kernel alone
     const bool live = q0 + qi < Nq && bt > kTopK;
-    jend[qi] = live ? min(j_begin + kFilterSlice, bt) : j_begin;
+    jend[qi] = live ? min((slice + 1) * fslice, bt) : 0;
     tau[qi] = live ? thr[(size_t)b * Nq + qq] : 0u;
-    const uint32_t* srow = scores + ((size_t)b * Nq + qq) * tstride;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int j4 = j_begin + p * 1024 + tid * 4;
-      v[qi][p] = j4 < jend[qi] ? *reinterpret_cast<const uint4*>(srow + j4) : zero_u4();
-    }
   }
-  uint32_t pm[4];  // bit (p*4+e): element passes
+  __syncthreads();
+  for (int j_begin = slice * fslice; j_begin < (slice + 1) * fslice; j_begin += kFilterSlice) {
+    // all loads first: 4 rows x 2 passes of 1024 blocks, 4 blocks per thread
+    uint4 v[4][2];
 #pragma unroll
-  for (int qi = 0; qi < 4; ++qi) {
-    pm[qi] = 0;
-    uint32_t n = 0;
+    for (int qi = 0; qi < 4; ++qi) {
+      const uint32_t* srow = scores + ((size_t)b * Nq + min(q0 + qi, Nq - 1)) * tstride;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t e4[4] = {v[qi][p].x, v[qi][p].y, v[qi][p].z, v[qi][p].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j_begin + p * 1024 + tid * 4 + e;
-        const bool pred = j < jend[qi] && e4[e] >= tau[qi];
-        pm[qi] |= (pred ? 1u : 0u) << (p * 4 + e);
-        n += (uint32_t)__popcll(__ballot(pred));
+      for (int p = 0; p < 2; ++p) {
+        const int j4 = j_begin + p * 1024 + tid * 4;
+        v[qi][p] = j4 < jend[qi] ? *reinterpret_cast<const uint4*>(srow + j4) : zero_u4();
       }
     }
-    if (lane == 0) wcnt[qi][wave] = n;
-  }
-  __syncthreads();
-  if (tid < 4) {
-    const uint32_t tot = wcnt[tid][0] + wcnt[tid][1] + wcnt[tid][2] + wcnt[tid][3];
-    wbase[tid] = (tot && q0 + tid < Nq) ? atomicAdd(&cand_cnt[(size_t)b * Nq + q0 + tid], tot) : 0u;
-  }
-  __syncthreads();
 #pragma unroll
-  for (int qi = 0; qi < 4; ++qi) {
-    if (q0 + qi >= Nq) break;
-    uint32_t off = wbase[qi];
-    for (int w = 0; w < wave; ++w) off += wcnt[qi][w];
-    uint64_t* crow = cand + ((size_t)b * Nq + q0 + qi) * (size_t)cap;
+    for (int qi = 0; qi < 4; ++qi) {
+      uint32_t pm = 0;  // bit (p*4+e): element passes
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t e4[4] = {v[qi][p].x, v[qi][p].y, v[qi][p].z, v[qi][p].w};
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t e4[4] = {v[qi][p].x, v[qi][p].y, v[qi][p].z, v[qi][p].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool pred = (pm[qi] >> (p * 4 + e)) & 1u;
-        const uint64_t mask = __ballot(pred);
-        if (pred) {
+        for (int e = 0; e < 4; ++e) {
           const int j = j_begin + p * 1024 + tid * 4 + e;
-          const uint32_t pos = off + (uint32_t)__popcll(mask & lanemask_lt());
-          if (pos < (uint32_t)cap) crow[pos] = make_key(e4[e], (uint32_t)j);
+          pm |= (j < jend[qi] && e4[e] >= tau[qi] ? 1u : 0u) << (p * 4 + e);
         }
-        off += (uint32_t)__popcll(mask);
+      }
+      if (pm == 0) continue;
+      const size_t row = (size_t)b * Nq + q0 + qi;
+      uint32_t pos = atomicAdd(&s_cnt[qi], (uint32_t)__popc(pm));
+      uint64_t* seg = cand + (row * nslices + slice) * (size_t)fslice;
+      while (pm) {
+        const int bit = __ffs(pm) - 1;
+        pm &= pm - 1;
+        const int p = bit >> 2, e = bit & 3;
+        const uint4 a = p ? v[qi][1] : v[qi][0];  // (selects, not a dynamic register index)
+        const uint32_t sc = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+        seg[pos++] = make_key(sc, (uint32_t)(j_begin + p * 1024 + tid * 4 + e));
       }
     }
   }
+  __syncthreads();
+  if (tid < 4 && q0 + tid < Nq) cand_cnt[((size_t)b * Nq + q0 + tid) * nslices + slice] = s_cnt[tid];
 }
 
 // ------------------------------------------------------------------ STREAM
@@ -1268,12 +1279,20 @@ TopkPath choose_topk_path(const Dims& d, uint32_t flags) {
 namespace {
 int table_stride(const Dims& d) { return ((d.Lmax / 4) + 3) & ~3; }
 int group_stride(const Dims& d) { return (((d.Lmax / 4) + kGroup - 1) / kGroup + 3) & ~3; }
+// Filter slices: at most 256 per row (the select kernel walks one segment per
+// thread pair or more), each a multiple of kFilterSlice blocks.
+int filter_slice(const Dims& d) {
+  const long long nbp = d.Lmax / 4;
+  const long long per = (nbp + 255) / 256;
+  return (int)((per + kFilterSlice - 1) / kFilterSlice * kFilterSlice);
+}
+int filter_slices(const Dims& d) { return (int)((d.Lmax / 4 + filter_slice(d) - 1) / filter_slice(d)); }
 struct TableWs {
   uint32_t* scores;
   uint32_t* gmax;
   uint32_t* thr;
-  uint32_t* cand_cnt;  // zeroed before the filter
-  uint64_t* cand;
+  uint32_t* cand_cnt;  // [rows][filter slices], written by the filter
+  uint64_t* cand;      // [rows][filter slices][filter slice]
 };
 struct StreamWs {
   uint64_t* lists;
@@ -1287,8 +1306,8 @@ TableWs carve_table(const Dims& d, void* ws, size_t* total) {
   w.scores = c.take<uint32_t>(rows * (size_t)table_stride(d));
   w.gmax = c.take<uint32_t>(rows * (size_t)group_stride(d));
   w.thr = c.take<uint32_t>(rows);
-  w.cand_cnt = c.take<uint32_t>(rows);
-  w.cand = c.take<uint64_t>(rows * kSelCap);
+  w.cand_cnt = c.take<uint32_t>(rows * filter_slices(d));
+  w.cand = c.take<uint64_t>(rows * (size_t)filter_slices(d) * filter_slice(d));
   if (total) *total = c.off;
   return w;
 }
@@ -1315,9 +1334,9 @@ size_t topk_workspace_bytes(const Dims& d, TopkPath path) {
 
 void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n) {
   if (path == TopkPath::kTable) {
-    TableWs w = carve_table(d, ws, nullptr);
-    *ptr = w.cand_cnt;
-    *n = (size_t)d.B * d.Nq;
+    (void)ws;  // nothing to clear: every count is written by the filter
+    *ptr = nullptr;
+    *n = 0;
   } else {
     *ptr = nullptr;
     *n = 0;
@@ -1332,20 +1351,18 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   if (path == TopkPath::kTable) {
     TableWs w = carve_table(d, ws, nullptr);
     const int ts = table_stride(d), gs = group_stride(d);
+    const int fs = filter_slice(d), nfs = filter_slices(d);
     const size_t rows = (size_t)d.B * d.Nq;
-    if (!ws_zeroed)
-      QSA_LAUNCH(fill_u32_kernel, dim3((unsigned)std::min<size_t>((rows + 255) / 256, 4096)),
-                 dim3(256), 0, s, w.cand_cnt, rows, 0u);
+    (void)ws_zeroed;
     const unsigned qg = (unsigned)((d.Nq + 3) / 4);
     const dim3 grid_s((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
-    const dim3 grid_f((unsigned)((d.Lmax / 4 + kFilterSlice - 1) / kFilterSlice), qg, (unsigned)d.B);
     QSA_LAUNCH(score_table_kernel, grid_s, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
                w.gmax, gs, d.Lmax, d.Nq);
-    QSA_LAUNCH(table_threshold_kernel, dim3((unsigned)rows), dim3(256), 0, s, w.gmax, gs, lens,
-               w.thr, d.Lmax, d.Nq);
-    QSA_LAUNCH(table_filter_kernel, grid_f, dim3(256), 0, s, w.scores, ts, w.thr, lens, w.cand,
-               w.cand_cnt, d.Lmax, d.Nq, kSelCap);
-    QSA_LAUNCH(select_kernel<false>, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, 1, kSelCap,
+    QSA_LAUNCH(table_threshold_kernel, dim3((unsigned)rows), dim3(kThrThreads), 0, s, w.gmax, gs,
+               lens, w.thr, d.Lmax, d.Nq);
+    QSA_LAUNCH(table_filter_kernel, dim3((unsigned)nfs, qg, (unsigned)d.B), dim3(256), 0, s,
+               w.scores, ts, w.thr, lens, w.cand, w.cand_cnt, d.Lmax, d.Nq, fs);
+    QSA_LAUNCH(select_kernel<false>, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, nfs, fs,
                (const int32_t*)nullptr, w.scores, ts, q_idx, k_cmp, lens, sel, n_sel, d.Lmax,
                d.Nq);
   } else {
