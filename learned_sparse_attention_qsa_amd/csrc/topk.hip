@@ -28,17 +28,17 @@
 //
 //  STREAM (many queries, prefill-shaped): a workgroup holds 64 queries x 4
 //  heads stationary in registers and streams the compressed keys through LDS
-//  in tiles of 64 blocks, MFMA 32x32x16.  Each query keeps a threshold tau =
-//  score of the 512th best key seen so far; because blocks arrive in
-//  ascending id order, a new block can only enter the top 512 if its score
-//  is strictly greater than tau (an equal score loses the tie to an earlier
-//  block).  Survivors are appended to a per-query list in HBM; when a list
-//  nears its capacity the owning wavefront selects its top 512 in place and
-//  raises tau.  No score table is written.
+//  in tiles of 64 blocks, MFMA 32x32x16.  A first pass over 1/32 of the tiles
+//  sets each query's bound tau (the lower bin edge of its 40th best sample
+//  score); the second pass keeps the blocks scoring strictly above tau
+//  (about 1,300 per query).  If at least 512 blocks pass, no block at or
+//  below tau can be in the top 512; the select kernel checks this.  No
+//  score table is written.
 //
-// Both engines finish with the same LDS radix select; rows the fast path
-// cannot hold (extreme ties in the table engine) are finished by an exact
-// fallback that recomputes or re-reads the whole row.
+// Both engines finish with the same select kernel (a register sort for short
+// lists, an LDS radix select otherwise); rows whose candidate list cannot be
+// trusted (an overflow, or fewer than 512 candidates) are finished by an
+// exact fallback that recomputes or re-reads the whole row.
 #include "common.h"
 #include "internal.h"
 
@@ -50,8 +50,7 @@ constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine
 constexpr int kFilterSlice = 2048; // blocks per filter workgroup (table engine)
 constexpr int kGroup = 16;         // blocks per group maximum (table engine)
 constexpr int kSelCap = 8192;      // candidates a select workgroup holds in LDS
-constexpr int kHistW = 256;        // stream engine: threshold-tracking bins per query
-constexpr int kHyst = 64;          // stream engine: new counts between threshold updates
+constexpr int kHistW = 256;        // stream engine: sample-histogram bins per query
 constexpr int kStreamTile = 64;    // blocks per key tile (stream engine)
 constexpr int kStreamQ = 64;       // queries per stream workgroup (16 per wavefront)
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -803,64 +802,39 @@ __global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __res
 }
 
 // ------------------------------------------------------------------ STREAM
-// In-place: keep the 512 largest of the n (> 512) distinct keys of `list`
-// at its front; returns the 512th largest key.  One wavefront; hist is a
-// 256-entry LDS scratch of that wavefront.
-__device__ uint64_t wave_compact(uint64_t* list, uint32_t n, uint32_t* hist) {
-  const int lane = lane_id();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  uint64_t prefix = 0, pmask = 0;
-  uint32_t k = kTopK;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
-    wave_sync_lds();
-    for (uint32_t i = lane; i < n; i += 64) {
-      const uint64_t key = list[i];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
-    }
-    wave_sync_lds();
-    uint32_t d, above;
-    wave_find_digit(hist, k, d, above);
-    k -= above;
-    prefix |= (uint64_t)d << shift;
-    pmask |= 0xffull << shift;
-    wave_sync_lds();
-  }
-  uint32_t w = 0;
-  for (uint32_t base = 0; base < n; base += 64) {
-    const uint32_t i = base + lane;
-    const uint64_t key = i < n ? list[i] : 0ull;
-    const bool keep = i < n && key >= prefix;
-    const uint64_t m = __ballot(keep);
-    if (keep) list[w + (uint32_t)__popcll(m & lanemask_lt())] = key;
-    w += (uint32_t)__popcll(m);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  return prefix;
-}
-
-// Stream engine, per query: threshold tau (a score; below 0 = accept all)
-// and a 256-bin histogram of the appended scores at bf16 resolution, bin i =
-// (score bits >> 16) - base (the last bin also holds everything above;
-// scores below the base go to a spare 257th bin that is never read).  Every
-// counted element has score bits >= base<<16 and was appended; so if the
-// bins from m up hold >= 512 counts, at least 512 blocks seen so far score
-// >= (base+m)<<16, and any later block scoring no more than that is beaten by
-// all of them (an equal score loses on the higher block id): tau can rise to
-// (base+m)<<16.
+// Stream engine.  A workgroup holds 64 queries x 4 heads stationary in
+// registers and streams the compressed keys through an LDS ring in tiles of
+// 64 blocks (MFMA 32x32x16).  Two phases over the same pipeline:
 //
-// Survivors are first queued in LDS (one 8-byte entry: score, local query,
-// block id) by the scoring lanes; once per tile the queue is drained with
-// all 64 lanes busy: list slot, list store, histogram update.  That keeps
-// the per-survivor work of the scoring pass to a handful of instructions.
+//  1. sample: every kSampleStride-th tile.  Each query histograms its sample
+//     scores (256 bins, 32 per octave, from a base four octaves below the
+//     best score of the first sample tile) and takes as its bound tau the
+//     lower edge of the bin holding its kSampleRank-th best sample score.
+//  2. filter: every tile; a block is a candidate if its score is strictly
+//     above tau.  Candidates are queued in LDS by the scoring lanes and
+//     drained 64 at a time into the query's list in HBM.
+//
+// tau is an estimate, so the result is verified, not assumed: if at least
+// 512 blocks score strictly above tau, every block at or below tau is beaten
+// by 512 others and the list holds the whole top 512; the select kernel then
+// finishes exactly.  Otherwise (or if a list overflowed) that row takes the
+// exact whole-row path.  With 1/32 of the tiles sampled and rank 40, about
+// 40 x 32 = 1,280 blocks per query pass, and the bound fails only when over
+// 40 of the samples lie above the true 512th score, about 1e-7 per query for
+// independent scores.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kRing = 8;        // LDS tile slots of the stream engine
-constexpr int kListCap = 16384; // candidate list entries per query
+constexpr int kRing = 8;           // LDS tile slots of the stream engine
+constexpr int kListCap = 4096;     // candidate list entries per query
+constexpr int kSampleStride = 32;  // one sample tile in 32
+constexpr int kSampleRank = 40;    // tau: the 40th best sample score (bin edge)
+// sample histogram: bins of (score bits >> 18), i.e. 32 per octave, 256 bins =
+// 8 octaves from a base 4 octaves (128 bins) below the first sample tile's best
+constexpr int kSampleShift = 18;
+constexpr int kSampleBase = 128;
 // survivors one tile can add to a wavefront's queue, plus fewer than 64 held over
 constexpr int kQueue = kStreamTile * 16 + 64;
-constexpr int kHistWords = kHistW / 2 + 1;  // 256 packed bins + the spare bin
+constexpr int kHistWords = kHistW / 2 + 1;  // 256 packed 16-bit bins + the spare bin
 
 // Barriers of the stream engine: no wait on vector-memory stores, so list
 // appends stay in flight across tiles.
@@ -873,6 +847,10 @@ __device__ __forceinline__ void stream_barrier_loader() {
   asm volatile("s_waitcnt vmcnt(40) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 static_assert(8 * (kRing - 3) == 40, "loader wait count");
+
+// Tile of the workgroup's stream at position i: the ns sample tiles first,
+// then every tile.
+__device__ __forceinline__ int stream_tile(int i, int ns) { return i < ns ? i * kSampleStride : i - ns; }
 
 // Loader wavefront: copy one 64-block tile of compressed keys straight from
 // HBM into ring slot `slot` (8 KiB, eight 16-byte-per-lane DMA loads).  The
@@ -919,29 +897,59 @@ __device__ __forceinline__ void mma_half(const bf16x8 (&bf)[4], const bf16x8 (&A
 __device__ __forceinline__ int rdl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
 // Per-wavefront state.  Slot (rt, c) of a lane scores local query
-// rt*8 + c*2 + (lane >> 5); the lane keeps a copy of that query's tau.
+// rt*8 + c*2 + (lane >> 5); the lane keeps that query's base / tau.
 struct Stream {
-  float tau_l[2][4];
-  int tau_v, base_v, trig_v;  // lane q < 16: query q's tau bits, base, next update point
+  float tau_l[2][4];          // filter bound of the slot's query (phase 2)
+  int base_l[2][4];           // histogram base of the slot's query (phase 1)
   int tq0;                    // position of local query (lane >> 5)
   int nq_left;                // queries of the batch from local query (lane >> 5) on
   uint64_t* lists;            // list of local query 0; query q at + q * kListCap
-  uint32_t (*h)[kHistWords];  // the wavefront's 16 histograms
-  uint32_t* hc;               // 16 counts currently in the histograms
+  uint32_t (*h)[kHistWords];  // the wavefront's 16 sample histograms
   uint32_t* cnt;              // 16 list lengths
-  uint32_t* mx;               // 16 best scores seen before the base is set
-  uint32_t* rs;               // 256-word radix scratch
-  uint64_t* queue;            // kQueue survivors of the current tile
+  uint32_t* mx;               // 16 best scores of the first sample tile
+  uint64_t* queue;            // survivors not yet drained
 };
 
-__device__ __forceinline__ int slot_query(int rt, int c) { return rt * 8 + c * 2 + (lane_id() >> 5); }
+__device__ __forceinline__ int slot_off(int rt, int c) { return rt * 8 + c * 2; }
 
+// Causal / batch mask of slot (rt, c) for block j.
+__device__ __forceinline__ bool slot_valid(const Stream& st, int rt, int c, int j) {
+  const int off = slot_off(rt, c);
+  const int tq = st.tq0 + off;
+  return off < st.nq_left && tq >= 0 && j < (tq >> 2);
+}
 
-// Filter one 32-block half against tau; queue the survivors behind the qn
-// already queued this tile.  kFull: every block of the tile is below every
-// query's own block.  Returns the new queue length.
+// Phase 1 epilogue of one 32-block half: histogram the sample scores (first
+// sample tile: track each query's best score instead).
+template <bool kFirst>
+__device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[2], int tile, int ct) {
+  const int lane = lane_id();
+  const int j = tile * kStreamTile + ct * 32 + (lane & 31);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t bits = relu_sum_bits(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
+                                          acc[rt][4 * c + 3]);
+      const bool valid = slot_valid(st, rt, c, j);
+      const int q = slot_off(rt, c) + (lane >> 5);
+      if (kFirst) {
+        if (valid) atomicMax(&st.mx[q], bits);
+      } else {
+        const int bin = (int)(bits >> kSampleShift) - st.base_l[rt][c];
+        if (valid && bin >= 0) {
+          const int bb = min(bin, kHistW - 1);
+          atomicAdd(&st.h[q][bb >> 1], 1u << ((bb & 1) * 16));
+        }
+      }
+    }
+}
+
+// Phase 2 epilogue of one 32-block half: queue the blocks scoring above
+// their query's bound behind the qn already queued.  kFull: every block of
+// the tile is below every query's own block.  Returns the new queue length.
 template <bool kFull>
-__device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2], int tile, int ct,
+__device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2], int tile, int ct,
                                                int qn) {
   const int lane = lane_id();
   const int j = tile * kStreamTile + ct * 32 + (lane & 31);
@@ -949,7 +957,7 @@ __device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2
   bool pass[2][4];
   uint64_t any = 0;
   // scores and pass tests of all 8 slots first, without branches, so the
-  // compiler can interleave them
+  // compiler can interleave them with the MFMAs
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -957,11 +965,7 @@ __device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2
       sc[rt][c] = relu_sum(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
                            acc[rt][4 * c + 3]);
       bool p = sc[rt][c] > st.tau_l[rt][c];
-      if (!kFull) {
-        const int off = rt * 8 + c * 2;
-        const int tq = st.tq0 + off;
-        p = p && off < st.nq_left && tq >= 0 && j < (tq >> 2);
-      }
+      if (!kFull) p = p && slot_valid(st, rt, c, j);
       pass[rt][c] = p;
       any |= __ballot(p);
     }
@@ -976,180 +980,116 @@ __device__ __forceinline__ int stream_epilogue(Stream& st, const f32x16 (&acc)[2
         const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)qn));
         st.queue[pos] = ((uint64_t)__float_as_uint(sc[rt][c]) << 32) |
-                        (uint64_t)(tag + ((uint32_t)(rt * 8 + c * 2) << 28));
+                        (uint64_t)(tag + ((uint32_t)slot_off(rt, c) << 28));
       }
       qn += __popcll(m);
     }
   return qn;
 }
 
-// Drain the tile's queue: append every survivor to its query's list and
-// count it in the histogram (first tile: only track the best score).
-template <bool kFirst>
+// Append the queued survivors to their queries' lists, 64 at a time.
 __device__ __forceinline__ void stream_drain(Stream& st, int qn) {
   const int lane = lane_id();
   wave_sync_lds();
   for (int i0 = 0; i0 < qn; i0 += 64) {
     const int i = i0 + lane;
-    const uint64_t e = st.queue[min(i, qn - 1)];
-    const uint32_t bits = (uint32_t)(e >> 32);
-    const uint32_t lo = (uint32_t)e;
-    const int q = (int)(lo >> 28);
-    const uint32_t j = lo & 0x0fffffffu;
-    // (a lane-crossing read takes its value only from active lanes: do it
-    // before the tail lanes drop out)
-    const int qbase = kFirst ? 0 : __shfl(st.base_v, q);
     if (i < qn) {
+      const uint64_t e = st.queue[i];
+      const uint32_t lo = (uint32_t)e;
+      const int q = (int)(lo >> 28);
       const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
-      // (the upkeep compacts a list before it can fill: pos < kListCap)
-      st.lists[(size_t)q * kListCap + min(pos, (uint32_t)kListCap - 1)] = make_key(bits, j);
-      if (kFirst) {
-        atomicMax(&st.mx[q], bits);
-      } else {
-        const int bin = (int)(bits >> 16) - qbase;
-        const int bb = bin < 0 ? kHistW : min(bin, kHistW - 1);
-        atomicAdd(&st.h[q][bb >> 1], 1u << ((bb & 1) * 16));
-        atomicAdd(&st.hc[q], bin < 0 ? 0u : 1u);
-      }
+      // a list that overflows keeps counting: the select kernel sees it
+      if (pos < (uint32_t)kListCap)
+        st.lists[(size_t)q * kListCap + pos] = make_key((uint32_t)(e >> 32), lo & 0x0fffffffu);
     }
   }
   wave_sync_lds();
 }
 
-// New tau / base of local query i: refresh the lanes' copies.
-__device__ __forceinline__ void stream_set_query(Stream& st, int i, int tau_bits, int base) {
+// After the sample phase: each query's bound from its histogram.  Sets the
+// lanes' slot copies and returns, on lane q < 16, the bits of query q's bound.
+__device__ __forceinline__ int stream_set_bounds(Stream& st, int bt_q_lane) {
   const int lane = lane_id();
-  if (lane == i) {
-    st.tau_v = tau_bits;
-    st.base_v = base;
+  int tau_v = 0;
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t* h = st.h[i];
+    const uint32_t w0 = h[2 * lane], w1 = h[2 * lane + 1];
+    uint32_t total = (w0 & 0xffffu) + (w0 >> 16) + (w1 & 0xffffu) + (w1 >> 16);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) total += (uint32_t)__shfl_xor((int)total, off);
+    int bound;
+    if (rdl(bt_q_lane, i) <= kListCap) {
+      bound = (int)0xbf800000u;  // -1.0f: the whole row fits the list, keep every block
+    } else if (total >= (uint32_t)kSampleRank) {
+      int m;
+      uint32_t sfx;
+      wave_suffix_bin4(w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16, kSampleRank, m, sfx);
+      bound = (max(0, (int)(st.mx[i] >> kSampleShift) - kSampleBase) + m) << kSampleShift;  // bin edge
+    } else {
+      bound = 0;  // too few samples above the base: keep every positive score
+    }
+    if (lane == i) tau_v = bound;
   }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      if (slot_query(rt, c) == i) st.tau_l[rt][c] = __uint_as_float((uint32_t)tau_bits);
+      st.tau_l[rt][c] = __int_as_float(__shfl(tau_v, slot_off(rt, c) + (lane >> 5)));
+  return tau_v;
 }
 
-// Raise tau of local query i from its histogram (one wavefront).
-__device__ __forceinline__ void stream_raise_tau(Stream& st, int i) {
-  const int lane = lane_id();
-  uint32_t* h = st.h[i];
-  const uint32_t w0 = h[2 * lane], w1 = h[2 * lane + 1];
-  int m;
-  uint32_t total;
-  wave_suffix_bin4(w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16, kTopK, m, total);
-  if (m > 0) {
-    uint32_t nw[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int src = 4 * lane + 2 * half + e + m;
-        uint32_t cc = 0;
-        if (src < kHistW) cc = (h[src >> 1] >> ((src & 1) * 16)) & 0xffffu;
-        packed |= cc << (16 * e);
-      }
-      nw[half] = packed;
-    }
-    wave_sync_lds();
-    h[2 * lane] = nw[0];
-    h[2 * lane + 1] = nw[1];
-  }
-  const int nb = rdl(st.base_v, i) + m;
-  const int nt = max(nb << 16, rdl(st.tau_v, i));
-  if (lane == 0) st.hc[i] = total;
-  if (lane == i) st.trig_v = (int)total + kHyst;
-  stream_set_query(st, i, nt, nb);
-  wave_sync_lds();
-}
-
-// Rare: the list of local query i is nearly full.  Keep its 512 best keys,
-// set tau to the exact 512th score and rebuild the histogram from them.
-__device__ __forceinline__ void stream_compact(Stream& st, int i) {
-  const int lane = lane_id();
-  uint64_t* list = st.lists + (size_t)i * kListCap;
-  const uint32_t n = st.cnt[i];
-  const uint64_t kth = wave_compact(list, n, st.rs);
-  const int tau_bits = (int)(uint32_t)(kth >> 32);
-  const int base = tau_bits >> 16;
-  st.h[i][2 * lane] = 0u;
-  st.h[i][2 * lane + 1] = 0u;
-  if (lane == 0) st.h[i][kHistW / 2] = 0u;
-  wave_sync_lds();
-  for (int k2 = lane; k2 < kTopK; k2 += 64) {
-    const uint32_t sb = (uint32_t)(list[k2] >> 32);
-    const int bin = min((int)(sb >> 16) - base, kHistW - 1);
-    atomicAdd(&st.h[i][bin >> 1], 1u << ((bin & 1) * 16));
-  }
-  if (lane == 0) {
-    st.hc[i] = kTopK;
-    st.cnt[i] = kTopK;
-  }
-  if (lane == i) st.trig_v = kTopK + kHyst;
-  stream_set_query(st, i, max(tau_bits, rdl(st.tau_v, i)), base);
-  wave_sync_lds();
-}
-
-// After a tile: raise tau where enough new counts arrived, compact nearly
-// full lists (rare).
-__device__ __forceinline__ void stream_upkeep(Stream& st) {
-  const int lane = lane_id();
-  const uint32_t hc = lane < 16 ? st.hc[lane] : 0u;
-  const uint32_t cnt = lane < 16 ? st.cnt[lane] : 0u;
-  uint64_t r = __ballot(lane < 16 && (int)hc >= st.trig_v);
-  while (r) {
-    const int i = __builtin_ctzll(r);
-    r &= r - 1;
-    stream_raise_tau(st, i);
-  }
-  // one tile adds at most 64 entries to a list
-  uint64_t f = __ballot(lane < 16 && cnt > (uint32_t)(kListCap - 2 * kStreamTile));
-  while (f) {
-    const int i = __builtin_ctzll(f);
-    f &= f - 1;
-    stream_compact(st, i);
-  }
-}
-
-// One tile k: MFMAs of its second half, filter of its first half (computed
-// in the previous step), MFMAs of the next tile's first half, filter of the
-// second half; then, once a full wavefront's worth of survivors is queued
-// (or on the first tile), the queue drain and the per-query upkeep; barrier.
-template <bool kFirst, bool kFull>
-__device__ __forceinline__ void stream_step(Stream& st, const bf16x8 (&A)[2][4],
-                                            uint4 (*ring)[kStreamTile * 8], f32x16 (&accA)[2],
-                                            f32x16 (&accB)[2], int k, int ntiles, int& qn) {
-  const int lane = lane_id();
+// One stream position k (tile `tile`): the MFMAs of its second half, the
+// epilogue of its first half (computed by the previous position), the MFMAs
+// of the next position's first half, the epilogue of the second half; then
+// a drain of the survivor queue when it holds a wavefront's worth, and the
+// barrier.  kPhase: 0 the first sample tile, 1 a sample tile, 2 a filter tile
+// below every query's own block, 3 a masked filter tile.  Each phase runs in
+// a loop of its own, so the epilogue interleaves with the MFMAs.
+template <int kPhase>
+__device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[2][4],
+                                           uint4 (*ring)[kStreamTile * 8], f32x16 (&accA)[2],
+                                           f32x16 (&accB)[2], int k, int tile, int& qn) {
   bf16x8 bf[4], bn[4];
   load_b(ring[k % kRing], 1, bf);
-  // (the slot of tile k+1 is always LDS of the ring; unused past the end)
+  // (the slot of position k+1 is always LDS of the ring; unused past the end)
   load_b(ring[(k + 1) % kRing], 0, bn);
   mma_half(bf, A, accB);
-  qn = stream_epilogue<kFull>(st, accA, k, 0, qn);
-  // (unconditional, also past the last tile: a conditional update would make
-  // the compiler copy the accumulators, and the copies wait for the MFMAs)
+  if (kPhase <= 1) {
+    sample_epilogue<kPhase == 0>(st, accA, tile, 0);
+  } else {
+    qn = filter_epilogue<kPhase == 2>(st, accA, tile, 0, qn);
+  }
+  // (unconditional, also past the last position: a conditional update would
+  // make the compiler copy the accumulators, and the copies wait for the MFMAs)
   mma_half(bn, A, accA);
-  qn = stream_epilogue<kFull>(st, accB, k, 1, qn);
-  if (kFirst) {
-    if (qn > 0) stream_drain<true>(st, qn);
-    qn = 0;
-    // histogram base: one octave below the best score of the first tile
+  if (kPhase <= 1) {
+    sample_epilogue<kPhase == 0>(st, accB, tile, 1);
+  } else {
+    qn = filter_epilogue<kPhase == 2>(st, accB, tile, 1, qn);
+    if (qn >= 64) {
+      stream_drain(st, qn);
+      qn = 0;
+    }
+  }
+  if (kPhase == 0) {
+    // histogram base: four octaves below the best score of the first sample
+    // tile (robust to a first tile holding outlier blocks)
+    const int lane = lane_id();
     wave_sync_lds();
-    const int base = lane < 16 ? max(0, (int)(st.mx[lane] >> 16) - 128) : 0;
-    for (int i = 0; i < 16; ++i) stream_set_query(st, i, (int)0xbf800000u, rdl(base, i));
-  } else if (qn >= 64) {
-    stream_drain<false>(st, qn);
-    qn = 0;
-    stream_upkeep(st);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st.base_l[rt][c] =
+            max(0, (int)(st.mx[slot_off(rt, c) + (lane >> 5)] >> kSampleShift) - kSampleBase);
   }
   stream_barrier_compute();
 }
 
 // Grid (ceil(Nq/64), B); 5 wavefronts: 4 compute wavefronts x 16 queries and
 // one loader wavefront feeding an 8-slot LDS ring of key tiles.  Compute
-// wavefronts run tile k+1's MFMAs before tile k's filtering (double-buffered
-// accumulators), so matrix and vector work overlap.
+// wavefronts run the next half-tile's MFMAs before the current half's
+// epilogue (double-buffered accumulators), so matrix and vector work overlap.
 __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
                                                            const uint16_t* __restrict__ k_cmp,
                                                            const int32_t* __restrict__ lens,
@@ -1159,10 +1099,8 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
                                                            int Nq) {
   __shared__ uint4 ring[kRing][kStreamTile * 8];
   __shared__ uint32_t s_h[kStreamQ][kHistWords];
-  __shared__ uint32_t s_hc[kStreamQ];
   __shared__ uint32_t s_mx[kStreamQ];
   __shared__ uint32_t s_cnt[kStreamQ];
-  __shared__ uint32_t s_rs[4][256];
   __shared__ uint64_t s_queue[4][kQueue];
 
   const int qbase = blockIdx.x * kStreamQ, b = blockIdx.y;
@@ -1172,20 +1110,22 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
   const int t_last = query_t(len, Nq, min(qbase + kStreamQ - 1, Nq - 1));
   const int bt_wg = t_last >= 0 ? (t_last >> 2) : 0;
   const int ntiles = (bt_wg + kStreamTile - 1) / kStreamTile;
+  const int ns = (ntiles + kSampleStride - 1) / kSampleStride;  // sample tiles
+  const int nseq = ns + ntiles;                                  // stream positions
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
   for (int i = tid; i < kStreamQ * kHistWords; i += blockDim.x) (&s_h[0][0])[i] = 0u;
   if (tid < kStreamQ) {
-    s_hc[tid] = 0u;
     s_mx[tid] = 0u;
     s_cnt[tid] = 0u;
   }
 
   if (wave == 4) {
     // ---------------- loader
-    for (int t = 0; t < kRing - 1; ++t) dma_tile(ring[t], kb, t, bt_wg);
+    for (int i = 0; i < kRing - 1; ++i) dma_tile(ring[i], kb, i < nseq ? stream_tile(i, ns) : 0, bt_wg);
     stream_barrier_loader();
-    for (int k = 0; k < ntiles; ++k) {
-      dma_tile(ring[(k + kRing - 1) % kRing], kb, k + kRing - 1, bt_wg);
+    for (int k = 0; k < nseq; ++k) {
+      const int i = k + kRing - 1;
+      dma_tile(ring[i % kRing], kb, i < nseq ? stream_tile(i, ns) : 0, bt_wg);
       stream_barrier_loader();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the workgroup
@@ -1196,10 +1136,8 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
   const int wq0 = qbase + wave * 16;
   Stream st;
   st.h = &s_h[wave * 16];
-  st.hc = &s_hc[wave * 16];
   st.mx = &s_mx[wave * 16];
   st.cnt = &s_cnt[wave * 16];
-  st.rs = s_rs[wave];
   st.queue = s_queue[wave];
   // Stationary A fragments: 2 row tiles x 4 k-steps.  Row (lane & 31) of row
   // tile rt is query wq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
@@ -1222,46 +1160,48 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int qq = wq0 + slot_query(rt, c);
+      const int qq = wq0 + slot_off(rt, c) + (lane >> 5);
       const int t = query_t(len, Nq, qq);
       bt_min = min(bt_min, (qq < Nq && t >= 0) ? (t >> 2) : 0);
-      st.tau_l[rt][c] = -1.f;
+      st.base_l[rt][c] = 0;
     }
   // tiles entirely below every query's own block need no causal mask
   for (int off = 32; off >= 1; off >>= 1) bt_min = min(bt_min, __shfl_xor(bt_min, off));
-  st.tau_v = (int)0xbf800000u;  // bits of -1.0f (as int: negative, below every score)
-  st.base_v = 0;
-  st.trig_v = kTopK + kHyst;
+  // lane q < 16: own block of local query q
+  const int tl = query_t(len, Nq, wq0 + lane);
+  const int bt_q_lane = (lane < 16 && wq0 + lane < Nq && tl >= 0) ? (tl >> 2) : 0;
   // Settle the A-fragment loads now, so no wait on vector memory (which
   // would also wait for the list appends) is needed inside the tile loop.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   stream_barrier_compute();
 
-  // Pipeline over 32-block halves: the MFMAs of the next half run, and its
-  // key fragments are read from LDS, while the current half is filtered.
-  // Three loops: the first tile, the tiles below every query's own block
-  // (no causal mask), and the last tiles (masked).
+  // Pipeline over 32-block halves: position k's second half and position
+  // k+1's first half are in flight while position k's first half is filtered.
   f32x16 accA[2], accB[2];
-  int qn = 0;  // survivors queued, not yet drained
-  if (ntiles > 0) {
+  int qn = 0;     // survivors queued, not yet drained
+  int tau_q = 0;  // lane q < 16: bits of local query q's bound
+  const int nfull = min(ntiles, bt_min / kStreamTile);
+  if (nseq > 0) {
     bf16x8 bf[4];
     load_b(ring[0], 0, bf);
     mma_half(bf, A, accA);
   }
-  const int nfull = min(ntiles, bt_min / kStreamTile);
-  if (ntiles > 0) {
-    if (nfull > 0)
-      stream_step<true, true>(st, A, ring, accA, accB, 0, ntiles, qn);
-    else
-      stream_step<true, false>(st, A, ring, accA, accB, 0, ntiles, qn);
+  if (nseq > 0) stream_pos<0>(st, A, ring, accA, accB, 0, 0, qn);
+  for (int k = 1; k < ns; ++k) stream_pos<1>(st, A, ring, accA, accB, k, k * kSampleStride, qn);
+  if (nseq > 0) {
+    wave_sync_lds();
+    tau_q = stream_set_bounds(st, bt_q_lane);
   }
-  for (int k = 1; k < nfull; ++k) stream_step<false, true>(st, A, ring, accA, accB, k, ntiles, qn);
-  for (int k = max(1, nfull); k < ntiles; ++k)
-    stream_step<false, false>(st, A, ring, accA, accB, k, ntiles, qn);
-  if (qn > 0) stream_drain<false>(st, qn);
+  for (int k = ns; k < ns + nfull; ++k) stream_pos<2>(st, A, ring, accA, accB, k, k - ns, qn);
+  for (int k = ns + nfull; k < nseq; ++k) stream_pos<3>(st, A, ring, accA, accB, k, k - ns, qn);
+  if (qn > 0) stream_drain(st, qn);
   wave_sync_lds();
-  if (lane < 16 && wq0 + lane < Nq) list_cnt[(size_t)b * Nq + wq0 + lane] = st.cnt[lane];
-  if (lane < 16 && wq0 + lane < Nq) tau_out[(size_t)b * Nq + wq0 + lane] = st.tau_v;
+  if (lane < 16 && wq0 + lane < Nq) {
+    list_cnt[(size_t)b * Nq + wq0 + lane] = st.cnt[lane];
+    // every list entry scores strictly above the bound: the select kernel
+    // keeps keys at or above it, i.e. all of them
+    tau_out[(size_t)b * Nq + wq0 + lane] = tau_q;
+  }
 }
 
 }  // namespace
