@@ -955,6 +955,7 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
   const int j = tile * kStreamTile + ct * 32 + (lane & 31);
   float sc[2][4];
   bool pass[2][4];
+  uint64_t mk[2][4];  // the slots' ballots (scalar registers)
   uint64_t any = 0;
   // scores and pass tests of all 8 slots first, without branches, so the
   // compiler can interleave them with the MFMAs
@@ -967,15 +968,18 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
       bool p = sc[rt][c] > st.tau_l[rt][c];
       if (!kFull) p = p && slot_valid(st, rt, c, j);
       pass[rt][c] = p;
-      any |= __ballot(p);
+      mk[rt][c] = __ballot(p);
+      any |= mk[rt][c];
     }
   if (any == 0) return qn;
   const uint32_t tag = (uint32_t)j | ((uint32_t)(lane >> 5) << 28);
+  // only slots with survivors do any vector work
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint64_t m = __ballot(pass[rt][c]);
+      const uint64_t m = mk[rt][c];
+      if (m == 0) continue;
       if (pass[rt][c]) {
         const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)qn));
@@ -1048,11 +1052,15 @@ __device__ __forceinline__ int stream_set_bounds(Stream& st, int bt_q_lane) {
 template <int kPhase>
 __device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[2][4],
                                            uint4 (*ring)[kStreamTile * 8], f32x16 (&accA)[2],
-                                           f32x16 (&accB)[2], int k, int tile, int& qn) {
-  bf16x8 bf[4], bn[4];
-  load_b(ring[k % kRing], 1, bf);
+                                           f32x16 (&accB)[2], bf16x8 (&bf)[4], int k, int tile,
+                                           int& qn) {
+  // bf: this position's second-half fragments, read during the previous
+  // position.  The next position's tile has landed (the loader waits for
+  // two tiles ahead), so both of its halves are read here, early.
+  bf16x8 bn[4], bf_next[4];
   // (the slot of position k+1 is always LDS of the ring; unused past the end)
   load_b(ring[(k + 1) % kRing], 0, bn);
+  load_b(ring[(k + 1) % kRing], 1, bf_next);
   mma_half(bf, A, accB);
   if (kPhase <= 1) {
     sample_epilogue<kPhase == 0>(st, accA, tile, 0);
@@ -1071,6 +1079,8 @@ __device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[2][4],
       qn = 0;
     }
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bf[i] = bf_next[i];
   if (kPhase == 0) {
     // histogram base: four octaves below the best score of the first sample
     // tile (robust to a first tile holding outlier blocks)
@@ -1181,19 +1191,21 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
   int qn = 0;     // survivors queued, not yet drained
   int tau_q = 0;  // lane q < 16: bits of local query q's bound
   const int nfull = min(ntiles, bt_min / kStreamTile);
+  bf16x8 bf[4];
   if (nseq > 0) {
-    bf16x8 bf[4];
-    load_b(ring[0], 0, bf);
-    mma_half(bf, A, accA);
+    bf16x8 b0[4];
+    load_b(ring[0], 0, b0);
+    load_b(ring[0], 1, bf);
+    mma_half(b0, A, accA);
   }
-  if (nseq > 0) stream_pos<0>(st, A, ring, accA, accB, 0, 0, qn);
-  for (int k = 1; k < ns; ++k) stream_pos<1>(st, A, ring, accA, accB, k, k * kSampleStride, qn);
+  if (nseq > 0) stream_pos<0>(st, A, ring, accA, accB, bf, 0, 0, qn);
+  for (int k = 1; k < ns; ++k) stream_pos<1>(st, A, ring, accA, accB, bf, k, k * kSampleStride, qn);
   if (nseq > 0) {
     wave_sync_lds();
     tau_q = stream_set_bounds(st, bt_q_lane);
   }
-  for (int k = ns; k < ns + nfull; ++k) stream_pos<2>(st, A, ring, accA, accB, k, k - ns, qn);
-  for (int k = ns + nfull; k < nseq; ++k) stream_pos<3>(st, A, ring, accA, accB, k, k - ns, qn);
+  for (int k = ns; k < ns + nfull; ++k) stream_pos<2>(st, A, ring, accA, accB, bf, k, k - ns, qn);
+  for (int k = ns + nfull; k < nseq; ++k) stream_pos<3>(st, A, ring, accA, accB, bf, k, k - ns, qn);
   if (qn > 0) stream_drain(st, qn);
   wave_sync_lds();
   if (lane < 16 && wq0 + lane < Nq) {
