@@ -945,46 +945,54 @@ __device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[
     }
 }
 
-// Phase 2 epilogue of one 32-block half: queue the blocks scoring above
-// their query's bound behind the qn already queued.  kFull: every block of
-// the tile is below every query's own block.  Returns the new queue length.
-template <bool kFull>
-__device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2], int tile, int ct,
-                                               int qn) {
-  const int lane = lane_id();
-  const int j = tile * kStreamTile + ct * 32 + (lane & 31);
+// Phase 2 epilogue of one 32-block half, in two parts so that the next
+// MFMAs can be issued between them: filter_scores computes the scores and
+// pass masks (straight-line vector code), filter_enqueue queues the blocks
+// scoring above their query's bound behind the qn already queued (only slots
+// with survivors do vector work).  kFull: every block of the tile is below
+// every query's own block.
+struct Filtered {
   float sc[2][4];
   bool pass[2][4];
   uint64_t mk[2][4];  // the slots' ballots (scalar registers)
-  uint64_t any = 0;
-  // scores and pass tests of all 8 slots first, without branches, so the
-  // compiler can interleave them with the MFMAs
+  uint64_t any;
+  uint32_t tag;       // block id | (lane half) << 28
+};
+
+template <bool kFull>
+__device__ __forceinline__ void filter_scores(const Stream& st, const f32x16 (&acc)[2], int tile,
+                                              int ct, Filtered& f) {
+  const int lane = lane_id();
+  const int j = tile * kStreamTile + ct * 32 + (lane & 31);
+  f.any = 0;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      sc[rt][c] = relu_sum(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
-                           acc[rt][4 * c + 3]);
-      bool p = sc[rt][c] > st.tau_l[rt][c];
+      f.sc[rt][c] = relu_sum(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
+                             acc[rt][4 * c + 3]);
+      bool p = f.sc[rt][c] > st.tau_l[rt][c];
       if (!kFull) p = p && slot_valid(st, rt, c, j);
-      pass[rt][c] = p;
-      mk[rt][c] = __ballot(p);
-      any |= mk[rt][c];
+      f.pass[rt][c] = p;
+      f.mk[rt][c] = __ballot(p);
+      f.any |= f.mk[rt][c];
     }
-  if (any == 0) return qn;
-  const uint32_t tag = (uint32_t)j | ((uint32_t)(lane >> 5) << 28);
-  // only slots with survivors do any vector work
+  f.tag = (uint32_t)j | ((uint32_t)(lane >> 5) << 28);
+}
+
+__device__ __forceinline__ int filter_enqueue(Stream& st, const Filtered& f, int qn) {
+  if (f.any == 0) return qn;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint64_t m = mk[rt][c];
+      const uint64_t m = f.mk[rt][c];
       if (m == 0) continue;
-      if (pass[rt][c]) {
+      if (f.pass[rt][c]) {
         const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
             (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)qn));
-        st.queue[pos] = ((uint64_t)__float_as_uint(sc[rt][c]) << 32) |
-                        (uint64_t)(tag + ((uint32_t)slot_off(rt, c) << 28));
+        st.queue[pos] = ((uint64_t)__float_as_uint(f.sc[rt][c]) << 32) |
+                        (uint64_t)(f.tag + ((uint32_t)slot_off(rt, c) << 28));
       }
       qn += __popcll(m);
     }
@@ -1064,16 +1072,17 @@ __device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[2][4],
   mma_half(bf, A, accB);
   if (kPhase <= 1) {
     sample_epilogue<kPhase == 0>(st, accA, tile, 0);
-  } else {
-    qn = filter_epilogue<kPhase == 2>(st, accA, tile, 0, qn);
-  }
-  // (unconditional, also past the last position: a conditional update would
-  // make the compiler copy the accumulators, and the copies wait for the MFMAs)
-  mma_half(bn, A, accA);
-  if (kPhase <= 1) {
+    // (unconditional, also past the last position: a conditional update would
+    // make the compiler copy the accumulators, and the copies wait for the MFMAs)
+    mma_half(bn, A, accA);
     sample_epilogue<kPhase == 0>(st, accB, tile, 1);
   } else {
-    qn = filter_epilogue<kPhase == 2>(st, accB, tile, 1, qn);
+    Filtered fa, fb;
+    filter_scores<kPhase == 2>(st, accA, tile, 0, fa);
+    mma_half(bn, A, accA);  // issued before the branchy enqueue: keeps the pipe busy
+    qn = filter_enqueue(st, fa, qn);
+    filter_scores<kPhase == 2>(st, accB, tile, 1, fb);
+    qn = filter_enqueue(st, fb, qn);
     if (qn >= 64) {
       stream_drain(st, qn);
       qn = 0;
