@@ -16,15 +16,15 @@
 //
 //  TABLE (few queries, decode-shaped): one streaming pass scores every block
 //  with MFMA (16x16x32, 4 queries x 4 heads per tile) and writes the fp32
-//  score table plus, for every 16-block group, the group's best score.  The
-//  512 largest group maxima belong to 512 distinct blocks, so the 512th
-//  largest group maximum is a lower bound of the row's 512th best score; a
-//  small per-row radix pass finds it (rounded down to 22 significant bits)
-//  from the group maxima alone.  A filter pass appends every key whose score
-//  reaches that bound (typically a few percent more than 512 keys) to a
-//  candidate list, and a select kernel sorts them in LDS.  Cost over the
-//  bare k_cmp scan: the score table (4 B per query per block) written once
-//  and read once.
+//  score table plus, for every 16-block group, the group's best score.  Any
+//  value that 512 group maxima reach is reached by 512 distinct blocks, so it
+//  bounds the row's 512th best score from below.  One workgroup per row then
+//  finds such a bound from the group maxima, lists the groups that reach it,
+//  reads only those groups' scores back from the table (typically 700 of
+//  the row's 16,384 groups at 1M context), and finds the exact top 512 among
+//  the blocks that reach it by histogram passes, with no sort: the list is
+//  built in ascending block order and compacted in place.  Cost over the
+//  bare k_cmp scan: the score table (4 B per query per block) written once.
 //
 //  STREAM (many queries, prefill-shaped): a workgroup holds 64 queries x 4
 //  heads stationary in registers and streams the compressed keys through LDS
@@ -35,19 +35,20 @@
 //  below tau can be in the top 512; the select kernel checks this.  No
 //  score table is written.
 //
-// Both engines finish with the same select kernel (a register sort for short
-// lists, an LDS radix select otherwise); rows whose candidate list cannot be
-// trusted (an overflow, or fewer than 512 candidates) are finished by an
-// exact fallback that recomputes or re-reads the whole row.
+// The stream engine finishes with a select kernel (a register sort for short
+// lists, an LDS radix select otherwise).  Rows whose candidates cannot be
+// trusted or held (an overflow, too few candidates, or very many equal
+// scores) are finished by an exact fallback that recomputes or re-reads the
+// whole row.
+
 #include "common.h"
 #include "internal.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kHistBins = 2048;    // radix bins of 11 bits (table threshold)
+constexpr int kHistBins = 2048;    // histogram bins of the table engine's pick
 constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine)
-constexpr int kFilterSlice = 2048; // blocks per filter workgroup (table engine)
 constexpr int kGroup = 16;         // blocks per group maximum (table engine)
 constexpr int kSelCap = 8192;      // candidates a select workgroup holds in LDS
 constexpr int kHistW = 256;        // stream engine: sample-histogram bins per query
@@ -397,7 +398,7 @@ __device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, con
     uint32_t off = written;
     for (int w = 0; w < wave; ++w) off += wsum[w];
     if (keep) srow[off + (uint32_t)__popcll(m & lanemask_lt())] = j;
-    for (int w = 0; w < 4; ++w) written += wsum[w];
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) written += wsum[w];
     __syncthreads();
   }
 }
@@ -615,190 +616,463 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
   }
 }
 
-// One workgroup (1,024 threads) per query row: a lower bound tau of the
-// row's 512th best score from its group maxima.  With G >= 512 groups the
-// 512th largest group maximum is such a bound (512 distinct blocks reach it);
-// two 11-bit radix passes find it to 22 bits, rounded down (still a lower
-// bound).  First every thread keeps its two largest maxima: when every thread
-// has two, the smallest of those 2,048 numbers is itself a valid bound, so
-// only maxima at or above it need counting.  Rows with fewer than 512 groups
-// keep every candidate (tau = 0).  Each thread reads 16 maxima per chunk
-// (four 16-byte loads in flight); later passes re-read them from the L2.
-constexpr int kThrThreads = 1024;
+// ------------------------------------------------------------------ PICK
+// Table engine, after the scoring pass: one workgroup (1,024 threads) per
+// query row turns the row's group maxima and score table into its selection.
+// Scores are non-negative, so bins of a linear scale order them; every
+// decision below is taken on such bins or on exact score bits.
+//
+//  1. bound: with G >= 512 groups, any value that 512 group maxima reach is
+//     reached by 512 distinct blocks, so it is a lower bound of the row's
+//     512th best score.  Each thread holds 16 consecutive maxima; a histogram
+//     of the per-thread maxima finds the bin of their 512th largest, and the
+//     smallest per-thread maximum in that bin or above is the bound bv.
+//  2. candidate groups: the groups whose maximum reaches bv, listed in
+//     ascending order by a block-wide prefix count.
+//  3. candidates: the blocks of those groups whose score reaches bv,
+//     read from the score table 16 B at a time, listed in ascending order
+//     (typically 600 to 800).
+//  4. cutoff: the exact 512th best key among the candidates.  A finer scale
+//     over the candidates' range finds its bin; a bin holding one score value
+//     (the usual case for integer scores) settles it, otherwise passes over
+//     the score bits, 11 at a time, do.
+//  5. output: blocks above the cutoff, plus the lowest-index blocks at the
+//     cutoff score, compacted in list order, which is ascending.
+// A row whose candidate groups or blocks exceed the LDS lists (many equal
+// scores) is finished by the exact whole-row select.
+constexpr int kPickThreads = 1024;
+constexpr int kPickWaves = kPickThreads / 64;  // 16: one lane of a 16-lane row each
+constexpr int kPickGroups = 2048;  // candidate groups a row keeps in LDS
+constexpr int kPickCand = 2048;    // candidate blocks a row keeps in LDS (2 per thread)
+constexpr int kPickRounds = kPickGroups / (kPickThreads / 4);
+static_assert(kPickWaves == 16, "per-wavefront values are combined within one 16-lane row");
 
-__device__ __forceinline__ void load_group_chunk(const uint32_t* g, int G, int c, uint32_t (&x)[16]) {
-  const uint4* g4 = reinterpret_cast<const uint4*>(g);
-  const int n4 = (G + 3) >> 2;
+// Wavefront primitives on DPP lane moves, which need no LDS traffic.
+// Controls: row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 =
+// 0x143.  Lanes whose source is outside the row, or whose row is masked off,
+// receive `old`.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, kCtrl, kRowMask, 0xf, false);
+}
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+// Inclusive prefix sum within each row of 16 lanes.
+__device__ __forceinline__ uint32_t row_incl_sum(uint32_t v) {
+  v += dpp_mov<0x111, 0xf>(0u, v);
+  v += dpp_mov<0x112, 0xf>(0u, v);
+  v += dpp_mov<0x114, 0xf>(0u, v);
+  v += dpp_mov<0x118, 0xf>(0u, v);
+  return v;
+}
+// Inclusive prefix sum over the wavefront.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v = row_incl_sum(v);
+  v += dpp_mov<0x142, 0xa>(0u, v);
+  v += dpp_mov<0x143, 0xc>(0u, v);
+  return v;
+}
+// Running maximum / minimum: lane 15 of each row holds its row's, lane 63
+// the wavefront's.
+__device__ __forceinline__ uint32_t row_scan_max(uint32_t v) {
+  v = max(v, dpp_mov<0x111, 0xf>(v, v));
+  v = max(v, dpp_mov<0x112, 0xf>(v, v));
+  v = max(v, dpp_mov<0x114, 0xf>(v, v));
+  v = max(v, dpp_mov<0x118, 0xf>(v, v));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_scan_max(v);
+  v = max(v, dpp_mov<0x142, 0xa>(v, v));
+  v = max(v, dpp_mov<0x143, 0xc>(v, v));
+  return lane_read(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_mov<0x111, 0xf>(v, v));
+  v = min(v, dpp_mov<0x112, 0xf>(v, v));
+  v = min(v, dpp_mov<0x114, 0xf>(v, v));
+  v = min(v, dpp_mov<0x118, 0xf>(v, v));
+  v = min(v, dpp_mov<0x142, 0xa>(v, v));
+  v = min(v, dpp_mov<0x143, 0xc>(v, v));
+  return lane_read(v, 63);
+}
+// After every wavefront w has stored a count in slot[w] (and a barrier): the
+// sum over the wavefronts below `wave` and the total.  `wave` is uniform.
+__device__ __forceinline__ void waves_prefix(const uint32_t* slot, int wave, uint32_t& below,
+                                             uint32_t& total) {
+  const uint32_t sc = row_incl_sum(slot[threadIdx.x & 15]);
+  total = lane_read(sc, 15);
+  const uint32_t incl = lane_read(sc, wave > 0 ? wave - 1 : 0);
+  below = wave > 0 ? incl : 0u;
+}
+
+// Whole workgroup of kPickThreads: over kHistBins bins in LDS (bin order =
+// value order), the highest bin whose suffix count reaches k (the caller
+// guarantees the total does), the count in the bins above it and its own
+// count.  Thread t owns bins 2t and 2t+1.  Ends past a barrier.
+__device__ __forceinline__ void pick_suffix_find(const uint32_t* h, uint32_t k, uint32_t* wtot,
+                                                 uint4* res, uint32_t& bin, uint32_t& above,
+                                                 uint32_t& count) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint2 c = reinterpret_cast<const uint2*>(h)[tid];
+  const uint32_t mine = c.x + c.y;
+  const uint32_t P = wave_incl_sum(mine);  // lanes up to this one
+  const uint32_t wt = lane_read(P, 63);
+  if (lane == 0) wtot[wave] = wt;
+  __syncthreads();
+  const uint32_t sc = row_incl_sum(wtot[lane & 15]);
+  const uint32_t hi = lane_read(sc, 15) - lane_read(sc, wave);  // wavefronts above
+  const uint32_t suf1 = hi + (wt - P) + c.y;  // suffix count from bin 2t+1
+  const uint32_t suf0 = suf1 + c.x;           // from bin 2t
+  if (suf1 >= k && suf1 - c.y < k)
+    res[0] = make_uint4(2 * tid + 1, suf1 - c.y, c.y, 0u);
+  else if (suf0 >= k && suf1 < k)
+    res[0] = make_uint4(2 * tid, suf1, c.x, 0u);
+  __syncthreads();
+  const uint4 r = res[0];
+  bin = r.x;
+  above = r.y;
+  count = r.z;
+}
+
+// Shift that maps spans up to `span` into kHistBins bins.
+__device__ __forceinline__ uint32_t pick_shift(uint32_t span) {
+  const uint32_t top = span >> 11;
+  return top == 0 ? 0u : 32u - (uint32_t)__clz((int)top);
+}
+
+// Bin of a score on the linear scale (x - lo) * scale, clamped to the
+// histogram; non-decreasing in x.
+__device__ __forceinline__ uint32_t lin_bin(uint32_t bits, float lo, float scale) {
+  const float f = (__uint_as_float(bits) - lo) * scale;
+  return f > 0.f ? min((uint32_t)f, (uint32_t)(kHistBins - 1)) : 0u;
+}
+
+// This thread's 16 group maxima of chunk c (groups 16 (1024 c + t) .. + 15)
+// and a mask of the valid ones (group < G).
+__device__ __forceinline__ uint32_t pick_chunk(const uint4* g4, int n4, int G, int c,
+                                               const uint4 (&first)[4], uint32_t (&x)[16]) {
+  const int i4 = 4 * (c * kPickThreads + (int)threadIdx.x);
   uint4 v[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = (c * 4 + u) * kThrThreads + (int)threadIdx.x;
-    v[u] = i < n4 ? g4[i] : zero_u4();
-  }
+  for (int u = 0; u < 4; ++u) v[u] = c == 0 ? first[u] : (i4 + u < n4 ? g4[i4 + u] : zero_u4());
+  uint32_t vm = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int e = 4 * ((c * 4 + u) * kThrThreads + (int)threadIdx.x);
     x[4 * u + 0] = v[u].x;
-    x[4 * u + 1] = e + 1 < G ? v[u].y : 0u;
-    x[4 * u + 2] = e + 2 < G ? v[u].z : 0u;
-    x[4 * u + 3] = e + 3 < G ? v[u].w : 0u;
+    x[4 * u + 1] = v[u].y;
+    x[4 * u + 2] = v[u].z;
+    x[4 * u + 3] = v[u].w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vm |= (4 * (i4 + u) + e < G ? 1u : 0u) << (4 * u + e);
   }
-}
-__device__ __forceinline__ bool group_valid(int G, int c, int k) {
-  const int u = k >> 2, e = k & 3;
-  return 4 * ((c * 4 + u) * kThrThreads + (int)threadIdx.x) + e < G;
+  return vm;
 }
 
-__global__ __launch_bounds__(kThrThreads) void table_threshold_kernel(
-    const uint32_t* __restrict__ gmax, int gstride, const int32_t* __restrict__ lens,
-    uint32_t* __restrict__ thr, int Lmax, int Nq) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t s_cut;
-  __shared__ int s_bin;
-  __shared__ uint32_t s_above;
-  const int row = blockIdx.x, b = row / Nq, q = row % Nq, tid = threadIdx.x;
+__global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
+    const uint32_t* __restrict__ scores, int tstride, const uint32_t* __restrict__ gmax,
+    int gstride, const int32_t* __restrict__ lens, int32_t* __restrict__ sel,
+    int32_t* __restrict__ n_sel, int Lmax, int Nq) {
+  __shared__ __align__(16) uint32_t hist[kHistBins];
+  __shared__ uint32_t glist[kPickGroups];
+  __shared__ uint32_t cbits[kPickCand];
+  __shared__ uint32_t cj[kPickCand];
+  __shared__ uint32_t wred[2][kPickWaves];
+  __shared__ uint32_t wcnt[kPickRounds][kPickWaves];
+  __shared__ uint32_t wtot[kPickWaves];
+  __shared__ uint4 res[1];
+  __shared__ uint32_t wsum[kPickWaves];
+  __shared__ uint32_t bcast[2];
+  __shared__ uint32_t s_bv;
+  __shared__ uint32_t s_mm[2];
+  const int row = blockIdx.x, b = row / Nq, q = row - b * Nq, tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the first chunk of group maxima is requested before lens arrives (a row
+  // holds gstride >= G entries, gstride a multiple of 4)
+  const uint4* g4 = reinterpret_cast<const uint4*>(gmax + (size_t)row * gstride);
+  const int n4 = gstride >> 2;
+  uint4 first[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * tid + u;
+    first[u] = i < n4 ? g4[i] : zero_u4();
+  }
+  hist[tid] = 0u;
+  hist[tid + kPickThreads] = 0u;
+  if (tid == 0) {
+    s_bv = 0xffffffffu;
+    s_mm[0] = 0xffffffffu;
+    s_mm[1] = 0u;
+  }
   const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
-  const int bt = t >= 0 ? (t >> 2) : 0;
+  int32_t* srow = sel + (size_t)row * kTopK;
+  if (write_trivial(t, srow, n_sel + row)) return;
+  const int bt = t >> 2;
   const int G = (bt + kGroup - 1) / kGroup;
-  if (bt <= kTopK || G < kTopK) {
-    if (tid == 0) thr[row] = 0u;
-    return;
-  }
-  const uint32_t* g = gmax + (size_t)row * gstride;
-  const int nchunks = (G + 16 * kThrThreads - 1) / (16 * kThrThreads);
-  uint32_t m1 = 0, m2 = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    uint32_t x[16];
-    load_group_chunk(g, G, c, x);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t v = group_valid(G, c, k) ? x[k] : 0u;
-      m2 = v >= m1 ? m1 : max(m2, v);
-      m1 = max(m1, v);
-    }
-  }
-  if (tid == 0) s_cut = 0xffffffffu;
-  for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0u;
-  __syncthreads();
-  // A thread with fewer than two maxima reports 0, which makes the cut 0: then
-  // every maximum is counted (always valid).
-  uint32_t wm = m2;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wm = min(wm, (uint32_t)__shfl_xor((int)wm, off));
-  if ((tid & 63) == 0) atomicMin(&s_cut, wm);
-  __syncthreads();
-  const uint32_t cut = s_cut;
-  for (int c = 0; c < nchunks; ++c) {
-    uint32_t x[16];
-    load_group_chunk(g, G, c, x);
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (group_valid(G, c, k) && x[k] >= cut) atomicAdd(&hist[x[k] >> 20], 1u);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    int bin;
-    uint32_t sfx;
-    wave_suffix_bin_2048(hist, kTopK, bin, sfx);
-    if (tid == 0) {
-      s_bin = bin;
-      s_above = sfx - hist[bin];
-    }
-  }
-  __syncthreads();
-  const uint32_t bin1 = (uint32_t)s_bin;
-  const uint32_t k2 = (uint32_t)kTopK - s_above;
-  for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0u;
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    uint32_t x[16];
-    load_group_chunk(g, G, c, x);
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (group_valid(G, c, k) && (x[k] >> 20) == bin1)
-        atomicAdd(&hist[(x[k] >> 9) & (kHistBins - 1)], 1u);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    int bin2;
-    uint32_t sfx;
-    wave_suffix_bin_2048(hist, k2, bin2, sfx);
-    if (tid == 0) thr[row] = (bin1 << 20) | ((uint32_t)bin2 << 9);
-  }
-}
+  const int nchunks = (G + 16 * kPickThreads - 1) / (16 * kPickThreads);
+  const uint32_t* trow = scores + (size_t)row * tstride;
 
-// Grid (nslices, ceil(Nq/4), B); workgroup w reads blocks [w * fslice, +
-// fslice) of 4 rows (fslice a multiple of kFilterSlice) and writes the keys
-// whose score reaches the row's bound to its own segment of the row's
-// candidate list (segment w, fslice keys: it cannot overflow), and the count
-// to cand_cnt[row][w].  No global atomics: candidates are rare (about 512 of
-// a row's blocks) and contended counters would serialize them.
-__global__ __launch_bounds__(256) void table_filter_kernel(const uint32_t* __restrict__ scores,
-                                                           int tstride,
-                                                           const uint32_t* __restrict__ thr,
-                                                           const int32_t* __restrict__ lens,
-                                                           uint64_t* __restrict__ cand,
-                                                           uint32_t* __restrict__ cand_cnt,
-                                                           int Lmax, int Nq, int fslice) {
-  __shared__ uint32_t s_cnt[4];
-  const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
-  const int nslices = gridDim.x;
-  const int len = clampi(lens[b], 0, Lmax);
-  const int tid = threadIdx.x;
-  if (tid < 4) s_cnt[tid] = 0u;
-  int jend[4];
-  uint32_t tau[4];
+  // ---- 1. bound: bv, a value that at least 512 group maxima reach
+  uint32_t m1 = 0;
+  bool any = false;
+  for (int c = 0; c < nchunks; ++c) {
+    uint32_t x[16];
+    const uint32_t vm = pick_chunk(g4, n4, G, c, first, x);
 #pragma unroll
-  for (int qi = 0; qi < 4; ++qi) {
-    const int qq = min(q0 + qi, Nq - 1);
-    const int t = query_t(len, Nq, qq);
-    const int bt = t >= 0 ? (t >> 2) : 0;
-    // rows with at most 512 candidates are finished by the select kernel alone
-    const bool live = q0 + qi < Nq && bt > kTopK;
-    jend[qi] = live ? min((slice + 1) * fslice, bt) : 0;
-    tau[qi] = live ? thr[(size_t)b * Nq + qq] : 0u;
+    for (int k = 0; k < 16; ++k) m1 = ((vm >> k) & 1u) ? max(m1, x[k]) : m1;
+    any = any || vm != 0u;
+  }
+  {
+    const uint32_t wmax = wave_max_u32(m1);
+    const uint32_t nany = (uint32_t)__popcll(__ballot(any));
+    if (lane == 0) {
+      wred[0][wave] = wmax;
+      wred[1][wave] = nany;
+    }
   }
   __syncthreads();
-  for (int j_begin = slice * fslice; j_begin < (slice + 1) * fslice; j_begin += kFilterSlice) {
-    // all loads first: 4 rows x 2 passes of 1024 blocks, 4 blocks per thread
-    uint4 v[4][2];
+  const uint32_t rowmax = lane_read(row_scan_max(wred[0][lane & 15]), 15);
+  const uint32_t nthr = lane_read(row_incl_sum(wred[1][lane & 15]), 15);
+  const float rowmax_f = __uint_as_float(rowmax);
+  const float scale = rowmax != 0u ? 2047.0f / rowmax_f : 0.f;
+  uint32_t bv = 0;
+  if (G >= kTopK) {
+    // With >= 512 threads holding maxima, their per-thread maxima (distinct
+    // groups) are counted, else every maximum; the smallest counted value in
+    // the bins from the one holding the 512th largest up is reached by >= 512
+    // groups.
+    const bool per_thread = nthr >= (uint32_t)kTopK;
+    if (per_thread) {
+      if (any) atomicAdd(&hist[lin_bin(m1, 0.f, scale)], 1u);
+    } else {
+      for (int c = 0; c < nchunks; ++c) {
+        uint32_t x[16];
+        const uint32_t vm = pick_chunk(g4, n4, G, c, first, x);
 #pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-      const uint32_t* srow = scores + ((size_t)b * Nq + min(q0 + qi, Nq - 1)) * tstride;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int j4 = j_begin + p * 1024 + tid * 4;
-        v[qi][p] = j4 < jend[qi] ? *reinterpret_cast<const uint4*>(srow + j4) : zero_u4();
+        for (int k = 0; k < 16; ++k)
+          if ((vm >> k) & 1u) atomicAdd(&hist[lin_bin(x[k], 0.f, scale)], 1u);
       }
     }
+    __syncthreads();
+    uint32_t bin_a, ab, cn;
+    pick_suffix_find(hist, kTopK, wtot, res, bin_a, ab, cn);
+    uint32_t mn = 0xffffffffu;
+    if (per_thread) {
+      if (any && lin_bin(m1, 0.f, scale) >= bin_a) mn = m1;
+    } else {
+      for (int c = 0; c < nchunks; ++c) {
+        uint32_t x[16];
+        const uint32_t vm = pick_chunk(g4, n4, G, c, first, x);
 #pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-      uint32_t pm = 0;  // bit (p*4+e): element passes
+        for (int k = 0; k < 16; ++k)
+          if (((vm >> k) & 1u) && lin_bin(x[k], 0.f, scale) >= bin_a) mn = min(mn, x[k]);
+      }
+    }
+    mn = wave_min_u32(mn);
+    if (lane == 0 && mn != 0xffffffffu) atomicMin(&s_bv, mn);
+    __syncthreads();
+    bv = s_bv;
+  }
+
+  // ---- 2. candidate groups, ascending
+  uint32_t ng = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    uint32_t x[16];
+    const uint32_t vm = pick_chunk(g4, n4, G, c, first, x);
+    uint32_t keep = 0;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint32_t e4[4] = {v[qi][p].x, v[qi][p].y, v[qi][p].z, v[qi][p].w};
+    for (int k = 0; k < 16; ++k) keep |= (((vm >> k) & 1u) && x[k] >= bv ? 1u : 0u) << k;
+    const uint32_t cnt = (uint32_t)__popc(keep);
+    const uint32_t P = wave_incl_sum(cnt);
+    if (c > 0) __syncthreads();  // wtot of the previous chunk has been read
+    if (lane == 0) wtot[wave] = lane_read(P, 63);
+    __syncthreads();
+    uint32_t below, all;
+    waves_prefix(wtot, wave, below, all);
+    uint32_t p = ng + below + P - cnt;
+    const uint32_t gi0 = 16u * (uint32_t)(c * kPickThreads + tid);
+    while (keep) {
+      const int k = __ffs(keep) - 1;
+      keep &= keep - 1;
+      if (p < (uint32_t)kPickGroups) glist[p] = gi0 + (uint32_t)k;
+      ++p;
+    }
+    ng += all;
+  }
+  __syncthreads();
+
+  // ---- 3. candidate blocks of those groups, ascending
+  uint32_t n = 0;
+  if (ng <= (uint32_t)kPickGroups) {
+    const int rounds = (int)((ng + kPickThreads / 4 - 1) / (kPickThreads / 4));
+    const int quarter = tid & 3;
+    uint4 v[kPickRounds];
+    int j0[kPickRounds];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j_begin + p * 1024 + tid * 4 + e;
-          pm |= (j < jend[qi] && e4[e] >= tau[qi] ? 1u : 0u) << (p * 4 + e);
+    for (int r = 0; r < kPickRounds; ++r) {
+      const uint32_t slot = (uint32_t)(r * (kPickThreads / 4) + (tid >> 2));
+      j0[r] = slot < ng ? (int)(glist[slot] * kGroup) + 4 * quarter : bt;
+      v[r] = (r < rounds && j0[r] < bt) ? *reinterpret_cast<const uint4*>(trow + j0[r])
+                                        : zero_u4();
+    }
+    uint32_t keep[kPickRounds], pre[kPickRounds];
+#pragma unroll
+    for (int r = 0; r < kPickRounds; ++r) {
+      keep[r] = 0;
+      pre[r] = 0;
+      if (r >= rounds) continue;
+      const uint32_t e4[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+      uint32_t tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool k = j0[r] + e < bt && e4[e] >= bv;
+        keep[r] |= (k ? 1u : 0u) << e;
+        const uint64_t m = __ballot(k);
+        pre[r] += (uint32_t)__popcll(m & lanemask_lt());
+        tot += (uint32_t)__popcll(m);
+      }
+      if (lane == 0) wcnt[r][wave] = tot;
+    }
+    __syncthreads();
+    // lane 16 i + w reads round (4 h + i)'s count of wavefront w: one row per round
+    uint32_t sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      sc[h] = rounds > 4 * h ? row_incl_sum(wcnt[4 * h + (lane >> 4)][lane & 15]) : 0u;
+    uint32_t base = 0;
+#pragma unroll
+    for (int r = 0; r < kPickRounds; ++r) {
+      if (r >= rounds) continue;
+      const uint32_t s = sc[r >> 2];
+      const int r16 = 16 * (r & 3);
+      const uint32_t all = lane_read(s, r16 + 15);
+      const uint32_t before = wave > 0 ? lane_read(s, r16 + (wave > 0 ? wave - 1 : 0)) : 0u;
+      uint32_t p = base + before + pre[r];
+      const uint32_t e4[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((keep[r] >> e) & 1u) {
+          if (p < (uint32_t)kPickCand) {
+            cbits[p] = e4[e];
+            cj[p] = (uint32_t)(j0[r] + e);
+          }
+          ++p;
         }
       }
-      if (pm == 0) continue;
-      const size_t row = (size_t)b * Nq + q0 + qi;
-      uint32_t pos = atomicAdd(&s_cnt[qi], (uint32_t)__popc(pm));
-      uint64_t* seg = cand + (row * nslices + slice) * (size_t)fslice;
-      while (pm) {
-        const int bit = __ffs(pm) - 1;
-        pm &= pm - 1;
-        const int p = bit >> 2, e = bit & 3;
-        const uint4 a = p ? v[qi][1] : v[qi][0];  // (selects, not a dynamic register index)
-        const uint32_t sc = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
-        seg[pos++] = make_key(sc, (uint32_t)(j_begin + p * 1024 + tid * 4 + e));
+      base += all;
+    }
+    n = base;
+  }
+  __syncthreads();
+
+  if (ng > (uint32_t)kPickGroups || n > (uint32_t)kPickCand) {
+    // too many candidates for the lists (many equal scores): exact slow path
+    select_whole_row<false>(trow, nullptr, nullptr, bt, srow, nullptr, hist, bcast, wsum);
+    if (tid == 0) n_sel[row] = kTopK;
+    return;
+  }
+
+  // ---- 4. the exact 512th best key among the n candidates
+  uint32_t mb[2], mj[2];
+  bool mv[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t i = 2u * (uint32_t)tid + e;
+    mv[e] = i < n;
+    mb[e] = mv[e] ? cbits[i] : 0u;
+    mj[e] = mv[e] ? cj[i] : 0u;
+  }
+  // the candidates' scale: [bv, rowmax]
+  const float lo4 = __uint_as_float(bv);
+  const float scale4 = rowmax_f > lo4 ? 2047.0f / (rowmax_f - lo4) : 0.f;
+  uint32_t fb[2];
+  hist[tid] = 0u;
+  hist[tid + kPickThreads] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    fb[e] = lin_bin(mb[e], lo4, scale4);
+    if (mv[e]) atomicAdd(&hist[fb[e]], 1u);
+  }
+  __syncthreads();
+  uint32_t cb, above, cnt;
+  pick_suffix_find(hist, kTopK, wtot, res, cb, above, cnt);
+  uint32_t k = (uint32_t)kTopK - above;  // still to take from bin cb
+  // within bin cb: keep bits >= keep_from, and `ties` blocks at tie_bits
+  uint32_t keep_from = 0, tie_bits = 0xffffffffu, ties = 0;
+  if (cnt != k) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (mv[e] && fb[e] == cb) {
+        atomicMin(&s_mm[0], mb[e]);
+        atomicMax(&s_mm[1], mb[e]);
+      }
+    }
+    __syncthreads();
+    const uint32_t mn = s_mm[0], mx = s_mm[1];
+    if (mn == mx) {
+      keep_from = mn + 1;
+      tie_bits = mn;
+      ties = k;
+    } else {
+      // several score values share the bin: refine on the bits
+      uint32_t lo = mn, width = mx - mn + 1u;
+      uint32_t s = pick_shift(mx - mn);
+      for (;;) {
+        hist[tid] = 0u;
+        hist[tid + kPickThreads] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (mv[e] && fb[e] == cb && mb[e] >= lo && mb[e] - lo < width)
+            atomicAdd(&hist[(mb[e] - lo) >> s], 1u);
+        __syncthreads();
+        uint32_t bn, ab2, cn2;
+        pick_suffix_find(hist, k, wtot, res, bn, ab2, cn2);
+        k -= ab2;
+        lo += bn << s;
+        if (cn2 == k) {  // the whole bin is kept
+          keep_from = lo;
+          break;
+        }
+        if (s == 0) {  // one score value: keep k of its blocks, lowest first
+          keep_from = lo + 1;
+          tie_bits = lo;
+          ties = k;
+          break;
+        }
+        width = 1u << s;
+        s = s > 11 ? s - 11 : 0u;
       }
     }
   }
+
+  // ---- 5. compaction in list order (ascending block ids)
+  uint32_t gk[2], tk[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    gk[e] = mv[e] && (fb[e] > cb || (fb[e] == cb && mb[e] >= keep_from)) ? 1u : 0u;
+    tk[e] = mv[e] && !gk[e] && fb[e] == cb && mb[e] == tie_bits ? 1u : 0u;
+  }
+  const uint32_t mine = (gk[0] + gk[1]) | ((tk[0] + tk[1]) << 16);
+  const uint32_t S = wave_incl_sum(mine);
+  // (the last find's reads of wtot are behind its barrier)
+  if (lane == 0) wtot[wave] = lane_read(S, 63);
   __syncthreads();
-  if (tid < 4 && q0 + tid < Nq) cand_cnt[((size_t)b * Nq + q0 + tid) * nslices + slice] = s_cnt[tid];
+  uint32_t before, all;
+  waves_prefix(wtot, wave, before, all);
+  uint32_t P = before + S - mine;  // exclusive prefix of this thread
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t A = P & 0xffffu, T = P >> 16;
+    const uint32_t pos = A + min(T, ties);
+    if ((gk[e] || (tk[e] && T < ties)) && pos < (uint32_t)kTopK) srow[pos] = (int32_t)mj[e];
+    P += gk[e] | (tk[e] << 16);
+  }
+  if (tid == 0) n_sel[row] = kTopK;
 }
 
 // ------------------------------------------------------------------ STREAM
@@ -1240,20 +1514,9 @@ TopkPath choose_topk_path(const Dims& d, uint32_t flags) {
 namespace {
 int table_stride(const Dims& d) { return ((d.Lmax / 4) + 3) & ~3; }
 int group_stride(const Dims& d) { return (((d.Lmax / 4) + kGroup - 1) / kGroup + 3) & ~3; }
-// Filter slices: at most 256 per row (the select kernel walks one segment per
-// thread pair or more), each a multiple of kFilterSlice blocks.
-int filter_slice(const Dims& d) {
-  const long long nbp = d.Lmax / 4;
-  const long long per = (nbp + 255) / 256;
-  return (int)((per + kFilterSlice - 1) / kFilterSlice * kFilterSlice);
-}
-int filter_slices(const Dims& d) { return (int)((d.Lmax / 4 + filter_slice(d) - 1) / filter_slice(d)); }
 struct TableWs {
-  uint32_t* scores;
-  uint32_t* gmax;
-  uint32_t* thr;
-  uint32_t* cand_cnt;  // [rows][filter slices], written by the filter
-  uint64_t* cand;      // [rows][filter slices][filter slice]
+  uint32_t* scores;  // [rows][table stride] score bits
+  uint32_t* gmax;    // [rows][group stride] group maxima
 };
 struct StreamWs {
   uint64_t* lists;
@@ -1266,9 +1529,6 @@ TableWs carve_table(const Dims& d, void* ws, size_t* total) {
   TableWs w;
   w.scores = c.take<uint32_t>(rows * (size_t)table_stride(d));
   w.gmax = c.take<uint32_t>(rows * (size_t)group_stride(d));
-  w.thr = c.take<uint32_t>(rows);
-  w.cand_cnt = c.take<uint32_t>(rows * filter_slices(d));
-  w.cand = c.take<uint64_t>(rows * (size_t)filter_slices(d) * filter_slice(d));
   if (total) *total = c.off;
   return w;
 }
@@ -1312,20 +1572,14 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   if (path == TopkPath::kTable) {
     TableWs w = carve_table(d, ws, nullptr);
     const int ts = table_stride(d), gs = group_stride(d);
-    const int fs = filter_slice(d), nfs = filter_slices(d);
     const size_t rows = (size_t)d.B * d.Nq;
     (void)ws_zeroed;
     const unsigned qg = (unsigned)((d.Nq + 3) / 4);
     const dim3 grid_s((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
     QSA_LAUNCH(score_table_kernel, grid_s, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
                w.gmax, gs, d.Lmax, d.Nq);
-    QSA_LAUNCH(table_threshold_kernel, dim3((unsigned)rows), dim3(kThrThreads), 0, s, w.gmax, gs,
-               lens, w.thr, d.Lmax, d.Nq);
-    QSA_LAUNCH(table_filter_kernel, dim3((unsigned)nfs, qg, (unsigned)d.B), dim3(256), 0, s,
-               w.scores, ts, w.thr, lens, w.cand, w.cand_cnt, d.Lmax, d.Nq, fs);
-    QSA_LAUNCH(select_kernel<false>, grid_q, dim3(256), 0, s, w.cand, w.cand_cnt, nfs, fs,
-               (const int32_t*)nullptr, w.scores, ts, q_idx, k_cmp, lens, sel, n_sel, d.Lmax,
-               d.Nq);
+    QSA_LAUNCH(table_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, s, w.scores, ts,
+               w.gmax, gs, lens, sel, n_sel, d.Lmax, d.Nq);
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
