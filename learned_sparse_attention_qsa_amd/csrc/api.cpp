@@ -262,8 +262,10 @@ qsa_status qsa_index_topk(const qsa_shape* shape, const uint16_t* q_idx, const u
   QSA_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
-  return hip_status(qsa::launch_index_topk(d, qsa::choose_topk_path(d, shape->flags), q_idx, k_cmp,
-                                           lens, sel, n_sel, ws, false, s));
+  // (no compression is fused here, so k_cmp is only read)
+  return hip_status(qsa::launch_index_topk(d, qsa::choose_topk_path(d, shape->flags), q_idx,
+                                           const_cast<uint16_t*>(k_cmp), lens, sel, n_sel, ws,
+                                           false, s));
 }
 
 qsa_status qsa_expand_blocks(const qsa_shape* shape, const int32_t* lens, const int32_t* sel,
@@ -339,10 +341,13 @@ qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint
   const qsa::TopkPath path = qsa::choose_topk_path(d, shape->flags);
   qsa::ZeroRange z0{nullptr, 0};
   if (d.Nq > 0) qsa::topk_zero_range(d, path, p.shared, &z0.p, &z0.n);
-  QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, z0, s)));
+  // decode-shaped calls compress inside the scoring pass; others first
+  const bool fuse = d.Nq > 0 && z0.n == 0 && qsa::topk_can_fuse_compress(d, path);
+  if (!fuse) QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, z0, s)));
   if (d.Nq == 0) return QSA_OK;
-  QSA_TRY(hip_status(
-      qsa::launch_index_topk(d, path, q_idx, k_cmp, lens, sel, n_sel, p.shared, z0.p != nullptr, s)));
+  const qsa::CompressFuse cf{k_idx, first_block};
+  QSA_TRY(hip_status(qsa::launch_index_topk(d, path, q_idx, k_cmp, lens, sel, n_sel, p.shared,
+                                            z0.p != nullptr, s, fuse ? &cf : nullptr)));
   return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.att.part_o,
                                               p.att.part_lse, s));
 }

@@ -64,6 +64,7 @@ struct AttnArgs {
   int B, Lmax, Nq, Hq, Hkv, G;
   float scale_log2;
   int split_tokens, n_split;
+  int tail_last;  // 1: the last split also takes the query's own block
 };
 
 // Running softmax state of one wavefront: 16 query columns (one per lane
@@ -123,7 +124,8 @@ __device__ __forceinline__ void softmax_pv(Run& r, float* z, const uint16_t* vt)
 
 // A 32-token tile of one KV head, in registers: the K fragments of the two
 // 16-token halves (MFMA A-operand layout: lane -> token lane&15, 16 bytes at
-// dims ks*32 + (lane>>4)*8) and the V rows (lane -> token lane/2, half lane&1).
+// dims ks*32 + (lane>>4)*8) and the V rows (v[i]: lane -> token 4i + lane/16,
+// 16 bytes at dims (lane&15)*8, so that 16 lanes read one 256-byte row).
 struct KVTile {
   uint4 k[2][4];
   uint4 v[8];
@@ -142,17 +144,19 @@ __device__ __forceinline__ void load_tile(KVTile& t, const uint16_t* kbase, cons
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) t.k[s][ks] = off >= 0 ? kp[ks * 4 + (lane >> 4)] : zero_u4();
   }
-  const long long off = row_of(k0 + (lane >> 1));
-  const uint4* vp = reinterpret_cast<const uint4*>(vbase + (off < 0 ? 0 : off)) + (lane & 1) * 8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t.v[i] = off >= 0 ? vp[i] : zero_u4();
+  for (int i = 0; i < 8; ++i) {
+    const long long off = row_of(k0 + 4 * i + (lane >> 4));
+    const uint4* vp = reinterpret_cast<const uint4*>(vbase + (off < 0 ? 0 : off)) + (lane & 15);
+    t.v[i] = off >= 0 ? *vp : zero_u4();
+  }
 }
 
 __device__ __forceinline__ void stash_v(uint16_t* vt, const KVTile& t) {
   const int lane = lane_id();
-  uint4* dst = reinterpret_cast<uint4*>(vt + (lane >> 1) * kVStride + (lane & 1) * 64);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = t.v[i];
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4*>(vt + (4 * i + (lane >> 4)) * kVStride + (lane & 15) * 8) = t.v[i];
 }
 
 // Logits of this lane's 8 tokens (two 16-token halves x 4 rows of the MFMA
@@ -253,7 +257,10 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     if (e < nsb && kb0 + e < ns) s_sel[e] = clampi(my_sel[i], 0, bt - 1);
   }
   __syncthreads();
-  const int k_end = min(ntok, k_begin + a.split_tokens);
+  // with tail_last, the last split also takes the query's own block (<= 4
+  // tokens past the 2,048 selected ones)
+  const int k_end =
+      a.tail_last && split == a.n_split - 1 ? ntok : min(ntok, k_begin + a.split_tokens);
   const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
   const uint16_t* kbase = a.k + g * kHeadDim;
   const uint16_t* vbase = a.v + g * kHeadDim;
@@ -422,13 +429,34 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   const float* pl = part_lse + rh * n_split;
   const float* po = part_o + rh * n_split * kHeadDim + d;
   float M = kNegInf;
-  for (int s0 = 0; s0 < n_split; s0 += kChunk) {
-#pragma unroll
-    for (int s = 0; s < kChunk; ++s)
-      if (s0 + s < n_split) M = fmaxf(M, pl[s0 + s]);
-  }
   float acc = 0.f, sw = 0.f;
-  if (M != kNegInf) {
+  if (n_split <= kChunk) {
+    // every partial in one round of loads
+    float w[kChunk], v[kChunk];
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s) {
+      const bool ok = s < n_split;
+      w[s] = ok ? pl[s] : kNegInf;
+      v[s] = ok ? po[(size_t)s * kHeadDim] : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s) M = fmaxf(M, w[s]);
+    if (M != kNegInf) {
+#pragma unroll
+      for (int s = 0; s < kChunk; ++s) {
+        const float e = w[s] == kNegInf ? 0.f : __expf(w[s] - M);
+        sw += e;
+        acc += e * v[s];
+      }
+    }
+  } else {
+    for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+#pragma unroll
+      for (int s = 0; s < kChunk; ++s)
+        if (s0 + s < n_split) M = fmaxf(M, pl[s0 + s]);
+    }
+  }
+  if (n_split > kChunk && M != kNegInf) {
     for (int s0 = 0; s0 < n_split; s0 += kChunk) {
       float w[kChunk], v[kChunk];
 #pragma unroll
@@ -455,19 +483,35 @@ int sparse_units(const Dims& d) {
   return d.Nq * d.Hkv * ((G + 15) / 16);
 }
 
-int sparse_splits(const Dims& d, int* split_tokens) {
+// Workgroups a decode-sized sparse attention aims for: 2 per compute unit,
+// each wavefront walking two or more 32-token tiles with the next one's
+// loads in flight.
+constexpr int kSparseTargetWG = 512;
+
+int sparse_splits(const Dims& d, int* split_tokens, int* tail_last) {
   // Decode-sized batches have few (query, KV head) units: split their token
-  // lists so that about 1,024 workgroups each gather one 32-token tile per
-  // wavefront (128 tokens), with all of a workgroup's loads in flight at once.
+  // lists so that about kSparseTargetWG workgroups share the gather.  Splits
+  // of one tile per wavefront leave the query's own block (<= 4 tokens) to a
+  // split of its own; longer splits take it into the last one.
   const long long units = (long long)d.B * sparse_units(d);
+  constexpr int kSelTok = kTopK * kBlock;
   int st = kMaxTok;
-  if (units < 1024) {
-    const long long want = (1024 + units - 1) / units;
-    st = (int)(kMaxTok / want) / (4 * kTile) * (4 * kTile);
+  if (units < kSparseTargetWG) {
+    const long long want = (kSparseTargetWG + units - 1) / units;
+    st = (int)(kSelTok / want) / (4 * kTile) * (4 * kTile);
     if (st < 4 * kTile) st = 4 * kTile;
   }
   *split_tokens = st;
-  return (kMaxTok + st - 1) / st;
+  if (st >= kSelTok) {
+    *tail_last = 0;
+    return 1;
+  }
+  if (st <= 4 * kTile) {
+    *tail_last = 0;
+    return (kMaxTok + st - 1) / st;
+  }
+  *tail_last = 1;
+  return (kSelTok + st - 1) / st;
 }
 
 int dense_splits(const Dims& d, int* split_tokens) {
@@ -488,8 +532,8 @@ int dense_splits(const Dims& d, int* split_tokens) {
 
 AttendLayout attend_layout(const Dims& d) {
   AttendLayout l{};
-  int st;
-  const int ns = sparse_splits(d, &st);
+  int st, tl;
+  const int ns = sparse_splits(d, &st, &tl);
   if (ns > 1) {
     const size_t rh = (size_t)d.B * d.Nq * d.Hq;
     l.partial_floats = rh * ns * kHeadDim;
@@ -519,7 +563,7 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
   a.Hkv = d.Hkv;
   a.G = d.Hq / d.Hkv;
   a.scale_log2 = d.scale * kLog2e;
-  a.n_split = sparse_splits(d, &a.split_tokens);
+  a.n_split = sparse_splits(d, &a.split_tokens, &a.tail_last);
   if (a.n_split > 1) {
     a.part_o = part_o;
     a.part_lse = part_lse;

@@ -47,6 +47,30 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double d) {
   return f32_to_bf16(__uint_as_float(u));
 }
 
+// One 16-byte chunk (8 dims) of a compressed block key: the same chunk of
+// the block's four token keys (rows[0], rows[8], rows[16], rows[24]: rows of
+// 64 bf16 are 8 chunks apart) summed in float64 in token order, which is
+// exact for any bf16 inputs of sane range, then rounded once to bf16.
+__device__ __forceinline__ uint4 compress_chunk(const uint4* rows) {
+  const uint4 r[4] = {rows[0], rows[8], rows[16], rows[24]};
+  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t x[4] = {r[t].x, r[t].y, r[t].z, r[t].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[2 * i] += (double)bf16_lo(x[i]);
+      s[2 * i + 1] += (double)bf16_hi(x[i]);
+    }
+  }
+  uint4 o;
+  o.x = f64_to_bf16(s[0]) | (f64_to_bf16(s[1]) << 16);
+  o.y = f64_to_bf16(s[2]) | (f64_to_bf16(s[3]) << 16);
+  o.z = f64_to_bf16(s[4]) | (f64_to_bf16(s[5]) << 16);
+  o.w = f64_to_bf16(s[6]) | (f64_to_bf16(s[7]) << 16);
+  return o;
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }

@@ -17,15 +17,6 @@
 namespace qsa {
 namespace {
 
-__device__ __forceinline__ void acc8(double* s, uint4 w) {
-  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[2 * i] += (double)bf16_lo(x[i]);
-    s[2 * i + 1] += (double)bf16_hi(x[i]);
-  }
-}
-
 __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k_idx,
                                                        const int32_t* __restrict__ lens,
                                                        const int32_t* __restrict__ first_block,
@@ -49,18 +40,8 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restric
        g < end; g += stride) {
     const long long j = g >> 3;
     const int c = (int)(g & 7);
-    const uint4* rows = src + j * 32 + c;  // row 4j at chunk c; rows are 8 uint4 apart
-    const uint4 r0 = rows[0], r1 = rows[8], r2 = rows[16], r3 = rows[24];
-    double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    acc8(s, r0);
-    acc8(s, r1);
-    acc8(s, r2);
-    acc8(s, r3);
-    uint4 o;
-    o.x = f64_to_bf16(s[0]) | (f64_to_bf16(s[1]) << 16);
-    o.y = f64_to_bf16(s[2]) | (f64_to_bf16(s[3]) << 16);
-    o.z = f64_to_bf16(s[4]) | (f64_to_bf16(s[5]) << 16);
-    o.w = f64_to_bf16(s[6]) | (f64_to_bf16(s[7]) << 16);
+    // row 4j at chunk c; rows are 8 uint4 apart
+    const uint4 o = compress_chunk(src + j * 32 + c);
     dst[j * 8 + c] = o;
   }
 }

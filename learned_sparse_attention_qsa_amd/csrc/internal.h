@@ -35,9 +35,20 @@ TopkPath choose_topk_path(const Dims& d, uint32_t flags);
 size_t topk_workspace_bytes(const Dims& d, TopkPath path);
 // Words of the workspace that must be zero before the scoring pass.
 void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n);
+// Key compression folded into the scoring pass (qsa_forward): the blocks from
+// first_block[b] (all when null) to floor(lens[b]/4) are compressed from
+// k_idx and written to k_cmp by the pass that scores them.
+struct CompressFuse {
+  const uint16_t* k_idx;
+  const int32_t* first_block;
+};
+// Whether launch_index_topk can take the compression over (else it is a
+// separate launch_compress before it).
+bool topk_can_fuse_compress(const Dims& d, TopkPath path);
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
-                             const uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
-                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s);
+                             uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
+                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s,
+                             const CompressFuse* fuse = nullptr);
 
 // ---- attend.hip
 // Scratch of the sparse attention when a query row is split over several

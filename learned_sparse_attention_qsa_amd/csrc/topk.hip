@@ -544,19 +544,40 @@ __global__ __launch_bounds__(256) void select_kernel(
 // the lane (r, kc) receives block r of the tile for query q0 + kc, all four
 // heads.  A tile is also one group: its maximum over the 16 lanes of a query
 // goes to gmax.
+//
+// With k_idx given (one workgroup row covers all of a sequence's queries),
+// the pass also compresses the sequence's new blocks [first_block, len/4):
+// each workgroup writes those of its slice to k_cmp before scoring them
+// (the vector L1 is shared by the workgroup's wavefronts, so a barrier
+// orders the writes before the reads).
 __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __restrict__ q_idx,
-                                                          const uint16_t* __restrict__ k_cmp,
+                                                          uint16_t* __restrict__ k_cmp,
                                                           const int32_t* __restrict__ lens,
                                                           uint32_t* __restrict__ scores,
                                                           int tstride,
                                                           uint32_t* __restrict__ gmax,
-                                                          int gstride, int Lmax, int Nq) {
+                                                          int gstride, int Lmax, int Nq,
+                                                          const uint16_t* __restrict__ k_idx,
+                                                          const int32_t* __restrict__ first_block) {
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
   const int len = clampi(lens[b], 0, Lmax);
   const int nbp = Lmax >> 2;
   const int t_last = query_t(len, Nq, min(q0 + 3, Nq - 1));
   const int j_begin = slice * kTableSlice;
   const int j_end = min(j_begin + kTableSlice, t_last >= 0 ? (t_last >> 2) : 0);
+  if (k_idx != nullptr) {
+    const int nb = len >> 2;
+    const int fb = first_block ? clampi(first_block[b], 0, nb) : 0;
+    const long long c0 = (long long)max(fb, j_begin) * 8;
+    const long long c1 = (long long)min(nb, j_begin + kTableSlice) * 8;
+    if (c0 < c1) {  // (uniform over the workgroup)
+      const uint4* src = reinterpret_cast<const uint4*>(k_idx + (size_t)b * Lmax * kIdxDim);
+      uint4* dst = reinterpret_cast<uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
+      for (long long g = c0 + threadIdx.x; g < c1; g += blockDim.x)
+        dst[g] = compress_chunk(src + (g >> 3) * 32 + (g & 7));
+      __syncthreads();
+    }
+  }
   if (j_begin >= j_end) return;
 
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -1564,9 +1585,16 @@ void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, siz
   }
 }
 
+bool topk_can_fuse_compress(const Dims& d, TopkPath path) {
+  // one scoring workgroup per slice and sequence: each new block is written once
+  return path == TopkPath::kTable && d.Nq <= 4;
+}
+
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
-                             const uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
-                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s) {
+                             uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
+                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s,
+                             const CompressFuse* fuse) {
+  if (fuse && !topk_can_fuse_compress(d, path)) return hipErrorInvalidValue;
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   const dim3 grid_q((unsigned)d.Nq, (unsigned)d.B);
   if (path == TopkPath::kTable) {
@@ -1577,7 +1605,8 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
     const unsigned qg = (unsigned)((d.Nq + 3) / 4);
     const dim3 grid_s((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
     QSA_LAUNCH(score_table_kernel, grid_s, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
-               w.gmax, gs, d.Lmax, d.Nq);
+               w.gmax, gs, d.Lmax, d.Nq, fuse ? fuse->k_idx : nullptr,
+               fuse ? fuse->first_block : nullptr);
     QSA_LAUNCH(table_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, s, w.scores, ts,
                w.gmax, gs, lens, sel, n_sel, d.Lmax, d.Nq);
   } else {

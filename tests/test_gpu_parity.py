@@ -269,11 +269,14 @@ def test_forward_cfg0(flags):
 
 
 def test_forward_cfg1_decode_128k():
+    # decode-shaped: the key compression runs inside the scoring pass
     say("forward cfg1")
     w = W.make(1)
     res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, w.n_query)
     shp = shape_of(w)
-    k_cmp = torch.zeros((w.batch, w.max_len // 4, 64), dtype=torch.bfloat16, device="cuda")
+    sentinel = 0x7fc1
+    k_cmp = torch.full((w.batch, w.max_len // 4, 64), sentinel, dtype=torch.int16,
+                       device="cuda").view(torch.bfloat16)
     sel = torch.empty((w.batch, w.n_query, 512), dtype=torch.int32, device="cuda")
     n_sel = torch.empty((w.batch, w.n_query), dtype=torch.int32, device="cuda")
     out, lse, _, _ = Q.forward(shp, dev_bf16(w.q_idx), dev_bf16(w.k_idx), k_cmp, dev_bf16(w.q),
@@ -281,6 +284,11 @@ def test_forward_cfg1_decode_128k():
     want_sel, want_n = padded_sel(res, w.batch, w.n_query, w.lens)
     np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
     np.testing.assert_array_equal(n_sel.cpu().numpy(), want_n)
+    kc = host_u16(k_cmp)
+    for b in range(w.batch):
+        nb = int(w.lens[b]) // 4
+        np.testing.assert_array_equal(kc[b, :nb], res["kc"][b], err_msg=f"k_cmp of sequence {b}")
+        assert (kc[b, nb:] == sentinel).all(), f"k_cmp written past block {nb} of sequence {b}"
     got = host_f64_from_bf16(out)
     keys = sorted(res["out"].keys())
     check_close(np.stack([got[b, i] for b, i in keys]), np.stack([res["out"][k] for k in keys]))
@@ -307,6 +315,9 @@ def test_forward_incremental_decode_steps():
         res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, lens, 4)
         want_sel, want_n = padded_sel(res, 2, 4, lens)
         np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
+        kc = host_u16(k_cmp)
+        for b in range(2):
+            np.testing.assert_array_equal(kc[b, :lens[b] // 4], res["kc"][b])
         got = host_f64_from_bf16(out)
         keys = sorted(res["out"].keys())
         check_close(np.stack([got[b, i] for b, i in keys]), np.stack([res["out"][k] for k in keys]))
