@@ -168,7 +168,7 @@ def decode_leg(args, Q, W, torch, np, flush):
     step_ms, kstats, wall = timed_steps(step, args.steps, flush, Q, torch)
     sel_h = sel.cpu().numpy()
     nsel_h = n_sel.cpu().numpy()
-    # algorithmic bytes per launch of each kernel
+    # algorithmic bytes per step of each kernel
     lens_h = w.lens.astype(np.int64)
     kcmp_bytes = int(sum(((int(l) - 1) // 4) * 128 for l in lens_h))
     union_tokens = 0
@@ -367,7 +367,9 @@ def main():
     dom_name, dom_stat = dom
     roof = None
     if dom_name in d["algo"]:
-        bound, nbytes, what = d["algo"][dom_name]
+        bound, step_nbytes, what = d["algo"][dom_name]
+        # the algorithmic bytes are per step; a step may split a kernel over launches
+        nbytes = step_nbytes / max(dom_stat["launches_per_step"], 1.0)
         ach = nbytes / (dom_stat["avg_us"] * 1e-6) / 1e9
         roof = {"bound": bound, "kernel": dom_name, "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,

@@ -45,6 +45,13 @@ struct CompressFuse {
 // Whether launch_index_topk can take the compression over (else it is a
 // separate launch_compress before it).
 bool topk_can_fuse_compress(const Dims& d, TopkPath path);
+// The table engine's two passes on their own (launch_index_topk runs both):
+// scoring (score table and group maxima in ws) and the per-row pick.
+hipError_t launch_table_score(const Dims& d, const uint16_t* q_idx, uint16_t* k_cmp,
+                              const int32_t* lens, void* ws, hipStream_t s,
+                              const CompressFuse* fuse);
+hipError_t launch_table_pick(const Dims& d, const int32_t* lens, int32_t* sel, int32_t* n_sel,
+                             void* ws, hipStream_t s);
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
                              uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
                              int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s,

@@ -1575,14 +1575,34 @@ size_t topk_workspace_bytes(const Dims& d, TopkPath path) {
 }
 
 void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n) {
-  if (path == TopkPath::kTable) {
-    (void)ws;  // nothing to clear: every count is written by the filter
-    *ptr = nullptr;
-    *n = 0;
-  } else {
-    *ptr = nullptr;
-    *n = 0;
-  }
+  (void)d;
+  (void)path;
+  (void)ws;  // nothing to clear: every word the engines read is written first
+  *ptr = nullptr;
+  *n = 0;
+}
+
+hipError_t launch_table_score(const Dims& d, const uint16_t* q_idx, uint16_t* k_cmp,
+                              const int32_t* lens, void* ws, hipStream_t s,
+                              const CompressFuse* fuse) {
+  if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  if (fuse && !topk_can_fuse_compress(d, TopkPath::kTable)) return hipErrorInvalidValue;
+  TableWs w = carve_table(d, ws, nullptr);
+  const unsigned qg = (unsigned)((d.Nq + 3) / 4);
+  const dim3 grid((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
+  QSA_LAUNCH(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores,
+             table_stride(d), w.gmax, group_stride(d), d.Lmax, d.Nq,
+             fuse ? fuse->k_idx : nullptr, fuse ? fuse->first_block : nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_pick(const Dims& d, const int32_t* lens, int32_t* sel, int32_t* n_sel,
+                             void* ws, hipStream_t s) {
+  if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  TableWs w = carve_table(d, ws, nullptr);
+  QSA_LAUNCH(table_pick_kernel, dim3((unsigned)((size_t)d.B * d.Nq)), dim3(kPickThreads), 0, s,
+             w.scores, table_stride(d), w.gmax, group_stride(d), lens, sel, n_sel, d.Lmax, d.Nq);
+  return hipGetLastError();
 }
 
 bool topk_can_fuse_compress(const Dims& d, TopkPath path) {
@@ -1598,17 +1618,10 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   const dim3 grid_q((unsigned)d.Nq, (unsigned)d.B);
   if (path == TopkPath::kTable) {
-    TableWs w = carve_table(d, ws, nullptr);
-    const int ts = table_stride(d), gs = group_stride(d);
-    const size_t rows = (size_t)d.B * d.Nq;
     (void)ws_zeroed;
-    const unsigned qg = (unsigned)((d.Nq + 3) / 4);
-    const dim3 grid_s((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
-    QSA_LAUNCH(score_table_kernel, grid_s, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores, ts,
-               w.gmax, gs, d.Lmax, d.Nq, fuse ? fuse->k_idx : nullptr,
-               fuse ? fuse->first_block : nullptr);
-    QSA_LAUNCH(table_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, s, w.scores, ts,
-               w.gmax, gs, lens, sel, n_sel, d.Lmax, d.Nq);
+    const hipError_t e = launch_table_score(d, q_idx, k_cmp, lens, ws, s, fuse);
+    if (e != hipSuccess) return e;
+    return launch_table_pick(d, lens, sel, n_sel, ws, s);
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
