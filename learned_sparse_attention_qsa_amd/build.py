@@ -24,6 +24,10 @@ HIP_FLAGS = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-result"]
 SOURCES = ["compress.hip", "expand.hip", "topk.hip", "attend.hip", "api.cpp"]
+# The stream scorer's MFMA results are read by a vector epilogue every tile:
+# the VGPR form of MFMA keeps them out of accumulation registers (no
+# v_accvgpr_read per value).
+FILE_FLAGS = {"topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:
@@ -35,7 +39,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [_hipcc(), "-O2", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

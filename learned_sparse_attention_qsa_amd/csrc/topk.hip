@@ -52,8 +52,7 @@ constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine
 constexpr int kGroup = 16;         // blocks per group maximum (table engine)
 constexpr int kSelCap = 8192;      // candidates a select workgroup holds in LDS
 constexpr int kHistW = 256;        // stream engine: sample-histogram bins per query
-constexpr int kStreamTile = 64;    // blocks per key tile (stream engine)
-constexpr int kStreamQ = 64;       // queries per stream workgroup (16 per wavefront)
+constexpr int kStreamQ = 64;       // queries per stream workgroup (32 per wavefront pair)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -1097,14 +1096,21 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
 }
 
 // ------------------------------------------------------------------ STREAM
-// Stream engine.  A workgroup holds 64 queries x 4 heads stationary in
-// registers and streams the compressed keys through an LDS ring in tiles of
-// 64 blocks (MFMA 32x32x16).  Two phases over the same pipeline:
+// Stream engine.  A workgroup takes 64 queries.  Wavefront w holds the A
+// fragments of the 32 queries of group w >> 1 (32 queries x 4 heads = 4 row
+// tiles x 4 k-steps, stationary in registers) and walks the 32-block column
+// tiles of parity w & 1, loading each tile's B fragments (compressed keys)
+// straight from memory into registers one tile ahead: every block is read
+// by two wavefronts, and the scan needs no LDS staging and no barriers.
+// MFMA 32x32x16; the 32 queries form two halves of 16 whose MFMAs and
+// epilogues alternate (one half's epilogue runs under the other half's
+// MFMAs).  Two phases over the same pipeline:
 //
-//  1. sample: every kSampleStride-th tile.  Each query histograms its sample
-//     scores (256 bins, 32 per octave, from a base four octaves below the
-//     best score of the first sample tile) and takes as its bound tau the
-//     lower edge of the bin holding its kSampleRank-th best sample score.
+//  1. sample: the column tiles c with c mod 64 in {0, 1} (1/32 of the
+//     blocks).  Each query histograms its sample scores (256 bins, 32 per
+//     octave, from a base four octaves below the best score of tiles 0 and
+//     1) and takes as its bound tau the lower edge of the bin holding its
+//     kSampleRank-th best sample score.
 //  2. filter: every tile; a block is a candidate if its score is strictly
 //     above tau.  Candidates are queued in LDS by the scoring lanes and
 //     drained 64 at a time into the query's list in HBM.
@@ -1113,96 +1119,69 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
 // 512 blocks score strictly above tau, every block at or below tau is beaten
 // by 512 others and the list holds the whole top 512; the select kernel then
 // finishes exactly.  Otherwise (or if a list overflowed) that row takes the
-// exact whole-row path.  With 1/32 of the tiles sampled and rank 40, about
+// exact whole-row path.  With 1/32 of the blocks sampled and rank 40, about
 // 40 x 32 = 1,280 blocks per query pass, and the bound fails only when over
 // 40 of the samples lie above the true 512th score, about 1e-7 per query for
 // independent scores.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-constexpr int kRing = 8;           // LDS tile slots of the stream engine
-constexpr int kListCap = 4096;     // candidate list entries per query
-constexpr int kSampleStride = 32;  // one sample tile in 32
-constexpr int kSampleRank = 40;    // tau: the 40th best sample score (bin edge)
+constexpr int kListCap = 4096;    // candidate list entries per query
+constexpr int kColTile = 32;      // blocks per MFMA column tile
+constexpr int kKeyBufs = 2;       // key tiles in registers: the current one and the next
+constexpr int kSampleStride = 64; // sample column tiles: c mod 64 in {0, 1}
+constexpr int kSampleRank = 40;   // tau: the 40th best sample score (bin edge)
 // sample histogram: bins of (score bits >> 18), i.e. 32 per octave, 256 bins =
-// 8 octaves from a base 4 octaves (128 bins) below the first sample tile's best
+// 8 octaves from a base 4 octaves (128 bins) below the best of tiles 0 and 1
 constexpr int kSampleShift = 18;
 constexpr int kSampleBase = 128;
-// survivors one tile can add to a wavefront's queue, plus fewer than 64 held over
-constexpr int kQueue = kStreamTile * 16 + 64;
+// survivors one position can add to a wavefront's queue, plus fewer than 64
+// held over
+constexpr int kQueue = 32 * kColTile + 64;
 constexpr int kHistWords = kHistW / 2 + 1;  // 256 packed 16-bit bins + the spare bin
 
-// Barriers of the stream engine: no wait on vector-memory stores, so list
-// appends stay in flight across tiles.
-__device__ __forceinline__ void stream_barrier_compute() {
+__device__ __forceinline__ void stream_barrier() {
+  // no wait on vector memory: the key prefetch stays in flight
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// Loader: the tiles up to two past the one just consumed must have landed;
-// the (kRing - 3) later tiles (8 loads each) may still be in flight.
-__device__ __forceinline__ void stream_barrier_loader() {
-  asm volatile("s_waitcnt vmcnt(40) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-static_assert(8 * (kRing - 3) == 40, "loader wait count");
 
-// Tile of the workgroup's stream at position i: the ns sample tiles first,
-// then every tile.
-__device__ __forceinline__ int stream_tile(int i, int ns) { return i < ns ? i * kSampleStride : i - ns; }
-
-// Loader wavefront: copy one 64-block tile of compressed keys straight from
-// HBM into ring slot `slot` (8 KiB, eight 16-byte-per-lane DMA loads).  The
-// slot is stored swizzled: block row r, 16-byte chunk c lives at r*8 + (c ^ (r&7)).
-// Rows past bt_wg load row 0 instead (their scores are masked by the consumer).
-__device__ __forceinline__ void dma_tile(uint4* slot, const uint4* kb, int tile, int bt_wg) {
+// B fragments of column tile c (MFMA B layout: lane -> block 32c + lane&31,
+// dims 16 ks + 8 (lane>>5)).  Blocks at or past bt_g read block 0 (their
+// scores are masked).
+__device__ __forceinline__ void load_cols(const uint4* kb, int c, int bt_g, uint4 (&bv)[4]) {
   const int lane = lane_id();
+  int j = c * kColTile + (lane & 31);
+  if (j >= bt_g) j = 0;
+  const uint4* p = kb + (size_t)j * 8 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int s16 = i * 64 + lane;
-    const int row = s16 >> 3;
-    const int ch = (s16 & 7) ^ (row & 7);
-    int j = tile * kStreamTile + row;
-    if (j >= bt_wg) j = 0;
-    __builtin_amdgcn_global_load_lds(kb + (size_t)j * 8 + ch, (lds_void_t*)(slot + i * 64), 16, 0, 0);
-  }
+  for (int ks = 0; ks < 4; ++ks) bv[ks] = p[2 * ks];
 }
 
-// B fragments (compressed keys) of one 32-block half (column tile ct) of a
-// 64-block tile, read from the LDS ring.
-__device__ __forceinline__ void load_b(const uint4* kt, int ct, bf16x8 (&bf)[4]) {
-  const int lane = lane_id();
-  const int row = ct * 32 + (lane & 31);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int ch = ks * 2 + (lane >> 5);
-    bf[ks] = as_bf16x8(kt[row * 8 + (ch ^ (row & 7))]);
-  }
-}
-
-// Scores of one 32-block half for the wavefront's 16 queries x 4 heads.
-__device__ __forceinline__ void mma_half(const bf16x8 (&bf)[4], const bf16x8 (&A)[2][4],
+// MFMAs of half kHalf (row tiles 2 kHalf, 2 kHalf + 1) against one column tile.
+template <int kHalf>
+__device__ __forceinline__ void mma_rows(const uint4 (&bv)[4], const bf16x8 (&A)[4][4],
                                          f32x16 (&acc)[2]) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[rt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) acc[rt] = mfma32(A[rt][ks], bf[ks], acc[rt]);
+    for (int r = 0; r < 2; ++r) acc[r] = mfma32(A[2 * kHalf + r][ks], as_bf16x8(bv[ks]), acc[r]);
 }
 
 __device__ __forceinline__ int rdl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
 // Per-wavefront state.  Slot (rt, c) of a lane scores local query
-// rt*8 + c*2 + (lane >> 5); the lane keeps that query's base / tau.
+// rt*8 + c*2 + (lane >> 5) of the group (0..31).
 struct Stream {
-  float tau_l[2][4];          // filter bound of the slot's query (phase 2)
-  int base_l[2][4];           // histogram base of the slot's query (phase 1)
+  float tau_l[4][4];          // filter bound of the slot's query (phase 2)
+  int base_l[4][4];           // histogram base of the slot's query (phase 1)
   int tq0;                    // position of local query (lane >> 5)
   int nq_left;                // queries of the batch from local query (lane >> 5) on
   uint64_t* lists;            // list of local query 0; query q at + q * kListCap
-  uint32_t (*h)[kHistWords];  // the wavefront's 16 sample histograms
-  uint32_t* cnt;              // 16 list lengths
-  uint32_t* mx;               // 16 best scores of the first sample tile
-  uint64_t* queue;            // survivors not yet drained
+  uint32_t (*h)[kHistWords];  // the group's 32 sample histograms
+  uint32_t* cnt;              // the group's 32 list lengths
+  uint32_t* mx;               // the group's 32 best scores of tiles 0 and 1
+  uint64_t* queue;            // this wavefront's survivors not yet drained
 };
 
 __device__ __forceinline__ int slot_off(int rt, int c) { return rt * 8 + c * 2; }
@@ -1214,18 +1193,19 @@ __device__ __forceinline__ bool slot_valid(const Stream& st, int rt, int c, int 
   return off < st.nq_left && tq >= 0 && j < (tq >> 2);
 }
 
-// Phase 1 epilogue of one 32-block half: histogram the sample scores (first
-// sample tile: track each query's best score instead).
-template <bool kFirst>
-__device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[2], int tile, int ct) {
+// Phase 1 epilogue of one half: histogram the sample scores (the first sample
+// tiles: track each query's best score instead).
+template <bool kFirst, int kHalf>
+__device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[2], int col) {
   const int lane = lane_id();
-  const int j = tile * kStreamTile + ct * 32 + (lane & 31);
+  const int j = col * kColTile + (lane & 31);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t bits = relu_sum_bits(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
-                                          acc[rt][4 * c + 3]);
+      const int rt = 2 * kHalf + r;
+      const uint32_t bits =
+          relu_sum_bits(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
       const bool valid = slot_valid(st, rt, c, j);
       const int q = slot_off(rt, c) + (lane >> 5);
       if (kFirst) {
@@ -1240,58 +1220,45 @@ __device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[
     }
 }
 
-// Phase 2 epilogue of one 32-block half, in two parts so that the next
-// MFMAs can be issued between them: filter_scores computes the scores and
-// pass masks (straight-line vector code), filter_enqueue queues the blocks
-// scoring above their query's bound behind the qn already queued (only slots
-// with survivors do vector work).  kFull: every block of the tile is below
-// every query's own block.
-struct Filtered {
-  float sc[2][4];
-  bool pass[2][4];
-  uint64_t mk[2][4];  // the slots' ballots (scalar registers)
-  uint64_t any;
-  uint32_t tag;       // block id | (lane half) << 28
-};
-
-template <bool kFull>
-__device__ __forceinline__ void filter_scores(const Stream& st, const f32x16 (&acc)[2], int tile,
-                                              int ct, Filtered& f) {
+// Phase 2 epilogue of one half: the scores, then the enqueue of the blocks
+// scoring above their query's bound behind the qn already queued.  Each lane
+// takes its place in the queue from a wavefront prefix count of its passing
+// slots (no per-slot branches); only lanes with survivors loop over them.  A
+// queue entry is score bits (31, the sign is 0) << 33 | local query << 28 |
+// block id.  kFull: every block of the tile is below every query's own block.
+template <bool kFull, int kHalf>
+__device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2], int col,
+                                               int qn) {
   const int lane = lane_id();
-  const int j = tile * kStreamTile + ct * 32 + (lane & 31);
-  f.any = 0;
+  const int j = col * kColTile + (lane & 31);
+  float sc[8];
+  uint32_t pm = 0;  // bit r*4 + c: slot (2 kHalf + r, c) passes
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      f.sc[rt][c] = relu_sum(acc[rt][4 * c], acc[rt][4 * c + 1], acc[rt][4 * c + 2],
-                             acc[rt][4 * c + 3]);
-      bool p = f.sc[rt][c] > st.tau_l[rt][c];
+      const int rt = 2 * kHalf + r;
+      sc[r * 4 + c] =
+          relu_sum(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
+      bool p = sc[r * 4 + c] > st.tau_l[rt][c];
       if (!kFull) p = p && slot_valid(st, rt, c, j);
-      f.pass[rt][c] = p;
-      f.mk[rt][c] = __ballot(p);
-      f.any |= f.mk[rt][c];
+      pm |= (p ? 1u : 0u) << (r * 4 + c);
     }
-  f.tag = (uint32_t)j | ((uint32_t)(lane >> 5) << 28);
-}
-
-__device__ __forceinline__ int filter_enqueue(Stream& st, const Filtered& f, int qn) {
-  if (f.any == 0) return qn;
+  if (__ballot(pm != 0u) == 0) return qn;
+  const uint32_t mine = (uint32_t)__popc(pm);
+  const uint32_t incl = wave_incl_sum(mine);
+  uint32_t pos = (uint32_t)qn + incl - mine;
+  while (pm) {
+    const int idx = __ffs(pm) - 1;
+    pm &= pm - 1;
+    float v = sc[0];  // (selects, not a dynamic register index)
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint64_t m = f.mk[rt][c];
-      if (m == 0) continue;
-      if (f.pass[rt][c]) {
-        const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)qn));
-        st.queue[pos] = ((uint64_t)__float_as_uint(f.sc[rt][c]) << 32) |
-                        (uint64_t)(f.tag + ((uint32_t)slot_off(rt, c) << 28));
-      }
-      qn += __popcll(m);
-    }
-  return qn;
+    for (int k = 1; k < 8; ++k) v = idx == k ? sc[k] : v;
+    const uint32_t q = (uint32_t)((2 * kHalf + (idx >> 2)) * 8 + (idx & 3) * 2 + (lane >> 5));
+    st.queue[pos++] =
+        ((uint64_t)__float_as_uint(v) << 33) | ((uint64_t)q << 28) | (uint64_t)(uint32_t)j;
+  }
+  return qn + (int)lane_read(incl, 63);
 }
 
 // Append the queued survivors to their queries' lists, 64 at a time.
@@ -1302,130 +1269,155 @@ __device__ __forceinline__ void stream_drain(Stream& st, int qn) {
     const int i = i0 + lane;
     if (i < qn) {
       const uint64_t e = st.queue[i];
-      const uint32_t lo = (uint32_t)e;
-      const int q = (int)(lo >> 28);
+      const int q = (int)((e >> 28) & 31u);
       const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
       // a list that overflows keeps counting: the select kernel sees it
       if (pos < (uint32_t)kListCap)
-        st.lists[(size_t)q * kListCap + pos] = make_key((uint32_t)(e >> 32), lo & 0x0fffffffu);
+        st.lists[(size_t)q * kListCap + pos] =
+            make_key((uint32_t)(e >> 33), (uint32_t)e & 0x0fffffffu);
     }
   }
   wave_sync_lds();
 }
 
-// After the sample phase: each query's bound from its histogram.  Sets the
-// lanes' slot copies and returns, on lane q < 16, the bits of query q's bound.
-__device__ __forceinline__ int stream_set_bounds(Stream& st, int bt_q_lane) {
-  const int lane = lane_id();
-  int tau_v = 0;
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t* h = st.h[i];
-    const uint32_t w0 = h[2 * lane], w1 = h[2 * lane + 1];
-    uint32_t total = (w0 & 0xffffu) + (w0 >> 16) + (w1 & 0xffffu) + (w1 >> 16);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) total += (uint32_t)__shfl_xor((int)total, off);
-    int bound;
-    if (rdl(bt_q_lane, i) <= kListCap) {
-      bound = (int)0xbf800000u;  // -1.0f: the whole row fits the list, keep every block
-    } else if (total >= (uint32_t)kSampleRank) {
-      int m;
-      uint32_t sfx;
-      wave_suffix_bin4(w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16, kSampleRank, m, sfx);
-      bound = (max(0, (int)(st.mx[i] >> kSampleShift) - kSampleBase) + m) << kSampleShift;  // bin edge
-    } else {
-      bound = 0;  // too few samples above the base: keep every positive score
-    }
-    if (lane == i) tau_v = bound;
-  }
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      st.tau_l[rt][c] = __int_as_float(__shfl(tau_v, slot_off(rt, c) + (lane >> 5)));
-  return tau_v;
+// Phase epilogue of one half, by phase: 0 the first sample tiles, 1 a sample
+// tile, 2 a filter tile below every query's own block, 3 a masked filter
+// tile.
+template <int kPhase, int kHalf>
+__device__ __forceinline__ void epilogue(Stream& st, const f32x16 (&acc)[2], int col, int& qn) {
+  if (kPhase <= 1)
+    sample_epilogue<kPhase == 0, kHalf>(st, acc, col);
+  else
+    qn = filter_epilogue<kPhase == 2, kHalf>(st, acc, col, qn);
 }
 
-// One stream position k (tile `tile`): the MFMAs of its second half, the
-// epilogue of its first half (computed by the previous position), the MFMAs
-// of the next position's first half, the epilogue of the second half; then
-// a drain of the survivor queue when it holds a wavefront's worth, and the
-// barrier.  kPhase: 0 the first sample tile, 1 a sample tile, 2 a filter tile
-// below every query's own block, 3 a masked filter tile.  Each phase runs in
-// a loop of its own, so the epilogue interleaves with the MFMAs.
+// Column tile of position i of a wavefront of parity par: ns sample tiles,
+// then every tile of its parity.
+__device__ __forceinline__ int stream_col(int i, int ns, int par) {
+  return i < ns ? i * kSampleStride + par : 2 * (i - ns) + par;
+}
+
+// One position of a wavefront's scan: column tile `col`, its B fragments in
+// bv[kBuf].  Issues the loads of the next position's tile (`colf`), then
+// half 0's MFMAs, the epilogue of the previous position's half 1 (when
+// `prev`: column `colp`), half 1's MFMAs and half 0's epilogue.  A drain of
+// the survivor queue goes first, so that its stores precede the loads.
+template <int kPhase, int kBuf, bool kPrev>
+__device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[4][4],
+                                           uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                           f32x16 (&accY)[2], int col, int colp, int colf,
+                                           const uint4* kb, int bt_g, int& qn) {
+  if (kPhase >= 2 && qn >= 64) {
+    stream_drain(st, qn);
+    qn = 0;
+  }
+  load_cols(kb, colf, bt_g, bv[kBuf ^ 1]);
+  mma_rows<0>(bv[kBuf], A, accX);
+  if (kPrev) epilogue<kPhase, 1>(st, accY, colp, qn);
+  mma_rows<1>(bv[kBuf], A, accY);
+  epilogue<kPhase, 0>(st, accX, col, qn);
+}
+
+// Position i of a phase's scan, its key tile in buffer kBuf.
+template <int kPhase, bool kPrev, int kBuf>
+__device__ __forceinline__ void stream_pos_at(Stream& st, const bf16x8 (&A)[4][4],
+                                              uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                              f32x16 (&accY)[2], int i, int ns, int par,
+                                              const uint4* kb, int bt_g, int& qn, int& colp) {
+  const int col = stream_col(i, ns, par), colf = stream_col(i + 1, ns, par);
+  stream_pos<kPhase, kBuf, kPrev>(st, A, bv, accX, accY, col, colp, colf, kb, bt_g, qn);
+  colp = col;
+}
+
+// Positions [i0, i1) of a phase whose first position uses buffer kB0: the
+// first one (no pending half), then pairs of straight-line positions, so
+// that the buffers never move between registers.
+template <int kPhase, int kB0>
+__device__ __forceinline__ void stream_positions(Stream& st, const bf16x8 (&A)[4][4],
+                                                 uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                                 f32x16 (&accY)[2], int i0, int i1, int ns,
+                                                 int par, const uint4* kb, int bt_g, int& qn,
+                                                 int& colp) {
+  stream_pos_at<kPhase, false, kB0>(st, A, bv, accX, accY, i0, ns, par, kb, bt_g, qn, colp);
+  int i = i0 + 1;
+  for (; i + 1 < i1; i += 2) {
+    stream_pos_at<kPhase, true, kB0 ^ 1>(st, A, bv, accX, accY, i, ns, par, kb, bt_g, qn, colp);
+    stream_pos_at<kPhase, true, kB0>(st, A, bv, accX, accY, i + 1, ns, par, kb, bt_g, qn, colp);
+  }
+  if (i < i1)
+    stream_pos_at<kPhase, true, kB0 ^ 1>(st, A, bv, accX, accY, i, ns, par, kb, bt_g, qn, colp);
+}
+
+// Positions [i0, i1) of one phase, then the last position's half-1 epilogue.
+// The queue holds at most 63 + 2 x 512 entries after a position and 63 + 512
+// after that last epilogue, within kQueue.
 template <int kPhase>
-__device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[2][4],
-                                           uint4 (*ring)[kStreamTile * 8], f32x16 (&accA)[2],
-                                           f32x16 (&accB)[2], bf16x8 (&bf)[4], int k, int tile,
-                                           int& qn) {
-  // bf: this position's second-half fragments, read during the previous
-  // position.  The next position's tile has landed (the loader waits for
-  // two tiles ahead), so both of its halves are read here, early.
-  bf16x8 bn[4], bf_next[4];
-  // (the slot of position k+1 is always LDS of the ring; unused past the end)
-  load_b(ring[(k + 1) % kRing], 0, bn);
-  load_b(ring[(k + 1) % kRing], 1, bf_next);
-  mma_half(bf, A, accB);
-  if (kPhase <= 1) {
-    sample_epilogue<kPhase == 0>(st, accA, tile, 0);
-    // (unconditional, also past the last position: a conditional update would
-    // make the compiler copy the accumulators, and the copies wait for the MFMAs)
-    mma_half(bn, A, accA);
-    sample_epilogue<kPhase == 0>(st, accB, tile, 1);
-  } else {
-    Filtered fa, fb;
-    filter_scores<kPhase == 2>(st, accA, tile, 0, fa);
-    mma_half(bn, A, accA);  // issued before the branchy enqueue: keeps the pipe busy
-    qn = filter_enqueue(st, fa, qn);
-    filter_scores<kPhase == 2>(st, accB, tile, 1, fb);
-    qn = filter_enqueue(st, fb, qn);
-    if (qn >= 64) {
+__device__ __forceinline__ void stream_phase(Stream& st, const bf16x8 (&A)[4][4],
+                                             uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                             f32x16 (&accY)[2], int i0, int i1, int ns, int par,
+                                             const uint4* kb, int bt_g, int& qn, int& colp) {
+  if (i1 <= i0) return;
+  // (position i uses buffer i & 1; positions are straight-line code, so that
+  // the compiler interleaves epilogues with MFMAs)
+  if (i0 & 1)
+    stream_positions<kPhase, 1>(st, A, bv, accX, accY, i0, i1, ns, par, kb, bt_g, qn, colp);
+  else
+    stream_positions<kPhase, 0>(st, A, bv, accX, accY, i0, i1, ns, par, kb, bt_g, qn, colp);
+  {
+    if (kPhase >= 2 && qn >= 64) {  // room for the pending half's survivors
       stream_drain(st, qn);
       qn = 0;
     }
+    epilogue<kPhase, 1>(st, accY, colp, qn);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) bf[i] = bf_next[i];
-  if (kPhase == 0) {
-    // histogram base: four octaves below the best score of the first sample
-    // tile (robust to a first tile holding outlier blocks)
-    const int lane = lane_id();
-    wave_sync_lds();
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        st.base_l[rt][c] =
-            max(0, (int)(st.mx[slot_off(rt, c) + (lane >> 5)] >> kSampleShift) - kSampleBase);
-  }
-  stream_barrier_compute();
 }
 
-// Grid (ceil(Nq/64), B); 5 wavefronts: 4 compute wavefronts x 16 queries and
-// one loader wavefront feeding an 8-slot LDS ring of key tiles.  Compute
-// wavefronts run the next half-tile's MFMAs before the current half's
-// epilogue (double-buffered accumulators), so matrix and vector work overlap.
-__global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
+// After the sample phase: the bound of local query q (lane q of the wavefront
+// computing it), from its histogram.
+__device__ __forceinline__ int query_bound(const Stream& st, int q, bool fits) {
+  const int lane = lane_id();
+  const uint32_t* h = st.h[q];
+  const uint32_t w0 = h[2 * lane], w1 = h[2 * lane + 1];
+  uint32_t total = (w0 & 0xffffu) + (w0 >> 16) + (w1 & 0xffffu) + (w1 >> 16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) total += (uint32_t)__shfl_xor((int)total, off);
+  if (fits) return (int)0xbf800000u;  // -1.0f: the whole row fits the list, keep every block
+  if (total < (uint32_t)kSampleRank) return 0;  // too few samples above the base: keep every positive score
+  int m;
+  uint32_t sfx;
+  wave_suffix_bin4(w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16, kSampleRank, m, sfx);
+  return (max(0, (int)(st.mx[q] >> kSampleShift) - kSampleBase) + m) << kSampleShift;  // bin edge
+}
+
+// Grid (ceil(Nq/64), B); 4 wavefronts: two per group of 32 queries, one per
+// column-tile parity.
+__global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
                                                            const uint16_t* __restrict__ k_cmp,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ lists,
                                                            uint32_t* __restrict__ list_cnt,
                                                            int32_t* __restrict__ tau_out, int Lmax,
                                                            int Nq) {
-  __shared__ uint4 ring[kRing][kStreamTile * 8];
   __shared__ uint32_t s_h[kStreamQ][kHistWords];
   __shared__ uint32_t s_mx[kStreamQ];
   __shared__ uint32_t s_cnt[kStreamQ];
+  __shared__ int32_t s_tau[kStreamQ];
   __shared__ uint64_t s_queue[4][kQueue];
 
   const int qbase = blockIdx.x * kStreamQ, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  // (wavefront-uniform, so that the scan's loop control stays scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 1, par = wave & 1;
   const int len = clampi(lens[b], 0, Lmax);
   const int nbp = Lmax >> 2;
-  const int t_last = query_t(len, Nq, min(qbase + kStreamQ - 1, Nq - 1));
-  const int bt_wg = t_last >= 0 ? (t_last >> 2) : 0;
-  const int ntiles = (bt_wg + kStreamTile - 1) / kStreamTile;
-  const int ns = (ntiles + kSampleStride - 1) / kSampleStride;  // sample tiles
-  const int nseq = ns + ntiles;                                  // stream positions
+  const int gq0 = qbase + grp * 32;  // first query of the group
+  const int t_last = query_t(len, Nq, min(gq0 + 31, Nq - 1));
+  const int bt_g = (gq0 < Nq && t_last >= 0) ? (t_last >> 2) : 0;  // blocks the group scans
+  const int ncol = (bt_g + kColTile - 1) / kColTile;
+  // this wavefront's positions: ns sample tiles, then nf filter tiles
+  const int ns = ncol > par ? (ncol - 1 - par) / kSampleStride + 1 : 0;
+  const int nf = ncol > par ? (ncol - 1 - par) / 2 + 1 : 0;
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
   for (int i = tid; i < kStreamQ * kHistWords; i += blockDim.x) (&s_h[0][0])[i] = 0u;
   if (tid < kStreamQ) {
@@ -1433,90 +1425,99 @@ __global__ __launch_bounds__(320) void score_stream_kernel(const uint16_t* __res
     s_cnt[tid] = 0u;
   }
 
-  if (wave == 4) {
-    // ---------------- loader
-    for (int i = 0; i < kRing - 1; ++i) dma_tile(ring[i], kb, i < nseq ? stream_tile(i, ns) : 0, bt_wg);
-    stream_barrier_loader();
-    for (int k = 0; k < nseq; ++k) {
-      const int i = k + kRing - 1;
-      dma_tile(ring[i % kRing], kb, i < nseq ? stream_tile(i, ns) : 0, bt_wg);
-      stream_barrier_loader();
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may outlive the workgroup
-    return;
-  }
-
-  // ---------------- compute wavefronts
-  const int wq0 = qbase + wave * 16;
   Stream st;
-  st.h = &s_h[wave * 16];
-  st.mx = &s_mx[wave * 16];
-  st.cnt = &s_cnt[wave * 16];
+  st.h = &s_h[grp * 32];
+  st.mx = &s_mx[grp * 32];
+  st.cnt = &s_cnt[grp * 32];
   st.queue = s_queue[wave];
-  // Stationary A fragments: 2 row tiles x 4 k-steps.  Row (lane & 31) of row
-  // tile rt is query wq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
-  bf16x8 A[2][4];
+  // Stationary A fragments: 4 row tiles x 4 k-steps.  Row (lane & 31) of row
+  // tile rt is query gq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
+  bf16x8 A[4][4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int qa = wq0 + rt * 8 + ((lane & 31) >> 2);
+  for (int rt = 0; rt < 4; ++rt) {
+    const int qa = gq0 + rt * 8 + ((lane & 31) >> 2);
     const uint4* p = reinterpret_cast<const uint4*>(
         q_idx + (((size_t)b * Nq + min(qa, Nq - 1)) * kIdxHeads + (lane & 3)) * kIdxDim);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       A[rt][ks] = as_bf16x8(qa < Nq ? p[ks * 2 + (lane >> 5)] : zero_u4());
   }
-  int bt_min = 0x7fffffff;
-  st.tq0 = query_t(len, Nq, wq0 + (lane >> 5));
-  st.nq_left = Nq - wq0 - (lane >> 5);
-  // (lists of rows past the batch are never written: their slots never pass)
-  st.lists = lists + ((size_t)b * Nq + wq0) * kListCap;
+  // The A fragments only feed MFMAs: keep them in accumulation registers, so
+  // that the MFMA results (read by the vector epilogue) fit in VGPRs.
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(A[rt][ks]));
+  int bt_min = 0x7fffffff;
+  st.tq0 = query_t(len, Nq, gq0 + (lane >> 5));
+  st.nq_left = Nq - gq0 - (lane >> 5);
+  // (lists of rows past the batch are never written: their slots never pass)
+  st.lists = lists + ((size_t)b * Nq + gq0) * kListCap;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int qq = wq0 + slot_off(rt, c) + (lane >> 5);
+      const int qq = gq0 + slot_off(rt, c) + (lane >> 5);
       const int t = query_t(len, Nq, qq);
       bt_min = min(bt_min, (qq < Nq && t >= 0) ? (t >> 2) : 0);
       st.base_l[rt][c] = 0;
+      st.tau_l[rt][c] = 0.f;
     }
   // tiles entirely below every query's own block need no causal mask
   for (int off = 32; off >= 1; off >>= 1) bt_min = min(bt_min, __shfl_xor(bt_min, off));
-  // lane q < 16: own block of local query q
-  const int tl = query_t(len, Nq, wq0 + lane);
-  const int bt_q_lane = (lane < 16 && wq0 + lane < Nq && tl >= 0) ? (tl >> 2) : 0;
-  // Settle the A-fragment loads now, so no wait on vector memory (which
-  // would also wait for the list appends) is needed inside the tile loop.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  stream_barrier_compute();
+  // full filter positions: column tiles 2m + par with (2m + par + 1) * 32 <= bt_min
+  const int nfull = min(nf, max(0, (bt_min / kColTile - par + 1) / 2));
+  // lane q < 32: own block of local query q
+  const int tl = query_t(len, Nq, gq0 + lane);
+  const int bt_q_lane = (lane < 32 && gq0 + lane < Nq && tl >= 0) ? (tl >> 2) : 0;
+  // B fragments of the first kKeyBufs - 1 positions
+  uint4 bv[kKeyBufs][4];
+#pragma unroll
+  for (int i = 0; i < kKeyBufs - 1; ++i) load_cols(kb, stream_col(i, ns, par), bt_g, bv[i]);
+  stream_barrier();  // LDS initialised
 
-  // Pipeline over 32-block halves: position k's second half and position
-  // k+1's first half are in flight while position k's first half is filtered.
-  f32x16 accA[2], accB[2];
-  int qn = 0;     // survivors queued, not yet drained
-  int tau_q = 0;  // lane q < 16: bits of local query q's bound
-  const int nfull = min(ntiles, bt_min / kStreamTile);
-  bf16x8 bf[4];
-  if (nseq > 0) {
-    bf16x8 b0[4];
-    load_b(ring[0], 0, b0);
-    load_b(ring[0], 1, bf);
-    mma_half(b0, A, accA);
+  f32x16 accX[2], accY[2];
+  int qn = 0;  // survivors queued, not yet drained
+  int colp = 0;
+  // phase 0: the first sample tile of each parity (column tiles 0 and 1)
+  stream_phase<0>(st, A, bv, accX, accY, 0, min(ns, 1), ns, par, kb, bt_g, qn, colp);
+  stream_barrier();
+  // histogram base: four octaves below the best score of tiles 0 and 1
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      st.base_l[rt][c] =
+          max(0, (int)(st.mx[slot_off(rt, c) + (lane >> 5)] >> kSampleShift) - kSampleBase);
+  stream_phase<1>(st, A, bv, accX, accY, 1, ns, ns, par, kb, bt_g, qn, colp);
+  stream_barrier();
+  // bounds: wavefront of parity par computes local queries [16 par, 16 par + 16)
+  {
+    int tau_v = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int q = 16 * par + i;
+      const int bound = query_bound(st, q, rdl(bt_q_lane, q) <= kListCap);
+      if (lane == i) tau_v = bound;
+    }
+    if (lane < 16) s_tau[grp * 32 + 16 * par + lane] = tau_v;
   }
-  if (nseq > 0) stream_pos<0>(st, A, ring, accA, accB, bf, 0, 0, qn);
-  for (int k = 1; k < ns; ++k) stream_pos<1>(st, A, ring, accA, accB, bf, k, k * kSampleStride, qn);
-  if (nseq > 0) {
-    wave_sync_lds();
-    tau_q = stream_set_bounds(st, bt_q_lane);
-  }
-  for (int k = ns; k < ns + nfull; ++k) stream_pos<2>(st, A, ring, accA, accB, bf, k, k - ns, qn);
-  for (int k = ns + nfull; k < nseq; ++k) stream_pos<3>(st, A, ring, accA, accB, bf, k, k - ns, qn);
+  stream_barrier();
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      st.tau_l[rt][c] = __int_as_float(s_tau[grp * 32 + slot_off(rt, c) + (lane >> 5)]);
+  stream_phase<2>(st, A, bv, accX, accY, ns, ns + nfull, ns, par, kb, bt_g, qn, colp);
+  stream_phase<3>(st, A, bv, accX, accY, ns + nfull, ns + nf, ns, par, kb, bt_g, qn, colp);
   if (qn > 0) stream_drain(st, qn);
-  wave_sync_lds();
-  if (lane < 16 && wq0 + lane < Nq) {
-    list_cnt[(size_t)b * Nq + wq0 + lane] = st.cnt[lane];
+  // no key load may outlive the workgroup (the prefetch runs past the end)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  stream_barrier();
+  if (tid < kStreamQ && qbase + tid < Nq) {
+    list_cnt[(size_t)b * Nq + qbase + tid] = s_cnt[tid];
     // every list entry scores strictly above the bound: the select kernel
     // keeps keys at or above it, i.e. all of them
-    tau_out[(size_t)b * Nq + wq0 + lane] = tau_q;
+    tau_out[(size_t)b * Nq + qbase + tid] = s_tau[tid];
   }
 }
 
@@ -1625,7 +1626,7 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
-    QSA_LAUNCH(score_stream_kernel, grid, dim3(320), 0, s, q_idx, k_cmp, lens, w.lists, w.cnt,
+    QSA_LAUNCH(score_stream_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.lists, w.cnt,
                w.tau, d.Lmax, d.Nq);
     QSA_LAUNCH(select_kernel<true>, grid_q, dim3(256), 0, s, w.lists, w.cnt, 1, kListCap,
                (const int32_t*)w.tau, (const uint32_t*)nullptr, 0, q_idx, k_cmp, lens, sel, n_sel,
