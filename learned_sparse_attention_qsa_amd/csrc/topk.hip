@@ -50,7 +50,7 @@ namespace {
 constexpr int kHistBins = 2048;    // histogram bins of the table engine's pick
 constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine)
 constexpr int kGroup = 16;         // blocks per group maximum (table engine)
-constexpr int kSelCap = 8192;      // candidates a select workgroup holds in LDS
+constexpr int kSelCap = 4096;      // candidates a select workgroup holds in LDS (a stream list)
 constexpr int kHistW = 256;        // stream engine: sample-histogram bins per query
 constexpr int kStreamQ = 64;       // queries per stream workgroup (32 per wavefront pair)
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -408,7 +408,7 @@ __device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, con
 // radix select finds the 512th key and the winners are sorted.  Rows with too
 // few or too many candidates take the exact whole-row path.
 template <bool kRecompute>
-__global__ __launch_bounds__(256) void select_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int nsub,
     int seg_cap, const int32_t* __restrict__ tau_final, const uint32_t* __restrict__ table,
     int tstride, const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp,
