@@ -162,6 +162,23 @@ def test_topk_increasing_scores(flags):
     check_topk(w, flags)
 
 
+@pytest.mark.parametrize("flags", ENGINES)
+def test_topk_wide_score_range(flags):
+    # a few hundred outlier blocks score up to ~100x the rest, so the table
+    # engine's linear bins are coarse and its cutoff bin holds several score
+    # values: the bit-level refinement decides (scores stay exact integers)
+    say("topk wide range", flags)
+    w = custom(seed=41, lens=(90001, 70000), nq=6, parts=("index",))
+    rng = np.random.default_rng(41)
+    for b in range(w.batch):
+        blocks = rng.choice(int(w.lens[b]) // 4 - 64, size=300, replace=False)
+        for j, f in zip(blocks, rng.choice([8.0, 64.0], size=blocks.shape[0])):
+            rows = w.k_idx[b, 4 * j:4 * j + 4].view(np.uint16).astype(np.uint32) << 16
+            vals = rows.view(np.float32) * np.float32(f)
+            w.k_idx[b, 4 * j:4 * j + 4] = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    check_topk(w, flags)
+
+
 def test_topk_engines_agree_on_cfg1():
     say("topk cfg1 engines")
     w = W.make(1, parts=("index",))
