@@ -27,11 +27,11 @@
 //  bare k_cmp scan: the score table (4 B per query per block) written once.
 //
 //  STREAM (many queries, prefill-shaped): a workgroup holds 64 queries x 4
-//  heads stationary in registers and streams the compressed keys through LDS
-//  in tiles of 64 blocks, MFMA 32x32x16.  A first pass over 1/32 of the tiles
-//  sets each query's bound tau (the lower bin edge of its 40th best sample
-//  score); the second pass keeps the blocks scoring strictly above tau
-//  (about 1,300 per query).  If at least 512 blocks pass, no block at or
+//  heads stationary in registers and streams the compressed keys straight
+//  into registers in tiles of 32 blocks, MFMA 32x32x16.  A first pass over
+//  1/32 of the tiles sets each query's bound tau (the lower bin edge of its
+//  40th best sample score); the second pass keeps the blocks scoring
+//  strictly above tau (about 1,400 per query).  If at least 512 blocks pass, no block at or
 //  below tau can be in the top 512; the select kernel checks this.  No
 //  score table is written.
 //
@@ -52,7 +52,7 @@ constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine
 constexpr int kGroup = 16;         // blocks per group maximum (table engine)
 constexpr int kSelCap = 4096;      // candidates a select workgroup holds in LDS (a stream list)
 constexpr int kHistW = 256;        // stream engine: sample-histogram bins per query
-constexpr int kStreamQ = 64;       // queries per stream workgroup (32 per wavefront pair)
+constexpr int kStreamQ = 64;       // queries per stream workgroup (two groups of 32)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -1096,45 +1096,55 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
 }
 
 // ------------------------------------------------------------------ STREAM
-// Stream engine.  A workgroup takes 64 queries.  Wavefront w holds the A
-// fragments of the 32 queries of group w >> 1 (32 queries x 4 heads = 4 row
+// Stream engine.  A workgroup takes 64 queries in two groups of 32 and has
+// 8 wavefronts, four per group (two per SIMD).  Wavefront w holds the A
+// fragments of the 32 queries of group w / 4 (32 queries x 4 heads = 4 row
 // tiles x 4 k-steps, stationary in registers) and walks the 32-block column
-// tiles of parity w & 1, loading each tile's B fragments (compressed keys)
-// straight from memory into registers one tile ahead: every block is read
-// by two wavefronts, and the scan needs no LDS staging and no barriers.
-// MFMA 32x32x16; the 32 queries form two halves of 16 whose MFMAs and
-// epilogues alternate (one half's epilogue runs under the other half's
-// MFMAs).  Two phases over the same pipeline:
+// tiles c with c mod 4 = w mod 4, loading each tile's B fragments
+// (compressed keys) straight from memory into registers one tile ahead:
+// every block is read by two wavefronts, and the scan needs no LDS staging
+// and no barriers.  MFMA 32x32x16; the 32 queries form two halves of 16
+// whose MFMAs and epilogues alternate (one half's epilogue runs under the
+// other half's MFMAs), and the second wavefront on each SIMD fills the
+// gaps.  Two phases over the same pipeline:
 //
-//  1. sample: the column tiles c with c mod 64 in {0, 1} (1/32 of the
-//     blocks).  Each query histograms its sample scores (256 bins, 32 per
-//     octave, from a base four octaves below the best score of tiles 0 and
-//     1) and takes as its bound tau the lower edge of the bin holding its
-//     kSampleRank-th best sample score.
+//  1. sample: about every 32nd column tile (c = 128 i + 33 p for the four
+//     parities p).  Each query histograms its sample scores (256 bins, 64
+//     per octave, from a base two octaves below the best score of the first
+//     sample tile of each parity) and takes as its bound tau the lower edge
+//     of the bin holding its kSampleRank-th best sample score.
 //  2. filter: every tile; a block is a candidate if its score is strictly
-//     above tau.  Candidates are queued in LDS by the scoring lanes and
-//     drained 64 at a time into the query's list in HBM.
+//     above tau.  A lane with a candidate among its 8 scores queues one LDS
+//     record of them; records are drained 64 at a time into the queries'
+//     lists in HBM.
 //
 // tau is an estimate, so the result is verified, not assumed: if at least
 // 512 blocks score strictly above tau, every block at or below tau is beaten
 // by 512 others and the list holds the whole top 512; the select kernel then
 // finishes exactly.  Otherwise (or if a list overflowed) that row takes the
 // exact whole-row path.  With 1/32 of the blocks sampled and rank 40, about
-// 40 x 32 = 1,280 blocks per query pass, and the bound fails only when over
-// 40 of the samples lie above the true 512th score, about 1e-7 per query for
+// 40 x 32 = 1,280 blocks per query pass (plus those of the part of a bin
+// below the 40th sample), and the bound fails only when over 40 of the
+// samples lie above the true 512th score, about 1e-7 per query for
 // independent scores.
 constexpr int kListCap = 4096;    // candidate list entries per query
 constexpr int kColTile = 32;      // blocks per MFMA column tile
 constexpr int kKeyBufs = 2;       // key tiles in registers: the current one and the next
-constexpr int kSampleStride = 64; // sample column tiles: c mod 64 in {0, 1}
+constexpr int kPar = 4;           // column-tile parities: wavefronts per group of 32 queries
+constexpr int kStreamWaves = 2 * kPar;
+// sample column tiles: c = 128 i + 33 p for parity p (each parity's own
+// tiles, about every 32nd tile)
+constexpr int kSampleStride = 32 * kPar;
+constexpr int kSampleStep = 33;
+static_assert(kSampleStep % kPar == 1 && kSampleStep * (kPar - 1) < kSampleStride, "sample tiles");
 constexpr int kSampleRank = 40;   // tau: the 40th best sample score (bin edge)
-// sample histogram: bins of (score bits >> 18), i.e. 32 per octave, 256 bins =
-// 8 octaves from a base 4 octaves (128 bins) below the best of tiles 0 and 1
-constexpr int kSampleShift = 18;
+// sample histogram: bins of (score bits >> 17), i.e. 64 per octave, 256 bins =
+// 4 octaves from a base 2 octaves (128 bins) below the best of the first tiles
+constexpr int kSampleShift = 17;
 constexpr int kSampleBase = 128;
-// survivors one position can add to a wavefront's queue, plus fewer than 64
-// held over
-constexpr int kQueue = 32 * kColTile + 64;
+// records one position can add to a wavefront's queue (one per lane and
+// half), plus fewer than 64 held over
+constexpr int kQueue = 2 * 64 + 64;
 constexpr int kHistWords = kHistW / 2 + 1;  // 256 packed 16-bit bins + the spare bin
 
 __device__ __forceinline__ void stream_barrier() {
@@ -1180,8 +1190,12 @@ struct Stream {
   uint64_t* lists;            // list of local query 0; query q at + q * kListCap
   uint32_t (*h)[kHistWords];  // the group's 32 sample histograms
   uint32_t* cnt;              // the group's 32 list lengths
-  uint32_t* mx;               // the group's 32 best scores of tiles 0 and 1
-  uint64_t* queue;            // this wavefront's survivors not yet drained
+  uint32_t* mx;               // the group's 32 best scores of the first sample tiles
+  // this wavefront's records not yet drained (see filter_epilogue)
+  float4* rec_lo;             // scores of slots 0..3
+  float4* rec_hi;             // scores of slots 4..7
+  uint32_t* rec_at;           // column tile << 7 | half << 6 | lane
+  const int32_t* tau;         // the group's 32 bounds (LDS)
 };
 
 __device__ __forceinline__ int slot_off(int rt, int c) { return rt * 8 + c * 2; }
@@ -1190,7 +1204,7 @@ __device__ __forceinline__ int slot_off(int rt, int c) { return rt * 8 + c * 2; 
 __device__ __forceinline__ bool slot_valid(const Stream& st, int rt, int c, int j) {
   const int off = slot_off(rt, c);
   const int tq = st.tq0 + off;
-  return off < st.nq_left && tq >= 0 && j < (tq >> 2);
+  return (off < st.nq_left) & (tq >= 0) & (j < (tq >> 2));
 }
 
 // Phase 1 epilogue of one half: histogram the sample scores (the first sample
@@ -1220,61 +1234,67 @@ __device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[
     }
 }
 
-// Phase 2 epilogue of one half: the scores, then the enqueue of the blocks
-// scoring above their query's bound behind the qn already queued.  Each lane
-// takes its place in the queue from a wavefront prefix count of its passing
-// slots (no per-slot branches); only lanes with survivors loop over them.  A
-// queue entry is score bits (31, the sign is 0) << 33 | local query << 28 |
-// block id.  kFull: every block of the tile is below every query's own block.
+// Phase 2 epilogue of one half: the scores and the enqueue.  Survivors are
+// rare (about 1 score in 200), so the scan only records where they are: a
+// lane with any of its 8 slots above its query's bound appends one record
+// (the 8 scores and the tile, half and lane they belong to) behind the qn
+// already queued, its place a masked bit count of the wavefront's mask of
+// such lanes.  No per-slot work, no branch but the skip of an empty half.
+// The drain later re-tests the 8 scores of each record.  kFull: every block
+// of the tile is below every query's own block; otherwise masked slots
+// score -inf.
 template <bool kFull, int kHalf>
 __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2], int col,
                                                int qn) {
   const int lane = lane_id();
   const int j = col * kColTile + (lane & 31);
   float sc[8];
-  uint32_t pm = 0;  // bit r*4 + c: slot (2 kHalf + r, c) passes
+  bool hit = false;
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int rt = 2 * kHalf + r;
-      sc[r * 4 + c] =
-          relu_sum(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
-      bool p = sc[r * 4 + c] > st.tau_l[rt][c];
-      if (!kFull) p = p && slot_valid(st, rt, c, j);
-      pm |= (p ? 1u : 0u) << (r * 4 + c);
+      float v = relu_sum(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
+      if (!kFull) v = slot_valid(st, rt, c, j) ? v : kNegInf;
+      sc[r * 4 + c] = v;
+      hit = hit | (v > st.tau_l[rt][c]);
     }
-  if (__ballot(pm != 0u) == 0) return qn;
-  const uint32_t mine = (uint32_t)__popc(pm);
-  const uint32_t incl = wave_incl_sum(mine);
-  uint32_t pos = (uint32_t)qn + incl - mine;
-  while (pm) {
-    const int idx = __ffs(pm) - 1;
-    pm &= pm - 1;
-    float v = sc[0];  // (selects, not a dynamic register index)
-#pragma unroll
-    for (int k = 1; k < 8; ++k) v = idx == k ? sc[k] : v;
-    const uint32_t q = (uint32_t)((2 * kHalf + (idx >> 2)) * 8 + (idx & 3) * 2 + (lane >> 5));
-    st.queue[pos++] =
-        ((uint64_t)__float_as_uint(v) << 33) | ((uint64_t)q << 28) | (uint64_t)(uint32_t)j;
+  const uint64_t m = __ballot(hit);
+  if (hit) {
+    const int at = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    st.rec_lo[at] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    st.rec_hi[at] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+    st.rec_at[at] = ((uint32_t)col << 7) | (uint32_t)(kHalf << 6) | (uint32_t)lane;
   }
-  return qn + (int)lane_read(incl, 63);
+  return qn + (int)__popcll(m);
 }
 
-// Append the queued survivors to their queries' lists, 64 at a time.
+// Append the survivors of the qn queued records to their queries' lists, one
+// record per lane: slot k of a record from lane l of half h scores block
+// 32 tile + l % 32 for local query (2h + k/4) * 8 + (k%4) * 2 + l/32.
 __device__ __forceinline__ void stream_drain(Stream& st, int qn) {
   const int lane = lane_id();
   wave_sync_lds();
   for (int i0 = 0; i0 < qn; i0 += 64) {
     const int i = i0 + lane;
     if (i < qn) {
-      const uint64_t e = st.queue[i];
-      const int q = (int)((e >> 28) & 31u);
-      const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
-      // a list that overflows keeps counting: the select kernel sees it
-      if (pos < (uint32_t)kListCap)
-        st.lists[(size_t)q * kListCap + pos] =
-            make_key((uint32_t)(e >> 33), (uint32_t)e & 0x0fffffffu);
+      const float4 lo = st.rec_lo[i], hi = st.rec_hi[i];
+      const uint32_t at = st.rec_at[i];
+      const float sc[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const uint32_t j = ((at >> 7) * kColTile) | (at & 31u);
+      const int qb = (int)((at >> 6) & 1u) * 16 + (int)((at >> 5) & 1u);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int q = qb + (k >> 2) * 8 + (k & 3) * 2;
+        if (sc[k] > __int_as_float(st.tau[q])) {
+          const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
+          // a list that overflows keeps counting: the select kernel sees it
+          if (pos < (uint32_t)kListCap)
+            st.lists[(size_t)q * kListCap + pos] = make_key(__float_as_uint(sc[k]), j);
+        }
+      }
     }
   }
   wave_sync_lds();
@@ -1294,7 +1314,7 @@ __device__ __forceinline__ void epilogue(Stream& st, const f32x16 (&acc)[2], int
 // Column tile of position i of a wavefront of parity par: ns sample tiles,
 // then every tile of its parity.
 __device__ __forceinline__ int stream_col(int i, int ns, int par) {
-  return i < ns ? i * kSampleStride + par : 2 * (i - ns) + par;
+  return i < ns ? i * kSampleStride + kSampleStep * par : kPar * (i - ns) + par;
 }
 
 // One position of a wavefront's scan: column tile `col`, its B fragments in
@@ -1349,7 +1369,7 @@ __device__ __forceinline__ void stream_positions(Stream& st, const bf16x8 (&A)[4
 }
 
 // Positions [i0, i1) of one phase, then the last position's half-1 epilogue.
-// The queue holds at most 63 + 2 x 512 entries after a position and 63 + 512
+// The queue holds at most 63 + 2 x 64 records after a position and 63 + 64
 // after that last epilogue, within kQueue.
 template <int kPhase>
 __device__ __forceinline__ void stream_phase(Stream& st, const bf16x8 (&A)[4][4],
@@ -1391,7 +1411,7 @@ __device__ __forceinline__ int query_bound(const Stream& st, int q, bool fits) {
 
 // Grid (ceil(Nq/64), B); 4 wavefronts: two per group of 32 queries, one per
 // column-tile parity.
-__global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
+__global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
                                                            const uint16_t* __restrict__ k_cmp,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ lists,
@@ -1402,13 +1422,14 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
   __shared__ uint32_t s_mx[kStreamQ];
   __shared__ uint32_t s_cnt[kStreamQ];
   __shared__ int32_t s_tau[kStreamQ];
-  __shared__ uint64_t s_queue[4][kQueue];
+  __shared__ float4 s_rec_lo[kStreamWaves][kQueue], s_rec_hi[kStreamWaves][kQueue];
+  __shared__ uint32_t s_rec_at[kStreamWaves][kQueue];
 
   const int qbase = blockIdx.x * kStreamQ, b = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id();
   // (wavefront-uniform, so that the scan's loop control stays scalar)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 1, par = wave & 1;
+  const int grp = wave / kPar, par = wave % kPar;
   const int len = clampi(lens[b], 0, Lmax);
   const int nbp = Lmax >> 2;
   const int gq0 = qbase + grp * 32;  // first query of the group
@@ -1416,8 +1437,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
   const int bt_g = (gq0 < Nq && t_last >= 0) ? (t_last >> 2) : 0;  // blocks the group scans
   const int ncol = (bt_g + kColTile - 1) / kColTile;
   // this wavefront's positions: ns sample tiles, then nf filter tiles
-  const int ns = ncol > par ? (ncol - 1 - par) / kSampleStride + 1 : 0;
-  const int nf = ncol > par ? (ncol - 1 - par) / 2 + 1 : 0;
+  const int ns = ncol > kSampleStep * par ? (ncol - 1 - kSampleStep * par) / kSampleStride + 1 : 0;
+  const int nf = ncol > par ? (ncol - 1 - par) / kPar + 1 : 0;
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
   for (int i = tid; i < kStreamQ * kHistWords; i += blockDim.x) (&s_h[0][0])[i] = 0u;
   if (tid < kStreamQ) {
@@ -1429,7 +1450,10 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
   st.h = &s_h[grp * 32];
   st.mx = &s_mx[grp * 32];
   st.cnt = &s_cnt[grp * 32];
-  st.queue = s_queue[wave];
+  st.rec_lo = s_rec_lo[wave];
+  st.rec_hi = s_rec_hi[wave];
+  st.rec_at = s_rec_at[wave];
+  st.tau = &s_tau[grp * 32];
   // Stationary A fragments: 4 row tiles x 4 k-steps.  Row (lane & 31) of row
   // tile rt is query gq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
   bf16x8 A[4][4];
@@ -1465,8 +1489,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
     }
   // tiles entirely below every query's own block need no causal mask
   for (int off = 32; off >= 1; off >>= 1) bt_min = min(bt_min, __shfl_xor(bt_min, off));
-  // full filter positions: column tiles 2m + par with (2m + par + 1) * 32 <= bt_min
-  const int nfull = min(nf, max(0, (bt_min / kColTile - par + 1) / 2));
+  // full filter positions: column tiles kPar m + par with (kPar m + par + 1) * 32 <= bt_min
+  const int nfull = min(nf, max(0, (bt_min / kColTile - par + kPar - 1) / kPar));
   // lane q < 32: own block of local query q
   const int tl = query_t(len, Nq, gq0 + lane);
   const int bt_q_lane = (lane < 32 && gq0 + lane < Nq && tl >= 0) ? (tl >> 2) : 0;
@@ -1479,10 +1503,10 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
   f32x16 accX[2], accY[2];
   int qn = 0;  // survivors queued, not yet drained
   int colp = 0;
-  // phase 0: the first sample tile of each parity (column tiles 0 and 1)
+  // phase 0: the first sample tile of each parity (column tiles 0 .. kPar - 1)
   stream_phase<0>(st, A, bv, accX, accY, 0, min(ns, 1), ns, par, kb, bt_g, qn, colp);
   stream_barrier();
-  // histogram base: four octaves below the best score of tiles 0 and 1
+  // histogram base: two octaves below the best score of those tiles
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -1491,15 +1515,16 @@ __global__ __launch_bounds__(256) void score_stream_kernel(const uint16_t* __res
           max(0, (int)(st.mx[slot_off(rt, c) + (lane >> 5)] >> kSampleShift) - kSampleBase);
   stream_phase<1>(st, A, bv, accX, accY, 1, ns, ns, par, kb, bt_g, qn, colp);
   stream_barrier();
-  // bounds: wavefront of parity par computes local queries [16 par, 16 par + 16)
+  // bounds: wavefront of parity par computes local queries [kQp par, kQp par + kQp)
   {
+    constexpr int kQp = 32 / kPar;
     int tau_v = 0;
-    for (int i = 0; i < 16; ++i) {
-      const int q = 16 * par + i;
+    for (int i = 0; i < kQp; ++i) {
+      const int q = kQp * par + i;
       const int bound = query_bound(st, q, rdl(bt_q_lane, q) <= kListCap);
       if (lane == i) tau_v = bound;
     }
-    if (lane < 16) s_tau[grp * 32 + 16 * par + lane] = tau_v;
+    if (lane < kQp) s_tau[grp * 32 + kQp * par + lane] = tau_v;
   }
   stream_barrier();
 #pragma unroll
@@ -1626,7 +1651,7 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
-    QSA_LAUNCH(score_stream_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.lists, w.cnt,
+    QSA_LAUNCH(score_stream_kernel, grid, dim3(64 * kStreamWaves), 0, s, q_idx, k_cmp, lens, w.lists, w.cnt,
                w.tau, d.Lmax, d.Nq);
     QSA_LAUNCH(select_kernel<true>, grid_q, dim3(256), 0, s, w.lists, w.cnt, 1, kListCap,
                (const int32_t*)w.tau, (const uint32_t*)nullptr, 0, q_idx, k_cmp, lens, sel, n_sel,
