@@ -1129,7 +1129,6 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
 // independent scores.
 constexpr int kListCap = 4096;    // candidate list entries per query
 constexpr int kColTile = 32;      // blocks per MFMA column tile
-constexpr int kKeyBufs = 2;       // key tiles in registers: the current one and the next
 constexpr int kPar = 4;           // column-tile parities: wavefronts per group of 32 queries
 constexpr int kStreamWaves = 2 * kPar;
 // sample column tiles: c = 128 i + 33 p for parity p (each parity's own
@@ -1153,15 +1152,25 @@ __device__ __forceinline__ void stream_barrier() {
 }
 
 // B fragments of column tile c (MFMA B layout: lane -> block 32c + lane&31,
-// dims 16 ks + 8 (lane>>5)).  Blocks at or past bt_g read block 0 (their
-// scores are masked).
-__device__ __forceinline__ void load_cols(const uint4* kb, int c, int bt_g, uint4 (&bv)[4]) {
-  const int lane = lane_id();
-  int j = c * kColTile + (lane & 31);
-  if (j >= bt_g) j = 0;
-  const uint4* p = kb + (size_t)j * 8 + (lane >> 5);
+// dims 16 ks + 8 (lane>>5)), through a buffer resource that spans the
+// tile's blocks below bt_g: the blocks at or past bt_g read as zeros (their
+// scores are masked).  The tile's address is scalar work; the lane offset
+// (voff bytes) is fixed.
+constexpr uint32_t kBufferConfig = 0x00020000u;  // raw 32-bit buffer, no swizzle
+__device__ __forceinline__ void load_cols(const uint4* kb, int c, int bt_g, uint32_t voff,
+                                          uint4 (&bv)[4]) {
+  // (every operand is wavefront-uniform; readfirstlane lets the compiler
+  // keep the descriptor in scalar registers, with no waterfall loop; the
+  // 32-byte steps go in the scalar offset)
+  const int valid = __builtin_amdgcn_readfirstlane(min(max(bt_g - c * kColTile, 0), kColTile));
+  const uint64_t a = reinterpret_cast<uint64_t>(kb + (size_t)c * kColTile * 8);
+  const uint64_t au = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(au), (short)0, valid * kIdxDim * 2, (int)kBufferConfig);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) bv[ks] = p[2 * ks];
+  for (int ks = 0; ks < 4; ++ks)
+    bv[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 32 * ks, 0));
 }
 
 // MFMAs of half kHalf (row tiles 2 kHalf, 2 kHalf + 1) against one column tile.
@@ -1191,11 +1200,12 @@ struct Stream {
   uint32_t (*h)[kHistWords];  // the group's 32 sample histograms
   uint32_t* cnt;              // the group's 32 list lengths
   uint32_t* mx;               // the group's 32 best scores of the first sample tiles
-  // this wavefront's records not yet drained (see filter_epilogue)
-  float4* rec_lo;             // scores of slots 0..3
-  float4* rec_hi;             // scores of slots 4..7
-  uint32_t* rec_at;           // column tile << 7 | half << 6 | lane
+  // this wavefront's records not yet drained (see filter_epilogue): 48 bytes
+  // each, the scores of slots 0..3, of slots 4..7, then column tile << 7 |
+  // half << 6 | lane
+  uint4* rec;
   const int32_t* tau;         // the group's 32 bounds (LDS)
+  uint32_t voff;              // byte offset of this lane's B fragment within a key tile
 };
 
 __device__ __forceinline__ int slot_off(int rt, int c) { return rt * 8 + c * 2; }
@@ -1264,11 +1274,16 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
   if (hit) {
     const int at = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    st.rec_lo[at] = make_float4(sc[0], sc[1], sc[2], sc[3]);
-    st.rec_hi[at] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-    st.rec_at[at] = ((uint32_t)col << 7) | (uint32_t)(kHalf << 6) | (uint32_t)lane;
+    uint4* rp = st.rec + 3 * at;
+    rp[0] = make_uint4(__float_as_uint(sc[0]), __float_as_uint(sc[1]), __float_as_uint(sc[2]),
+                       __float_as_uint(sc[3]));
+    rp[1] = make_uint4(__float_as_uint(sc[4]), __float_as_uint(sc[5]), __float_as_uint(sc[6]),
+                       __float_as_uint(sc[7]));
+    reinterpret_cast<uint32_t*>(rp + 2)[0] =
+        ((uint32_t)col << 7) | (uint32_t)(kHalf << 6) | (uint32_t)lane;
   }
-  return qn + (int)__popcll(m);
+  // (uniform: readfirstlane keeps the queue count scalar)
+  return __builtin_amdgcn_readfirstlane(qn + (int)__popcll(m));
 }
 
 // Append the survivors of the qn queued records to their queries' lists, one
@@ -1276,13 +1291,16 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
 // 32 tile + l % 32 for local query (2h + k/4) * 8 + (k%4) * 2 + l/32.
 __device__ __forceinline__ void stream_drain(Stream& st, int qn) {
   const int lane = lane_id();
+  qn = __builtin_amdgcn_readfirstlane(qn);
   wave_sync_lds();
   for (int i0 = 0; i0 < qn; i0 += 64) {
     const int i = i0 + lane;
     if (i < qn) {
-      const float4 lo = st.rec_lo[i], hi = st.rec_hi[i];
-      const uint32_t at = st.rec_at[i];
-      const float sc[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const uint4 lo = st.rec[3 * i], hi = st.rec[3 * i + 1];
+      const uint32_t at = st.rec[3 * i + 2].x;
+      const float sc[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(lo.z),
+                           __uint_as_float(lo.w), __uint_as_float(hi.x), __uint_as_float(hi.y),
+                           __uint_as_float(hi.z), __uint_as_float(hi.w)};
       const uint32_t j = ((at >> 7) * kColTile) | (at & 31u);
       const int qb = (int)((at >> 6) & 1u) * 16 + (int)((at >> 5) & 1u);
 #pragma unroll
@@ -1311,12 +1329,6 @@ __device__ __forceinline__ void epilogue(Stream& st, const f32x16 (&acc)[2], int
     qn = filter_epilogue<kPhase == 2, kHalf>(st, acc, col, qn);
 }
 
-// Column tile of position i of a wavefront of parity par: ns sample tiles,
-// then every tile of its parity.
-__device__ __forceinline__ int stream_col(int i, int ns, int par) {
-  return i < ns ? i * kSampleStride + kSampleStep * par : kPar * (i - ns) + par;
-}
-
 // One position of a wavefront's scan: column tile `col`, its B fragments in
 // bv[kBuf].  Issues the loads of the next position's tile (`colf`), then
 // half 0's MFMAs, the epilogue of the previous position's half 1 (when
@@ -1324,27 +1336,31 @@ __device__ __forceinline__ int stream_col(int i, int ns, int par) {
 // the survivor queue goes first, so that its stores precede the loads.
 template <int kPhase, int kBuf, bool kPrev>
 __device__ __forceinline__ void stream_pos(Stream& st, const bf16x8 (&A)[4][4],
-                                           uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                           uint4 (&bv)[2][4], f32x16 (&accX)[2],
                                            f32x16 (&accY)[2], int col, int colp, int colf,
                                            const uint4* kb, int bt_g, int& qn) {
   if (kPhase >= 2 && qn >= 64) {
     stream_drain(st, qn);
     qn = 0;
   }
-  load_cols(kb, colf, bt_g, bv[kBuf ^ 1]);
+  load_cols(kb, colf, bt_g, st.voff, bv[kBuf ^ 1]);
   mma_rows<0>(bv[kBuf], A, accX);
   if (kPrev) epilogue<kPhase, 1>(st, accY, colp, qn);
   mma_rows<1>(bv[kBuf], A, accY);
   epilogue<kPhase, 0>(st, accX, col, qn);
 }
 
-// Position i of a phase's scan, its key tile in buffer kBuf.
+// Position i of a phase's scan, its key tile in buffer kBuf.  Filter phases:
+// position i >= ns scans column tile kPar (i - ns) + par; sample phases:
+// i < ns, tile kSampleStride i + kSampleStep par, and the position after the
+// last sample one is the first filter tile.
 template <int kPhase, bool kPrev, int kBuf>
 __device__ __forceinline__ void stream_pos_at(Stream& st, const bf16x8 (&A)[4][4],
-                                              uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                              uint4 (&bv)[2][4], f32x16 (&accX)[2],
                                               f32x16 (&accY)[2], int i, int ns, int par,
                                               const uint4* kb, int bt_g, int& qn, int& colp) {
-  const int col = stream_col(i, ns, par), colf = stream_col(i + 1, ns, par);
+  const int col = kPhase >= 2 ? kPar * (i - ns) + par : i * kSampleStride + kSampleStep * par;
+  const int colf = kPhase >= 2 ? col + kPar : (i + 1 < ns ? col + kSampleStride : par);
   stream_pos<kPhase, kBuf, kPrev>(st, A, bv, accX, accY, col, colp, colf, kb, bt_g, qn);
   colp = col;
 }
@@ -1354,7 +1370,7 @@ __device__ __forceinline__ void stream_pos_at(Stream& st, const bf16x8 (&A)[4][4
 // that the buffers never move between registers.
 template <int kPhase, int kB0>
 __device__ __forceinline__ void stream_positions(Stream& st, const bf16x8 (&A)[4][4],
-                                                 uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                                 uint4 (&bv)[2][4], f32x16 (&accX)[2],
                                                  f32x16 (&accY)[2], int i0, int i1, int ns,
                                                  int par, const uint4* kb, int bt_g, int& qn,
                                                  int& colp) {
@@ -1373,7 +1389,7 @@ __device__ __forceinline__ void stream_positions(Stream& st, const bf16x8 (&A)[4
 // after that last epilogue, within kQueue.
 template <int kPhase>
 __device__ __forceinline__ void stream_phase(Stream& st, const bf16x8 (&A)[4][4],
-                                             uint4 (&bv)[kKeyBufs][4], f32x16 (&accX)[2],
+                                             uint4 (&bv)[2][4], f32x16 (&accX)[2],
                                              f32x16 (&accY)[2], int i0, int i1, int ns, int par,
                                              const uint4* kb, int bt_g, int& qn, int& colp) {
   if (i1 <= i0) return;
@@ -1383,13 +1399,11 @@ __device__ __forceinline__ void stream_phase(Stream& st, const bf16x8 (&A)[4][4]
     stream_positions<kPhase, 1>(st, A, bv, accX, accY, i0, i1, ns, par, kb, bt_g, qn, colp);
   else
     stream_positions<kPhase, 0>(st, A, bv, accX, accY, i0, i1, ns, par, kb, bt_g, qn, colp);
-  {
-    if (kPhase >= 2 && qn >= 64) {  // room for the pending half's survivors
-      stream_drain(st, qn);
-      qn = 0;
-    }
-    epilogue<kPhase, 1>(st, accY, colp, qn);
+  if (kPhase >= 2 && qn >= 64) {  // room for the pending half's survivors
+    stream_drain(st, qn);
+    qn = 0;
   }
+  epilogue<kPhase, 1>(st, accY, colp, qn);
 }
 
 // After the sample phase: the bound of local query q (lane q of the wavefront
@@ -1422,8 +1436,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   __shared__ uint32_t s_mx[kStreamQ];
   __shared__ uint32_t s_cnt[kStreamQ];
   __shared__ int32_t s_tau[kStreamQ];
-  __shared__ float4 s_rec_lo[kStreamWaves][kQueue], s_rec_hi[kStreamWaves][kQueue];
-  __shared__ uint32_t s_rec_at[kStreamWaves][kQueue];
+  __shared__ uint4 s_rec[kStreamWaves][3 * kQueue];
 
   const int qbase = blockIdx.x * kStreamQ, b = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id();
@@ -1437,8 +1450,11 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   const int bt_g = (gq0 < Nq && t_last >= 0) ? (t_last >> 2) : 0;  // blocks the group scans
   const int ncol = (bt_g + kColTile - 1) / kColTile;
   // this wavefront's positions: ns sample tiles, then nf filter tiles
-  const int ns = ncol > kSampleStep * par ? (ncol - 1 - kSampleStep * par) / kSampleStride + 1 : 0;
-  const int nf = ncol > par ? (ncol - 1 - par) / kPar + 1 : 0;
+  // (the scan's bounds are wavefront-uniform: readfirstlane keeps its loop
+  // control and column arithmetic scalar)
+  const int ns = __builtin_amdgcn_readfirstlane(
+      ncol > kSampleStep * par ? (ncol - 1 - kSampleStep * par) / kSampleStride + 1 : 0);
+  const int nf = __builtin_amdgcn_readfirstlane(ncol > par ? (ncol - 1 - par) / kPar + 1 : 0);
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
   for (int i = tid; i < kStreamQ * kHistWords; i += blockDim.x) (&s_h[0][0])[i] = 0u;
   if (tid < kStreamQ) {
@@ -1450,10 +1466,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   st.h = &s_h[grp * 32];
   st.mx = &s_mx[grp * 32];
   st.cnt = &s_cnt[grp * 32];
-  st.rec_lo = s_rec_lo[wave];
-  st.rec_hi = s_rec_hi[wave];
-  st.rec_at = s_rec_at[wave];
+  st.rec = s_rec[wave];
   st.tau = &s_tau[grp * 32];
+  st.voff = (uint32_t)(((lane & 31) * 8 + (lane >> 5)) * 16);
   // Stationary A fragments: 4 row tiles x 4 k-steps.  Row (lane & 31) of row
   // tile rt is query gq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
   bf16x8 A[4][4];
@@ -1490,14 +1505,15 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   // tiles entirely below every query's own block need no causal mask
   for (int off = 32; off >= 1; off >>= 1) bt_min = min(bt_min, __shfl_xor(bt_min, off));
   // full filter positions: column tiles kPar m + par with (kPar m + par + 1) * 32 <= bt_min
-  const int nfull = min(nf, max(0, (bt_min / kColTile - par + kPar - 1) / kPar));
+  const int nfull = __builtin_amdgcn_readfirstlane(
+      min(nf, max(0, (bt_min / kColTile - par + kPar - 1) / kPar)));
   // lane q < 32: own block of local query q
   const int tl = query_t(len, Nq, gq0 + lane);
   const int bt_q_lane = (lane < 32 && gq0 + lane < Nq && tl >= 0) ? (tl >> 2) : 0;
-  // B fragments of the first kKeyBufs - 1 positions
-  uint4 bv[kKeyBufs][4];
-#pragma unroll
-  for (int i = 0; i < kKeyBufs - 1; ++i) load_cols(kb, stream_col(i, ns, par), bt_g, bv[i]);
+  // B fragments of the first position (the first sample tile, or with no
+  // sample tiles the first filter tile)
+  uint4 bv[2][4];
+  load_cols(kb, ns > 0 ? kSampleStep * par : par, bt_g, st.voff, bv[0]);
   stream_barrier();  // LDS initialised
 
   f32x16 accX[2], accY[2];
