@@ -483,10 +483,11 @@ int sparse_units(const Dims& d) {
   return d.Nq * d.Hkv * ((G + 15) / 16);
 }
 
-// Workgroups a decode-sized sparse attention aims for: 2 per compute unit,
-// each wavefront walking two or more 32-token tiles with the next one's
-// loads in flight.
-constexpr int kSparseTargetWG = 512;
+// Workgroups a decode-sized sparse attention aims for: one per compute unit,
+// each wavefront walking four or more 32-token tiles with the next one's
+// loads in flight (fewer, longer splits also leave merge_kernel fewer
+// partials).
+constexpr int kSparseTargetWG = 256;
 
 int sparse_splits(const Dims& d, int* split_tokens, int* tail_last) {
   // Decode-sized batches have few (query, KV head) units: split their token
