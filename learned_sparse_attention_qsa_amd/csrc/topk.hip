@@ -35,8 +35,8 @@
 //  below tau can be in the top 512; the select kernel checks this.  No
 //  score table is written.
 //
-// The stream engine finishes with a select kernel (a register sort for short
-// lists, an LDS radix select otherwise).  Rows whose candidates cannot be
+// The stream engine finishes with a select kernel (an LDS radix select of the
+// 512th key, then a sort of the winners' ids).  Rows whose candidates cannot be
 // trusted or held (an overflow, too few candidates, or very many equal
 // scores) are finished by an exact fallback that recomputes or re-reads the
 // whole row.
@@ -153,99 +153,6 @@ __device__ void bitonic_sort_512(int32_t* a) {
       __syncthreads();
     }
   }
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Bitonic sort, descending, of N = 256 * NPT 64-bit values; thread t holds
-// elements t*NPT .. t*NPT + NPT - 1 in v.  Exchanges within a thread use
-// registers, within a wavefront lane shuffles, across wavefronts the LDS
-// buffer xch (N values); only those last stages need barriers.  256 threads.
-template <int NPT>
-__device__ __forceinline__ void block_sort_desc(uint64_t (&v)[NPT], uint64_t* xch) {
-  constexpr int N = 256 * NPT;
-  const int t = threadIdx.x;
-  // fully unrolled: j must be a compile-time constant for the register cases
-#pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < NPT) {
-#pragma unroll
-        for (int s = 0; s < NPT; ++s) {
-          if (s & j) continue;
-          const int i = t * NPT + s;
-          const bool desc = (i & k) == 0;
-          const uint64_t a = v[s], b = v[s | j];
-          const bool sw = (a < b) == desc;
-          v[s] = sw ? b : a;
-          v[s | j] = sw ? a : b;
-        }
-      } else {
-        uint64_t o[NPT];
-        if (j < 64 * NPT) {
-#pragma unroll
-          for (int s = 0; s < NPT; ++s) o[s] = shfl_xor_u64(v[s], j / NPT);
-        } else {
-          __syncthreads();
-#pragma unroll
-          for (int s = 0; s < NPT; ++s) xch[t * NPT + s] = v[s];
-          __syncthreads();
-#pragma unroll
-          for (int s = 0; s < NPT; ++s) o[s] = xch[(t * NPT + s) ^ j];
-        }
-#pragma unroll
-        for (int s = 0; s < NPT; ++s) {
-          const int i = t * NPT + s;
-          const bool desc = (i & k) == 0;
-          const bool keep_max = ((i & j) == 0) == desc;
-          v[s] = keep_max ? (v[s] > o[s] ? v[s] : o[s]) : (v[s] < o[s] ? v[s] : o[s]);
-        }
-      }
-    }
-  }
-}
-
-// Select's finish for at most 256 * NPT candidates held in v (0 = empty, below
-// every key): sort them (descending), then sort the block ids of the first 512
-// ascending into outb.  xch: LDS scratch of 256 * NPT keys.
-template <int NPT>
-__device__ __forceinline__ void finish_sorted(uint64_t (&v)[NPT], uint64_t* xch, int32_t* outb) {
-  const int t = threadIdx.x;
-  block_sort_desc<NPT>(v, xch);
-  __syncthreads();
-  // the 512 best keys sit at positions 0..511: pass their ids through LDS
-  // and sort them ascending (as complemented ids, descending)
-#pragma unroll
-  for (int s = 0; s < NPT; ++s) {
-    const int i = t * NPT + s;
-    if (i < kTopK) outb[i] = (int32_t)key_block(v[s]);
-  }
-  __syncthreads();
-  uint64_t w[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) w[s] = 0xffffffffull - (uint32_t)outb[2 * t + s];
-  block_sort_desc<2>(w, xch);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) outb[2 * t + s] = (int32_t)(0xffffffffu - (uint32_t)w[s]);
-  __syncthreads();
-}
-
-// The same for n <= 256 * NPT candidates in keys[0..n) (LDS, also the scratch).
-template <int NPT>
-__device__ __forceinline__ void finish_small(uint64_t* keys, uint32_t n, int32_t* outb) {
-  const int t = threadIdx.x;
-  uint64_t v[NPT];
-#pragma unroll
-  for (int s = 0; s < NPT; ++s) {
-    const uint32_t i = (uint32_t)(t * NPT + s);
-    v[s] = i < n ? keys[i] : 0ull;
-  }
-  finish_sorted<NPT>(v, keys, outb);
 }
 
 __device__ __forceinline__ int query_t(int len, int Nq, int q) { return len - Nq + q; }
@@ -405,8 +312,10 @@ __device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, con
 // One workgroup per query row.  Fast path: the row's candidates (nsub
 // segments of up to seg_cap keys, segment lengths in cand_cnt; only keys whose
 // score reaches the row's final threshold, when one is given) go to LDS, a
-// radix select finds the 512th key and the winners are sorted.  Rows with too
-// few or too many candidates take the exact whole-row path.
+// radix select finds the 512th key and the winners' ids are sorted.  (A full
+// sort of the candidates costs about twice as much at the ~1,400 candidates
+// of a 1M-context row.)  Rows with too few or too many candidates take the
+// exact whole-row path.
 template <bool kRecompute>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     const uint64_t* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int nsub,
@@ -449,34 +358,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
   }
   const uint64_t* src = cand + (row * nsub + (seg < nsub ? seg : 0)) * (size_t)seg_cap;
-  if (nsub == 1 && n_seg <= 1024u && cand_cnt[row] <= (uint32_t)seg_cap) {
-    // short list: straight into registers, 4 keys per thread, then sort
-    uint64_t v[4];
-    int mine = 0;
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const uint32_t i = (uint32_t)(tid * 4 + s2);
-      const uint64_t key = i < n_seg ? src[i] : 0ull;
-      const bool keep = i < n_seg && (int)(uint32_t)(key >> 32) >= tau;
-      v[s2] = keep ? key : 0ull;
-      mine += keep ? 1 : 0;
-    }
-    atomicAdd(&outn, (uint32_t)mine);
-    __syncthreads();
-    if (outn >= (uint32_t)kTopK) {
-      finish_sorted<4>(v, keys, outb);
-      for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
-      if (tid == 0) n_sel[row] = kTopK;
-      return;
-    }
-    // too few: the exact whole-row path below
-    __syncthreads();
-    if (tid == 0) {
-      outn = 0;
-      bad = 1;
-    }
-    __syncthreads();
-  }
   uint32_t longest = n_seg;
   for (int off = 32; off >= 1; off >>= 1) longest = max(longest, (uint32_t)__shfl_xor((int)longest, off));
   for (uint32_t i0 = 0; i0 < longest; i0 += 8 * tps) {
@@ -505,25 +386,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const bool ok = bad == 0 && n >= (uint32_t)kTopK && n <= (uint32_t)kSelCap;
   __syncthreads();
   if (ok) {
-    if (n <= 2048u) {
-      // few candidates: sort them all, keep the first 512, sort their ids
-      if (n <= 1024u)
-        finish_small<4>(keys, n, outb);
-      else
-        finish_small<8>(keys, n, outb);
-      for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
-      if (tid == 0) n_sel[row] = kTopK;
-      return;
-    } else {
-      const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
-      if (tid == 0) outn = 0;
-      __syncthreads();
-      for (uint32_t i = tid; i < n; i += blockDim.x) {
-        const uint64_t key = keys[i];
-        if (key >= kth) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
-      }
-      __syncthreads();
+    // the 512th best key by an LDS radix select, then the keys at or above
+    // it (exactly 512: keys are distinct) and their ids sorted ascending
+    const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
+    if (tid == 0) outn = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += blockDim.x) {
+      const uint64_t key = keys[i];
+      if (key >= kth) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
     }
+    __syncthreads();
     bitonic_sort_512(outb);
     for (int i = tid; i < kTopK; i += blockDim.x) srow[i] = outb[i];
     if (tid == 0) n_sel[row] = kTopK;
