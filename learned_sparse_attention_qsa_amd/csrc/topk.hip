@@ -108,9 +108,12 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* h, uint32_t k, u
 }
 
 // Whole workgroup (blockDim.x threads): the k-th largest of n distinct keys in
-// LDS, by most-significant-digit radix select over eight 8-bit digits.
+// LDS, by most-significant-digit radix select over 8-bit digits.  Once the
+// digit's bin holds exactly the keys still needed, the k-th largest is the
+// smallest of them and the remaining digits are skipped (one pass for the
+// minimum instead).  bcast: 3 words of LDS, mn: one 64-bit LDS word.
 __device__ uint64_t block_kth_largest(const uint64_t* keys, int n, uint32_t k, uint32_t* hist,
-                                      uint32_t* bcast) {
+                                      uint32_t* bcast, uint64_t* mn) {
   uint64_t prefix = 0, pmask = 0;
   const int tid = threadIdx.x;
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -127,12 +130,24 @@ __device__ uint64_t block_kth_largest(const uint64_t* keys, int n, uint32_t k, u
       if (tid == 0) {
         bcast[0] = d;
         bcast[1] = above;
+        bcast[2] = hist[d];
+        *mn = ~0ull;
       }
     }
     __syncthreads();
     k -= bcast[1];
     prefix |= (uint64_t)bcast[0] << shift;
     pmask |= 0xffull << shift;
+    if (bcast[2] == k && shift > 0) {
+      // every key with this prefix is among the k largest: the k-th is the
+      // smallest of them
+      for (int i = tid; i < n; i += blockDim.x) {
+        const uint64_t key = keys[i];
+        if ((key & pmask) == prefix) atomicMin(mn, key);
+      }
+      __syncthreads();
+      return *mn;
+    }
   }
   return prefix;
 }
@@ -325,7 +340,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     int Lmax, int Nq) {
   __shared__ uint64_t keys[kSelCap];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t bcast[2];
+  __shared__ uint32_t bcast[3];
+  __shared__ uint64_t s_min;
   __shared__ int32_t outb[kTopK];
   __shared__ uint32_t outn;
   __shared__ uint32_t bad;
@@ -388,7 +404,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   if (ok) {
     // the 512th best key by an LDS radix select, then the keys at or above
     // it (exactly 512: keys are distinct) and their ids sorted ascending
-    const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast);
+    const uint64_t kth = block_kth_largest(keys, (int)n, kTopK, hist, bcast, &s_min);
     if (tid == 0) outn = 0;
     __syncthreads();
     for (uint32_t i = tid; i < n; i += blockDim.x) {
