@@ -1132,6 +1132,21 @@ __device__ __forceinline__ void sample_epilogue(Stream& st, const f32x16 (&acc)[
     }
 }
 
+// The filter's test value of a block: u = max(s01 + s23, s01, s23) with
+// s01 = max(a + b, a, b) and s23 = max(c + d, c, d).  relu(x) + relu(y) =
+// max(x + y, x, y, 0), with the same rounding as the sum of the relu'd
+// values wherever it is not 0, so relu(u) is the block's score bit for bit
+// and, for a bound tau >= 0 or tau = -inf, u > tau exactly when the score
+// is.  Three 3-input maxima and three adds: one instruction fewer than four
+// relus and three adds.
+__device__ __forceinline__ float max3f(float x, float y, float z) {
+  return __builtin_fmaxf(__builtin_fmaxf(x, y), z);
+}
+__device__ __forceinline__ float relu_sum_test(float a, float b, float c, float d) {
+  const float s01 = max3f(a + b, a, b), s23 = max3f(c + d, c, d);
+  return max3f(s01 + s23, s01, s23);
+}
+
 // Phase 2 epilogue of one half: the scores and the enqueue.  Survivors are
 // rare (about 1 score in 200), so the scan only records where they are: a
 // lane with any of its 8 slots above its query's bound appends one record
@@ -1153,7 +1168,7 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int rt = 2 * kHalf + r;
-      float v = relu_sum(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
+      float v = relu_sum_test(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
       if (!kFull) v = slot_valid(st, rt, c, j) ? v : kNegInf;
       sc[r * 4 + c] = v;
       hit = hit | (v > st.tau_l[rt][c]);
@@ -1198,7 +1213,7 @@ __device__ __forceinline__ void stream_drain(Stream& st, int qn) {
           const uint32_t pos = atomicAdd(&st.cnt[q], 1u);
           // a list that overflows keeps counting: the select kernel sees it
           if (pos < (uint32_t)kListCap)
-            st.lists[(size_t)q * kListCap + pos] = make_key(__float_as_uint(sc[k]), j);
+            st.lists[(size_t)q * kListCap + pos] = make_key(__float_as_uint(relu(sc[k])), j);
         }
       }
     }
@@ -1303,7 +1318,7 @@ __device__ __forceinline__ int query_bound(const Stream& st, int q, bool fits) {
   uint32_t total = (w0 & 0xffffu) + (w0 >> 16) + (w1 & 0xffffu) + (w1 >> 16);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) total += (uint32_t)__shfl_xor((int)total, off);
-  if (fits) return (int)0xbf800000u;  // -1.0f: the whole row fits the list, keep every block
+  if (fits) return (int)0xff800000u;  // -inf: the whole row fits the list, keep every block
   if (total < (uint32_t)kSampleRank) return 0;  // too few samples above the base: keep every positive score
   int m;
   uint32_t sfx;
