@@ -250,6 +250,20 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     ns = clampi(a.n_sel[row], 0, bt < kTopK ? bt : kTopK);
     ntok = 4 * ns + (t - 4 * bt) + 1;
   }
+  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
+  const uint16_t* kbase = a.k + g * kHeadDim;
+  const uint16_t* vbase = a.v + g * kHeadDim;
+  // With tail_last, the query's own block (tokens 4 bt .. t, known from lens
+  // alone) is wavefront 0's extra tile in the last split: its rows are
+  // requested now, before the selection arrives, and it is processed ahead
+  // of the selected tiles, so that it does not add a round trip at the end.
+  const bool own_tail = kMulti && a.tail_last && split == a.n_split - 1 && wave == 0 && t >= 0;
+  KVTile tail;
+  if (own_tail)
+    load_tile(tail, kbase, vbase, 0, [&](int kk) -> long long {
+      const int tok = 4 * (t >> 2) + kk;
+      return tok <= t ? (long long)(kv_seq + (size_t)tok * a.Hkv) * kHeadDim : -1;
+    });
   // ids outside [0, bt) are a caller bug: clamped so no access leaves the row
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -257,13 +271,10 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     if (e < nsb && kb0 + e < ns) s_sel[e] = clampi(my_sel[i], 0, bt - 1);
   }
   __syncthreads();
-  // with tail_last, the last split also takes the query's own block (<= 4
-  // tokens past the 2,048 selected ones)
-  const int k_end =
-      a.tail_last && split == a.n_split - 1 ? ntok : min(ntok, k_begin + a.split_tokens);
-  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
-  const uint16_t* kbase = a.k + g * kHeadDim;
-  const uint16_t* vbase = a.v + g * kHeadDim;
+  // the selected tokens of this split (with tail_last the query's own block
+  // is handled apart, above; otherwise it follows the selected ones)
+  const int k_end = a.tail_last ? min(4 * ns, k_begin + a.split_tokens)
+                                : min(ntok, k_begin + a.split_tokens);
   auto row_of = [&](int kk) -> long long {
     if (kk >= k_end) return -1;
     const int tok = kk < 4 * ns ? 4 * s_sel[(kk >> 2) - kb0] + (kk & 3) : 4 * bt + (kk - 4 * ns);
@@ -275,6 +286,20 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   KVTile cur;
   const int first = k_begin + wave * kTile;
   if (first < k_end) load_tile(cur, kbase, vbase, first, row_of);
+  if (own_tail) {
+    stash_v(vt, tail);
+    float z[8];
+    qk_logits(tail, qf, a.scale_log2, z);
+    const int n_own = t - 4 * bt + 1;  // 1..4 tokens
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (s2 * 16 + (lane >> 4) * 4 + i >= n_own) z[s2 * 4 + i] = kNegInf;
+    wave_sync_lds();
+    softmax_pv(r, z, vt);
+    wave_sync_lds();
+  }
   for (int k0 = first; k0 < k_end; k0 += 4 * kTile) {
     stash_v(vt, cur);
     KVTile nxt;
