@@ -212,11 +212,14 @@ __device__ __forceinline__ void finish(const Run& r, bool col_valid, uint16_t* o
 // partial (o, lse) that merge_kernel combines.  (A merge by the last
 // workgroup to arrive would need a device-scope fence per workgroup, and on
 // this chip such a fence writes back the whole L2 of its XCD.)
-template <bool kMulti>  // false: every wavefront has at most one 32-token tile
-__global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
+// kMulti false: every wavefront has at most one 32-token tile; kWaves: 4 or 8.
+template <bool kMulti, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kSelPer = kTopK / kThreads;  // selection entries each thread prefetches
   __shared__ int32_t s_sel[kTopK];
-  __shared__ __align__(16) uint16_t s_v[4][kTile * kVStride];  // V tiles; then merge scratch
-  __shared__ float s_m[4][16], s_l[4][16], s_f[4][16], s_inv[16];
+  __shared__ __align__(16) uint16_t s_v[kWaves][kTile * kVStride];  // V tiles; then merge scratch
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16], s_f[kWaves][16], s_inv[16];
   const int unit = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int hchunks = (a.G + 15) >> 4;
@@ -229,11 +232,11 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   // This split's slice of the selection, loaded before n_sel is known (the
   // loads do not wait on each other): blocks [kb0, kb0 + split_tokens / 4).
   const int kb0 = k_begin >> 2;
-  const int nsb = min(a.split_tokens >> 2, kTopK - kb0);  // <= 512 = 2 per thread
-  int32_t my_sel[2] = {0, 0};
+  const int nsb = min(a.split_tokens >> 2, kTopK - kb0);  // <= 512 = kSelPer per thread
+  int32_t my_sel[kSelPer];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (tid + 256 * i < nsb) my_sel[i] = a.sel[row * kTopK + kb0 + tid + 256 * i];
+  for (int i = 0; i < kSelPer; ++i)
+    my_sel[i] = tid + kThreads * i < nsb ? a.sel[row * kTopK + kb0 + tid + kThreads * i] : 0;
   const int h0 = g * a.G + hc * 16;
   const int nh = min(16, a.G - hc * 16);
   const int col = lane & 15;
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     });
   // ids outside [0, bt) are a caller bug: clamped so no access leaves the row
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < kSelPer; ++i) {
+    const int e = tid + kThreads * i;
     if (e < nsb && kb0 + e < ns) s_sel[e] = clampi(my_sel[i], 0, bt - 1);
   }
   __syncthreads();
@@ -300,10 +303,11 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     softmax_pv(r, z, vt);
     wave_sync_lds();
   }
-  for (int k0 = first; k0 < k_end; k0 += 4 * kTile) {
+  for (int k0 = first; k0 < k_end; k0 += kWaves * kTile) {
     stash_v(vt, cur);
     KVTile nxt;
-    if (kMulti && k0 + 4 * kTile < k_end) load_tile(nxt, kbase, vbase, k0 + 4 * kTile, row_of);
+    if (kMulti && k0 + kWaves * kTile < k_end)
+      load_tile(nxt, kbase, vbase, k0 + kWaves * kTile, row_of);
     float z[8];
     qk_logits(cur, qf, a.scale_log2, z);
 #pragma unroll
@@ -317,12 +321,12 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     if (!kMulti) break;
     cur = nxt;
   }
-  // ---- merge the four wavefronts (LDS)
+  // ---- merge the wavefronts (LDS)
   float l = r.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();  // every wavefront is done with its V tile: reuse s_v
-  float* O = reinterpret_cast<float*>(&s_v[0][0]);  // [4][16][128]
+  float* O = reinterpret_cast<float*>(&s_v[0][0]);  // [kWaves][16][128]
   {
     const int gq = lane >> 4;
 #pragma unroll
@@ -338,9 +342,9 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
   const bool partial = a.n_split > 1;
   if (tid < 16) {
     float M = kNegInf;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][tid]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][tid]);
     float L = 0.f;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float f = (M == kNegInf || s_m[w][tid] == kNegInf) ? 0.f : exp2f(s_m[w][tid] - M);
       s_f[w][tid] = f;
       L += f * s_l[w][tid];
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(AttnArgs a) {
     const int c = i >> 7, d = i & 127;
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o += s_f[w][c] * O[(w * 16 + c) * kHeadDim + d];
+    for (int w = 0; w < kWaves; ++w) o += s_f[w][c] * O[(w * 16 + c) * kHeadDim + d];
     o *= s_inv[c];
     const size_t rh = row * a.Hq + h0 + c;
     if (partial)
@@ -596,9 +600,14 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
   }
   const dim3 grid((unsigned)sparse_units(d), (unsigned)a.n_split, (unsigned)d.B);
   if (a.split_tokens <= 4 * kTile)
-    QSA_LAUNCH(sparse_attend_kernel<false>, grid, dim3(256), 0, s, a);
+    QSA_LAUNCH_AS("sparse_attend_kernel<false>", (sparse_attend_kernel<false, 4>), grid,
+                  dim3(256), 0, s, a);
+  else if (a.n_split > 1)  // decode-sized: eight wavefronts walk a split's tiles
+    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 8>), grid, dim3(512),
+                  0, s, a);
   else
-    QSA_LAUNCH(sparse_attend_kernel<true>, grid, dim3(256), 0, s, a);
+    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 4>), grid, dim3(256),
+                  0, s, a);
   if (a.n_split > 1)
     QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
                part_o, part_lse, out, lse, d.Nq, d.Hq, a.n_split);

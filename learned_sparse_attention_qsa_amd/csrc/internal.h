@@ -99,3 +99,11 @@ struct Carve {
     hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);     \
     ::qsa::profile_after((stream));                                          \
   } while (0)
+// The same with the name the per-launch timing records (for template
+// instances whose argument list holds a comma).
+#define QSA_LAUNCH_AS(name, kernel, grid, block, shmem, stream, ...)          \
+  do {                                                                       \
+    ::qsa::profile_before((stream), name);                                   \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);     \
+    ::qsa::profile_after((stream));                                          \
+  } while (0)
