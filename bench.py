@@ -86,8 +86,9 @@ def kernel_stats(records, n_steps):
 
 def timed_steps(step, n, flush, Q, torch):
     """n steps, flush before each (untimed), per-step HIP events; then up to
-    20 more steps with the library's per-launch events (kept out of the step
-    times: the extra event records add their own time to the stream)."""
+    20 more steps with the library's per-launch events (carried by each
+    kernel's dispatch, so they time the kernel alone; kept out of the step
+    times all the same)."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     torch.cuda.synchronize()

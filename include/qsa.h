@@ -176,13 +176,14 @@ qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q,
 /* Kernel timing hook, for benchmarks and profilers (not part of the method).
  * qsa_profile_attach hands the library n_events caller-created hipEvent_t
  * handles (created with timing enabled, owned by the caller).  From then on,
- * on the calling thread, the i-th kernel the library enqueues is bracketed by
- * events[2i] (recorded on its stream just before the launch) and events[2i+1]
- * (just after), until n_events/2 launches have been recorded.
+ * on the calling thread, the i-th kernel the library enqueues carries
+ * events[2i] and events[2i+1] in its own dispatch (hipExtLaunchKernel's start
+ * and stop events), so their interval is that kernel's execution, until
+ * n_events/2 launches have been recorded.
  * qsa_profile_detach stops recording and returns the number of bracketed
  * launches; qsa_profile_kernel_name(i) names the i-th one ("" when out of
- * range; valid until the next attach on this thread).  Recording adds two
- * event markers per launch and nothing else. */
+ * range; valid until the next attach on this thread).  Recording adds no
+ * packets to the stream. */
 qsa_status qsa_profile_attach(void** events, int32_t n_events);
 int32_t qsa_profile_detach(void);
 const char* qsa_profile_kernel_name(int32_t i);

@@ -289,9 +289,10 @@ def dense_gqa_decode(shp: QsaShape, q, k, v, lens, out=None, lse=None, ws=None,
 
 
 class KernelTimer:
-    """Brackets every kernel the library launches on this thread with HIP
-    events (qsa_profile_attach), for benchmarks.  Use as a context manager;
-    afterwards `records()` lists (kernel name, milliseconds) in launch order."""
+    """Times every kernel the library launches on this thread with a pair of
+    HIP events carried by the kernel's own dispatch (qsa_profile_attach), for
+    benchmarks.  Use as a context manager; afterwards `records()` lists
+    (kernel name, milliseconds of execution) in launch order."""
 
     def __init__(self, max_launches: int = 512):
         self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]

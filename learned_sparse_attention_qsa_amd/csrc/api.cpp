@@ -21,24 +21,18 @@ constexpr int kMaxProfiled = 1024;
 thread_local void** t_events = nullptr;
 thread_local int t_cap = 0;
 thread_local int t_count = 0;
-thread_local bool t_open = false;
 thread_local const char* t_names[kMaxProfiled];
 }  // namespace
 
 namespace qsa {
-void profile_before(hipStream_t s, const char* name) {
-  t_open = false;
-  if (!t_events || t_count >= kMaxProfiled || 2 * t_count + 1 >= t_cap) return;
-  if (hipEventRecord(static_cast<hipEvent_t>(t_events[2 * t_count]), s) != hipSuccess) return;
+bool profile_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!t_events || t_count >= kMaxProfiled || 2 * t_count + 1 >= t_cap) return false;
+  *start = static_cast<hipEvent_t>(t_events[2 * t_count]);
+  *stop = static_cast<hipEvent_t>(t_events[2 * t_count + 1]);
   t_names[t_count] = name;
-  t_open = true;
+  return true;
 }
-void profile_after(hipStream_t s) {
-  if (!t_open) return;
-  t_open = false;
-  if (hipEventRecord(static_cast<hipEvent_t>(t_events[2 * t_count + 1]), s) == hipSuccess)
-    ++t_count;
-}
+void profile_commit() { ++t_count; }
 }  // namespace qsa
 
 namespace {
@@ -188,7 +182,6 @@ qsa_status qsa_profile_attach(void** events, int32_t n_events) {
   t_events = events;
   t_cap = n_events;
   t_count = 0;
-  t_open = false;
   return QSA_OK;
 }
 

@@ -3,6 +3,7 @@
 // synchronises, and returns hipGetLastError() of its launches.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -74,9 +75,11 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
                                float* lse, void* ws, hipStream_t s);
 
 // Profiling hook: when a caller has attached HIP events (qsa_profile_attach),
-// every launch records one event before and one after itself on its stream.
-void profile_before(hipStream_t s, const char* name);
-void profile_after(hipStream_t s);
+// profile_events hands out the next start/stop pair and every launch carries
+// them in its own dispatch packet, so the recorded interval is the kernel's
+// execution alone (no separate marker packets on the stream).
+bool profile_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
+void profile_commit();
 
 // Workspace carving: aligned bump allocation inside the caller's buffer.
 struct Carve {
@@ -93,17 +96,14 @@ struct Carve {
 
 }  // namespace qsa
 
-#define QSA_LAUNCH(kernel, grid, block, shmem, stream, ...)                  \
-  do {                                                                       \
-    ::qsa::profile_before((stream), #kernel);                                \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);     \
-    ::qsa::profile_after((stream));                                          \
+#define QSA_LAUNCH_AS(name, kernel, grid, block, shmem, stream, ...)                       \
+  do {                                                                                    \
+    hipEvent_t qsa_start_ = nullptr, qsa_stop_ = nullptr;                                 \
+    const bool qsa_timed_ = ::qsa::profile_events(name, &qsa_start_, &qsa_stop_);         \
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, qsa_start_, qsa_stop_, 0u,  \
+                          __VA_ARGS__);                                                   \
+    if (qsa_timed_) ::qsa::profile_commit();                                              \
   } while (0)
-// The same with the name the per-launch timing records (for template
-// instances whose argument list holds a comma).
-#define QSA_LAUNCH_AS(name, kernel, grid, block, shmem, stream, ...)          \
-  do {                                                                       \
-    ::qsa::profile_before((stream), name);                                   \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);     \
-    ::qsa::profile_after((stream));                                          \
-  } while (0)
+// The same with the kernel's spelling as the recorded name.
+#define QSA_LAUNCH(kernel, grid, block, shmem, stream, ...) \
+  QSA_LAUNCH_AS(#kernel, kernel, grid, block, shmem, stream, __VA_ARGS__)
