@@ -375,14 +375,24 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
 }
 
 // ------------------------------------------------------------------ dense
-// Grid (n_split, Hkv * ceil(Nq*G/16), B); one wavefront per workgroup, 16
-// (query, head) columns, all tokens 0..len-1 of the split range, causal mask
-// per column.  Always writes partials (merged by merge_kernel).
-__global__ __launch_bounds__(64) void dense_decode_kernel(AttnArgs a) {
-  __shared__ __align__(16) uint16_t s_v[kTile * kVStride];
+// Column units: chunk cc of 16 (query, head) columns of KV head g is unit
+// g * cchunks + cc, cchunks = ceil(Nq*G/16).  Grid (n_split, ceil(units / 8),
+// B); a workgroup holds up to eight wavefronts, one per unit, and each walks
+// all tokens 0..len-1 of the split range with a causal mask per column.  The
+// wavefronts of a workgroup read the same tokens in step: the chunks of one
+// KV head share its rows, and the KV heads' rows of a token are adjacent
+// 256-byte pieces of one 1 KiB row, so each token's K and V cross the fabric
+// once, as whole rows.  Always writes partials (merged by merge_kernel).
+constexpr int kDenseWaves = 8;
+__global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs a) {
+  __shared__ __align__(16) uint16_t s_vw[kDenseWaves][kTile * kVStride];
   const int split = blockIdx.x, b = blockIdx.z;
   const int cchunks = (a.Nq * a.G + 15) >> 4;
-  const int g = blockIdx.y / cchunks, cc = blockIdx.y % cchunks;
+  const int wave = threadIdx.x >> 6;
+  const int u = blockIdx.y * kDenseWaves + wave;
+  if (u >= a.Hkv * cchunks) return;  // (no workgroup barrier below)
+  const int g = u / cchunks, cc = u % cchunks;
+  uint16_t* s_v = s_vw[wave];
   const int lane = lane_id();
   const int len = clampi(a.lens[b], 0, a.Lmax);
   const int col = lane & 15;
@@ -545,7 +555,7 @@ int sparse_splits(const Dims& d, int* split_tokens, int* tail_last) {
 }
 
 int dense_splits(const Dims& d, int* split_tokens) {
-  // About 8K single-wavefront workgroups in total, at least 256 tokens each.
+  // About 8K wavefronts in total, at least 256 tokens each.
   const long long cchunks = ((long long)d.Nq * (d.Hq / d.Hkv) + 15) / 16;
   const long long units = (long long)d.B * d.Hkv * cchunks;
   long long n_split = (8192 + units - 1) / units;
@@ -647,10 +657,12 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
   const size_t rh = (size_t)d.B * d.Nq * d.Hq;
   a.part_o = c.take<float>(rh * a.n_split * kHeadDim);
   a.part_lse = c.take<float>(rh * a.n_split);
-  const int cchunks = (d.Nq * a.G + 15) / 16;
+  const int units = d.Hkv * ((d.Nq * a.G + 15) / 16);
+  const int waves = units < kDenseWaves ? units : kDenseWaves;
   QSA_LAUNCH(dense_decode_kernel,
-             dim3((unsigned)a.n_split, (unsigned)(d.Hkv * cchunks), (unsigned)d.B), dim3(64), 0, s,
-             a);
+             dim3((unsigned)a.n_split, (unsigned)((units + kDenseWaves - 1) / kDenseWaves),
+                  (unsigned)d.B),
+             dim3(64 * (unsigned)waves), 0, s, a);
   QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
              a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
   return hipGetLastError();

@@ -342,9 +342,10 @@ def test_forward_incremental_decode_steps():
 
 # ------------------------------------------------------------------ dense comparator
 
-def test_dense_decode_small():
-    say("dense small")
-    w = custom(lens=(5000, 333, 12), nq=6, hq=16, hkv=2)
+@pytest.mark.parametrize("nq", [6, 9])  # 3 and 5 chunks of 16 (query, head) columns per KV head
+def test_dense_decode_small(nq):
+    say(f"dense small nq={nq}")
+    w = custom(lens=(5000, 333, 12), nq=nq, hq=16, hkv=2)
     ref = O.dense_decode(w.q, w.k, w.v, w.lens, w.n_query)
     out, lse = Q.dense_gqa_decode(shape_of(w), dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
                                   dev_i32(w.lens))
