@@ -204,24 +204,33 @@ __device__ __forceinline__ void finish(const Run& r, bool col_valid, uint16_t* o
 }
 
 // ------------------------------------------------------------------ sparse
-// Grid (Nq * Hkv * hchunks, n_split, B): one workgroup per (query row, KV
-// head g, chunk of <= 16 query heads of g's group, token split).  Its four
-// wavefronts take interleaved 32-token tiles of the split (tile i goes to
-// wavefront i mod 4), each with its own online softmax, and are merged in
-// LDS.  With one split the result is final; otherwise the workgroup writes a
-// partial (o, lse) that merge_kernel combines.  (A merge by the last
-// workgroup to arrive would need a device-scope fence per workgroup, and on
-// this chip such a fence writes back the whole L2 of its XCD.)
-// kMulti false: every wavefront has at most one 32-token tile; kWaves: 4 or 8.
-template <bool kMulti, int kWaves>
+// A unit is (query row, KV head g, chunk of <= 16 query heads of g's
+// group); unit u = (q * Hkv + g) * hchunks + hc.  Grid (Nq * Hkv * hchunks /
+// kUnits, n_split, B): one workgroup per kUnits consecutive units of one
+// query and one token split.  Wavefront w serves unit w mod kUnits and takes
+// every (kWaves / kUnits)-th 32-token tile of the split from tile
+// w / kUnits on, with its own online softmax; the wavefronts of a unit are
+// merged in LDS.  With kUnits = 4 the four KV heads of a query sit in one
+// workgroup and read their 256-byte pieces of each token's 1 KiB K and V
+// rows in step, so a row is fetched whole.  With one split the result is
+// final; otherwise the workgroup writes a partial (o, lse) that merge_kernel
+// combines.  (A merge by the last workgroup to arrive would need a
+// device-scope fence per workgroup, and on this chip such a fence writes
+// back the whole L2 of its XCD.)  kMulti false: every wavefront has at most
+// one 32-token tile.  kUnits > 1 needs G <= 16 (one head chunk per KV head).
+template <bool kMulti, int kWaves, int kUnits>
 __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) {
   constexpr int kThreads = 64 * kWaves;
+  constexpr int kWpu = kWaves / kUnits;      // wavefronts per unit
   constexpr int kSelPer = kTopK / kThreads;  // selection entries each thread prefetches
+  static_assert(kWaves % kUnits == 0, "whole wavefronts per unit");
   __shared__ int32_t s_sel[kTopK];
   __shared__ __align__(16) uint16_t s_v[kWaves][kTile * kVStride];  // V tiles; then merge scratch
-  __shared__ float s_m[kWaves][16], s_l[kWaves][16], s_f[kWaves][16], s_inv[16];
-  const int unit = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16], s_f[kWaves][16], s_inv[kUnits][16];
+  const int split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wu = wave % kUnits, wi = wave / kUnits;  // unit of this wavefront, rank in it
+  const int unit = blockIdx.x * kUnits + wu;
   const int hchunks = (a.G + 15) >> 4;
   const int q = unit / (a.Hkv * hchunks);
   const int g = (unit / hchunks) % a.Hkv, hc = unit % hchunks;
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   // alone) is wavefront 0's extra tile in the last split: its rows are
   // requested now, before the selection arrives, and it is processed ahead
   // of the selected tiles, so that it does not add a round trip at the end.
-  const bool own_tail = kMulti && a.tail_last && split == a.n_split - 1 && wave == 0 && t >= 0;
+  const bool own_tail = kMulti && a.tail_last && split == a.n_split - 1 && wi == 0 && t >= 0;
   KVTile tail;
   if (own_tail)
     load_tile(tail, kbase, vbase, 0, [&](int kk) -> long long {
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   Run r;
   run_init(r);
   KVTile cur;
-  const int first = k_begin + wave * kTile;
+  const int first = k_begin + wi * kTile;
   if (first < k_end) load_tile(cur, kbase, vbase, first, row_of);
   if (own_tail) {
     stash_v(vt, tail);
@@ -303,11 +312,11 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
     softmax_pv(r, z, vt);
     wave_sync_lds();
   }
-  for (int k0 = first; k0 < k_end; k0 += kWaves * kTile) {
+  for (int k0 = first; k0 < k_end; k0 += kWpu * kTile) {
     stash_v(vt, cur);
     KVTile nxt;
-    if (kMulti && k0 + kWaves * kTile < k_end)
-      load_tile(nxt, kbase, vbase, k0 + kWaves * kTile, row_of);
+    if (kMulti && k0 + kWpu * kTile < k_end)
+      load_tile(nxt, kbase, vbase, k0 + kWpu * kTile, row_of);
     float z[8];
     qk_logits(cur, qf, a.scale_log2, z);
 #pragma unroll
@@ -340,19 +349,27 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   }
   __syncthreads();
   const bool partial = a.n_split > 1;
-  if (tid < 16) {
+  // first query head of unit uu of this workgroup (every unit of a workgroup
+  // has the same nh: kUnits > 1 only with one head chunk per KV head)
+  auto head0 = [&](int uu) -> int {
+    const int un = blockIdx.x * kUnits + uu;
+    return ((un / hchunks) % a.Hkv) * a.G + (un % hchunks) * 16;
+  };
+  if (tid < 16 * kUnits) {
+    const int uu = tid >> 4, c = tid & 15;
     float M = kNegInf;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][tid]);
+    for (int j = 0; j < kWpu; ++j) M = fmaxf(M, s_m[uu + kUnits * j][c]);
     float L = 0.f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = (M == kNegInf || s_m[w][tid] == kNegInf) ? 0.f : exp2f(s_m[w][tid] - M);
-      s_f[w][tid] = f;
-      L += f * s_l[w][tid];
+    for (int j = 0; j < kWpu; ++j) {
+      const int w = uu + kUnits * j;
+      const float f = (M == kNegInf || s_m[w][c] == kNegInf) ? 0.f : exp2f(s_m[w][c] - M);
+      s_f[w][c] = f;
+      L += f * s_l[w][c];
     }
-    s_inv[tid] = L > 0.f ? 1.f / L : 0.f;
+    s_inv[uu][c] = L > 0.f ? 1.f / L : 0.f;
     const float lse_v = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
-    if (tid < nh) {
-      const size_t rh = row * a.Hq + h0 + tid;
+    if (c < nh) {
+      const size_t rh = row * a.Hq + head0(uu) + c;
       if (partial)
         a.part_lse[rh * a.n_split + split] = lse_v;
       else if (a.lse)
@@ -360,13 +377,18 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
     }
   }
   __syncthreads();
-  for (int i = tid; i < nh * kHeadDim; i += blockDim.x) {
-    const int c = i >> 7, d = i & 127;
+  for (int i = tid; i < kUnits * nh * kHeadDim; i += blockDim.x) {
+    const int uu = kUnits == 1 ? 0 : i / (nh * kHeadDim);
+    const int rem = i - uu * nh * kHeadDim;
+    const int c = rem >> 7, d = rem & 127;
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += s_f[w][c] * O[(w * 16 + c) * kHeadDim + d];
-    o *= s_inv[c];
-    const size_t rh = row * a.Hq + h0 + c;
+    for (int j = 0; j < kWpu; ++j) {
+      const int w = uu + kUnits * j;
+      o += s_f[w][c] * O[(w * 16 + c) * kHeadDim + d];
+    }
+    o *= s_inv[uu][c];
+    const size_t rh = row * a.Hq + head0(uu) + c;
     if (partial)
       a.part_o[(rh * a.n_split + split) * kHeadDim + d] = o;
     else
@@ -528,13 +550,30 @@ int sparse_units(const Dims& d) {
 // partials).
 constexpr int kSparseTargetWG = 256;
 
+// Units of one query that share a workgroup: for batches with enough rows
+// to fill the chip without splits, the four KV heads of a group of four when
+// each KV head's query heads fit one chunk (eight wavefronts, two per KV
+// head; 7 % faster on the 16K-query chunk than a workgroup per KV head),
+// else one.  (Decode-sized batches split the token list instead; there the
+// grouping was slower: more splits for the same number of workgroups.)
+int sparse_group(const Dims& d) {
+  const int G = d.Hq / d.Hkv;
+  if (G > 16 || d.Hkv % 4 != 0) return 1;
+  return (long long)d.B * sparse_units(d) / 4 >= kSparseTargetWG ? 4 : 1;
+}
+
 int sparse_splits(const Dims& d, int* split_tokens, int* tail_last) {
   // Decode-sized batches have few (query, KV head) units: split their token
   // lists so that about kSparseTargetWG workgroups share the gather.  Splits
   // of one tile per wavefront leave the query's own block (<= 4 tokens) to a
   // split of its own; longer splits take it into the last one.
-  const long long units = (long long)d.B * sparse_units(d);
   constexpr int kSelTok = kTopK * kBlock;
+  if (sparse_group(d) > 1) {  // whole token lists
+    *split_tokens = kMaxTok;
+    *tail_last = 0;
+    return 1;
+  }
+  const long long units = (long long)d.B * sparse_units(d);
   int st = kMaxTok;
   if (units < kSparseTargetWG) {
     const long long want = (kSparseTargetWG + units - 1) / units;
@@ -608,16 +647,20 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
     a.part_o = part_o;
     a.part_lse = part_lse;
   }
-  const dim3 grid((unsigned)sparse_units(d), (unsigned)a.n_split, (unsigned)d.B);
-  if (a.split_tokens <= 4 * kTile)
-    QSA_LAUNCH_AS("sparse_attend_kernel<false>", (sparse_attend_kernel<false, 4>), grid,
+  const int grp = sparse_group(d);
+  const dim3 grid((unsigned)(sparse_units(d) / grp), (unsigned)a.n_split, (unsigned)d.B);
+  if (grp > 1)  // four KV heads per workgroup, two wavefronts each, one split
+    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 8, 4>), grid,
+                  dim3(512), 0, s, a);
+  else if (a.split_tokens <= 4 * kTile)
+    QSA_LAUNCH_AS("sparse_attend_kernel<false>", (sparse_attend_kernel<false, 4, 1>), grid,
                   dim3(256), 0, s, a);
   else if (a.n_split > 1)  // decode-sized: eight wavefronts walk a split's tiles
-    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 8>), grid, dim3(512),
-                  0, s, a);
+    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 8, 1>), grid,
+                  dim3(512), 0, s, a);
   else
-    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 4>), grid, dim3(256),
-                  0, s, a);
+    QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 4, 1>), grid,
+                  dim3(256), 0, s, a);
   if (a.n_split > 1)
     QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
                part_o, part_lse, out, lse, d.Nq, d.Hq, a.n_split);

@@ -248,14 +248,17 @@ def test_sparse_attend_head_layouts(hq, hkv):
     check_attend_with_oracle_sel(w, res)
 
 
-def test_sparse_attend_many_rows_single_split():
+# 8/1: a workgroup per (query, KV head); 32/4 and 4/4: the four KV heads of a
+# query in one workgroup (at least 1,024 (query, KV head) units)
+@pytest.mark.parametrize("nq,hq,hkv", [(1100, 8, 1), (300, 32, 4), (260, 4, 4)])
+def test_sparse_attend_many_rows_single_split(nq, hq, hkv):
     # enough query rows that no split/merge is used
-    say("attend many rows")
-    w = W.make_custom(9, [6000], 1100, 8, 1)
-    qs = [(0, i) for i in range(0, 1100, 37)] + [(0, 1099)]
+    say("attend many rows", nq, hq, hkv)
+    w = W.make_custom(9, [6000], nq, hq, hkv)
+    qs = [(0, i) for i in range(0, nq, 37)] + [(0, nq - 1)]
     res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, w.n_query, queries=qs)
     sel_all, n_all = padded_sel(O.qsa_forward(w.q_idx, w.k_idx, None, None, None, w.lens,
-                                              w.n_query), 1, 1100, w.lens)
+                                              w.n_query), 1, nq, w.lens)
     out, lse = Q.sparse_attend(shape_of(w), dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
                                dev_i32(w.lens), dev_i32(sel_all), dev_i32(n_all))
     got = host_f64_from_bf16(out)
