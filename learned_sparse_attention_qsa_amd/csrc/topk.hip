@@ -253,44 +253,81 @@ __device__ __forceinline__ void wave_suffix_bin_2048(const uint32_t* h, uint32_t
 }
 
 // ------------------------------------------------------------------ select
-// Exact top-512 of one query straight from its whole row, walking the blocks
-// in order (so the output comes out ascending).  Slow path for rows whose
-// candidate list does not fit the fast path.  kRecompute: no score table
-// exists (stream engine), scores are recomputed from q_idx and k_cmp.
+// Exact top-512 of one query straight from its whole row.  Slow path for
+// rows whose candidate list does not fit the fast path (very many equal or
+// near-equal scores).  kRecompute: no score table exists (stream engine),
+// scores are recomputed from q_idx and k_cmp.  The 512th best key is
+// (v, the lowest indices among scores equal to v): an LDS radix select over
+// the 32 score bits (four passes of 8 bits, each ending early once the
+// chosen digit's bin holds exactly the keys still needed, or once every
+// score left in play is equal) gives v's prefix and how many of the scores
+// equal to it are needed; a last walk over the blocks in ascending order
+// keeps every higher score and the first that many equal ones, and stops
+// once 512 are kept (an all-equal row ends after its first 512 blocks).
+// hist: 256 words; bcast: 6 words; wsum: two words per wavefront.
 template <bool kRecompute>
 __device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, const uint16_t* kc,
                                  int bt, int32_t* srow, float* qf, uint32_t* hist,
                                  uint32_t* bcast, uint32_t* wsum) {
   const int tid = threadIdx.x;
+  const int nw = (int)(blockDim.x >> 6);
   if (kRecompute) {
     for (int i = tid; i < kIdxHeads * kIdxDim; i += blockDim.x)
       qf[i] = __uint_as_float((uint32_t)qrow[i] << 16);
     __syncthreads();
   }
-  auto key_of = [&](int j) -> uint64_t {
-    uint32_t bits;
-    if (kRecompute) {
-      float d[4] = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = kc + (size_t)j * kIdxDim;
-      for (int e = 0; e < kIdxDim; ++e) {
-        const float kv = __uint_as_float((uint32_t)kr[e] << 16);
+  // score bits of block j (dims accumulated in order, as a scalar dot would)
+  auto score_of = [&](int j) -> uint32_t {
+    if (!kRecompute) return trow[j];
+    const uint4* kr = reinterpret_cast<const uint4*>(kc + (size_t)j * kIdxDim);
+    // (an opaque copy of the query pointer, so that the 256 query values are
+    // read from LDS per block instead of being held in registers)
+    typedef __attribute__((address_space(3))) const float lds_float;
+    lds_float* qv = (lds_float*)qf;
+    asm volatile("" : "+v"(qv));
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll 2
+    for (int c = 0; c < kIdxDim / 8; ++c) {
+      const uint4 u = kr[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int h = 0; h < 4; ++h) d[h] = fmaf(qf[h * kIdxDim + e], kv, d[h]);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = w[e >> 1];
+        const float kv = __uint_as_float((e & 1) ? (h & 0xffff0000u) : (h << 16));
+        const int dd = c * 8 + e;
+        d0 = fmaf(qv[dd], kv, d0);
+        d1 = fmaf(qv[kIdxDim + dd], kv, d1);
+        d2 = fmaf(qv[2 * kIdxDim + dd], kv, d2);
+        d3 = fmaf(qv[3 * kIdxDim + dd], kv, d3);
       }
-      bits = relu_sum_bits(d[0], d[1], d[2], d[3]);
-    } else {
-      bits = trow[j];
     }
-    return make_key(bits, (uint32_t)j);
+    return relu_sum_bits(d0, d1, d2, d3);
   };
-  uint64_t prefix = 0, pmask = 0;
-  uint32_t k = kTopK;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t k = kTopK;  // keys still needed among those matching the prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+    if (tid == 0) {
+      bcast[4] = 0xffffffffu;  // min, max of the scores matching the prefix
+      bcast[5] = 0u;
+    }
     __syncthreads();
+    uint32_t mn = 0xffffffffu, mx = 0u;
     for (int j = tid; j < bt; j += blockDim.x) {
-      const uint64_t key = key_of(j);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+      const uint32_t sb = score_of(j);
+      if ((sb & pmask) == prefix) {
+        atomicAdd(&hist[(sb >> shift) & 255u], 1u);
+        mn = min(mn, sb);
+        mx = max(mx, sb);
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    }
+    if ((tid & 63) == 0) {
+      atomicMin(&bcast[4], mn);
+      atomicMax(&bcast[5], mx);
     }
     __syncthreads();
     if (tid < 64) {
@@ -299,27 +336,63 @@ __device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, con
       if (tid == 0) {
         bcast[0] = d;
         bcast[1] = above;
+        bcast[2] = hist[d];
       }
     }
     __syncthreads();
+    if (bcast[4] == bcast[5]) {  // every score in play is the same value
+      prefix = bcast[4];
+      pmask = 0xffffffffu;
+      __syncthreads();
+      break;
+    }
     k -= bcast[1];
-    prefix |= (uint64_t)bcast[0] << shift;
-    pmask |= 0xffull << shift;
+    prefix |= bcast[0] << shift;
+    pmask |= 0xffu << shift;
+    const bool exact = bcast[2] == k;  // the bin holds exactly the keys needed
     __syncthreads();
+    if (exact) break;
   }
-  const uint64_t kth = prefix;
+  // blocks in ascending order: every score above the prefix range, and the
+  // first k of those inside it
   const int lane = lane_id(), wave = tid >> 6;
-  uint32_t written = 0;
-  for (int base = 0; base < bt; base += blockDim.x) {
+  uint32_t kept = 0, eq_seen = 0;
+  for (int base = 0; base < bt && kept < (uint32_t)kTopK; base += blockDim.x) {
     const int j = base + tid;
-    const bool keep = j < bt && key_of(j) >= kth;
-    const uint64_t m = __ballot(keep);
-    if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+    uint32_t sb = 0;
+    if (j < bt) sb = score_of(j);
+    const bool in = j < bt;
+    const bool gt = in && (sb & pmask) > prefix;
+    const bool eq = in && (sb & pmask) == prefix;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    if (lane == 0) {
+      wsum[2 * wave] = (uint32_t)__popcll(mg);
+      wsum[2 * wave + 1] = (uint32_t)__popcll(me);
+    }
     __syncthreads();
-    uint32_t off = written;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (keep) srow[off + (uint32_t)__popcll(m & lanemask_lt())] = j;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) written += wsum[w];
+    uint32_t eq_before = eq_seen, eq_all = 0, kept_before = kept;
+    for (int w = 0; w < nw; ++w) {
+      if (w < wave) eq_before += wsum[2 * w + 1];
+      eq_all += wsum[2 * w + 1];
+    }
+    const uint32_t my_eq = eq_before + (uint32_t)__popcll(me & lanemask_lt());
+    const bool keep = gt || (eq && my_eq < k);
+    // kept in this chunk: every gt, and the equal ones still needed
+    const uint64_t mk = __ballot(keep);
+    __syncthreads();
+    if (lane == 0) wsum[2 * wave] = (uint32_t)__popcll(mk);
+    __syncthreads();
+    uint32_t kept_all = 0;
+    for (int w = 0; w < nw; ++w) {
+      if (w < wave) kept_before += wsum[2 * w];
+      kept_all += wsum[2 * w];
+    }
+    if (keep) {
+      const uint32_t pos = kept_before + (uint32_t)__popcll(mk & lanemask_lt());
+      if (pos < (uint32_t)kTopK) srow[pos] = j;
+    }
+    kept += kept_all;
+    eq_seen += eq_all;
     __syncthreads();
   }
 }
@@ -340,13 +413,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     int Lmax, int Nq) {
   __shared__ uint64_t keys[kSelCap];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t bcast[3];
+  __shared__ uint32_t bcast[6];
   __shared__ uint64_t s_min;
   __shared__ int32_t outb[kTopK];
   __shared__ uint32_t outn;
   __shared__ uint32_t bad;
   __shared__ float qf[kIdxHeads * kIdxDim];
-  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t wsum[8];
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const size_t row = (size_t)b * Nq + q;
   // threads_per_seg threads walk each segment; the segment length is read
@@ -691,8 +764,8 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
   __shared__ uint32_t wcnt[kPickRounds][kPickWaves];
   __shared__ uint32_t wtot[kPickWaves];
   __shared__ uint4 res[1];
-  __shared__ uint32_t wsum[kPickWaves];
-  __shared__ uint32_t bcast[2];
+  __shared__ uint32_t wsum[2 * kPickWaves];
+  __shared__ uint32_t bcast[6];
   __shared__ uint32_t s_bv;
   __shared__ uint32_t s_mm[2];
   const int row = blockIdx.x, b = row / Nq, q = row - b * Nq, tid = threadIdx.x;

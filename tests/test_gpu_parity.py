@@ -149,6 +149,28 @@ def test_topk_all_equal_scores(flags):
 
 
 @pytest.mark.parametrize("flags", ENGINES)
+def test_topk_ties_at_the_cut(flags):
+    # three score values: ~300 blocks score 8, ~6,000 score 4, the rest 0, so
+    # the 512th key is a 4 and the lowest-index 4s fill the remainder; the
+    # stream engine's candidate list overflows and the whole-row path decides
+    say("topk ties at the cut", flags)
+    w = custom(lens=(60000, 59999), nq=6, parts=("index",))
+    rng = np.random.default_rng(7)
+    cls = rng.choice(3, size=(2, w.max_len // 4), p=[0.58, 0.40, 0.02]).astype(np.float32)
+    w.k_idx[:] = 0
+    w.k_idx[:, 0::4, 0] = (cls.view(np.uint32) >> 16).astype(np.uint16)
+    w.q_idx[:] = bf16_const(w.q_idx.shape, 1.0)
+    res = oracle_select(w)
+    for (b, i), s in res["sel"].items():
+        t = int(w.lens[b]) - w.n_query + i
+        sc = cls[b, :t // 4]
+        n_top = int((sc == 2).sum())
+        assert 0 < n_top < 512 and np.array_equal(np.sort(s), s)
+        assert set(np.flatnonzero(sc == 2).tolist()) <= set(s.tolist())
+    check_topk(w, flags, res)
+
+
+@pytest.mark.parametrize("flags", ENGINES)
 def test_topk_increasing_scores(flags):
     # scores grow with the block id: every new block beats the running
     # threshold (worst case for the streaming engine)
