@@ -390,3 +390,29 @@ def test_dense_decode_cfg1_sampled():
                                 dev_i32(w.lens))
     got = host_f64_from_bf16(out)
     check_close(np.stack([got[b, i] for b, i in keys]), np.stack([ref[k][0] for k in keys]))
+
+
+# ------------------------------------------------------------------ timing hook
+
+def test_kernel_timer_records_every_launch():
+    # the per-launch events ride in each dispatch: one record per kernel, in
+    # launch order, each a positive duration, and the results unchanged
+    say("kernel timer")
+    w = custom(lens=(9000, 5000), nq=4, hq=16, hkv=2)
+    shp = shape_of(w, Q.FLAG_TOPK_TABLE)
+    k_cmp = gpu_kcmp(w)
+    args = (dev_bf16(w.q_idx), dev_bf16(w.k_idx), k_cmp, dev_bf16(w.q), dev_bf16(w.k),
+            dev_bf16(w.v), dev_i32(w.lens))
+    out0, _ = Q.forward(shp, *args)[:2]
+    timer = Q.KernelTimer(max_launches=16)
+    with timer:
+        out1, _ = Q.forward(shp, *args)[:2]
+    recs = timer.records()
+    names = [n for n, _ in recs]
+    known = ("compress_kernel", "score_table_kernel", "table_pick_kernel", "sparse_attend_kernel",
+             "merge_kernel")
+    assert all(n.startswith(known) for n in names), names
+    assert names.index("score_table_kernel") < names.index("table_pick_kernel"), names
+    assert any(n.startswith("sparse_attend_kernel") for n in names), names
+    assert all(ms > 0.0 for _, ms in recs), recs
+    assert torch.equal(out0, out1)
