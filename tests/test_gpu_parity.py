@@ -291,6 +291,31 @@ def test_sparse_attend_many_rows_single_split(nq, hq, hkv):
 # ------------------------------------------------------------------ forward
 
 @pytest.mark.parametrize("flags", ENGINES)
+def test_forward_very_short_sequences(flags):
+    # contexts of 4..11 tokens with 4 queries each: the first queries have no
+    # completed block before their own (nothing to select, attention over
+    # tokens 4 bt .. t only), the later ones select every earlier block
+    say("forward very short", flags)
+    w = custom(lens=(4, 5, 7, 8, 11), nq=4)
+    res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, w.n_query)
+    shp = shape_of(w, flags)
+    k_cmp = torch.zeros((w.batch, w.max_len // 4, 64), dtype=torch.bfloat16, device="cuda")
+    sel = torch.empty((w.batch, w.n_query, 512), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((w.batch, w.n_query), dtype=torch.int32, device="cuda")
+    out, lse, _, _ = Q.forward(shp, dev_bf16(w.q_idx), dev_bf16(w.k_idx), k_cmp, dev_bf16(w.q),
+                               dev_bf16(w.k), dev_bf16(w.v), dev_i32(w.lens), sel=sel, n_sel=n_sel)
+    want_sel, want_n = padded_sel(res, w.batch, w.n_query, w.lens)
+    np.testing.assert_array_equal(n_sel.cpu().numpy(), want_n)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
+    got = host_f64_from_bf16(out)
+    keys = sorted(res["out"].keys())
+    check_close(np.stack([got[b, i] for b, i in keys]), np.stack([res["out"][k] for k in keys]))
+    g_lse = lse.cpu().numpy()
+    assert max(abs(g_lse[b, i] - res["lse"][(b, i)]).max() for b, i in keys) < 2e-3
+
+
+
+@pytest.mark.parametrize("flags", ENGINES)
 def test_forward_cfg0(flags):
     say("forward cfg0", flags)
     w = W.make(0)
