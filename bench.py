@@ -11,23 +11,32 @@ are flushed (untimed, by reading a 1 GiB buffer) before every step, as the
 other layers of a model would.
 
 The same line carries
-  roofline      the dominant kernel's algorithmic bytes (or flops) per launch
-                over its HIP-event-timed average duration, against MI355X peak;
-  kernels       average duration of every kernel of the step (HIP events on
-                the launch stream, via the library's profiling hook);
-  prefill       the 1M-context, last-16,384-token-chunk prefill step (batch 1),
-                with the indexer-scoring MFMA fraction;
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average duration (HIP events carried by the kernel's own
+                dispatches, over a second pass of the same steps), against
+                MI355X peak;
+  kernels       average duration of every kernel of the step;
+  cold          the same step with the compressed-key cache rebuilt from
+                scratch (every block compressed inside the call);
   dense         the dense causal GQA decode comparator at the decode shape;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the decode step
-                (with its selections checked against the GPU's).
+  prefill       the 1M-context, last-16,384-token-chunk prefill step (batch 1),
+                with the indexer's MFMA fraction and the attention's;
+  configs       the other three workloads (tiny 4K, 128K decode, 256K prefill
+                chunk), steady-state forward, each against its roofline;
+  ceilings      the part's measured memory ceilings under the path's access
+                patterns (cold 128 MiB streaming read, random 256 B / 1 KiB /
+                4 KiB gathers over an 8 GiB K/V cache);
+  cpu_baseline  the CPU oracle on bounded samples of the decode step and the
+                prefill step, per stage, on the host cores.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+       python bench.py --ceilings          (only the memory ceilings)
+       python bench.py --copy-calibration  (counter calibration copy)
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -45,25 +54,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--dense-steps", type=int, default=5)
+    ap.add_argument("--cold-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other three workloads")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the memory ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
-    ap.add_argument("--other-configs", action="store_true",
-                    help="instead of the headline run: one JSON line per parity workload "
-                         "(tiny 4K, 128K decode, 256K prefill chunk), steady-state forward")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of each oracle sample (decode, prefill)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the memory ceilings and print them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer three times and exit (the reference "
                          "kernel for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # --------------------------------------------------------------------- helpers
@@ -75,23 +86,38 @@ def to_dev(a, torch, np):
     return torch.from_numpy(a).to("cuda")
 
 
+def base_name(name: str) -> str:
+    """A recorded kernel name without its template arguments."""
+    return name.split("<", 1)[0]
+
+
 def kernel_stats(records, n_steps):
+    """Per-kernel average duration (us) and launches per step, keyed by the
+    kernel's base name (template instantiations of one kernel are one entry;
+    their recorded names are listed under "variants")."""
     agg = {}
     for name, ms in records:
-        s = agg.setdefault(name, [0.0, 0])
+        s = agg.setdefault(base_name(name), [0.0, 0, set()])
         s[0] += ms
         s[1] += 1
+        s[2].add(name)
     out = {}
-    for name, (tot, cnt) in agg.items():
+    for name, (tot, cnt, names) in agg.items():
         out[name] = {"avg_us": 1000.0 * tot / cnt, "launches_per_step": cnt / n_steps}
+        if names != {name}:
+            out[name]["variants"] = sorted(names)
     return out
 
 
 def timed_steps(step, n, flush, Q, torch):
-    """n steps, flush before each (untimed), per-step HIP events; then up to
-    20 more steps with the library's per-launch events (carried by each
-    kernel's dispatch, so they time the kernel alone; kept out of the step
-    times all the same)."""
+    """n steps, each after an untimed flush, with HIP events on the stream
+    around each step; then the same n steps again with per-kernel HIP events
+    carried by each kernel's own dispatch packet (the library's profiling
+    hook).  The two passes are separate because the dispatch-carried events
+    lengthen the gap between dependent kernels by several microseconds, so
+    the step times come from the first pass and the kernel durations from the
+    second.  Returns (step times in ms, kernel stats, wall seconds of the
+    first pass)."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     torch.cuda.synchronize()
@@ -104,13 +130,13 @@ def timed_steps(step, n, flush, Q, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    nk = min(n, 20)
+    nk = min(n, 60)
     timer = Q.KernelTimer(max_launches=16 * nk + 16)
+    torch.cuda.synchronize()
     with timer:
-        for i in range(nk):
+        for _ in range(nk):
             flush()
             step()
-    torch.cuda.synchronize()
     return step_ms, kernel_stats(timer.records(), nk), wall
 
 
@@ -136,45 +162,42 @@ def measured_traffic(kernel):
         return None
 
 
+def roofline_of(kstats, algo):
+    """Roofline record of the dominant kernel (largest time per step) of a
+    leg.  algo: base kernel name -> (bound, work per step, unit of work,
+    description); "hbm" work is bytes, "mfma" work is flop."""
+    if not kstats:
+        return None
+    name, st = max(kstats.items(), key=lambda kv: kv[1]["avg_us"] * kv[1]["launches_per_step"])
+    if name not in algo:
+        return {"kernel": name, "bound": None, "achieved": None, "peak": None,
+                "frac": None, "traffic": None, "note": "no algorithmic work recorded"}
+    bound, per_step, what = algo[name]
+    per_launch = per_step / max(st["launches_per_step"], 1.0)
+    sec = st["avg_us"] * 1e-6
+    if bound == "hbm":
+        ach, peak, unit = per_launch / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = per_launch / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "kernel": name, "achieved": ach, "peak": peak, "unit": unit,
+            "frac": ach / peak, "traffic": measured_traffic(name),
+            "algorithmic_" + ("bytes" if bound == "hbm" else "flop"): per_launch,
+            "work_is": what}
+
+
 def pct(xs, p):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))]
 
 
-# --------------------------------------------------------------------- legs
-
-def decode_leg(args, Q, W, torch, np, flush):
-    log("[bench] decode-1m-b4x4: generating inputs")
-    w = W.make(4)
-    B, L, Nq = w.batch, w.max_len, w.n_query
-    shp = Q.shape(B, L, Nq, w.q_heads, w.kv_heads)
-    dev = {n: to_dev(getattr(w, n), torch, np) for n in ("q_idx", "k_idx", "q", "k", "v")}
-    lens = to_dev(w.lens, torch, np)
-    prev = to_dev((w.lens - Nq).astype(np.int32), torch, np)
-    first = to_dev(((w.lens - Nq) // 4).astype(np.int32), torch, np)
-    k_cmp = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
-    Q.compress_keys(shp, dev["k_idx"], prev, k_cmp)  # cache state of the previous step
-    out = torch.empty((B, Nq, w.q_heads, 128), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, Nq, w.q_heads), dtype=torch.float32, device="cuda")
-    sel = torch.empty((B, Nq, 512), dtype=torch.int32, device="cuda")
-    n_sel = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
-    ws = Q.workspace(shp, Q.OP_FORWARD)
-
-    def step():
-        Q.forward(shp, dev["q_idx"], dev["k_idx"], k_cmp, dev["q"], dev["k"], dev["v"], lens,
-                  first_block=first, out=out, lse=lse, sel=sel, n_sel=n_sel, ws=ws)
-
-    log(f"[bench] decode: {args.warmup} warmup + {args.steps} timed steps")
-    for _ in range(args.warmup):
-        flush()
-        step()
-    torch.cuda.synchronize()
-    step_ms, kstats, wall = timed_steps(step, args.steps, flush, Q, torch)
-    sel_h = sel.cpu().numpy()
-    nsel_h = n_sel.cpu().numpy()
-    # algorithmic bytes per step of each kernel
+def decode_bytes(w, sel_h, nsel_h, np):
+    """Algorithmic HBM bytes of one decode step: the compressed keys of every
+    candidate block (each sequence's 4 queries share the scan), the union per
+    sequence of the gathered K and V rows (4 KV heads x 256 B each), Q, O and
+    the indexer queries."""
+    B, Nq = w.batch, w.n_query
     lens_h = w.lens.astype(np.int64)
-    kcmp_bytes = int(sum(((int(l) - 1) // 4) * 128 for l in lens_h))
+    kcmp = int(sum(((int(l) - 1) // 4) * 128 for l in lens_h))
     union_tokens = 0
     for b in range(B):
         toks = set()
@@ -186,29 +209,105 @@ def decode_leg(args, Q, W, torch, np, flush):
             toks.update(range(4 * bt, t + 1))
         union_tokens += len(toks)
     q_bytes = B * Nq * w.q_heads * 128 * 2
-    attn_bytes = union_tokens * w.kv_heads * 128 * 2 * 2 + 2 * q_bytes
-    algo = {
-        "score_table_kernel": ("hbm", kcmp_bytes + B * Nq * 4 * 64 * 2,
-                               "compressed keys of every candidate block (128 B each) + indexer queries"),
-        "score_stream_kernel": ("hbm", kcmp_bytes + B * Nq * 4 * 64 * 2,
+    attn = union_tokens * w.kv_heads * 128 * 2 * 2 + 2 * q_bytes
+    qidx = B * Nq * 4 * 64 * 2
+    return kcmp, attn, qidx
+
+
+def decode_algo(kcmp, attn, qidx, B):
+    return {
+        "score_table_kernel": ("hbm", kcmp + qidx,
+                               "compressed keys of every candidate block (128 B each) + "
+                               "indexer queries"),
+        "scan_filter_kernel": ("hbm", kcmp + qidx,
+                               "compressed keys of every candidate block (128 B each) + "
+                               "indexer queries"),
+        "score_stream_kernel": ("hbm", kcmp + qidx,
                                 "compressed keys of every candidate block + indexer queries"),
-        "sparse_attend_kernel": ("hbm", attn_bytes,
-                                 "union over each sequence's 4 queries of the gathered K and V rows "
-                                 "(4 KV heads x 256 B each) + Q + O"),
+        "sparse_attend_kernel": ("hbm", attn,
+                                 "union over each sequence's 4 queries of the gathered K and V "
+                                 "rows (4 KV heads x 256 B each) + Q + O"),
+        "block_attend_kernel": ("hbm", attn,
+                                "union over each sequence's 4 queries of the gathered K and V "
+                                "rows (4 KV heads x 256 B each) + Q + O"),
         "compress_kernel": ("hbm", B * (512 + 128), "one new block per sequence: 4 keys in, 1 out"),
     }
-    return dict(w=w, shp=shp, dev=dev, lens=lens, step_ms=step_ms, kstats=kstats, wall=wall,
-                sel=sel_h, n_sel=nsel_h, algo=algo, kcmp_bytes=kcmp_bytes,
-                attn_bytes=attn_bytes, out=out)
+
+
+def prefill_work(w, np):
+    t = np.arange(int(w.lens[0]) - w.n_query, int(w.lens[0]), dtype=np.int64)
+    idx_flops = float(np.sum(512.0 * (t // 4)))
+    n_tok = 4 * np.minimum(512, t // 4) + (t % 4) + 1
+    attn_flops = float(np.sum(n_tok) * w.q_heads * 128 * 4)
+    return idx_flops, attn_flops
+
+
+class Workspace:
+    """Device tensors of one workload, with the compressed-key cache holding
+    every block before the call's queries (the steady state)."""
+
+    def __init__(self, w, Q, torch, np):
+        B, L, Nq = w.batch, w.max_len, w.n_query
+        self.w = w
+        self.shp = Q.shape(B, L, Nq, w.q_heads, w.kv_heads)
+        self.dev = {n: to_dev(getattr(w, n), torch, np) for n in ("q_idx", "k_idx", "q", "k", "v")}
+        self.lens = to_dev(w.lens, torch, np)
+        prev = to_dev((w.lens - Nq).astype(np.int32), torch, np)
+        self.first = to_dev(((w.lens - Nq) // 4).astype(np.int32), torch, np)
+        self.k_cmp = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
+        Q.compress_keys(self.shp, self.dev["k_idx"], prev, self.k_cmp)
+        self.out = torch.empty((B, Nq, w.q_heads, 128), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((B, Nq, w.q_heads), dtype=torch.float32, device="cuda")
+        self.sel = torch.empty((B, Nq, 512), dtype=torch.int32, device="cuda")
+        self.n_sel = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
+        self.ws = Q.workspace(self.shp, Q.OP_FORWARD)
+        self.Q = Q
+
+    def step(self, cold=False):
+        d = self.dev
+        self.Q.forward(self.shp, d["q_idx"], d["k_idx"], self.k_cmp, d["q"], d["k"], d["v"],
+                       self.lens, first_block=None if cold else self.first, out=self.out,
+                       lse=self.lse, sel=self.sel, n_sel=self.n_sel, ws=self.ws)
+
+
+# --------------------------------------------------------------------- legs
+
+def decode_leg(args, Q, W, torch, np, flush):
+    log("[bench] decode-1m-b4x4: generating inputs")
+    w = W.make(4)
+    ws = Workspace(w, Q, torch, np)
+    log(f"[bench] decode: {args.warmup} warmup + {args.steps} timed steps")
+    for _ in range(args.warmup):
+        flush()
+        ws.step()
+    torch.cuda.synchronize()
+    step_ms, kstats, wall = timed_steps(ws.step, args.steps, flush, Q, torch)
+    sel_h = ws.sel.cpu().numpy()
+    nsel_h = ws.n_sel.cpu().numpy()
+    kcmp, attn, qidx = decode_bytes(w, sel_h, nsel_h, np)
+    # cold: the whole compressed-key cache rebuilt inside the call
+    log(f"[bench] decode cold: {args.cold_steps} steps with a full compressed-key rebuild")
+    cold_ms, cold_k, _ = timed_steps(lambda: ws.step(cold=True), args.cold_steps, flush, Q, torch)
+    ws.step()  # leave the steady-state cache and selection behind
+    torch.cuda.synchronize()
+    return dict(w=w, ws=ws, step_ms=step_ms, kstats=kstats, wall=wall, sel=sel_h, n_sel=nsel_h,
+                algo=decode_algo(kcmp, attn, qidx, w.batch), kcmp_bytes=kcmp, attn_bytes=attn,
+                qidx_bytes=qidx,
+                cold={"ms_per_step": sum(cold_ms) / len(cold_ms), "steps": len(cold_ms),
+                      "kernels": cold_k,
+                      "note": "every block of the 1M-token contexts compressed inside the call "
+                              "(k_idx 512 MiB read, k_cmp 128 MiB written), then the step"})
 
 
 def dense_leg(args, Q, torch, flush, d):
-    shp, dev, lens = d["shp"], d["dev"], d["lens"]
-    ws = Q.workspace(shp, Q.OP_DENSE_DECODE)
-    out = torch.empty_like(d["out"])
+    ws_ = d["ws"]
+    shp, dev, lens = ws_.shp, ws_.dev, ws_.lens
+    wsp = Q.workspace(shp, Q.OP_DENSE_DECODE)
+    out = torch.empty_like(ws_.out)
 
     def step():
-        Q.dense_gqa_decode(shp, dev["q"], dev["k"], dev["v"], lens, out=out, ws=ws, want_lse=False)
+        Q.dense_gqa_decode(shp, dev["q"], dev["k"], dev["v"], lens, out=out, ws=wsp,
+                           want_lse=False)
 
     flush()
     step()
@@ -218,153 +317,281 @@ def dense_leg(args, Q, torch, flush, d):
     kv_bytes = int(sum(int(l) for l in w.lens)) * w.kv_heads * 128 * 2 * 2
     ms = sum(step_ms) / len(step_ms)
     return {"ms_per_step": ms, "kernels": kstats,
-            "hbm_gbs": kv_bytes / (ms * 1e-3) / 1e9, "kv_bytes": kv_bytes}
+            "hbm_gbs": kv_bytes / (ms * 1e-3) / 1e9, "kv_bytes": kv_bytes,
+            "roofline": roofline_of(kstats, {"dense_decode_kernel": ("hbm", kv_bytes,
+                                                                     "every K and V row of the "
+                                                                     "context")})}
 
 
-def prefill_leg(args, Q, W, torch, np, flush):
-    log("[bench] prefill-1m-chunk16k: generating inputs")
-    w = W.make(3)
-    B, L, Nq = w.batch, w.max_len, w.n_query
-    shp = Q.shape(B, L, Nq, w.q_heads, w.kv_heads)
-    dev = {n: to_dev(getattr(w, n), torch, np) for n in ("q_idx", "k_idx", "q", "k", "v")}
-    lens = to_dev(w.lens, torch, np)
-    prev = to_dev((w.lens - Nq).astype(np.int32), torch, np)
-    first = to_dev(((w.lens - Nq) // 4).astype(np.int32), torch, np)
-    k_cmp = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
-    Q.compress_keys(shp, dev["k_idx"], prev, k_cmp)
-    out = torch.empty((B, Nq, w.q_heads, 128), dtype=torch.bfloat16, device="cuda")
-    sel = torch.empty((B, Nq, 512), dtype=torch.int32, device="cuda")
-    n_sel = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
-    ws = Q.workspace(shp, Q.OP_FORWARD)
-
-    def step():
-        Q.forward(shp, dev["q_idx"], dev["k_idx"], k_cmp, dev["q"], dev["k"], dev["v"], lens,
-                  first_block=first, out=out, sel=sel, n_sel=n_sel, ws=ws, want_lse=False)
-
-    flush()
-    step()
-    torch.cuda.synchronize()
-    log(f"[bench] prefill: {args.prefill_steps} timed steps")
-    step_ms, kstats, _ = timed_steps(step, args.prefill_steps, flush, Q, torch)
-    t = np.arange(int(w.lens[0]) - Nq, int(w.lens[0]), dtype=np.int64)
-    idx_flops = float(np.sum(512.0 * (t // 4)))
-    n_tok = 4 * np.minimum(512, t // 4) + (t % 4) + 1
-    attn_flops = float(np.sum(n_tok) * w.q_heads * 128 * 4)
+def prefill_record(w, step_ms, kstats, np):
+    idx_flops, attn_flops = prefill_work(w, np)
     ms = sum(step_ms) / len(step_ms)
-    res = {"workload": w.name, "value": Nq / (ms * 1e-3), "unit": "q-tok/s", "ms_per_step": ms,
-           "steps": len(step_ms), "kernels": kstats,
+    res = {"workload": w.name, "value": w.batch * w.n_query / (ms * 1e-3), "unit": "q-tok/s",
+           "ms_per_step": ms, "steps": len(step_ms), "kernels": kstats,
            "indexer_flops": idx_flops, "attention_flops": attn_flops}
-    sk = kstats.get("score_stream_kernel") or kstats.get("score_table_kernel")
+    sk = kstats.get("score_stream_kernel")
     if sk:
         ach = idx_flops / (sk["avg_us"] * 1e-6) / 1e12
         res["indexer_mfma"] = {"kernel": "score_stream_kernel", "achieved": ach,
                                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": ach / MFMA_BF16_PEAK_TFLOPS}
+                               "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                               "traffic": measured_traffic("score_stream_kernel")}
     ak = kstats.get("sparse_attend_kernel")
     if ak:
         ach = attn_flops / (ak["avg_us"] * 1e-6) / 1e12
-        res["attention_mfma"] = {"achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": ach / MFMA_BF16_PEAK_TFLOPS}
-    del dev, k_cmp, out, sel, n_sel, ws
-    torch.cuda.empty_cache()
+        kv_unique = int(w.lens[0]) * w.kv_heads * 128 * 2 * 2
+        res["attention_mfma"] = {"kernel": "sparse_attend_kernel", "achieved": ach,
+                                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                                 "unique_kv_bytes": kv_unique,
+                                 "unique_kv_hbm_frac": kv_unique / (ak["avg_us"] * 1e-6) / 1e9
+                                 / HBM_PEAK_GBS,
+                                 "traffic": measured_traffic("sparse_attend_kernel")}
     return res
 
 
-def cpu_baseline(args, d, np):
-    """The oracle, untuned, on a bounded sample of the decode step."""
+def prefill_leg(args, Q, W, torch, np, flush, cfg=3, steps=None):
+    w = W.make(cfg)
+    log(f"[bench] {w.name}: inputs ready")
+    ws = Workspace(w, Q, torch, np)
+    flush()
+    ws.step()
+    torch.cuda.synchronize()
+    n = steps or args.prefill_steps
+    log(f"[bench] {w.name}: {n} timed steps")
+    step_ms, kstats, _ = timed_steps(ws.step, n, flush, Q, torch)
+    res = prefill_record(w, step_ms, kstats, np)
+    del ws
+    torch.cuda.empty_cache()
+    return res, w
+
+
+def other_configs(Q, W, torch, np, flush):
+    """The tiny 4K, 128K decode and 256K prefill-chunk workloads, steady-state
+    forward (the compressed-key cache holds the blocks before the call's
+    queries), each with its roofline."""
+    res = {}
+    for cfg in (0, 1, 2):
+        w = W.make(cfg)
+        ws = Workspace(w, Q, torch, np)
+        for _ in range(3):
+            flush()
+            ws.step()
+        torch.cuda.synchronize()
+        n = 50 if w.n_query <= 64 else 5
+        step_ms, kstats, _ = timed_steps(ws.step, n, flush, Q, torch)
+        ms = float(np.median(step_ms))
+        if cfg == 2:
+            rec = prefill_record(w, step_ms, kstats, np)
+            rec["ms_per_step"] = ms
+            rec["value"] = w.batch * w.n_query / (ms * 1e-3)
+        else:
+            sel_h, nsel_h = ws.sel.cpu().numpy(), ws.n_sel.cpu().numpy()
+            kcmp, attn, qidx = decode_bytes(w, sel_h, nsel_h, np)
+            step_bytes = kcmp + attn + qidx
+            rec = {"workload": w.name, "value": w.batch * w.n_query / (ms * 1e-3),
+                   "unit": "q-tok/s", "ms_per_step": ms, "steps": n, "kernels": kstats,
+                   "step_hbm": {"algorithmic_bytes": step_bytes,
+                                "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
+                                "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                   "roofline": roofline_of(kstats, decode_algo(kcmp, attn, qidx, w.batch))}
+            if cfg == 0:
+                rec["note"] = ("64 queries over a 4,096-token context: too small to load the "
+                               "part, so launch and round-trip latencies dominate")
+        res[w.name] = rec
+        log(f"[bench] {w.name}: {ms * 1e3:.1f} us per step")
+        del ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def ceilings(Q, torch, flush, reps=10):
+    """Memory ceilings under the path's access patterns, each kernel timed by
+    the HIP events its own dispatch carries, after an untimed flush."""
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261203)
+
+    def run(fn):
+        fn()  # one untimed pass: first touch of the buffer's pages
+        timer = Q.KernelTimer(max_launches=reps + 2)
+        torch.cuda.synchronize()
+        with timer:
+            for _ in range(reps):
+                flush()
+                fn()
+        recs = timer.records()
+        us = sorted(1000.0 * ms for _, ms in recs)
+        return us[len(us) // 2]
+
+    out = {}
+    scan_bytes = 128 << 20  # one decode step's compressed keys: 4 x 262,143 x 128 B ~ 128 MiB
+    buf = torch.empty(scan_bytes, dtype=torch.uint8, device="cuda")
+    for wgs in (256, 1024):
+        us = run(lambda: Q.ceil_stream_read(buf, wgs, sink))
+        out[f"stream_read_128MiB_wg{wgs}"] = {"us": us, "gbs": scan_bytes / (us * 1e-6) / 1e9}
+    del buf
+    # the decode K/V cache: 4 sequences x 1M tokens x 4 KV heads x 128 dims,
+    # K and V: 8 GiB; the gathers read what 16 query rows of 2,048 selected
+    # tokens would (random micro-blocks of each row's sequence)
+    kv = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    rows, blocks = 16, 512
+    seq_tokens = 1 << 20
+    blk = torch.randint(0, seq_tokens // 4, (rows, blocks), generator=gen, device="cuda")
+    seq = (torch.arange(rows, device="cuda") // 4).view(rows, 1)
+    kv_half = 4 << 30
+    for row_bytes, name in ((4096, "block_4KiB"), (1024, "token_row_1KiB"), (256, "head_row_256B")):
+        # byte offset of K (and V) pieces of every selected block of every row
+        base = (seq * (1 << 30) + blk * 4096)  # K half; V half = + 4 GiB
+        base = torch.cat([base.reshape(-1), base.reshape(-1) + kv_half])
+        per_blk = 4096 // row_bytes
+        if row_bytes == 256:
+            # one KV head's 256-byte piece of each of the block's 4 tokens
+            idx = (base.view(-1, 1) + torch.arange(4, device="cuda").view(1, 4) * 1024) // 256
+        else:
+            idx = (base.view(-1, 1) + torch.arange(per_blk, device="cuda").view(1, per_blk)
+                   * row_bytes) // row_bytes
+        idx = idx.reshape(-1).contiguous()
+        nbytes = idx.numel() * row_bytes
+        us = run(lambda: Q.ceil_gather(kv, idx, row_bytes, 2048, sink))
+        out[f"gather_{name}"] = {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+    del kv
+    torch.cuda.empty_cache()
+    out["note"] = ("kernel durations from dispatch-carried HIP events, median of "
+                   f"{reps}, each after a 1 GiB flush; head_row_256B reads one KV head's "
+                   "piece of each token (a quarter of the bytes of the others)")
+    return out
+
+
+# --------------------------------------------------------------------- CPU oracle
+
+def host_cores():
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return aff, max(1, min(16, aff)), model
+
+
+def cpu_baseline(args, d, w3, np):
+    """The oracle as it stands, on bounded samples of the decode step and the
+    prefill step, timed per stage on the host cores."""
     import threadpoolctl
 
     import oracle as O
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(16, cores))
+    aff, threads, model = host_cores()
+    log(f"[bench] cpu baseline: oracle on {threads} threads ({aff} CPUs in affinity)")
     w = d["w"]
     Nq = w.n_query
-    log(f"[bench] cpu baseline: oracle decode step, {cores} BLAS threads")
-    with threadpoolctl.threadpool_limits(cores):
-        # compressed-key cache of the previous step, as the GPU had it (untimed)
+    stages = ("compress", "score", "select", "expand", "attend")
+    res = {}
+    with threadpoolctl.threadpool_limits(threads):
+        # ---- decode: every query of the batch, repeated until the budget is spent
         caches = {}
-        for b in range(w.batch):
+        for b in range(w.batch):  # the cache of the previous step, as the GPU had it (untimed)
             prev = int(w.lens[b]) - Nq
             caches[b] = O.bf16_bits_to_f64(O.compress_keys(w.k_idx[b], prev))
-        done = 0
-        reps = 0
-        match = True
+        tm = dict.fromkeys(stages, 0.0)
+        done, reps, match = 0, 0, True
         t0 = time.perf_counter()
         while True:
             for b in range(w.batch):
                 length = int(w.lens[b])
                 prev = length - Nq
-                new = O.bf16_bits_to_f64(O.compress_keys(w.k_idx[b], length, first_block=prev // 4))
+                c0 = time.perf_counter()
+                new = O.bf16_bits_to_f64(O.compress_keys(w.k_idx[b], length,
+                                                         first_block=prev // 4))
                 kc = np.concatenate([caches[b][: prev // 4], new])
+                tm["compress"] += time.perf_counter() - c0
                 for i in range(Nq):
                     t = prev + i
+                    c0 = time.perf_counter()
                     s = O.block_scores(O.bf16_bits_to_f64(w.q_idx[b, i]), kc[: t // 4])
+                    c1 = time.perf_counter()
                     sel = O.select_blocks(s)
+                    c2 = time.perf_counter()
                     tok = O.expand_tokens(sel, t)
+                    c3 = time.perf_counter()
                     O.attend(O.bf16_bits_to_f64(w.q[b, i]), O.bf16_bits_to_f64(w.k[b, tok]),
                              O.bf16_bits_to_f64(w.v[b, tok]), w.scale)
+                    c4 = time.perf_counter()
+                    tm["score"] += c1 - c0
+                    tm["select"] += c2 - c1
+                    tm["expand"] += c3 - c2
+                    tm["attend"] += c4 - c3
                     done += 1
                     if reps == 0:
                         g = d["sel"][b, i, : d["n_sel"][b, i]]
                         match = match and np.array_equal(g, sel)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or el > 30:
+            if el >= args.cpu_seconds:
                 break
-    return {"value": done / el, "unit": "q-tok/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{reps} pass(es) over the 16 decode queries of the 1M-context batch: "
-                       "incremental compression of the new block, scoring of every earlier "
-                       "block, top-512, expansion and float64 attention; compressed-key cache "
-                       "prepared untimed"),
-            "seconds": el, "selections_match_gpu": bool(match)}
+        res.update({"value": done / el, "unit": "q-tok/s", "cores": threads, "kind": "oracle",
+                    "sample": (f"{reps} pass(es) over the 16 decode queries of the 1M-context "
+                               "batch: incremental compression of the new block, scoring of "
+                               "every earlier block, top-512, expansion and float64 attention; "
+                               "compressed-key cache of the earlier tokens prepared untimed"),
+                    "seconds": el, "selections_match_gpu": bool(match),
+                    "stage_seconds": tm, "affinity_cpus": aff, "cpu_model": model})
+        # ---- prefill: queries of the 1M chunk in order until the budget is spent
+        if w3 is not None:
+            length = int(w3.lens[0])
+            Nq3 = w3.n_query
+            prev = length - Nq3
+            kc_prev = O.bf16_bits_to_f64(O.compress_keys(w3.k_idx[0], prev))  # untimed
+            tm3 = dict.fromkeys(stages, 0.0)
+            t0 = time.perf_counter()
+            new = O.bf16_bits_to_f64(O.compress_keys(w3.k_idx[0], length,
+                                                     first_block=prev // 4))
+            kc = np.concatenate([kc_prev[: prev // 4], new])
+            tm3["compress"] = time.perf_counter() - t0
+            done = 0
+            while done < Nq3:
+                t = prev + done
+                c0 = time.perf_counter()
+                s = O.block_scores(O.bf16_bits_to_f64(w3.q_idx[0, done]), kc[: t // 4])
+                c1 = time.perf_counter()
+                sel = O.select_blocks(s)
+                c2 = time.perf_counter()
+                tok = O.expand_tokens(sel, t)
+                c3 = time.perf_counter()
+                O.attend(O.bf16_bits_to_f64(w3.q[0, done]), O.bf16_bits_to_f64(w3.k[0, tok]),
+                         O.bf16_bits_to_f64(w3.v[0, tok]), w3.scale)
+                c4 = time.perf_counter()
+                tm3["score"] += c1 - c0
+                tm3["select"] += c2 - c1
+                tm3["expand"] += c3 - c2
+                tm3["attend"] += c4 - c3
+                done += 1
+                if time.perf_counter() - t0 >= args.cpu_seconds:
+                    break
+            el = time.perf_counter() - t0
+            # the chunk's compression is paid once per 16,384 queries: scale it
+            per_query = (el - tm3["compress"]) / done + tm3["compress"] / Nq3
+            res["prefill"] = {"value": 1.0 / per_query, "unit": "q-tok/s", "queries": done,
+                              "seconds": el, "stage_seconds": tm3,
+                              "sample": (f"the first {done} of the 16,384 queries of the "
+                                         "1M-context last-chunk prefill, after compressing the "
+                                         "chunk's 4,096 new blocks (its cost spread over the "
+                                         "whole chunk)")}
+    return res
 
 
 # --------------------------------------------------------------------- main
 
-def other_configs(Q, W, torch, np, flush):
-    """Steady-state forward of the smaller workloads: the compressed-key cache
-    holds the blocks before the call's queries, as in the headline legs."""
-    for cfg in (0, 1, 2):
-        w = W.make(cfg)
-        B, L, Nq = w.batch, w.max_len, w.n_query
-        shp = Q.shape(B, L, Nq, w.q_heads, w.kv_heads)
-        dev = {n: to_dev(getattr(w, n), torch, np) for n in ("q_idx", "k_idx", "q", "k", "v")}
-        lens = to_dev(w.lens, torch, np)
-        prev = to_dev((w.lens - Nq).astype(np.int32), torch, np)
-        first = to_dev(((w.lens - Nq) // 4).astype(np.int32), torch, np)
-        k_cmp = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
-        Q.compress_keys(shp, dev["k_idx"], prev, k_cmp)
-        out = torch.empty((B, Nq, w.q_heads, 128), dtype=torch.bfloat16, device="cuda")
-        sel = torch.empty((B, Nq, 512), dtype=torch.int32, device="cuda")
-        n_sel = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
-        ws = Q.workspace(shp, Q.OP_FORWARD)
-
-        def step():
-            Q.forward(shp, dev["q_idx"], dev["k_idx"], k_cmp, dev["q"], dev["k"], dev["v"], lens,
-                      first_block=first, out=out, sel=sel, n_sel=n_sel, ws=ws, want_lse=False)
-
-        for _ in range(3):
-            flush()
-            step()
-        torch.cuda.synchronize()
-        step_ms, kstats, _ = timed_steps(step, 50 if Nq <= 64 else 5, flush, Q, torch)
-        ms = float(np.median(step_ms))
-        idx_flops, kcmp_bytes = 0.0, 0
-        for b in range(B):
-            t = np.arange(int(w.lens[b]) - Nq, int(w.lens[b]), dtype=np.int64)
-            idx_flops += float(np.sum(512.0 * (t // 4)))
-            kcmp_bytes += ((int(w.lens[b]) - 1) // 4) * 128
-        print(json.dumps({"workload": w.name, "value": B * Nq / (ms * 1e-3), "unit": "q-tok/s",
-                          "ms_per_step": ms, "indexer_flops": idx_flops,
-                          "kcmp_bytes": kcmp_bytes, "kernels": kstats}), flush=True)
-
-
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the QSA path here has no multi-GPU leg "
@@ -399,8 +626,8 @@ def main():
     def flush():
         torch.sum(flush_buf, dim=0, out=flush_sink)
 
-    if args.other_configs:
-        other_configs(Q, W, torch, np, flush)
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(Q, torch, flush)}), flush=True)
         return
 
     d = decode_leg(args, Q, W, torch, np, flush)
@@ -408,20 +635,7 @@ def main():
     ms = sum(step_ms) / len(step_ms)
     w = d["w"]
     q_tok = w.batch * w.n_query
-    kstats = d["kstats"]
-    dom = max(kstats.items(), key=lambda kv: kv[1]["avg_us"] * kv[1]["launches_per_step"])
-    dom_name, dom_stat = dom
-    roof = None
-    if dom_name in d["algo"]:
-        bound, step_nbytes, what = d["algo"][dom_name]
-        # the algorithmic bytes are per step; a step may split a kernel over launches
-        nbytes = step_nbytes / max(dom_stat["launches_per_step"], 1.0)
-        ach = nbytes / (dom_stat["avg_us"] * 1e-6) / 1e9
-        roof = {"bound": bound, "kernel": dom_name, "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic(dom_name),
-                "algorithmic_bytes": nbytes, "bytes_are": what}
-    step_bytes = d["kcmp_bytes"] + d["attn_bytes"]
+    step_bytes = d["kcmp_bytes"] + d["attn_bytes"] + d["qidx_bytes"]
     line = {
         "metric": METRIC,
         "value": q_tok / (ms * 1e-3),
@@ -445,8 +659,9 @@ def main():
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
                      "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": roof,
-        "kernels": kstats,
+        "roofline": roofline_of(d["kstats"], d["algo"]),
+        "kernels": d["kstats"],
+        "cold": d["cold"],
     }
     if not args.no_dense:
         log("[bench] dense comparator")
@@ -456,10 +671,17 @@ def main():
     d_light = {k: d[k] for k in ("w", "sel", "n_sel")}
     del d
     torch.cuda.empty_cache()
+    w3 = None
     if not args.no_prefill:
-        line["prefill"] = prefill_leg(args, Q, W, torch, np, flush)
+        line["prefill"], w3 = prefill_leg(args, Q, W, torch, np, flush)
+        torch.cuda.empty_cache()
+    if not args.no_configs:
+        line["configs"] = other_configs(Q, W, torch, np, flush)
+    if not args.no_ceilings:
+        log("[bench] memory ceilings")
+        line["ceilings"] = ceilings(Q, torch, flush)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args, d_light, np)
+        line["cpu_baseline"] = cpu_baseline(args, d_light, w3, np)
     print(json.dumps(line), flush=True)
 
 

@@ -154,10 +154,18 @@ qsa_status qsa_sparse_attend(const qsa_shape* shape, const uint16_t* q,
                              const int32_t* sel, const int32_t* n_sel, uint16_t* out,
                              float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* The whole layer step: compression of blocks [first_block[b], lens[b]/4)
- * into the caller-owned cache k_cmp, scoring and top-k, expansion and sparse
- * attention, all enqueued on one stream.  sel_out / n_sel_out may be NULL;
- * when given they receive the selection.  lse may be NULL. */
+/* The whole sparse-attention module in one call: the measured module is the
+ * indexer together with the sparse core attention (section "Three speed
+ * claims, three different experiments"), whose steps are compression, block
+ * ranking, expansion of the winners and attention over them (section "A
+ * million-token window with a selective view").  Compresses blocks
+ * [first_block[b], lens[b]/4) of k_idx into the caller-owned cache k_cmp
+ * (first_block NULL = every block), then runs qsa_index_topk,
+ * qsa_expand_blocks and qsa_sparse_attend on it, all enqueued on one stream;
+ * outputs as those calls define them.  sel_out / n_sel_out may be NULL (then
+ * the selection stays in the workspace); when given, both must be.  lse may
+ * be NULL.  Blocks of k_cmp before first_block[b] must already hold the
+ * compressed keys, as an earlier call wrote them. */
 qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx,
                        const uint16_t* k_idx, uint16_t* k_cmp, const int32_t* first_block,
                        const uint16_t* q, const uint16_t* k, const uint16_t* v,

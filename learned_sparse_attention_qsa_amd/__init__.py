@@ -46,6 +46,9 @@ EXPORTS = (
     "qsa_profile_attach",
     "qsa_profile_detach",
     "qsa_profile_kernel_name",
+    # include/qsa_ceilings.h: memory-system ceilings for benchmarks
+    "qsa_ceil_stream_read",
+    "qsa_ceil_gather",
 )
 
 
@@ -99,6 +102,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_profile_detach.restype = i32
     lib.qsa_profile_kernel_name.argtypes = [i32]
     lib.qsa_profile_kernel_name.restype = ctypes.c_char_p
+    lib.qsa_ceil_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.qsa_ceil_stream_read.restype = i32
+    lib.qsa_ceil_gather.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp, vp]
+    lib.qsa_ceil_gather.restype = i32
     _lib = lib
     return lib
 
@@ -286,6 +293,31 @@ def dense_gqa_decode(shp: QsaShape, q, k, v, lens, out=None, lse=None, ws=None,
                                              _p(out), _p(lse), _p(ws), nb, _stream(dev))
     _check(st, "qsa_dense_gqa_decode")
     return out, lse
+
+
+def ceil_stream_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor) -> None:
+    """Streaming read of the whole of `buf` (qsa_ceil_stream_read)."""
+    if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda):
+        raise ValueError("buf and sink must be contiguous GPU tensors")
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().qsa_ceil_stream_read(_p(buf), nbytes, workgroups, _p(sink),
+                                               _stream(buf.device)), "qsa_ceil_stream_read")
+
+
+def ceil_gather(base: torch.Tensor, row_index: torch.Tensor, row_bytes: int, workgroups: int,
+                sink: torch.Tensor) -> None:
+    """Random gather of row_bytes-byte pieces row_index[i] of `base`
+    (qsa_ceil_gather); every piece must lie inside `base`."""
+    if not (base.is_cuda and base.is_contiguous() and row_index.is_cuda and sink.is_cuda):
+        raise ValueError("base, row_index and sink must be GPU tensors")
+    if row_index.dtype != torch.int64 or not row_index.is_contiguous():
+        raise ValueError("row_index must be contiguous int64")
+    nbytes = base.numel() * base.element_size()
+    n = row_index.numel()
+    if n and (int(row_index.min()) < 0 or (int(row_index.max()) + 1) * row_bytes > nbytes):
+        raise ValueError("a gathered piece lies outside base")
+    _check(load_library().qsa_ceil_gather(_p(base), _p(row_index), n, row_bytes, workgroups,
+                                          _p(sink), _stream(base.device)), "qsa_ceil_gather")
 
 
 class KernelTimer:

@@ -468,12 +468,6 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   finish(r, col_valid, nullptr, nullptr, po, pl, true);
 }
 
-__global__ void fill_words_kernel(uint32_t* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
 // ------------------------------------------------------------------ merge
 // Grid (Hq, Nq, B), 128 threads (one per output dim).  Combines the n_split
 // partial (o, lse) pairs of one (query, head): o = sum_s e^(lse_s - M) o_s /

@@ -20,13 +20,7 @@ namespace {
 __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restrict__ k_idx,
                                                        const int32_t* __restrict__ lens,
                                                        const int32_t* __restrict__ first_block,
-                                                       uint16_t* __restrict__ k_cmp, int Lmax,
-                                                       ZeroRange z) {
-  {
-    const size_t stride = (size_t)gridDim.x * gridDim.y * blockDim.x;
-    const size_t first = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    for (size_t i = first; i < z.n; i += stride) z.p[i] = 0u;
-  }
+                                                       uint16_t* __restrict__ k_cmp, int Lmax) {
   const int b = blockIdx.y;
   const int len = clampi(lens[b], 0, Lmax);
   const int nb = len >> 2;
@@ -49,8 +43,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restric
 }  // namespace
 
 hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* lens,
-                           const int32_t* first_block, uint16_t* k_cmp, ZeroRange z,
-                           hipStream_t s) {
+                           const int32_t* first_block, uint16_t* k_cmp, hipStream_t s) {
   if (d.B == 0) return hipSuccess;
   // Grid-stride: enough workgroups to keep HBM busy on a full rebuild, few
   // enough that an incremental call (one new block per sequence) is cheap.
@@ -60,7 +53,7 @@ hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* 
   if (wg > cap) wg = cap;
   if (wg < 1) wg = 1;
   QSA_LAUNCH(compress_kernel, dim3((unsigned)wg, (unsigned)d.B), dim3(256), 0, s, k_idx,
-                     lens, first_block, k_cmp, d.Lmax, z);
+                     lens, first_block, k_cmp, d.Lmax);
   return hipGetLastError();
 }
 

@@ -16,15 +16,8 @@ struct Dims {
 };
 
 // ---- compress.hip
-// A word range the same launch clears (the top-k engine's histograms and
-// counters when the whole path runs back to back).
-struct ZeroRange {
-  uint32_t* p;
-  size_t n;
-};
 hipError_t launch_compress(const Dims& d, const uint16_t* k_idx, const int32_t* lens,
-                           const int32_t* first_block, uint16_t* k_cmp, ZeroRange z,
-                           hipStream_t s);
+                           const int32_t* first_block, uint16_t* k_cmp, hipStream_t s);
 
 // ---- expand.hip
 hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
@@ -34,8 +27,6 @@ hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
 enum class TopkPath { kTable, kStream };
 TopkPath choose_topk_path(const Dims& d, uint32_t flags);
 size_t topk_workspace_bytes(const Dims& d, TopkPath path);
-// Words of the workspace that must be zero before the scoring pass.
-void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n);
 // Key compression folded into the scoring pass (qsa_forward): the blocks from
 // first_block[b] (all when null) to floor(lens[b]/4) are compressed from
 // k_idx and written to k_cmp by the pass that scores them.
@@ -55,7 +46,7 @@ hipError_t launch_table_pick(const Dims& d, const int32_t* lens, int32_t* sel, i
                              void* ws, hipStream_t s);
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
                              uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
-                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s,
+                             int32_t* n_sel, void* ws, hipStream_t s,
                              const CompressFuse* fuse = nullptr);
 
 // ---- attend.hip

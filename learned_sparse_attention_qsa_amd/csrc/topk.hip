@@ -1592,14 +1592,6 @@ size_t topk_workspace_bytes(const Dims& d, TopkPath path) {
   return total;
 }
 
-void topk_zero_range(const Dims& d, TopkPath path, void* ws, uint32_t** ptr, size_t* n) {
-  (void)d;
-  (void)path;
-  (void)ws;  // nothing to clear: every word the engines read is written first
-  *ptr = nullptr;
-  *n = 0;
-}
-
 hipError_t launch_table_score(const Dims& d, const uint16_t* q_idx, uint16_t* k_cmp,
                               const int32_t* lens, void* ws, hipStream_t s,
                               const CompressFuse* fuse) {
@@ -1630,13 +1622,12 @@ bool topk_can_fuse_compress(const Dims& d, TopkPath path) {
 
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
                              uint16_t* k_cmp, const int32_t* lens, int32_t* sel,
-                             int32_t* n_sel, void* ws, bool ws_zeroed, hipStream_t s,
+                             int32_t* n_sel, void* ws, hipStream_t s,
                              const CompressFuse* fuse) {
   if (fuse && !topk_can_fuse_compress(d, path)) return hipErrorInvalidValue;
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   const dim3 grid_q((unsigned)d.Nq, (unsigned)d.B);
   if (path == TopkPath::kTable) {
-    (void)ws_zeroed;
     const hipError_t e = launch_table_score(d, q_idx, k_cmp, lens, ws, s, fuse);
     if (e != hipSuccess) return e;
     return launch_table_pick(d, lens, sel, n_sel, ws, s);

@@ -11,5 +11,6 @@ from .qsa_oracle import (  # noqa: F401
     BLOCK, TOPK, IDX_HEADS, IDX_DIM, HEAD_DIM,
     bf16_bits_to_f64, f64_to_bf16_bits,
     compress_keys, block_scores, select_blocks, expand_tokens,
-    attend, query_positions, qsa_query, qsa_forward, dense_decode,
+    attend, query_positions, qsa_forward, dense_decode,
+    block_scores_rows, select_blocks_rows, select_rows,
 )

@@ -178,23 +178,99 @@ def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float):
 
 
 # --------------------------------------------------------------------------
+# The same scoring and selection for many query rows at once
+# --------------------------------------------------------------------------
+
+def block_scores_rows(q_idx: np.ndarray, kc: np.ndarray) -> np.ndarray:
+    """Indexer scores of every compressed block for n queries of one sequence.
+
+    q_idx: float64 [n][4][64]; kc: float64 [m][64].  Returns float64 [n][m]
+    with s[i][j] = sum over heads of max(0, q_idx[i, h] . kc[j]): the score of
+    block_scores, for n rows in one matrix product (the indexer ranks the
+    micro-blocks per query, section "A million-token window with a selective
+    view").  Exact for the small-integer inputs used here.
+    """
+    n = q_idx.shape[0]
+    per_head = (q_idx.reshape(n * IDX_HEADS, -1) @ kc.T).reshape(n, IDX_HEADS, kc.shape[0])
+    return np.maximum(per_head, 0.0).sum(axis=1)
+
+
+def select_blocks_rows(scores: np.ndarray, bt: np.ndarray, k: int = TOPK):
+    """Top-k selection of select_blocks for n rows at once.
+
+    scores: float64 [n][m] (non-negative); bt: int [n], row i's candidates are
+    blocks 0 .. bt[i] - 1 (later columns are ignored).  Returns (sel int64
+    [n][k] ascending, padded with -1; n_sel int64 [n]).  Per row: all
+    candidates when bt <= k; otherwise v is the k-th largest candidate score,
+    every block above v is kept and the rest of the budget goes to the
+    lowest-numbered blocks scoring exactly v.
+    """
+    n, m = scores.shape
+    bt = np.minimum(np.asarray(bt, dtype=np.int64), m)
+    sel = np.full((n, k), -1, dtype=np.int64)
+    n_sel = np.minimum(bt, k)
+    short = bt <= k
+    for i in np.nonzero(short)[0]:
+        sel[i, :bt[i]] = np.arange(bt[i])
+    rows = np.nonzero(~short)[0]
+    if rows.size == 0:
+        return sel, n_sel
+    # blocks at or past a row's own block score -1, below every candidate
+    s = np.where(np.arange(m)[None, :] < bt[rows, None], scores[rows], -1.0)
+    v = np.partition(s, m - k, axis=1)[:, m - k]          # k-th largest per row
+    above = s > v[:, None]
+    equal = s == v[:, None]
+    need = k - above.sum(axis=1)
+    keep = above | (equal & (np.cumsum(equal, axis=1) <= need[:, None]))
+    r_idx, j_idx = np.nonzero(keep)                        # row-major: ascending j
+    sel[rows] = j_idx.reshape(rows.size, k)
+    return sel, n_sel
+
+
+def select_rows(q_idx_bits, k_idx_bits, lens, n_query: int, rows, k: int = TOPK,
+                chunk: int | None = None, threads: int = 1):
+    """Selections of the given (b, i) query rows, computed with the row-batched
+    scorer and selector (chunks of `chunk` rows of one sequence, by default
+    about 2**24 scores per chunk, on `threads` threads).
+    Returns {(b, i): (sel ascending int64, n_sel)}."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    by_seq = {}
+    for b, i in rows:
+        by_seq.setdefault(int(b), []).append(int(i))
+    out = {}
+    for b, idxs in by_seq.items():
+        length = int(lens[b])
+        kc = bf16_bits_to_f64(compress_keys(k_idx_bits[b], length))
+        idxs = sorted(set(idxs))
+        step = chunk or max(8, (1 << 24) // max(1, length // BLOCK))
+        parts = [idxs[c:c + step] for c in range(0, len(idxs), step)]
+
+        def work(part):
+            t = length - n_query + np.asarray(part, dtype=np.int64)
+            q = bf16_bits_to_f64(q_idx_bits[b, part])
+            m = int(t.max()) // BLOCK
+            s = block_scores_rows(q, kc[:m])
+            sel, n_sel = select_blocks_rows(s, t // BLOCK, k)
+            return [((b, i), (sel[r, :n_sel[r]], int(n_sel[r]))) for r, i in enumerate(part)]
+
+        if threads > 1 and len(parts) > 1:
+            with ThreadPoolExecutor(threads) as ex:
+                for res in ex.map(work, parts):
+                    out.update(res)
+        else:
+            for part in parts:
+                out.update(work(part))
+    return out
+
+
+# --------------------------------------------------------------------------
 # Whole path
 # --------------------------------------------------------------------------
 
 def query_positions(length: int, n_query: int) -> np.ndarray:
     """Positions of the n_query query tokens: the last n_query of the sequence."""
     return np.arange(length - n_query, length, dtype=np.int64)
-
-
-def qsa_query(q_idx_i, kc_all, q_i, k_seq, v_seq, t: int, scale: float, k: int = TOPK):
-    """All steps for the query at position t.  Inputs are float64 arrays:
-    q_idx_i [4][64], kc_all [>= t//4][64], q_i [Hq][128], k_seq/v_seq [L][Hkv][128]."""
-    bt = t // BLOCK
-    s = block_scores(q_idx_i, kc_all[:bt])
-    sel = select_blocks(s, k)
-    tok = expand_tokens(sel, t)
-    o, lse = attend(q_i, k_seq[tok], v_seq[tok], scale)
-    return sel, tok, o, lse
 
 
 def qsa_forward(q_idx_bits, k_idx_bits, q_bits, k_bits, v_bits, lens, n_query: int,

@@ -13,15 +13,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_symbols():
-    with open(os.path.join(ROOT, "include", "qsa.h")) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            with open(os.path.join(inc, fn)) as f:
+                names |= set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", f.read()))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = Q.load_library()
     declared = header_symbols()
-    assert len(declared) == 11
+    assert len(declared) == 13
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -121,3 +125,18 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(Q, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         Q.load_library(str(tmp_path / "nope.so"))
+
+
+def test_ceiling_probes_reject_bad_arguments():
+    lib = Q.load_library()
+    sink = FAKE
+    assert lib.qsa_ceil_stream_read(None, 1024, 4, sink, None) == Q.ERR_NULL
+    assert lib.qsa_ceil_stream_read(MISALIGNED, 1024, 4, sink, None) == Q.ERR_ALIGN
+    assert lib.qsa_ceil_stream_read(FAKE, 1000, 4, sink, None) == Q.ERR_ALIGN
+    assert lib.qsa_ceil_stream_read(FAKE, 1024, 0, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_stream_read(FAKE, 0, 4, sink, None) == Q.OK
+    assert lib.qsa_ceil_gather(FAKE, FAKE, 10, 1000, 4, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_gather(FAKE, FAKE, 10, 8, 4, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_gather(FAKE, FAKE, -1, 256, 4, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_gather(FAKE, None, 10, 256, 4, sink, None) == Q.ERR_NULL
+    assert lib.qsa_ceil_gather(FAKE, FAKE, 0, 256, 4, sink, None) == Q.OK

@@ -44,3 +44,57 @@ def test_traffic_record_follows_the_source(tmp_path, monkeypatch):
     src.write_text("kernel v2\n")  # the kernel changed since the counters were taken
     assert bench.measured_traffic("k") is None
 
+
+
+def test_kernel_stats_merge_template_variants_under_the_base_name():
+    recs = [("sparse_attend_kernel<true>", 0.010), ("merge_kernel", 0.002),
+            ("sparse_attend_kernel<true>", 0.012), ("merge_kernel", 0.004)]
+    st = bench.kernel_stats(recs, 2)
+    assert set(st) == {"sparse_attend_kernel", "merge_kernel"}
+    assert st["sparse_attend_kernel"]["avg_us"] == pytest.approx(11.0)
+    assert st["sparse_attend_kernel"]["variants"] == ["sparse_attend_kernel<true>"]
+    assert "variants" not in st["merge_kernel"]
+
+
+def test_roofline_of_recorded_template_names():
+    # attention dominant: the roofline must come out, keyed by the base name
+    recs = [("score_table_kernel", 0.010), ("sparse_attend_kernel<true>", 0.020)]
+    st = bench.kernel_stats(recs, 1)
+    algo = {"score_table_kernel": ("hbm", 80e6, "x"), "sparse_attend_kernel": ("hbm", 100e6, "y")}
+    r = bench.roofline_of(st, algo)
+    assert r["kernel"] == "sparse_attend_kernel"
+    assert r["achieved"] == pytest.approx(100e6 / 20e-6 / 1e9)
+    assert r["frac"] == pytest.approx(r["achieved"] / bench.HBM_PEAK_GBS)
+
+
+def test_prefill_record_emits_attention_and_indexer_fractions():
+    import numpy as np
+
+    class Wl:
+        name, batch, n_query, q_heads, kv_heads = "p", 1, 16384, 32, 4
+        lens = np.array([1 << 20], np.int32)
+
+    st = bench.kernel_stats([("score_stream_kernel", 2.0), ("select_kernel<true>", 0.3),
+                             ("sparse_attend_kernel<true>", 8.0)], 1)
+    rec = bench.prefill_record(Wl, [10.3], st, np)
+    assert rec["indexer_mfma"]["frac"] > 0
+    assert rec["attention_mfma"]["frac"] > 0
+    assert rec["attention_mfma"]["unique_kv_hbm_frac"] > 0
+
+
+def test_decode_algorithmic_bytes_count_the_union_of_gathered_tokens():
+    import numpy as np
+
+    class Wl:
+        batch, n_query, q_heads, kv_heads = 1, 2, 8, 1
+        lens = np.array([4 * 600 + 2], np.int32)   # t = 2400, 2401 share block 600
+
+    sel = np.full((1, 2, 512), -1, np.int32)
+    n_sel = np.array([[512, 512]], np.int32)
+    sel[0, 0] = np.arange(512)
+    sel[0, 1] = np.arange(1, 513)                  # overlaps the first row in 511 blocks
+    kcmp, attn, qidx = bench.decode_bytes(Wl, sel, n_sel, np)
+    assert kcmp == (2401 // 4) * 128
+    union = 4 * 513 + 2                             # blocks 0..512 + tokens 2400, 2401
+    assert attn == union * 1 * 128 * 2 * 2 + 2 * (2 * 8 * 128 * 2)
+    assert qidx == 2 * 4 * 64 * 2

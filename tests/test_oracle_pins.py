@@ -231,6 +231,62 @@ def test_select_invariant_under_key_scaling():
     np.testing.assert_array_equal(O.select_blocks(s1), O.select_blocks(s4))
 
 
+# ---------------------------------------------------------------- row-batched scoring and selection
+
+def test_scores_rows_brute_force_python_ints():
+    rng = np.random.default_rng(15)
+    q = rng.integers(-8, 9, (5, 4, 64))
+    kc = rng.integers(-32, 33, (23, 64))
+    s = O.block_scores_rows(q.astype(float), kc.astype(float))
+    assert s.shape == (5, 23)
+    for i in range(5):
+        for j in range(23):
+            want = 0
+            for h in range(4):
+                want += max(0, sum(int(q[i, h, d]) * int(kc[j, d]) for d in range(64)))
+            assert s[i, j] == want
+
+
+def test_select_rows_vs_full_sort_ragged_candidates():
+    # every row has its own candidate count bt; columns at or past bt are ignored
+    rng = np.random.default_rng(31)
+    for trial in range(200):
+        n = int(rng.integers(1, 12))
+        m = int(rng.integers(1, 400))
+        k = int(rng.integers(1, 50))
+        levels = int(rng.integers(1, 6))
+        s = rng.integers(0, levels, (n, m)).astype(float)
+        bt = rng.integers(0, m + 1, n)
+        bt[0] = m
+        sel, n_sel = O.select_blocks_rows(s, bt, k)
+        for i in range(n):
+            want = brute_topk(s[i, :bt[i]], k)
+            assert n_sel[i] == want.shape[0]
+            np.testing.assert_array_equal(sel[i, :n_sel[i]], want)
+            assert (sel[i, n_sel[i]:] == -1).all()
+
+
+def test_select_rows_k512_matches_per_row_select():
+    rng = np.random.default_rng(32)
+    s = rng.integers(0, 40, (6, 3000)).astype(float)
+    bt = np.array([3000, 2999, 513, 512, 100, 2048])
+    sel, n_sel = O.select_blocks_rows(s, bt, 512)
+    for i in range(6):
+        want = brute_topk(s[i, :bt[i]], 512)
+        np.testing.assert_array_equal(sel[i, :n_sel[i]], want)
+
+
+def test_select_rows_end_to_end_matches_single_query_path():
+    # the batched path through select_rows gives the per-query oracle's selections
+    w = W.make_custom(14, [5000, 3100], 37, 8, 1, parts=("index",))
+    rows = [(b, i) for b in range(2) for i in range(37)]
+    got = O.select_rows(w.q_idx, w.k_idx, w.lens, w.n_query, rows, chunk=16, threads=2)
+    ref = O.qsa_forward(w.q_idx, w.k_idx, None, None, None, w.lens, w.n_query)
+    for r in rows:
+        np.testing.assert_array_equal(got[r][0], ref["sel"][r])
+        assert got[r][1] == ref["sel"][r].shape[0]
+
+
 # ---------------------------------------------------------------- tail / expand
 
 @pytest.mark.parametrize("n", [4093, 4094, 4095, 4096, 1, 2, 3, 4, 5])
