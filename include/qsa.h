@@ -64,7 +64,8 @@ enum {
   QSA_ERR_SHAPE = 3,      /* unsupported or inconsistent shape */
   QSA_ERR_WORKSPACE = 4,  /* workspace missing or smaller than qsa_workspace_bytes */
   QSA_ERR_DEVICE = 5,     /* current device is not gfx950 / no device */
-  QSA_ERR_HIP = 6         /* a HIP runtime call or kernel launch failed */
+  QSA_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
+  QSA_ERR_SCRATCH = 7     /* the shape needs more scratch than qsa_forward_noalloc holds */
 };
 
 #define QSA_IDX_HEADS 4
@@ -171,6 +172,25 @@ qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx,
                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int32_t* lens, uint16_t* out, float* lse, int32_t* sel_out,
                        int32_t* n_sel_out, void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under stream capture,
+ * serving loops or harnesses that forbid allocation): qsa_forward with the
+ * same arguments except the workspace.  Its scratch memory is a device array
+ * of QSA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; shapes whose qsa_workspace_bytes(shape, QSA_OP_FORWARD)
+ * exceeds it are rejected with QSA_ERR_SCRATCH before anything is launched
+ * (the 1M-context batch-4 x 4 decode needs well under it; a 16K-query
+ * prefill chunk does not fit and needs qsa_forward).  The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.  Every
+ * call on one GPU shares that GPU's array, so calls that overlap in time on
+ * one GPU (different streams or threads) race; serialise them.  Results are
+ * those of qsa_forward. */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qsa_status qsa_forward_noalloc(const qsa_shape* shape, const uint16_t* q_idx,
+                               const uint16_t* k_idx, uint16_t* k_cmp,
+                               const int32_t* first_block, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* lens, uint16_t* out, float* lse,
+                               int32_t* sel_out, int32_t* n_sel_out, void* stream);
 
 /* Comparator: dense causal GQA over every position 0..t of each query (the
  * pages' speed baseline is grouped-query attention over the full context,

@@ -28,7 +28,8 @@ TOPK = 512
 HEAD_DIM = 128
 MAX_TOK = TOPK * BLOCK + BLOCK
 
-OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP, ERR_SCRATCH = range(8)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 OP_COMPRESS, OP_INDEX_TOPK, OP_EXPAND, OP_SPARSE_ATTEND, OP_FORWARD, OP_DENSE_DECODE = range(6)
 FLAG_TOPK_TABLE = 1
 FLAG_TOPK_STREAM = 2
@@ -42,6 +43,7 @@ EXPORTS = (
     "qsa_expand_blocks",
     "qsa_sparse_attend",
     "qsa_forward",
+    "qsa_forward_noalloc",
     "qsa_dense_gqa_decode",
     "qsa_profile_attach",
     "qsa_profile_detach",
@@ -94,7 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_sparse_attend.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_dense_gqa_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for name in EXPORTS[2:8]:
+    lib.qsa_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    for name in EXPORTS[2:9]:
         getattr(lib, name).restype = i32
     lib.qsa_profile_attach.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.qsa_profile_attach.restype = i32
@@ -273,6 +276,37 @@ def forward(shp: QsaShape, q_idx, k_idx, k_cmp, q, k, v, lens, first_block=None,
                                     _p(first_block), _p(q), _p(k), _p(v), _p(lens), _p(out),
                                     _p(lse), _p(sel), _p(n_sel), _p(ws), nb, _stream(dev))
     _check(st, "qsa_forward")
+    return out, lse, sel, n_sel
+
+
+def forward_noalloc(shp: QsaShape, q_idx, k_idx, k_cmp, q, k, v, lens, out, first_block=None,
+                    lse=None, sel=None, n_sel=None):
+    """qsa_forward_noalloc: forward() without a workspace; the library's own
+    per-GPU scratch array serves instead.  Outputs are caller-given (nothing
+    is allocated here either).  Returns (out, lse, sel, n_sel)."""
+    B, L, Nq, Hq, Hkv = shp.batch, shp.max_len, shp.n_query, shp.q_heads, shp.kv_heads
+    _need(q_idx, "q_idx", (B, Nq, IDX_HEADS, IDX_DIM), _BF)
+    _need(k_idx, "k_idx", (B, L, IDX_DIM), _BF)
+    _need(k_cmp, "k_cmp", (B, L // BLOCK, IDX_DIM), _BF)
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    _need(k, "k", (B, L, Hkv, HEAD_DIM), _BF)
+    _need(v, "v", (B, L, Hkv, HEAD_DIM), _BF)
+    _need(lens, "lens", (B,), _I32)
+    _need(out, "out", (B, Nq, Hq, HEAD_DIM), _BF)
+    if first_block is not None:
+        _need(first_block, "first_block", (B,), _I32)
+    if lse is not None:
+        _need(lse, "lse", (B, Nq, Hq), (torch.float32,))
+    if (sel is None) != (n_sel is None):
+        raise ValueError("give both sel and n_sel, or neither")
+    if sel is not None:
+        _need(sel, "sel", (B, Nq, TOPK), _I32)
+        _need(n_sel, "n_sel", (B, Nq), _I32)
+    st = load_library().qsa_forward_noalloc(ctypes.byref(shp), _p(q_idx), _p(k_idx), _p(k_cmp),
+                                            _p(first_block), _p(q), _p(k), _p(v), _p(lens),
+                                            _p(out), _p(lse), _p(sel), _p(n_sel),
+                                            _stream(q.device))
+    _check(st, "qsa_forward_noalloc")
     return out, lse, sel, n_sel
 
 

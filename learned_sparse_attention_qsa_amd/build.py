@@ -23,7 +23,8 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-result"]
-SOURCES = ["compress.hip", "expand.hip", "topk.hip", "attend.hip", "ceilings.hip", "api.cpp"]
+SOURCES = ["compress.hip", "expand.hip", "topk.hip", "attend.hip", "ceilings.hip", "noalloc.hip",
+           "api.cpp"]
 # The stream scorer's MFMA results are read by a vector epilogue every tile:
 # the VGPR form of MFMA keeps them out of accumulation registers (no
 # v_accvgpr_read per value).

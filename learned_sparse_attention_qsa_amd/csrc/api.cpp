@@ -219,6 +219,8 @@ const char* qsa_status_string(qsa_status status) {
       return "current device is not an MI355X (gfx950)";
     case QSA_ERR_HIP:
       return "HIP runtime error";
+    case QSA_ERR_SCRATCH:
+      return "shape needs more scratch memory than qsa_forward_noalloc holds";
     default:
       return "unknown status";
   }

@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = Q.load_library()
     declared = header_symbols()
-    assert len(declared) == 13
+    assert len(declared) == 14
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     seen = set()
-    for st in range(7):
+    for st in range(8):
         s = Q.status_string(st)
         assert s and s not in seen
         seen.add(s)
@@ -140,3 +140,17 @@ def test_ceiling_probes_reject_bad_arguments():
     assert lib.qsa_ceil_gather(FAKE, FAKE, -1, 256, 4, sink, None) == Q.ERR_SHAPE
     assert lib.qsa_ceil_gather(FAKE, None, 10, 256, 4, sink, None) == Q.ERR_NULL
     assert lib.qsa_ceil_gather(FAKE, FAKE, 0, 256, 4, sink, None) == Q.OK
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_launch():
+    lib = Q.load_library()
+    big = Q.shape(1, 1 << 20, 16384, 32, 4)   # a 16K-query prefill chunk's workspace
+    assert Q.workspace_bytes(big, Q.OP_FORWARD) > Q.NOALLOC_SCRATCH_BYTES
+    args = [FAKE] * 12 + [None]
+    assert lib.qsa_forward_noalloc(ctypes.byref(big), *args) == Q.ERR_SCRATCH
+    assert lib.qsa_forward_noalloc(None, *args) == Q.ERR_NULL
+    dec = Q.shape(4, 1 << 20, 4, 32, 4)        # the 1M-context decode fits
+    assert 0 < Q.workspace_bytes(dec, Q.OP_FORWARD) <= Q.NOALLOC_SCRATCH_BYTES
+    bad = Q.shape(1, 6, 1, 8, 1)               # max_len not a multiple of 4
+    assert lib.qsa_forward_noalloc(ctypes.byref(bad), *args) == Q.ERR_SHAPE
+    assert Q.status_string(Q.ERR_SCRATCH).startswith("shape needs more scratch")
