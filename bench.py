@@ -69,6 +69,8 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of each oracle sample (decode, prefill)")
+    ap.add_argument("--topk-engine", choices=("auto", "table", "stream", "scan"), default="auto",
+                    help="force the top-k engine of every leg (default: the library's choice)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the memory ceilings and print them")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -242,14 +244,19 @@ def prefill_work(w, np):
     return idx_flops, attn_flops
 
 
+ENGINE_FLAGS = {"auto": 0, "table": 1, "stream": 2, "scan": 4}
+
+
 class Workspace:
     """Device tensors of one workload, with the compressed-key cache holding
     every block before the call's queries (the steady state)."""
 
+    flags = 0  # top-k engine flag of every workspace (bench.py --topk-engine)
+
     def __init__(self, w, Q, torch, np):
         B, L, Nq = w.batch, w.max_len, w.n_query
         self.w = w
-        self.shp = Q.shape(B, L, Nq, w.q_heads, w.kv_heads)
+        self.shp = Q.shape(B, L, Nq, w.q_heads, w.kv_heads, 0.0, Workspace.flags)
         self.dev = {n: to_dev(getattr(w, n), torch, np) for n in ("q_idx", "k_idx", "q", "k", "v")}
         self.lens = to_dev(w.lens, torch, np)
         prev = to_dev((w.lens - Nq).astype(np.int32), torch, np)
@@ -615,6 +622,7 @@ def main(argv=None):
         print("copied 1 GiB three times", flush=True)
         return
     Q.load_library()
+    Workspace.flags = ENGINE_FLAGS[args.topk_engine]
     # 1 GiB, four times the infinity cache.  The flush READS it: that evicts the
     # step's inputs from the infinity cache and the L2s and leaves only clean
     # lines behind.  (Writing it would leave ~0.25 GiB of dirty lines whose

@@ -79,6 +79,8 @@ enum {
  * results; they differ in speed and workspace.  0 = automatic. */
 #define QSA_FLAG_TOPK_TABLE 1u  /* score table + global histogram threshold */
 #define QSA_FLAG_TOPK_STREAM 2u /* streaming per-query threshold, no score table */
+#define QSA_FLAG_TOPK_SCAN 4u   /* sampled per-row bound, candidate segments per slice
+                                   (shapes it cannot take fall back to STREAM) */
 
 typedef struct {
   int32_t batch;     /* B >= 0 */
@@ -87,7 +89,7 @@ typedef struct {
   int32_t q_heads;   /* Hq: core query heads, >= 1 */
   int32_t kv_heads;  /* Hkv: core KV heads, >= 1, divides Hq, Hq/Hkv <= 64 */
   float scale;       /* softmax scale; <= 0 selects 1/sqrt(128) */
-  uint32_t flags;    /* QSA_FLAG_* ; 0 = automatic */
+  uint32_t flags;    /* at most one QSA_FLAG_TOPK_* ; 0 = automatic */
 } qsa_shape;
 
 /* Workspace query.  op is one of QSA_OP_*.  Returns the number of bytes the

@@ -33,6 +33,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 OP_COMPRESS, OP_INDEX_TOPK, OP_EXPAND, OP_SPARSE_ATTEND, OP_FORWARD, OP_DENSE_DECODE = range(6)
 FLAG_TOPK_TABLE = 1
 FLAG_TOPK_STREAM = 2
+FLAG_TOPK_SCAN = 4
 
 # Every symbol include/qsa.h declares.
 EXPORTS = (

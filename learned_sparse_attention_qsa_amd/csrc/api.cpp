@@ -64,7 +64,7 @@ qsa_status check_shape(const qsa_shape* s, Dims* d) {
   if (s->q_heads < 1 || s->kv_heads < 1 || (s->q_heads % s->kv_heads) != 0) return QSA_ERR_SHAPE;
   if (s->q_heads / s->kv_heads > 64) return QSA_ERR_SHAPE;
   if (s->batch > 65535 || s->n_query > (1 << 24) || s->q_heads > 65535) return QSA_ERR_SHAPE;
-  if ((s->flags & ~3u) != 0 || s->flags == 3u) return QSA_ERR_SHAPE;
+  if ((s->flags & ~7u) != 0 || (s->flags & (s->flags - 1u)) != 0) return QSA_ERR_SHAPE;
   d->B = s->batch;
   d->Lmax = s->max_len;
   d->Nq = s->n_query;

@@ -24,7 +24,7 @@ hipError_t launch_expand(const Dims& d, const int32_t* lens, const int32_t* sel,
                          const int32_t* n_sel, int32_t* tok, int32_t* n_tok, hipStream_t s);
 
 // ---- topk.hip
-enum class TopkPath { kTable, kStream };
+enum class TopkPath { kTable, kStream, kScan };
 TopkPath choose_topk_path(const Dims& d, uint32_t flags);
 size_t topk_workspace_bytes(const Dims& d, TopkPath path);
 // Key compression folded into the scoring pass (qsa_forward): the blocks from

@@ -67,6 +67,23 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Histogram increment of bin d for every lane with `active`: the lanes that
+// share the first active lane's bin add their count with one LDS atomic, the
+// others one each.  Keys that agree on a digit (the leading digits of similar
+// scores) then cost one atomic per wavefront instead of 64 on one address,
+// and diverse digits cost no more than plain atomics.  Every lane of the
+// wavefront must reach the call (active may differ per lane).
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, uint32_t d, bool active) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int leader = __builtin_amdgcn_readfirstlane(__ffsll((long long)act) - 1);
+  const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+  const bool same = active && d == dl;
+  const uint64_t m = __ballot(same);
+  if (lane_id() == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(m));
+  if (active && !same) atomicAdd(&hist[d], 1u);
+}
+
 // One wavefront: given a 256-bin histogram h (bin = digit) and a rank k >= 1
 // counted from the largest digit, find the digit holding the k-th largest
 // element and the number of elements in strictly larger digits.  The caller
@@ -119,9 +136,10 @@ __device__ uint64_t block_kth_largest(const uint64_t* keys, int n, uint32_t k, u
   for (int shift = 56; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x) {
-      const uint64_t key = keys[i];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+    for (int i0 = 0; i0 < n; i0 += blockDim.x) {
+      const int i = i0 + tid;
+      const uint64_t key = i < n ? keys[i] : 0ull;
+      hist_add_wave(hist, (uint32_t)(key >> shift) & 255u, i < n && (key & pmask) == prefix);
     }
     __syncthreads();
     if (tid < 64) {
@@ -140,11 +158,20 @@ __device__ uint64_t block_kth_largest(const uint64_t* keys, int n, uint32_t k, u
     pmask |= 0xffull << shift;
     if (bcast[2] == k && shift > 0) {
       // every key with this prefix is among the k largest: the k-th is the
-      // smallest of them
+      // smallest of them (reduced per wavefront, then one atomic each)
+      uint64_t m = ~0ull;
       for (int i = tid; i < n; i += blockDim.x) {
         const uint64_t key = keys[i];
-        if ((key & pmask) == prefix) atomicMin(mn, key);
+        if ((key & pmask) == prefix) m = key < m ? key : m;
       }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)m, off);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        m = o < m ? o : m;
+      }
+      if ((tid & 63) == 0 && m != ~0ull) atomicMin(mn, m);
       __syncthreads();
       return *mn;
     }
@@ -313,10 +340,12 @@ __device__ void select_whole_row(const uint32_t* trow, const uint16_t* qrow, con
     }
     __syncthreads();
     uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int j = tid; j < bt; j += blockDim.x) {
-      const uint32_t sb = score_of(j);
-      if ((sb & pmask) == prefix) {
-        atomicAdd(&hist[(sb >> shift) & 255u], 1u);
+    for (int j0 = 0; j0 < bt; j0 += blockDim.x) {
+      const int j = j0 + tid;
+      const uint32_t sb = j < bt ? score_of(j) : 0u;
+      const bool in = j < bt && (sb & pmask) == prefix;
+      hist_add_wave(hist, (sb >> shift) & 255u, in);
+      if (in) {
         mn = min(mn, sb);
         mx = max(mx, sb);
       }
@@ -1538,16 +1567,636 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   }
 }
 
+// ------------------------------------------------------------------ SCAN
+// Scan engine (decode-shaped calls: a few queries per sequence over a long
+// context).  One pass over the compressed keys keeps only the blocks that can
+// be in a row's top 512, and a per-row select finishes exactly; no score
+// table is written.
+//
+// scan_filter_kernel: grid (n_slices, ceil(Nq/4), B), 512 threads.  A
+// workgroup holds the 4 queries x 4 heads of one query group as the MFMA A
+// operand (16x16x32: the lane (r, kc) receives block r of a 16-block tile
+// for query kc, all four heads) and handles one slice of the sequence's
+// blocks:
+//  1. at once, before lens or first_block are known, it requests the first
+//     two batches of its slice's tiles and the 1,024 sample blocks (every
+//     (Lmax/4/1,024)-th block: the same for every workgroup of the
+//     sequence), so the memory system is busy from the start; once lens and
+//     first_block arrive, blocks past the query group's own blocks are
+//     masked and blocks not yet in the cache (j >= first_block, k_idx given)
+//     are compressed in registers from k_idx instead (and written to the
+//     cache by the lanes that scan them);
+//  2. each query's bound tau is the lower edge of the bin (64 bins per
+//     octave of the score) holding its 12th best valid sample score (samples
+//     below the group's first query's own block): every workgroup of a row
+//     derives the same tau;
+//  3. it streams the slice (wavefront w takes the 16-block tiles w, w + 8,
+//     ..., four tiles per batch with the next batch's loads in flight) and
+//     appends every block scoring >= tau to the row's LDS list, then writes
+//     the list as the row's segment for this slice, with its length (which
+//     may exceed the segment's capacity: the select sees that).
+// Rows whose group's first query has fewer than 2,048 candidate blocks, or
+// fewer than 12 valid samples, keep every block (tau = 0).
+//
+// Why the result is exact.  Every candidate scores >= tau.  If the row's
+// candidates number at least 512 (and no segment overflowed), at least 512
+// blocks score >= tau, so the row's 512th best score is >= tau and every
+// block of its top 512 is a candidate.  Otherwise the select takes the exact
+// whole-row path.  With 1,024 samples spread over n blocks, the bound lies
+// above the 512th best block only if 12 samples fall among the top 512
+// (expected 1,024 x 512 / n: 2 at n = 262,144), about 2e-6 per row for
+// independent scores; the candidates then number about 12 n / 1,024 (3,072
+// at n = 262,144) plus the blocks in the bound's bin.
+constexpr int kScanWaves = 8;
+constexpr int kScanThreads = 64 * kScanWaves;
+constexpr int kScanSegCap = 512;       // candidates a row keeps per slice
+constexpr int kScanSampleN = 1024;     // sample blocks per sequence
+constexpr int kScanSampleRank = 12;    // tau: the bin of the 12th best sample score
+constexpr int kScanSampleMin = 2048;   // fewer candidate blocks: keep every block
+constexpr int kScanSampleShift = 17;   // sample bins: score bits >> 17 (64 per octave)
+constexpr int kScanU = 4;              // 16-block tiles per wavefront batch
+constexpr int kScanCandCap = 8192;     // candidates a select workgroup holds in LDS
+constexpr int kScanMaxSlices = 2048;   // slices a select workgroup can walk
+constexpr int kScanMaxSliceBlocks = 8192;
+constexpr int kScanBitmapBlocks = 262144;  // rows up to this many blocks rank by bitmaps
+
+// One wavefront: the lower edge (as float bits) of the bin, 64 per octave,
+// holding the k-th largest of the 16 values each lane holds (non-negative
+// float bits), over the 256 bins below and including the largest value's;
+// 0 when fewer than k values lie in those bins.  h: this wavefront's
+// 256-word LDS histogram.
+__device__ uint32_t wave_kth_bin_edge(const uint32_t (&v)[16], uint32_t k, uint32_t* h) {
+  const int lane = lane_id();
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) mx = max(mx, v[e]);
+  const int top = (int)(wave_max_u32(mx) >> kScanSampleShift);
+  const int base = max(0, top - 255);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[lane + 64 * i] = 0u;
+  wave_sync_lds();
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int bin = (int)(v[e] >> kScanSampleShift) - base;
+    if (bin >= 0) atomicAdd(&h[bin], 1u);
+  }
+  wave_sync_lds();
+  const uint32_t c0 = h[4 * lane], c1 = h[4 * lane + 1], c2 = h[4 * lane + 2], c3 = h[4 * lane + 3];
+  uint32_t tot = c0 + c1 + c2 + c3;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += (uint32_t)__shfl_xor((int)tot, off);
+  if (tot < k) return 0u;
+  int bin;
+  uint32_t sfx;
+  wave_suffix_bin4(c0, c1, c2, c3, k, bin, sfx);
+  return (uint32_t)(base + bin) << kScanSampleShift;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_filter_kernel(
+    const uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_cmp,
+    const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ first_block, uint64_t* __restrict__ seg,
+    uint32_t* __restrict__ seg_cnt, int Lmax, int Nq, int slice_blocks, int n_slices) {
+  __shared__ uint64_t s_seg[4][kScanSegCap];
+  __shared__ uint32_t s_samp[4][kScanSampleN];
+  __shared__ uint32_t s_hist[4][256];
+  __shared__ uint32_t s_cnt[4];
+  __shared__ uint32_t s_tau[4];
+  const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, kc = lane >> 4;
+  const int nbp = Lmax >> 2;
+  const int j_begin = slice * slice_blocks;
+  const int j_cap = min(j_begin + slice_blocks, nbp);  // the slice, as far as the cache goes
+  const int samp_stride = max(1, nbp / kScanSampleN);
+  const uint4* src = reinterpret_cast<const uint4*>(k_idx + (size_t)b * Lmax * kIdxDim);
+  uint4* kb = reinterpret_cast<uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
+
+  // 1. requests that need neither lens nor first_block: the query group's
+  // fragments and the lane's sample blocks first (they are needed first and
+  // the waits count loads in order), then the slice's first two batches
+  // (tiles w + 8 (4 bi + u), lane (r, kc): dims 8 kc .. and 32 + 8 kc .. of
+  // block r).  Loads are unconditional, from addresses clamped into the
+  // cache: a block past the range reads some other block, and its score is
+  // masked where it is used (each MFMA output column depends on its own block
+  // only).  (Conditional loads would make the compiler wait for every load in
+  // flight.)
+  // (A rows of queries past the batch repeat the last query; their lanes'
+  // results are never kept)
+  const uint4* qp = reinterpret_cast<const uint4*>(
+      q_idx + (((size_t)b * Nq + min(q0 + (r >> 2), Nq - 1)) * kIdxHeads + (r & 3)) * kIdxDim);
+  const bf16x8 a0 = as_bf16x8(qp[kc]), a1 = as_bf16x8(qp[4 + kc]);
+  constexpr int kSampT = kScanSampleN / (16 * kScanWaves);  // sample tiles per wavefront
+  uint4 sA[kSampT][2];
+#pragma unroll
+  for (int tt = 0; tt < kSampT; ++tt) {
+    const int j = min((wave * (kScanSampleN / kScanWaves) + tt * 16 + r) * samp_stride, nbp - 1);
+    sA[tt][0] = kb[(size_t)j * 8 + kc];
+    sA[tt][1] = kb[(size_t)j * 8 + 4 + kc];
+  }
+  uint4 bA[kScanU][2], bB[kScanU][2];
+  auto load = [&](uint4 (&bv)[kScanU][2], int bi) {
+#pragma unroll
+    for (int u = 0; u < kScanU; ++u) {
+      const int j = min(j_begin + (wave + kScanWaves * (kScanU * bi + u)) * 16 + r, nbp - 1);
+      bv[u][0] = kb[(size_t)j * 8 + kc];
+      bv[u][1] = kb[(size_t)j * 8 + 4 + kc];
+    }
+  };
+  load(bA, 0);
+  load(bB, 1);
+  if (tid < 4) s_cnt[tid] = 0u;
+
+  // the group's queries ascend in position: its first and last valid one
+  const int len = clampi(lens[b], 0, Lmax);
+  const int nb = len >> 2;
+  const int t_first = query_t(len, Nq, q0);
+  const int t_last = query_t(len, Nq, min(q0 + 3, Nq - 1));
+  const int bt_min = t_first >= 0 ? (t_first >> 2) : 0;
+  const int bt_g = t_last >= 0 ? (t_last >> 2) : 0;
+  const int qo = q0 + kc;  // this lane's query
+  const int t_o = query_t(len, Nq, qo);
+  const int bt_o = (qo < Nq && t_o >= 0) ? (t_o >> 2) : 0;
+  const int j_end = min(j_begin + slice_blocks, bt_g);
+  const bool active = j_begin < j_end;  // (uniform)
+  int fb = nb;  // blocks from fb on are not in the cache yet
+  if (k_idx != nullptr) fb = first_block ? clampi(first_block[b], 0, nb) : 0;
+  // blocks not yet in the cache, compressed here: in the prefetched batches
+  // (then written to the cache) and among the samples
+  auto fix_new = [&](uint4 (&bv)[kScanU][2], int bi) {
+#pragma unroll
+    for (int u = 0; u < kScanU; ++u) {
+      const int j = j_begin + (wave + kScanWaves * (kScanU * bi + u)) * 16 + r;
+      if (j >= fb && j < j_end) {
+        bv[u][0] = compress_chunk(src + (size_t)j * 32 + kc);
+        bv[u][1] = compress_chunk(src + (size_t)j * 32 + 4 + kc);
+        kb[(size_t)j * 8 + kc] = bv[u][0];
+        kb[(size_t)j * 8 + 4 + kc] = bv[u][1];
+      }
+    }
+  };
+  if (fb < j_end && active) {  // (uniform)
+    fix_new(bA, 0);
+    fix_new(bB, 1);
+  }
+  // the slice's new blocks the scan does not cover
+  if (k_idx != nullptr) {
+    const long long c0 = (long long)max(fb, active ? j_end : j_begin) * 8;
+    const long long c1 = (long long)min(nb, j_cap) * 8;
+    for (long long g = c0 + tid; g < c1; g += kScanThreads)
+      kb[g] = compress_chunk(src + (g >> 3) * 32 + (g & 7));
+  }
+
+  // 2. the bound tau of each query of the group
+  const bool sampled = active && bt_min >= kScanSampleMin;  // (uniform)
+  if (sampled) {
+#pragma unroll
+    for (int tt = 0; tt < kSampT; ++tt) {
+      const int i = wave * (kScanSampleN / kScanWaves) + tt * 16 + r;
+      const int j = i * samp_stride;
+      uint4 b0 = sA[tt][0], b1 = sA[tt][1];
+      if (j >= fb && j < bt_min) {  // not in the cache yet: compress it here
+        b0 = compress_chunk(src + (size_t)j * 32 + kc);
+        b1 = compress_chunk(src + (size_t)j * 32 + 4 + kc);
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(a0, as_bf16x8(b0), acc);
+      acc = mfma16(a1, as_bf16x8(b1), acc);
+      // samples at or past the group's first own block count as 0
+      s_samp[kc][i] = j < bt_min ? relu_sum_bits(acc[0], acc[1], acc[2], acc[3]) : 0u;
+    }
+  }
+  __syncthreads();  // samples in LDS
+  if (wave < 4) {
+    uint32_t tau = 0u;  // keep every block
+    if (sampled) {
+      uint32_t v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = s_samp[wave][lane * 16 + e];
+      tau = wave_kth_bin_edge(v, kScanSampleRank, s_hist[wave]);
+    }
+    if (lane == 0) s_tau[wave] = tau;
+  }
+  __syncthreads();
+
+  // 3. the scan of [j_begin, j_end)
+  if (active) {
+    const uint32_t tau_o = s_tau[kc];
+    const int lim = min(bt_o, j_end);  // this lane's query's candidates in the slice
+    const int ntiles = (j_end - j_begin + 15) >> 4;
+    constexpr int kStep = kScanWaves * kScanU;  // tiles per batch of the workgroup
+    const int nbatch =
+        __builtin_amdgcn_readfirstlane(ntiles > wave ? (ntiles - wave + kStep - 1) / kStep : 0);
+    auto load_fix = [&](uint4 (&bv)[kScanU][2], int bi) {
+      load(bv, bi);
+      if (fb < j_end) fix_new(bv, bi);  // (uniform)
+    };
+    auto proc = [&](const uint4 (&bv)[kScanU][2], int bi) {
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(a0, as_bf16x8(bv[u][0]), acc);
+        acc = mfma16(a1, as_bf16x8(bv[u][1]), acc);
+        const int j = j_begin + (wave + kScanWaves * (kScanU * bi + u)) * 16 + r;
+        const uint32_t bits = relu_sum_bits(acc[0], acc[1], acc[2], acc[3]);
+        const bool pass = j < lim && bits >= tau_o;
+        const uint64_t m = __ballot(pass);
+        if (m == 0) continue;
+        const uint32_t mq = (uint32_t)(m >> (16 * kc)) & 0xffffu;
+        uint32_t base = 0;
+        if (r == 0 && mq != 0u) base = atomicAdd(&s_cnt[kc], (uint32_t)__popc(mq));
+        base = (uint32_t)__shfl((int)base, lane & 48);
+        const uint32_t pos = base + (uint32_t)__popc(mq & ((1u << r) - 1u));
+        if (pass && pos < (uint32_t)kScanSegCap) s_seg[kc][pos] = make_key(bits, (uint32_t)j);
+      }
+    };
+    for (int bi = 0; bi < nbatch; bi += 2) {
+      proc(bA, bi);
+      if (bi + 2 < nbatch) load_fix(bA, bi + 2);
+      if (bi + 1 >= nbatch) break;
+      proc(bB, bi + 1);
+      if (bi + 3 < nbatch) load_fix(bB, bi + 3);
+    }
+  }
+  __syncthreads();
+  // 4. the group's segments of this slice (an empty one when nothing was scanned)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q0 + q >= Nq) break;
+    const size_t sidx = ((size_t)b * Nq + q0 + q) * n_slices + slice;
+    const uint32_t n = s_cnt[q];
+    if (tid == 0) seg_cnt[sidx] = n;
+    const uint32_t nk = min(n, (uint32_t)kScanSegCap);
+    for (uint32_t i = tid; i < nk; i += kScanThreads) seg[sidx * kScanSegCap + i] = s_seg[q][i];
+  }
+}
+
+// Block-wide exclusive prefix sum of one value per thread (512 threads) and
+// the total; s_red: kScanWaves words.  Ends past a barrier.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* s_red, uint32_t& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(v);
+  __syncthreads();  // s_red free
+  if (lane == 63) s_red[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kScanWaves; ++w) {
+    const uint32_t x = s_red[w];
+    before += w < wave ? x : 0u;
+    all += x;
+  }
+  total = all;
+  return before + incl - v;
+}
+
+// Per row (grid (Nq, B), 512 threads): the row's candidates from its slices'
+// segments into LDS, then
+//  * the cut: a 2,048-bin linear histogram of the candidates' scores over
+//    [lowest, highest] finds the bin holding the 512th best; while that bin
+//    holds several score values it is narrowed by histograms of its score
+//    bits, 11 at a time, until one value v remains (usually at once): the
+//    winners are the scores above v and the lowest-id candidates scoring v;
+//  * the order: winners and ties at v are marked in two bitmaps over the
+//    row's blocks; a prefix popcount over the tie bitmap keeps the first
+//    (lowest-id) ties needed, and one over the merged bitmap writes the ids
+//    in ascending order.  Rows of more than kScanBitmapBlocks blocks rank
+//    each winner by counting the winners below it instead.
+// Rows with too few candidates (tau above the 512th best score), an
+// overflowed segment or more candidates than the LDS list holds take the
+// exact whole-row path.
+__global__ __launch_bounds__(kScanThreads) void scan_select_kernel(
+    const uint64_t* __restrict__ seg, const uint32_t* __restrict__ seg_cnt,
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp,
+    const int32_t* __restrict__ lens, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+    int Lmax, int Nq, int slice_blocks, int n_slices) {
+  __shared__ __align__(16) uint64_t keys[kScanCandCap];
+  // winners, ties; word w at w + w / 16 (so that the 16 consecutive words a
+  // thread owns start in different banks)
+  __shared__ __align__(16) uint32_t bm[2 * (kScanBitmapBlocks / 32) * 17 / 16];
+  __shared__ uint32_t s_pre[kScanMaxSlices + 1];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t s_red[2 * kScanWaves];
+  __shared__ uint32_t bcast[8];
+  __shared__ int32_t outb[kTopK];
+  __shared__ uint32_t outn;
+  __shared__ uint32_t s_bad;
+  __shared__ uint32_t s_mm[4];
+  __shared__ float qf[kIdxHeads * kIdxDim];
+  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = lane_id();
+  const int wave = tid >> 6;
+  const size_t row = (size_t)b * Nq + q;
+  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
+  int32_t* srow = sel + row * kTopK;
+  if (write_trivial(t, srow, n_sel + row)) return;
+  const int bt = t >> 2;
+  const int n_used = min(n_slices, (bt + slice_blocks - 1) / slice_blocks);  // (<= kScanMaxSlices)
+  const uint32_t* cnt = seg_cnt + row * n_slices;
+  const uint64_t* rseg = seg + row * n_slices * (size_t)kScanSegCap;
+  if (tid == 0) {
+    s_bad = 0u;
+    outn = 0u;
+    s_mm[0] = 0xffffffffu;
+    s_mm[1] = 0u;
+    s_mm[2] = 0xffffffffu;
+    s_mm[3] = 0u;
+  }
+  __syncthreads();
+  // exclusive prefix of the segment lengths, 512 at a time
+  uint32_t carry = 0;
+  for (int s0 = 0; s0 < n_used; s0 += kScanThreads) {
+    const int s = s0 + tid;
+    uint32_t c = s < n_used ? cnt[s] : 0u;
+    const bool over = c > (uint32_t)kScanSegCap;
+    if (over) c = 0u;
+    if (__ballot(over) != 0 && lane == 0) s_bad = 1u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_sum(c, s_red, tot);
+    if (s < n_used) s_pre[s] = carry + ex;
+    carry += tot;
+  }
+  const uint32_t total = carry;
+  if (tid == 0) s_pre[n_used] = total;
+  __syncthreads();
+  const bool ok = s_bad == 0u && total >= (uint32_t)kTopK && total <= (uint32_t)kScanCandCap;
+  if (!ok) {
+    const int nbp = Lmax >> 2;
+    select_whole_row<true>(nullptr, q_idx + row * kIdxHeads * kIdxDim,
+                           k_cmp + (size_t)b * nbp * kIdxDim, bt, srow, qf, hist, bcast, s_red);
+    if (tid == 0) n_sel[row] = kTopK;
+    return;
+  }
+  // ---- the candidates into LDS: wavefront w copies segments w, w + 8, ...,
+  // four at a time, the first 128 entries of each with two independent loads
+  // per lane (segments hold about 50 on average), any rest one by one
+  for (int s0 = wave; s0 < n_used; s0 += 4 * kScanWaves) {
+    uint64_t v[4][2];
+    uint32_t n4[4], o4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + kScanWaves * k;
+      n4[k] = s < n_used ? s_pre[s + 1] - s_pre[s] : 0u;
+      o4[k] = s < n_used ? s_pre[s] : 0u;
+      // (unconditional loads inside the row's segment storage; entries past
+      // a segment's length are not kept)
+      const size_t sb = (size_t)min(s, n_used - 1) * kScanSegCap;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) v[k][m] = rseg[sb + lane + 64 * m];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t i = (uint32_t)(lane + 64 * m);
+        if (i < n4[k]) keys[o4[k] + i] = v[k][m];
+      }
+      const int s = s0 + kScanWaves * k;
+      for (uint32_t i = 128 + lane; i < n4[k]; i += 64) keys[o4[k] + i] = rseg[(size_t)s * kScanSegCap + i];
+    }
+  }
+  for (int i = tid; i < kHistBins; i += kScanThreads) hist[i] = 0u;
+  __syncthreads();
+  // the lowest and highest candidate score
+  {
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (uint32_t e = tid; e < total; e += kScanThreads) {
+      const uint32_t sc = (uint32_t)(keys[e] >> 32);
+      lo = min(lo, sc);
+      hi = max(hi, sc);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+      atomicMin(&s_mm[0], lo);
+      atomicMax(&s_mm[1], hi);
+    }
+  }
+  __syncthreads();
+  const uint32_t lo = s_mm[0], hi = s_mm[1];
+  // ---- the cut: the bin of a 2,048-bin linear histogram over [lowest,
+  // highest] that holds the 512th best score
+  const float lo_f = __uint_as_float(lo);
+  const float scale = hi > lo ? 2047.0f / (__uint_as_float(hi) - lo_f) : 0.f;
+  for (uint32_t e = tid; e < total; e += kScanThreads)
+    atomicAdd(&hist[lin_bin((uint32_t)(keys[e] >> 32), lo_f, scale)], 1u);
+  __syncthreads();
+  uint32_t cb, above;
+  {
+    // thread t owns bins 4t .. 4t + 3; suffix counts from the top
+    const uint4 c = reinterpret_cast<const uint4*>(hist)[tid];
+    const uint32_t own = c.x + c.y + c.z + c.w;
+    uint32_t tot;
+    const uint32_t ex = block_excl_sum(own, s_red, tot);
+    const uint32_t cc[4] = {c.x, c.y, c.z, c.w};
+    uint32_t sfx = tot - ex - own;  // bins above this thread's four
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (sfx < (uint32_t)kTopK && sfx + cc[i] >= (uint32_t)kTopK) {
+        bcast[0] = (uint32_t)(4 * tid + i);
+        bcast[1] = sfx;
+      }
+      sfx += cc[i];
+    }
+    __syncthreads();
+    cb = bcast[0];
+    above = bcast[1];
+  }
+  // The cut bin's lowest and highest score; while it holds several values,
+  // narrow it: a histogram of (bits - lowest) >> shift over the candidates
+  // in it (11 bits at a time) finds the sub-bin holding the cut, until one
+  // value remains.  Then v is that value and `need` the candidates scoring
+  // exactly v that are kept.
+  uint32_t need = kTopK - above;  // still to take from the cut bin
+  uint32_t blo = 0u, bhi = 0xffffffffu;  // the cut bin's score range (bits), inclusive
+  bool first = true;
+  for (;;) {
+    uint32_t bmn = 0xffffffffu, bmx = 0u;
+    for (uint32_t e = tid; e < total; e += kScanThreads) {
+      const uint32_t sc = (uint32_t)(keys[e] >> 32);
+      const bool in = first ? lin_bin(sc, lo_f, scale) == cb : (sc >= blo && sc <= bhi);
+      if (in) {
+        bmn = min(bmn, sc);
+        bmx = max(bmx, sc);
+      }
+    }
+    bmn = wave_min_u32(bmn);
+    bmx = wave_max_u32(bmx);
+    if (lane == 0) {
+      atomicMin(&s_mm[2], bmn);
+      atomicMax(&s_mm[3], bmx);
+    }
+    for (int i = tid; i < kHistBins; i += kScanThreads) hist[i] = 0u;
+    __syncthreads();
+    blo = s_mm[2];
+    bhi = s_mm[3];
+    first = false;
+    if (blo == bhi) break;  // (uniform) one value: v = blo
+    const uint32_t span = bhi - blo;
+    const uint32_t shift = pick_shift(span);  // (span >> shift) < 2048
+    for (uint32_t e = tid; e < total; e += kScanThreads) {
+      const uint32_t sc = (uint32_t)(keys[e] >> 32);
+      if (sc >= blo && sc <= bhi) atomicAdd(&hist[(sc - blo) >> shift], 1u);
+    }
+    __syncthreads();
+    {
+      const uint4 c = reinterpret_cast<const uint4*>(hist)[tid];
+      const uint32_t own = c.x + c.y + c.z + c.w;
+      uint32_t tot;
+      const uint32_t ex = block_excl_sum(own, s_red, tot);
+      const uint32_t cc[4] = {c.x, c.y, c.z, c.w};
+      uint32_t sfx = tot - ex - own;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (sfx < need && sfx + cc[i] >= need) {
+          bcast[0] = (uint32_t)(4 * tid + i);
+          bcast[1] = sfx;
+        }
+        sfx += cc[i];
+      }
+      if (tid == 0) {
+        s_mm[2] = 0xffffffffu;
+        s_mm[3] = 0u;
+      }
+      __syncthreads();
+    }
+    const uint32_t sub = bcast[0];
+    need -= bcast[1];  // the sub-bins above the cut's are kept whole
+    // the cut sub-bin's range: [blo + sub << shift, blo + (sub + 1) << shift - 1]
+    const uint32_t nlo = blo + (sub << shift);
+    bhi = min(bhi, nlo + ((1u << shift) - 1u));
+    blo = nlo;
+  }
+  // winners: every score above v; ties: exactly v, of which the `need`
+  // lowest-id ones are kept
+  const uint32_t v = blo;
+  auto is_win = [&](uint64_t key) -> bool { return (uint32_t)(key >> 32) > v; };
+  auto is_tie = [&](uint64_t key) -> bool { return (uint32_t)(key >> 32) == v; };
+  if (bt <= kScanBitmapBlocks) {
+    // ---- bitmaps over the row's blocks: winners (words [0, W)) and ties
+    // (words [W, 2W)); thread t owns words [t cw, t cw + cw) of each
+    const int W = (bt + 31) >> 5;
+    const int cw = (W + kScanThreads - 1) / kScanThreads;  // <= 16
+    auto P = [](int w) { return w + (w >> 4); };           // padded place of word w
+    for (int i = tid; i < P(2 * W); i += kScanThreads) bm[i] = 0u;
+    __syncthreads();
+    for (uint32_t e = tid; e < total; e += kScanThreads) {
+      const uint64_t key = keys[e];
+      const int j = (int)key_block(key);
+      if (is_win(key)) atomicOr(&bm[P(j >> 5)], 1u << (j & 31));
+      else if (is_tie(key)) atomicOr(&bm[P(W + (j >> 5))], 1u << (j & 31));
+    }
+    __syncthreads();
+    const int w0 = tid * cw, n_own = max(0, min(W, w0 + cw) - w0);
+    uint32_t tw[16], ww[16];
+    uint32_t ntie = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool in = i < n_own;
+      tw[i] = in ? bm[P(W + w0 + i)] : 0u;
+      ww[i] = in ? bm[P(w0 + i)] : 0u;
+      ntie += (uint32_t)__popc(tw[i]);
+    }
+    uint32_t tot;
+    uint32_t tie_before = block_excl_sum(ntie, s_red, tot);
+    // keep the first `need` ties (lowest ids) and merge them into the winners
+    uint32_t nwin = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t t2 = tw[i];
+      while (t2 != 0u && tie_before < need) {
+        const uint32_t bit = t2 & (0u - t2);
+        ww[i] |= bit;
+        ++tie_before;
+        t2 ^= bit;
+      }
+      nwin += (uint32_t)__popc(ww[i]);
+    }
+    uint32_t pos = block_excl_sum(nwin, s_red, tot);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t x = ww[i];
+      while (x != 0u) {
+        const int bit = __ffs((int)x) - 1;
+        if (pos < (uint32_t)kTopK) srow[pos] = (int32_t)(32 * (w0 + i) + bit);
+        ++pos;
+        x &= x - 1u;
+      }
+    }
+  } else {
+    // ---- long rows: the winners, then the ties with fewer than `need`
+    // lower-id ties (by counting), each placed by the number of winners below
+    __syncthreads();
+    for (uint32_t e = tid; e < total; e += kScanThreads) {
+      const uint64_t key = keys[e];
+      bool take = is_win(key);
+      if (!take && is_tie(key)) {
+        const uint32_t j = key_block(key);
+        uint32_t below = 0;
+        for (uint32_t i = 0; i < total; ++i) {
+          const uint64_t k2 = keys[i];
+          below += (is_tie(k2) && key_block(k2) < j) ? 1u : 0u;
+        }
+        take = below < need;
+      }
+      if (take) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
+    }
+    __syncthreads();
+    const int32_t my = outb[tid];
+    uint32_t rank = 0;
+    const int4* o4 = reinterpret_cast<const int4*>(outb);
+#pragma unroll 8
+    for (int i = 0; i < kTopK / 4; ++i) {
+      const int4 o = o4[i];
+      rank += (uint32_t)(o.x < my) + (uint32_t)(o.y < my) + (uint32_t)(o.z < my) +
+              (uint32_t)(o.w < my);
+    }
+    srow[rank] = my;
+  }
+  if (tid == 0) n_sel[row] = kTopK;
+}
+static_assert(kScanThreads == kTopK, "the long-row order gives each winner one thread");
+
+
 }  // namespace
 
 // ------------------------------------------------------------------ host side
 
+namespace {
+// Slices of the scan engine: about one workgroup per compute unit over the
+// batch's (sequence, query group) pairs, at most kScanMaxSliceBlocks blocks
+// each (so that a slice's expected candidates stay far below a segment's
+// capacity), a multiple of the 16-block tile.
+struct ScanGeom {
+  int slice_blocks, n_slices;
+};
+ScanGeom scan_geom(const Dims& d) {
+  const long long nbp = d.Lmax / 4;
+  const long long groups = (long long)d.B * ((d.Nq + 3) / 4);
+  const long long want = groups > 0 ? (256 + groups - 1) / groups : 1;
+  long long sb = (nbp + want - 1) / want;
+  if (sb > kScanMaxSliceBlocks) sb = kScanMaxSliceBlocks;
+  sb = (sb + 15) / 16 * 16;
+  if (sb < 16) sb = 16;
+  return {(int)sb, (int)((nbp + sb - 1) / sb)};
+}
+bool scan_fits(const Dims& d) { return d.Nq <= 64 && scan_geom(d).n_slices <= kScanMaxSlices; }
+}  // namespace
+
+// Automatic choice: decode-shaped calls (at most 64 queries per sequence)
+// take the table engine while its score table fits 512 MiB (at a 1M-token
+// context, batch 4 x 4: 70 us per step against 76 us for the scan engine,
+// whose sampled bound costs more latency at the start of its pass than the
+// table's write and read-back), longer contexts the scan engine, whose
+// workspace grows with the slices instead of the context; prefill-shaped
+// calls the stream engine.
 TopkPath choose_topk_path(const Dims& d, uint32_t flags) {
   if (flags & 1u) return TopkPath::kTable;
   if (flags & 2u) return TopkPath::kStream;
+  if (flags & 4u) return scan_fits(d) ? TopkPath::kScan : TopkPath::kStream;
   const double table_bytes = (double)d.B * d.Nq * (d.Lmax / 4) * 4.0;
-  return (d.Nq <= 64 && table_bytes <= 512.0 * 1024 * 1024) ? TopkPath::kTable
-                                                             : TopkPath::kStream;
+  if (d.Nq <= 64 && table_bytes <= 512.0 * 1024 * 1024) return TopkPath::kTable;
+  return scan_fits(d) ? TopkPath::kScan : TopkPath::kStream;
 }
 
 namespace {
@@ -1571,6 +2220,20 @@ TableWs carve_table(const Dims& d, void* ws, size_t* total) {
   if (total) *total = c.off;
   return w;
 }
+struct ScanWs {
+  uint64_t* seg;     // [rows][n_slices][kScanSegCap] candidate keys
+  uint32_t* cnt;     // [rows][n_slices] segment lengths
+};
+ScanWs carve_scan(const Dims& d, void* ws, size_t* total) {
+  Carve c{static_cast<char*>(ws), 0};
+  const size_t rows = (size_t)d.B * d.Nq;
+  const ScanGeom g = scan_geom(d);
+  ScanWs w;
+  w.seg = c.take<uint64_t>(rows * (size_t)g.n_slices * kScanSegCap);
+  w.cnt = c.take<uint32_t>(rows * (size_t)g.n_slices);
+  if (total) *total = c.off;
+  return w;
+}
 StreamWs carve_stream(const Dims& d, void* ws, size_t* total) {
   Carve c{static_cast<char*>(ws), 0};
   const size_t rows = (size_t)d.B * d.Nq;
@@ -1587,6 +2250,8 @@ size_t topk_workspace_bytes(const Dims& d, TopkPath path) {
   size_t total = 0;
   if (path == TopkPath::kTable)
     carve_table(d, nullptr, &total);
+  else if (path == TopkPath::kScan)
+    carve_scan(d, nullptr, &total);
   else
     carve_stream(d, nullptr, &total);
   return total;
@@ -1617,7 +2282,7 @@ hipError_t launch_table_pick(const Dims& d, const int32_t* lens, int32_t* sel, i
 
 bool topk_can_fuse_compress(const Dims& d, TopkPath path) {
   // one scoring workgroup per slice and sequence: each new block is written once
-  return path == TopkPath::kTable && d.Nq <= 4;
+  return (path == TopkPath::kTable || path == TopkPath::kScan) && d.Nq <= 4;
 }
 
 hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx,
@@ -1631,6 +2296,16 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
     const hipError_t e = launch_table_score(d, q_idx, k_cmp, lens, ws, s, fuse);
     if (e != hipSuccess) return e;
     return launch_table_pick(d, lens, sel, n_sel, ws, s);
+  } else if (path == TopkPath::kScan) {
+    ScanWs w = carve_scan(d, ws, nullptr);
+    const ScanGeom g = scan_geom(d);
+    const dim3 grid((unsigned)g.n_slices, (unsigned)((d.Nq + 3) / 4), (unsigned)d.B);
+    QSA_LAUNCH(scan_filter_kernel, grid, dim3(kScanThreads), 0, s, q_idx, k_cmp, lens,
+               fuse ? fuse->k_idx : nullptr, fuse ? fuse->first_block : nullptr, w.seg, w.cnt,
+               d.Lmax, d.Nq, g.slice_blocks, g.n_slices);
+    QSA_LAUNCH(scan_select_kernel, grid_q, dim3(kScanThreads), 0, s, (const uint64_t*)w.seg,
+               (const uint32_t*)w.cnt, q_idx, (const uint16_t*)k_cmp, lens, sel, n_sel, d.Lmax,
+               d.Nq, g.slice_blocks, g.n_slices);
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);

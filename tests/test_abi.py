@@ -44,9 +44,15 @@ def test_workspace_sizes():
     dec = Q.shape(4, 1 << 20, 4, 32, 4)
     assert Q.workspace_bytes(dec, Q.OP_COMPRESS) == 0
     assert Q.workspace_bytes(dec, Q.OP_EXPAND) == 0
-    # the score table of the decode shape: 16 rows x 262,144 blocks x 4 B
+    # the decode shape takes the score table engine: 16 rows x 262,144 blocks x 4 B
     assert Q.workspace_bytes(dec, Q.OP_INDEX_TOPK) >= 16 * 262144 * 4
     assert Q.workspace_bytes(dec, Q.OP_FORWARD) >= Q.workspace_bytes(dec, Q.OP_INDEX_TOPK)
+    scan = Q.shape(4, 1 << 20, 4, 32, 4, flags=Q.FLAG_TOPK_SCAN)
+    # the scan engine: candidate segments of 64 slices x 512 keys per row
+    assert Q.workspace_bytes(scan, Q.OP_INDEX_TOPK) == 16 * 64 * (512 * 8 + 4)
+    # beyond a 512 MiB score table the decode shape takes the scan engine
+    long_dec = Q.shape(4, 1 << 26, 4, 32, 4)   # a 1 GiB table: 2,048 slices of 8,192 blocks
+    assert Q.workspace_bytes(long_dec, Q.OP_INDEX_TOPK) == 16 * 2048 * (512 * 8 + 4)
     pre = Q.shape(1, 1 << 20, 16384, 32, 4)
     # prefill uses the streaming engine: no score table (would be 16 GiB)
     assert Q.workspace_bytes(pre, Q.OP_INDEX_TOPK) < 3 << 30
@@ -66,6 +72,8 @@ BAD_SHAPES = [
     Q.shape(1, 8, 1, 130, 2),        # group of 65 heads
     Q.shape(1, 8, 1, 8, 1, flags=3),  # both engines forced
     Q.shape(1, 8, 1, 8, 1, flags=8),  # unknown flag
+    Q.shape(1, 8, 1, 8, 1, flags=5),  # table and scan engines forced
+    Q.shape(1, 8, 1, 8, 1, flags=6),  # stream and scan engines forced
     Q.shape(1, (1 << 30) + 4, 1, 8, 1),  # beyond 2^30 tokens
 ]
 

@@ -15,7 +15,7 @@ from gpu_util import (check_close, dev_bf16, dev_i32, host_u16, host_f64_from_bf
 
 pytestmark = pytest.mark.gpu
 
-ENGINES = [Q.FLAG_TOPK_TABLE, Q.FLAG_TOPK_STREAM]
+ENGINES = [Q.FLAG_TOPK_TABLE, Q.FLAG_TOPK_STREAM, Q.FLAG_TOPK_SCAN]
 
 
 def say(*a):
@@ -201,14 +201,58 @@ def test_topk_wide_score_range(flags):
     check_topk(w, flags)
 
 
+def scale_blocks(w, b, blocks, f):
+    """Multiply the indexer keys of the given micro-blocks of sequence b by f
+    (small integers stay exact)."""
+    for j in blocks:
+        rows = w.k_idx[b, 4 * j:4 * j + 4].astype(np.uint32) << 16
+        vals = rows.view(np.float32) * np.float32(f)
+        w.k_idx[b, 4 * j:4 * j + 4] = (vals.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_topk_scan_bound_above_the_cut():
+    # 100 outlier blocks, 20 of them spread like the scan engine's samples:
+    # its sampled bound then lies above all but the outliers, fewer than 512
+    # blocks reach it, and the row takes the exact whole-row path
+    say("topk scan: bound above the 512th score")
+    w = custom(seed=43, lens=(80001,), nq=4, parts=("index",))
+    bt_min = (int(w.lens[0]) - w.n_query) // 4
+    spread = [i * bt_min // 1024 for i in range(0, 1024, 51)][:20]
+    rng = np.random.default_rng(43)
+    others = rng.choice(bt_min, size=80, replace=False).tolist()
+    scale_blocks(w, 0, sorted(set(spread) | set(others)), 16.0)
+    check_topk(w, Q.FLAG_TOPK_SCAN)
+
+
+def test_topk_scan_segment_overflow():
+    # 700 consecutive outlier blocks: one slice holds more candidates than its
+    # segment, and the row takes the exact whole-row path
+    say("topk scan: segment overflow")
+    w = custom(seed=44, lens=(600001,), nq=4, parts=("index",))
+    scale_blocks(w, 0, range(70000, 70700), 4.0)
+    check_topk(w, Q.FLAG_TOPK_SCAN)
+
+
+def test_topk_scan_more_candidates_than_the_list_holds():
+    # every score is 0 over 15,000 blocks: all are candidates, more than the
+    # select's LDS list holds; the lowest 512 ids win
+    say("topk scan: candidate list overflow")
+    w = custom(lens=(60001,), nq=3, parts=("index",))
+    w.k_idx[:] = 0
+    check_topk(w, Q.FLAG_TOPK_SCAN)
+
+
 def test_topk_engines_agree_on_cfg1():
     say("topk cfg1 engines")
     w = W.make(1, parts=("index",))
     k_cmp = gpu_kcmp(w)
     a = run_topk(w, Q.FLAG_TOPK_TABLE, k_cmp)
     b = run_topk(w, Q.FLAG_TOPK_STREAM, k_cmp)
+    c = run_topk(w, Q.FLAG_TOPK_SCAN, k_cmp)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[0], c[0])
+    np.testing.assert_array_equal(a[1], c[1])
     res = oracle_select(w)
     want_sel, want_n = padded_sel(res, w.batch, w.n_query, w.lens)
     np.testing.assert_array_equal(a[0], want_sel)
