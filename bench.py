@@ -23,6 +23,11 @@ The same line carries
                 with the indexer's MFMA fraction and the attention's;
   configs       the other three workloads (tiny 4K, 128K decode, 256K prefill
                 chunk), steady-state forward, each against its roofline;
+  sweep         the decode step (batch 4 x 4) and the last-16K-chunk prefill
+                at contexts of 8K, 32K, 128K, 256K and 1M tokens;
+  streaming     a whole 1M-token prompt prefilled in 64 chunks of 16,384
+                tokens (each compressing only its own micro-blocks), then
+                decode steps of 4 tokens appended to the caches;
   ceilings      the part's measured memory ceilings under the path's access
                 patterns (cold 128 MiB streaming read, random 256 B / 1 KiB /
                 4 KiB gathers over an 8 GiB K/V cache);
@@ -66,6 +71,10 @@ def parse(argv=None):
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     ap.add_argument("--no-configs", action="store_true", help="skip the other three workloads")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the memory ceilings")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 8K..1M context-length sweep of the decode step and prefill chunk")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the whole-prompt streaming run (1M prompt in 16K chunks, then decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of each oracle sample (decode, prefill)")
@@ -412,6 +421,125 @@ def other_configs(Q, W, torch, np, flush):
     return res
 
 
+def device_inputs(torch, B, L, Nq, Hq, Hkv, seed, positions=None):
+    """Seeded synthetic inputs generated on the device (for the sweep and the
+    streaming run, whose sizes would take the host generator minutes):
+    indexer queries and keys uniform integers in [-8, 8], core Q/K/V
+    standard normal, all rounded to bf16 (the integers exactly).  positions:
+    query rows to generate (default Nq)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    n = Nq if positions is None else positions
+    bf = torch.bfloat16
+
+    def ints(*shape):
+        return torch.randint(-8, 9, shape, generator=g, device="cuda", dtype=torch.int32).to(bf)
+
+    def normal(*shape):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(bf)
+
+    return {"q_idx": ints(B, n, 4, 64), "k_idx": ints(B, L, 64), "q": normal(B, n, Hq, 128),
+            "k": normal(B, L, Hkv, 128), "v": normal(B, L, Hkv, 128)}
+
+
+def sweep(Q, torch, np, flush):
+    """The decode step (batch 4 x 4, lens L .. L-3) and the prefill of the last
+    16,384 positions (batch 1; the whole prompt when it is shorter) at each
+    context length, steady state (the compressed-key cache holds the blocks
+    before the call's queries), 32/4 heads, device-generated inputs."""
+    res = {}
+    for L in (8192, 32768, 131072, 262144, 1048576):
+        rec = {}
+        for kind in ("decode", "prefill"):
+            if kind == "decode":
+                B, Nq = 4, 4
+                lens_h = np.array([L, L - 1, L - 2, L - 3], np.int32)
+            else:
+                B, Nq = 1, min(16384, L)
+                lens_h = np.array([L], np.int32)
+            d = device_inputs(torch, B, L, Nq, 32, 4, seed=L + (0 if kind == "decode" else 1))
+            shp = Q.shape(B, L, Nq, 32, 4, 0.0, Workspace.flags)
+            lens = torch.from_numpy(lens_h).cuda()
+            prev = torch.from_numpy(lens_h - Nq).cuda()
+            first = torch.from_numpy((lens_h - Nq) // 4).cuda()
+            k_cmp = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
+            if (lens_h - Nq).max() > 0:
+                Q.compress_keys(shp, d["k_idx"], prev, k_cmp)
+            out = torch.empty((B, Nq, 32, 128), dtype=torch.bfloat16, device="cuda")
+            wsp = Q.workspace(shp, Q.OP_FORWARD)
+
+            def step():
+                Q.forward(shp, d["q_idx"], d["k_idx"], k_cmp, d["q"], d["k"], d["v"], lens,
+                          first_block=first, out=out, ws=wsp, want_lse=False)
+
+            for _ in range(3):
+                flush()
+                step()
+            n = 30 if kind == "decode" else 3
+            step_ms, kst, _ = timed_steps(step, n, flush, Q, torch)
+            ms = float(np.median(step_ms))
+            r = {"ms_per_step": ms, "value": B * Nq / (ms * 1e-3), "unit": "q-tok/s",
+                 "kernels": {k: round(v["avg_us"], 2) for k, v in kst.items()}}
+            if kind == "decode":
+                kcmp_bytes = int(sum(((int(l) - 1) // 4) * 128 for l in lens_h))
+                r["kcmp_scan_gbs"] = None
+                sk = kst.get("score_table_kernel") or kst.get("scan_filter_kernel")
+                if sk:
+                    r["kcmp_scan_gbs"] = kcmp_bytes / (sk["avg_us"] * 1e-6) / 1e9
+            else:
+                t = np.arange(L - Nq, L, dtype=np.int64)
+                idx_flops = float(np.sum(512.0 * (t // 4)))
+                sk = kst.get("score_stream_kernel")
+                if sk:
+                    r["indexer_mfma_frac"] = idx_flops / (sk["avg_us"] * 1e-6) / 1e12 \
+                        / MFMA_BF16_PEAK_TFLOPS
+            rec[kind] = r
+            del d, k_cmp, out, wsp
+            torch.cuda.empty_cache()
+        res[str(L)] = rec
+        log(f"[bench] sweep {L}: decode {rec['decode']['ms_per_step'] * 1e3:.1f} us, "
+            f"prefill {rec['prefill']['ms_per_step']:.2f} ms")
+    return res
+
+
+def streaming(Q, torch, np, prompt=1 << 20, chunk=16384, steps=16, m=4):
+    """A whole prompt of `prompt` tokens prefilled in chunks through
+    qsa_forward (each call compressing only its chunk's micro-blocks), then
+    `steps` decode steps of m tokens appended to the caches; batch 1, 32/4
+    heads, device-generated inputs.  Wall time of the whole prefill and the
+    decode steps by HIP events."""
+    from learned_sparse_attention_qsa_amd import streaming as S
+
+    total = prompt + steps * m
+    cap = (total + 3) // 4 * 4
+    d = device_inputs(torch, 1, total, 0, 32, 4, seed=7777, positions=total)
+    seq = S.Sequence(cap, 32, 4, flags=Workspace.flags)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    S.prefill(seq, d["q_idx"][0, :prompt], d["k_idx"][0, :prompt], d["q"][0, :prompt],
+              d["k"][0, :prompt], d["v"][0, :prompt], chunk)
+    ev[1].record()
+    for s in range(steps):
+        lo = prompt + s * m
+        S.decode_step(seq, d["q_idx"][0, lo:lo + m], d["k_idx"][0, lo:lo + m],
+                      d["q"][0, lo:lo + m], d["k"][0, lo:lo + m], d["v"][0, lo:lo + m])
+    ev[2].record()
+    torch.cuda.synchronize()
+    pre_ms = ev[0].elapsed_time(ev[1])
+    dec_ms = ev[1].elapsed_time(ev[2])
+    n_chunks = (prompt + chunk - 1) // chunk
+    del d, seq
+    torch.cuda.empty_cache()
+    return {"prompt_tokens": prompt, "chunk": chunk, "chunks": n_chunks,
+            "prefill_ms": pre_ms, "prefill_q_tok_per_s": prompt / (pre_ms * 1e-3),
+            "prefill_ms_per_chunk": pre_ms / n_chunks, "decode_steps": steps,
+            "decode_tokens_per_step": m, "decode_ms_per_step": dec_ms / steps,
+            "decode_q_tok_per_s": steps * m / (dec_ms * 1e-3),
+            "note": ("caches not flushed between calls (the run is one continuous stream of "
+                     "work); includes the per-chunk appends of K/V and indexer keys")}
+
+
 def ceilings(Q, torch, flush, reps=10):
     """Memory ceilings under the path's access patterns, each kernel timed by
     the HIP events its own dispatch carries, after an untimed flush."""
@@ -685,6 +813,11 @@ def main(argv=None):
         torch.cuda.empty_cache()
     if not args.no_configs:
         line["configs"] = other_configs(Q, W, torch, np, flush)
+    if not args.no_sweep:
+        line["sweep"] = sweep(Q, torch, np, flush)
+    if not args.no_streaming:
+        log("[bench] streaming: 1M prompt in 16K chunks, then decode steps")
+        line["streaming"] = streaming(Q, torch, np)
     if not args.no_ceilings:
         log("[bench] memory ceilings")
         line["ceilings"] = ceilings(Q, torch, flush)

@@ -655,6 +655,7 @@ constexpr int kPickWaves = kPickThreads / 64;  // 16: one lane of a 16-lane row 
 constexpr int kPickGroups = 2048;  // candidate groups a row keeps in LDS
 constexpr int kPickCand = 2048;    // candidate blocks a row keeps in LDS (2 per thread)
 constexpr int kPickRounds = kPickGroups / (kPickThreads / 4);
+constexpr int kPickDirectGroups = 1536;  // rows of fewer groups (and > kPickCand blocks): bound from block scores
 static_assert(kPickWaves == 16, "per-wavefront values are combined within one 16-lane row");
 
 // Wavefront primitives on DPP lane moves, which need no LDS traffic.
@@ -849,7 +850,26 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
   const float rowmax_f = __uint_as_float(rowmax);
   const float scale = rowmax != 0u ? 2047.0f / rowmax_f : 0.f;
   uint32_t bv = 0;
-  if (G >= kTopK) {
+  if (G < kPickDirectGroups && bt > kPickCand) {
+    // Too few groups for their maxima to bound the 512th score tightly (with
+    // 512 groups the bound is the smallest maximum) while the row's blocks
+    // exceed the candidate list: the bound comes from the block scores
+    // themselves (a linear histogram of the row's scores, then the smallest
+    // score in the bin of the 512th best or above).
+    for (int j = tid; j < bt; j += kPickThreads) atomicAdd(&hist[lin_bin(trow[j], 0.f, scale)], 1u);
+    __syncthreads();
+    uint32_t bin_a, ab, cn;
+    pick_suffix_find(hist, kTopK, wtot, res, bin_a, ab, cn);
+    uint32_t mn = 0xffffffffu;
+    for (int j = tid; j < bt; j += kPickThreads) {
+      const uint32_t x = trow[j];
+      if (lin_bin(x, 0.f, scale) >= bin_a) mn = min(mn, x);
+    }
+    mn = wave_min_u32(mn);
+    if (lane == 0 && mn != 0xffffffffu) atomicMin(&s_bv, mn);
+    __syncthreads();
+    bv = s_bv;
+  } else if (G >= kTopK) {
     // With >= 512 threads holding maxima, their per-thread maxima (distinct
     // groups) are counted, else every maximum; the smallest counted value in
     // the bins from the one holding the 512th largest up is reached by >= 512
@@ -1099,10 +1119,12 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
 // gaps.  Two phases over the same pipeline:
 //
 //  1. sample: about every 32nd column tile (c = 128 i + 33 p for the four
-//     parities p).  Each query histograms its sample scores (256 bins, 64
-//     per octave, from a base two octaves below the best score of the first
-//     sample tile of each parity) and takes as its bound tau the lower edge
-//     of the bin holding its kSampleRank-th best sample score.
+//     parities p).  The first sample tile of each parity sets each query's
+//     histogram base (3 octaves below its best score there); then every
+//     sample tile, the first ones again included, goes into the query's
+//     histogram (256 bins, 64 per octave; higher scores count in the top
+//     bin), and its bound tau is the lower edge of the bin holding its
+//     kSampleRank-th best sample score.
 //  2. filter: every tile; a block is a candidate if its score is strictly
 //     above tau.  A lane with a candidate among its 8 scores queues one LDS
 //     record of them; records are drained 64 at a time into the queries'
@@ -1128,9 +1150,10 @@ constexpr int kSampleStep = 33;
 static_assert(kSampleStep % kPar == 1 && kSampleStep * (kPar - 1) < kSampleStride, "sample tiles");
 constexpr int kSampleRank = 40;   // tau: the 40th best sample score (bin edge)
 // sample histogram: bins of (score bits >> 17), i.e. 64 per octave, 256 bins =
-// 4 octaves from a base 2 octaves (128 bins) below the best of the first tiles
+// 4 octaves from a base 3 octaves (192 bins) below the best of the first
+// tiles; higher samples count in the top bin
 constexpr int kSampleShift = 17;
-constexpr int kSampleBase = 128;
+constexpr int kSampleBase = 192;
 // records one position can add to a wavefront's queue (one per lane and
 // half), plus fewer than 64 held over
 constexpr int kQueue = 2 * 64 + 64;
@@ -1527,14 +1550,18 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   // phase 0: the first sample tile of each parity (column tiles 0 .. kPar - 1)
   stream_phase<0>(st, A, bv, accX, accY, 0, min(ns, 1), ns, par, kb, bt_g, qn, colp);
   stream_barrier();
-  // histogram base: two octaves below the best score of those tiles
+  // histogram base: three octaves below the best score of those tiles
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       st.base_l[rt][c] =
           max(0, (int)(st.mx[slot_off(rt, c) + (lane >> 5)] >> kSampleShift) - kSampleBase);
-  stream_phase<1>(st, A, bv, accX, accY, 1, ns, ns, par, kb, bt_g, qn, colp);
+  // every sample tile into the histograms, the first one of this parity
+  // again (its fragments reloaded into buffer 0; buffer 1 already holds the
+  // next position's)
+  if (ns > 0) load_cols(kb, kSampleStep * par, bt_g, st.voff, bv[0]);
+  stream_phase<1>(st, A, bv, accX, accY, 0, ns, ns, par, kb, bt_g, qn, colp);
   stream_barrier();
   // bounds: wavefront of parity par computes local queries [kQp par, kQp par + kQp)
   {
