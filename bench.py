@@ -306,7 +306,21 @@ def decode_leg(args, Q, W, torch, np, flush):
     cold_ms, cold_k, _ = timed_steps(lambda: ws.step(cold=True), args.cold_steps, flush, Q, torch)
     ws.step()  # leave the steady-state cache and selection behind
     torch.cuda.synchronize()
+    # selection quality: the share of the dense attention mass (pooled per
+    # micro-block, the indexer's training target) that the selection keeps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    teacher = Q.block_teacher(ws.shp, ws.dev["q"], ws.dev["k"], ws.dev["v"], ws.lens)
+    ev[1].record()
+    recall = Q.teacher_recall(ws.shp, ws.lens, teacher, ws.sel, ws.n_sel).cpu().numpy()
+    quality = {"recall_mean": float(recall.mean()), "recall_min": float(recall.min()),
+               "teacher_ms": ev[0].elapsed_time(ev[1]),
+               "note": "dense attention mass (averaged over heads) on the selected blocks and "
+                       "the own block; random synthetic keys, so the mass is spread thinly"}
+    del teacher
+    torch.cuda.empty_cache()
     return dict(w=w, ws=ws, step_ms=step_ms, kstats=kstats, wall=wall, sel=sel_h, n_sel=nsel_h,
+                quality=quality,
                 algo=decode_algo(kcmp, attn, qidx, w.batch), kcmp_bytes=kcmp, attn_bytes=attn,
                 qidx_bytes=qidx,
                 cold={"ms_per_step": sum(cold_ms) / len(cold_ms), "steps": len(cold_ms),
@@ -377,6 +391,16 @@ def prefill_leg(args, Q, W, torch, np, flush, cfg=3, steps=None):
     log(f"[bench] {w.name}: {n} timed steps")
     step_ms, kstats, _ = timed_steps(ws.step, n, flush, Q, torch)
     res = prefill_record(w, step_ms, kstats, np)
+    # needle survival: the share of each query's planted micro-blocks (indexer
+    # keys x4) that its selection keeps
+    if w.needle_starts and w.needle_starts[0]:
+        sel_h, nsel_h = ws.sel.cpu().numpy()[0], ws.n_sel.cpu().numpy()[0]
+        blocks = np.array(sorted(j for s in w.needle_starts[0] for j in range(s // 4, s // 4 + 16)))
+        hit = np.zeros(w.n_query)
+        for i in range(w.n_query):
+            hit[i] = np.isin(blocks, sel_h[i, :nsel_h[i]]).mean()
+        res["needle_survival"] = {"mean": float(hit.mean()), "min": float(hit.min()),
+                                  "spans": len(w.needle_starts[0]), "blocks": int(blocks.size)}
     del ws
     torch.cuda.empty_cache()
     return res, w
@@ -798,6 +822,7 @@ def main(argv=None):
         "roofline": roofline_of(d["kstats"], d["algo"]),
         "kernels": d["kstats"],
         "cold": d["cold"],
+        "selection_quality": d["quality"],
     }
     if not args.no_dense:
         log("[bench] dense comparator")

@@ -101,7 +101,8 @@ enum {
   QSA_OP_EXPAND = 2,
   QSA_OP_SPARSE_ATTEND = 3,
   QSA_OP_FORWARD = 4,
-  QSA_OP_DENSE_DECODE = 5
+  QSA_OP_DENSE_DECODE = 5,
+  QSA_OP_BLOCK_TEACHER = 6
 };
 size_t qsa_workspace_bytes(const qsa_shape* shape, int32_t op);
 
@@ -202,6 +203,33 @@ qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q,
                                 const uint16_t* k, const uint16_t* v,
                                 const int32_t* lens, uint16_t* out, float* lse,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* The indexer's training target: the indexer is trained together with the
+ * model and learns from the full-attention distribution (page "Qwen's
+ * million-token window has a 2,048-token keyhole", section "The indexer is
+ * trained, not bolted on").  Reading: that distribution pooled per
+ * micro-block and averaged over the core query heads.  For every query row
+ * writes teacher[b][i][j] (float, layout [B][Nq][Lmax/4]) =
+ *   (1/Hq) sum_h sum_{s in block j, s <= t} exp(scale q_h . k_s - lse_h),
+ * lse_h the dense causal log-sum-exp of head h over 0..t (so each row sums
+ * to 1 over blocks 0..floor(t/4), the last one partial); entries past the
+ * query's own block are 0.  A dense pass over K and V (for lse) and one over
+ * K; float accumulation, the per-block sums added atomically (the last bits
+ * of an entry may differ from run to run).  Workspace: QSA_OP_BLOCK_TEACHER. */
+qsa_status qsa_block_teacher(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* lens, float* teacher,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Selection recall: the share of a row's teacher mass on the positions QSA
+ * attends to, its kept micro-blocks and its own block (whether the selection
+ * keeps what the dense attention looks at, section "What a serious
+ * evaluation should preserve").  recall[b][i] = sum_{j in sel} teacher[j] +
+ * teacher[floor(t/4)], with (sel, n_sel) as qsa_index_topk writes them and
+ * teacher as qsa_block_teacher writes it.  Equals the mean over heads of
+ * exp(lse_sparse - lse_dense) up to rounding. */
+qsa_status qsa_teacher_recall(const qsa_shape* shape, const int32_t* lens, const float* teacher,
+                              const int32_t* sel, const int32_t* n_sel, float* recall,
+                              void* stream);
 
 /* Kernel timing hook, for benchmarks and profilers (not part of the method).
  * qsa_profile_attach hands the library n_events caller-created hipEvent_t

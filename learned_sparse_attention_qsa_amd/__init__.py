@@ -30,7 +30,8 @@ MAX_TOK = TOPK * BLOCK + BLOCK
 
 OK, ERR_NULL, ERR_ALIGN, ERR_SHAPE, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP, ERR_SCRATCH = range(8)
 NOALLOC_SCRATCH_BYTES = 64 << 20
-OP_COMPRESS, OP_INDEX_TOPK, OP_EXPAND, OP_SPARSE_ATTEND, OP_FORWARD, OP_DENSE_DECODE = range(6)
+(OP_COMPRESS, OP_INDEX_TOPK, OP_EXPAND, OP_SPARSE_ATTEND, OP_FORWARD, OP_DENSE_DECODE,
+ OP_BLOCK_TEACHER) = range(7)
 FLAG_TOPK_TABLE = 1
 FLAG_TOPK_STREAM = 2
 FLAG_TOPK_SCAN = 4
@@ -46,6 +47,8 @@ EXPORTS = (
     "qsa_forward",
     "qsa_forward_noalloc",
     "qsa_dense_gqa_decode",
+    "qsa_block_teacher",
+    "qsa_teacher_recall",
     "qsa_profile_attach",
     "qsa_profile_detach",
     "qsa_profile_kernel_name",
@@ -98,7 +101,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_dense_gqa_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    for name in EXPORTS[2:9]:
+    lib.qsa_block_teacher.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_teacher_recall.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+    for name in EXPORTS[2:11]:
         getattr(lib, name).restype = i32
     lib.qsa_profile_attach.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.qsa_profile_attach.restype = i32
@@ -353,6 +358,43 @@ def ceil_gather(base: torch.Tensor, row_index: torch.Tensor, row_bytes: int, wor
         raise ValueError("a gathered piece lies outside base")
     _check(load_library().qsa_ceil_gather(_p(base), _p(row_index), n, row_bytes, workgroups,
                                           _p(sink), _stream(base.device)), "qsa_ceil_gather")
+
+
+def block_teacher(shp: QsaShape, q, k, v, lens, teacher=None, ws=None):
+    """qsa_block_teacher: dense attention mass per micro-block, averaged over
+    the heads; returns teacher [B][Nq][Lmax/4] float32."""
+    B, L, Nq, Hq, Hkv = shp.batch, shp.max_len, shp.n_query, shp.q_heads, shp.kv_heads
+    dev = q.device
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    _need(k, "k", (B, L, Hkv, HEAD_DIM), _BF)
+    _need(v, "v", (B, L, Hkv, HEAD_DIM), _BF)
+    _need(lens, "lens", (B,), _I32)
+    if teacher is None:
+        teacher = torch.empty((B, Nq, L // BLOCK), dtype=torch.float32, device=dev)
+    _need(teacher, "teacher", (B, Nq, L // BLOCK), (torch.float32,))
+    ws, nb = _ws(shp, OP_BLOCK_TEACHER, ws, dev)
+    st = load_library().qsa_block_teacher(ctypes.byref(shp), _p(q), _p(k), _p(v), _p(lens),
+                                          _p(teacher), _p(ws), nb, _stream(dev))
+    _check(st, "qsa_block_teacher")
+    return teacher
+
+
+def teacher_recall(shp: QsaShape, lens, teacher, sel, n_sel, recall=None):
+    """qsa_teacher_recall: share of each row's teacher mass on its kept blocks
+    and its own block; returns recall [B][Nq] float32."""
+    B, L, Nq = shp.batch, shp.max_len, shp.n_query
+    dev = teacher.device
+    _need(lens, "lens", (B,), _I32)
+    _need(teacher, "teacher", (B, Nq, L // BLOCK), (torch.float32,))
+    _need(sel, "sel", (B, Nq, TOPK), _I32)
+    _need(n_sel, "n_sel", (B, Nq), _I32)
+    if recall is None:
+        recall = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+    _need(recall, "recall", (B, Nq), (torch.float32,))
+    st = load_library().qsa_teacher_recall(ctypes.byref(shp), _p(lens), _p(teacher), _p(sel),
+                                           _p(n_sel), _p(recall), _stream(dev))
+    _check(st, "qsa_teacher_recall")
+    return recall
 
 
 class KernelTimer:

@@ -142,6 +142,8 @@ size_t ws_bytes_for(const Dims& d, uint32_t flags, int32_t op) {
     }
     case QSA_OP_DENSE_DECODE:
       return qsa::dense_workspace_bytes(d);
+    case QSA_OP_BLOCK_TEACHER:
+      return qsa::teacher_workspace_bytes(d);
     default:
       return 0;
   }
@@ -362,6 +364,41 @@ qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
   return hip_status(qsa::launch_dense_decode(d, q, k, v, lens, out, lse, ws, s));
+}
+
+qsa_status qsa_block_teacher(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* lens, float* teacher, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(teacher));
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_BLOCK_TEACHER, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_block_teacher(d, q, k, v, lens, teacher, ws, s));
+}
+
+qsa_status qsa_teacher_recall(const qsa_shape* shape, const int32_t* lens, const float* teacher,
+                              const int32_t* sel, const int32_t* n_sel, float* recall,
+                              void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(teacher));
+  QSA_TRY(need(sel));
+  QSA_TRY(need_i32(n_sel));
+  QSA_TRY(need_i32(recall));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_teacher_recall(d, teacher, lens, sel, n_sel, recall, s));
 }
 
 }  // extern "C"

@@ -468,6 +468,127 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   finish(r, col_valid, nullptr, nullptr, po, pl, true);
 }
 
+// ------------------------------------------------------------------ teacher
+// The indexer's training target: dense attention probabilities pooled per
+// micro-block and averaged over the query heads,
+//   T[b][i][j] = (1/Hq) sum_h sum_{s in block j, s <= t} exp(scale q_h.k_s - lse_h)
+// with lse_h the dense causal log-sum-exp of head h (from the dense pass).
+// Same grid and column units as dense_decode_kernel, K only: a lane's eight
+// logits of a 32-token tile (qk_logits) are the four tokens of one
+// micro-block in each 16-token half, so the lane sums them into its
+// column's mass of that block; the columns of one query (G consecutive
+// lanes when G divides 16) are summed across lanes and one lane adds the
+// result to T, which the launcher clears first.
+__global__ __launch_bounds__(64 * kDenseWaves) void block_teacher_kernel(AttnArgs a,
+                                                                         const float* __restrict__ lse_dense,
+                                                                         float* __restrict__ teacher) {
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int cchunks = (a.Nq * a.G + 15) >> 4;
+  const int wave = threadIdx.x >> 6;
+  const int u = blockIdx.y * kDenseWaves + wave;
+  if (u >= a.Hkv * cchunks) return;  // (no workgroup barrier below)
+  const int g = u / cchunks, cc = u % cchunks;
+  const int lane = lane_id();
+  const int len = clampi(a.lens[b], 0, a.Lmax);
+  const int col = lane & 15;
+  const int c = cc * 16 + col;  // (query, head) column
+  const bool col_valid = c < a.Nq * a.G;
+  const int qi = col_valid ? c / a.G : 0;
+  const int h = g * a.G + (col_valid ? c % a.G : 0);
+  const int tq = len - a.Nq + qi;
+  const size_t row = (size_t)b * a.Nq + qi;
+  bf16x8 qf[4];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + (row * a.Hq + h) * kHeadDim);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[ks] = as_bf16x8(col_valid && tq >= 0 ? qp[ks * 4 + (lane >> 4)] : zero_u4());
+  }
+  const float lse2 = col_valid && tq >= 0 ? lse_dense[row * a.Hq + h] * kLog2e : 0.f;
+  const int c_last = min(cc * 16 + 15, a.Nq * a.G - 1);
+  const int t_hi = len - a.Nq + c_last / a.G;
+  const int k_begin = split * a.split_tokens;  // a multiple of 32
+  const int k_end = min(t_hi + 1, k_begin + a.split_tokens);
+  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
+  const uint16_t* kbase = a.k + g * kHeadDim;
+  const int nbp = a.Lmax >> 2;
+  const bool grouped = a.G <= 16 && (16 % a.G) == 0;
+  const float inv_hq = 1.0f / (float)a.Hq;
+  KVTile cur;
+  auto load_k = [&](KVTile& t, int k0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kk = k0 + s * 16 + (lane & 15);
+      const uint4* kp = reinterpret_cast<const uint4*>(
+          kbase + (size_t)(kv_seq + (size_t)min(kk, len > 0 ? len - 1 : 0) * a.Hkv) * kHeadDim);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) t.k[s][ks] = kk < k_end ? kp[ks * 4 + (lane >> 4)] : zero_u4();
+    }
+  };
+  if (k_begin < k_end) load_k(cur, k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += kTile) {
+    KVTile nxt;
+    if (k0 + kTile < k_end) load_k(nxt, k0 + kTile);
+    float z[8];
+    qk_logits(cur, qf, a.scale_log2, z);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int tok0 = k0 + s * 16 + (lane >> 4) * 4;  // the block's first token
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = tok0 + i;
+        m += (col_valid && kk <= tq && kk < k_end) ? exp2f(z[s * 4 + i] - lse2) : 0.f;
+      }
+      m *= inv_hq;
+      const int jb = tok0 >> 2;
+      if (grouped) {
+        // sum over the G lanes of the query (consecutive lanes of the row)
+        for (int off = 1; off < a.G; off <<= 1) m += __shfl_xor(m, off);
+        if ((col % a.G) == 0 && col_valid && tok0 <= tq && m != 0.f)
+          atomicAdd(&teacher[row * nbp + jb], m);
+      } else if (col_valid && tok0 <= tq && m != 0.f) {
+        atomicAdd(&teacher[row * nbp + jb], m);
+      }
+    }
+    cur = nxt;
+  }
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// Share of the teacher's mass on the positions a row attends to: its kept
+// blocks and its own block.  One workgroup (256 threads) per row.
+__global__ __launch_bounds__(256) void teacher_recall_kernel(const float* __restrict__ teacher,
+                                                             const int32_t* __restrict__ lens,
+                                                             const int32_t* __restrict__ sel,
+                                                             const int32_t* __restrict__ n_sel,
+                                                             float* __restrict__ recall, int Lmax,
+                                                             int Nq) {
+  __shared__ float wsum[4];
+  const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t row = (size_t)b * Nq + q;
+  const int t = clampi(lens[b], 0, Lmax) - Nq + q;
+  const int nbp = Lmax >> 2;
+  float acc = 0.f;
+  if (t >= 0) {
+    const int bt = t >> 2;
+    const int ns = clampi(n_sel[row], 0, min(bt, kTopK));
+    const float* tr = teacher + row * nbp;
+    for (int i = tid; i < ns; i += blockDim.x) acc += tr[clampi(sel[row * kTopK + i], 0, bt - 1)];
+    if (tid == 0) acc += tr[bt];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) recall[row] = t >= 0 ? (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]) : 0.f;
+}
+
 // ------------------------------------------------------------------ merge
 // Grid (Hq, Nq, B), 128 threads (one per output dim).  Combines the n_split
 // partial (o, lse) pairs of one (query, head): o = sum_s e^(lse_s - M) o_s /
@@ -658,6 +779,57 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
   if (a.n_split > 1)
     QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
                part_o, part_lse, out, lse, d.Nq, d.Hq, a.n_split);
+  return hipGetLastError();
+}
+
+size_t teacher_workspace_bytes(const Dims& d) {
+  Carve c{nullptr, 0};
+  c.take<char>(dense_workspace_bytes(d));
+  c.take<uint16_t>((size_t)d.B * d.Nq * d.Hq * kHeadDim);  // dense output (unused)
+  c.take<float>((size_t)d.B * d.Nq * d.Hq);                // dense lse
+  return c.off;
+}
+
+hipError_t launch_block_teacher(const Dims& d, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const int32_t* lens, float* teacher, void* ws,
+                                hipStream_t s) {
+  if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  Carve c{static_cast<char*>(ws), 0};
+  void* dws = c.take<char>(dense_workspace_bytes(d));
+  uint16_t* dout = c.take<uint16_t>((size_t)d.B * d.Nq * d.Hq * kHeadDim);
+  float* dlse = c.take<float>((size_t)d.B * d.Nq * d.Hq);
+  hipError_t e = launch_dense_decode(d, q, k, v, lens, dout, dlse, dws, s);
+  if (e != hipSuccess) return e;
+  const size_t nt = (size_t)d.B * d.Nq * (d.Lmax / 4);
+  QSA_LAUNCH(fill_f32_kernel, dim3(1024), dim3(256), 0, s, teacher, nt, 0.f);
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lens = lens;
+  a.B = d.B;
+  a.Lmax = d.Lmax;
+  a.Nq = d.Nq;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.Hq / d.Hkv;
+  a.scale_log2 = d.scale * kLog2e;
+  a.n_split = dense_splits(d, &a.split_tokens);
+  const int units = d.Hkv * ((d.Nq * a.G + 15) / 16);
+  const int waves = units < kDenseWaves ? units : kDenseWaves;
+  QSA_LAUNCH(block_teacher_kernel,
+             dim3((unsigned)a.n_split, (unsigned)((units + kDenseWaves - 1) / kDenseWaves),
+                  (unsigned)d.B),
+             dim3(64 * (unsigned)waves), 0, s, a, (const float*)dlse, teacher);
+  return hipGetLastError();
+}
+
+hipError_t launch_teacher_recall(const Dims& d, const float* teacher, const int32_t* lens,
+                                 const int32_t* sel, const int32_t* n_sel, float* recall,
+                                 hipStream_t s) {
+  if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  QSA_LAUNCH(teacher_recall_kernel, dim3((unsigned)d.Nq, (unsigned)d.B), dim3(256), 0, s, teacher,
+             lens, sel, n_sel, recall, d.Lmax, d.Nq);
   return hipGetLastError();
 }
 

@@ -61,6 +61,15 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
                                 const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
                                 float* part_lse, hipStream_t s);
 size_t dense_workspace_bytes(const Dims& d);
+// The indexer's training target (dense attention mass per micro-block, over
+// the heads) and the share of it a selection keeps.
+size_t teacher_workspace_bytes(const Dims& d);
+hipError_t launch_block_teacher(const Dims& d, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const int32_t* lens, float* teacher, void* ws,
+                                hipStream_t s);
+hipError_t launch_teacher_recall(const Dims& d, const float* teacher, const int32_t* lens,
+                                 const int32_t* sel, const int32_t* n_sel, float* recall,
+                                 hipStream_t s);
 hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* lens, uint16_t* out,
                                float* lse, void* ws, hipStream_t s);

@@ -13,4 +13,5 @@ from .qsa_oracle import (  # noqa: F401
     compress_keys, block_scores, select_blocks, expand_tokens,
     attend, query_positions, qsa_forward, dense_decode,
     block_scores_rows, select_blocks_rows, select_rows,
+    block_teacher, selection_recall, needle_survival,
 )

@@ -333,3 +333,50 @@ def dense_decode(q_bits, k_bits, v_bits, lens, n_query: int, scale: float | None
         vr = bf16_bits_to_f64(v_bits[b, :t + 1])
         out[(b, i)] = attend(bf16_bits_to_f64(q_bits[b, i]), kr, vr, scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# The indexer's training target and what the selection keeps of it
+# --------------------------------------------------------------------------
+
+def block_teacher(q: np.ndarray, k_rows: np.ndarray, t: int, scale: float) -> np.ndarray:
+    """Dense attention mass of every micro-block for the query at position t.
+
+    The indexer learns from the full-attention distribution (page "Qwen's
+    million-token window has a 2,048-token keyhole", section "The indexer is
+    trained, not bolted on").  Reading: the target is that distribution
+    pooled per micro-block and averaged over the core query heads,
+      T[j] = (1/Hq) sum_h sum_{s in block j, s <= t} softmax_h(scale q_h . k_s),
+    over blocks 0 .. floor(t/4), the last one holding only tokens up to t.
+    q: float64 [Hq][D]; k_rows: float64 [>= t+1][Hkv][D] (the sequence's keys).
+    Returns float64 [floor(t/4) + 1]; it sums to 1.
+    """
+    hq = q.shape[0]
+    hkv = k_rows.shape[1]
+    group = hq // hkv
+    n = t + 1
+    bt = t // BLOCK
+    pooled = np.zeros(bt + 1, dtype=np.float64)
+    for h in range(hq):
+        z = scale * (k_rows[:n, h // group, :] @ q[h])
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        pooled += np.bincount(np.arange(n) // BLOCK, weights=p, minlength=bt + 1)
+    return pooled / hq
+
+
+def selection_recall(teacher: np.ndarray, sel: np.ndarray) -> float:
+    """Share of the teacher's mass on the positions QSA attends to: the kept
+    micro-blocks and the query's own block (always attended, opening section
+    of the page)."""
+    return float(teacher[np.asarray(sel, dtype=np.int64)].sum() + teacher[-1])
+
+
+def needle_survival(sel: np.ndarray, needle_blocks) -> float:
+    """Share of the planted micro-blocks that the selection keeps (the pages
+    ask whether the evidence a long-context task needs survives the
+    selection: section "What a serious evaluation should preserve")."""
+    nb = np.asarray(sorted(needle_blocks), dtype=np.int64)
+    if nb.size == 0:
+        return 1.0
+    return float(np.isin(nb, np.asarray(sel, dtype=np.int64)).mean())

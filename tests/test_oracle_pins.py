@@ -377,3 +377,66 @@ def test_qsa_differs_from_dense_beyond_2052():
     tok = res["tok"][(0, 0)]
     assert tok.shape[0] == 2049  # 512 blocks + a one-token tail (t = 2052)
     assert 2052 in tok
+
+
+# ---------------------------------------------------------------- teacher, recall, survival
+
+def test_teacher_brute_force_and_mass():
+    rng = np.random.default_rng(70)
+    hq, hkv, t = 4, 2, 13
+    q = rng.standard_normal((hq, 8))
+    k = rng.standard_normal((t + 1, hkv, 8))
+    scale = 0.3
+    T = O.block_teacher(q, k, t, scale)
+    assert T.shape == (t // 4 + 1,)
+    want = np.zeros(t // 4 + 1)
+    for h in range(hq):
+        logits = [scale * sum(q[h, d] * k[s, h // 2, d] for d in range(8)) for s in range(t + 1)]
+        mx = max(logits)
+        e = [math.exp(x - mx) for x in logits]
+        for s in range(t + 1):
+            want[s // 4] += e[s] / sum(e) / hq
+    np.testing.assert_allclose(T, want, rtol=1e-12, atol=1e-15)
+    assert abs(T.sum() - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("t", [4095, 4096, 4097, 4098])
+def test_teacher_uniform_keys(t):
+    # K = 0: every position equally likely, so a block holds 4/(t+1) and the
+    # query's own block (t mod 4) + 1 of t + 1
+    q = np.random.default_rng(t).standard_normal((8, 16))
+    k = np.zeros((t + 1, 1, 16))
+    T = O.block_teacher(q, k, t, 0.1)
+    np.testing.assert_allclose(T[:-1], 4.0 / (t + 1), rtol=1e-12)
+    assert T[-1] == pytest.approx((t % 4 + 1) / (t + 1), rel=1e-12)
+
+
+def test_recall_is_the_lse_gap_and_one_for_short_contexts():
+    # the teacher mass on the attended tokens, per head, is exp(lse_sparse -
+    # lse_dense): the attention oracle's two log-sum-exps give it independently
+    w = W.make_custom(71, [3000], 3, 8, 2)
+    res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, w.n_query)
+    dense = O.dense_decode(w.q, w.k, w.v, w.lens, w.n_query)
+    kr = O.bf16_bits_to_f64(w.k[0])
+    for i in range(3):
+        t = 3000 - 3 + i
+        qi = O.bf16_bits_to_f64(w.q[0, i])
+        T = O.block_teacher(qi, kr, t, w.scale)
+        rec = O.selection_recall(T, res["sel"][(0, i)])
+        via_lse = float(np.mean(np.exp(res["lse"][(0, i)] - dense[(0, i)][1])))
+        assert 0.0 < rec < 1.0
+        assert rec == pytest.approx(via_lse, rel=1e-9)
+    short = W.make_custom(72, [2052], 2, 8, 1)
+    r2 = O.qsa_forward(short.q_idx, short.k_idx, short.q, short.k, short.v, short.lens, 2)
+    for i in range(2):
+        t = 2050 + i
+        T = O.block_teacher(O.bf16_bits_to_f64(short.q[0, i]), O.bf16_bits_to_f64(short.k[0]), t,
+                            short.scale)
+        assert O.selection_recall(T, r2["sel"][(0, i)]) == pytest.approx(1.0, abs=1e-12)
+
+
+def test_needle_survival_counts_kept_planted_blocks():
+    sel = np.array([3, 5, 9, 40, 41])
+    assert O.needle_survival(sel, [40, 41, 42, 43]) == 0.5
+    assert O.needle_survival(sel, []) == 1.0
+    assert O.needle_survival(sel, [5]) == 1.0
