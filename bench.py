@@ -319,8 +319,34 @@ def decode_leg(args, Q, W, torch, np, flush):
                        "the own block; random synthetic keys, so the mass is spread thinly"}
     del teacher
     torch.cuda.empty_cache()
+    # backward passes on the same batch: the sparse attention's gradients
+    # (dk/dv added into zeroed float32 caches) and the indexer scores'
+    # gradient for a dense dL/ds
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    d_out = torch.randn(ws.out.shape, generator=g, device="cuda").to(torch.bfloat16)
+    d_s = torch.randn((w.batch, w.n_query, w.max_len // 4), generator=g, device="cuda")
+    dk = torch.zeros(ws.dev["k"].shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    dq_idx = torch.zeros(ws.dev["q_idx"].shape, dtype=torch.float32, device="cuda")
+    dk_cmp = torch.zeros(ws.k_cmp.shape, dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    Q.sparse_attend_backward(ws.shp, ws.dev["q"], ws.dev["k"], ws.dev["v"], ws.lens, ws.sel,
+                             ws.n_sel, ws.out, ws.lse, d_out, dk=dk, dv=dv)
+    ev[1].record()
+    Q.index_scores_backward(ws.shp, ws.dev["q_idx"], ws.k_cmp, ws.lens, d_s, dq_idx=dq_idx,
+                            dk_cmp=dk_cmp)
+    ev[2].record()
+    torch.cuda.synchronize()
+    backward = {"attend_backward_us": 1000 * ev[0].elapsed_time(ev[1]),
+                "index_scores_backward_us": 1000 * ev[1].elapsed_time(ev[2]),
+                "note": "one call each on the decode batch, caches warm; float32 vector math, "
+                        "dk/dv and dk_cmp added atomically"}
+    del d_out, d_s, dk, dv, dq_idx, dk_cmp
+    torch.cuda.empty_cache()
     return dict(w=w, ws=ws, step_ms=step_ms, kstats=kstats, wall=wall, sel=sel_h, n_sel=nsel_h,
-                quality=quality,
+                quality=quality, backward=backward,
                 algo=decode_algo(kcmp, attn, qidx, w.batch), kcmp_bytes=kcmp, attn_bytes=attn,
                 qidx_bytes=qidx,
                 cold={"ms_per_step": sum(cold_ms) / len(cold_ms), "steps": len(cold_ms),
@@ -823,6 +849,7 @@ def main(argv=None):
         "kernels": d["kstats"],
         "cold": d["cold"],
         "selection_quality": d["quality"],
+        "backward": d["backward"],
     }
     if not args.no_dense:
         log("[bench] dense comparator")

@@ -231,6 +231,46 @@ qsa_status qsa_teacher_recall(const qsa_shape* shape, const int32_t* lens, const
                               const int32_t* sel, const int32_t* n_sel, float* recall,
                               void* stream);
 
+/* Backward passes: the indexer and the model are trained together (section
+ * "The indexer is trained, not bolted on"), so the sparse attention and the
+ * indexer's scoring have gradients.  Float32 arithmetic; gradients of K, V,
+ * k_cmp and k_idx are ADDED into caller-zeroed float32 buffers (atomically:
+ * the last bits may vary from run to run), so chunks of a sequence can
+ * accumulate into one buffer.
+ *
+ * qsa_sparse_attend_backward: given the forward's selection (sel, n_sel), its
+ * output `out` (bf16) and log-sum-exp `lse`, and d_out = dL/dout (bf16, the
+ * layout of out), over each query's token list (as qsa_sparse_attend):
+ *   dq[h]  = scale sum_s ds_s k_s            (written, float [B][Nq][Hq][128])
+ *   dk[s] += scale sum_h ds_s q_h, dv[s] += sum_h p_s d_out_h
+ *                                             (added, float [B][Lmax][Hkv][128])
+ * with p the attention weights, ds_s = p_s (d_out_h . v_s - d_out_h . out_h). */
+qsa_status qsa_sparse_attend_backward(const qsa_shape* shape, const uint16_t* q,
+                                      const uint16_t* k, const uint16_t* v, const int32_t* lens,
+                                      const int32_t* sel, const int32_t* n_sel,
+                                      const uint16_t* out, const float* lse,
+                                      const uint16_t* d_out, float* dq, float* dk, float* dv,
+                                      void* stream);
+
+/* qsa_index_scores_backward: given d_scores = dL/ds (float [B][Nq][Lmax/4],
+ * entries of each query's candidate blocks j < floor(t/4) read, others
+ * ignored) of the indexer scores s_j = sum_h max(0, q_idx[h] . k_cmp[j]):
+ *   dq_idx[h] += sum_j d_scores_j [q_idx[h] . k_cmp[j] > 0] k_cmp[j]
+ *                                            (added, float [B][Nq][4][64])
+ *   dk_cmp[j] += sum_i sum_h d_scores_ij [q_ih . k_cmp[j] > 0] q_ih
+ *                                            (added, float [B][Lmax/4][64]). */
+qsa_status qsa_index_scores_backward(const qsa_shape* shape, const uint16_t* q_idx,
+                                     const uint16_t* k_cmp, const int32_t* lens,
+                                     const float* d_scores, float* dq_idx, float* dk_cmp,
+                                     void* stream);
+
+/* qsa_compress_keys_backward: the compressed key is the sum of its block's
+ * four token keys (section "A million-token window with a selective view"),
+ * so dk_idx[b][4j + r] += dk_cmp[b][j] for r < 4 and every completed block
+ * j < lens[b]/4 (float [B][Lmax][64] and [B][Lmax/4][64]). */
+qsa_status qsa_compress_keys_backward(const qsa_shape* shape, const int32_t* lens,
+                                      const float* dk_cmp, float* dk_idx, void* stream);
+
 /* Kernel timing hook, for benchmarks and profilers (not part of the method).
  * qsa_profile_attach hands the library n_events caller-created hipEvent_t
  * handles (created with timing enabled, owned by the caller).  From then on,

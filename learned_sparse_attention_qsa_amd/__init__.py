@@ -49,6 +49,9 @@ EXPORTS = (
     "qsa_dense_gqa_decode",
     "qsa_block_teacher",
     "qsa_teacher_recall",
+    "qsa_sparse_attend_backward",
+    "qsa_index_scores_backward",
+    "qsa_compress_keys_backward",
     "qsa_profile_attach",
     "qsa_profile_detach",
     "qsa_profile_kernel_name",
@@ -103,7 +106,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.qsa_block_teacher.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_teacher_recall.argtypes = [sp, vp, vp, vp, vp, vp, vp]
-    for name in EXPORTS[2:11]:
+    lib.qsa_sparse_attend_backward.argtypes = [sp] + [vp] * 13
+    lib.qsa_index_scores_backward.argtypes = [sp] + [vp] * 7
+    lib.qsa_compress_keys_backward.argtypes = [sp, vp, vp, vp, vp]
+    for name in EXPORTS[2:14]:
         getattr(lib, name).restype = i32
     lib.qsa_profile_attach.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.qsa_profile_attach.restype = i32
@@ -395,6 +401,79 @@ def teacher_recall(shp: QsaShape, lens, teacher, sel, n_sel, recall=None):
                                            _p(n_sel), _p(recall), _stream(dev))
     _check(st, "qsa_teacher_recall")
     return recall
+
+
+def _f32(t, name, shape_):
+    _need(t, name, shape_, (torch.float32,))
+
+
+def sparse_attend_backward(shp: QsaShape, q, k, v, lens, sel, n_sel, out, lse, d_out,
+                           dq=None, dk=None, dv=None):
+    """qsa_sparse_attend_backward.  dq is written; dk and dv (float32) are
+    added into (zero-filled here when not given).  Returns (dq, dk, dv)."""
+    B, L, Nq, Hq, Hkv = shp.batch, shp.max_len, shp.n_query, shp.q_heads, shp.kv_heads
+    dev = q.device
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    _need(k, "k", (B, L, Hkv, HEAD_DIM), _BF)
+    _need(v, "v", (B, L, Hkv, HEAD_DIM), _BF)
+    _need(lens, "lens", (B,), _I32)
+    _need(sel, "sel", (B, Nq, TOPK), _I32)
+    _need(n_sel, "n_sel", (B, Nq), _I32)
+    _need(out, "out", (B, Nq, Hq, HEAD_DIM), _BF)
+    _f32(lse, "lse", (B, Nq, Hq))
+    _need(d_out, "d_out", (B, Nq, Hq, HEAD_DIM), _BF)
+    if dq is None:
+        dq = torch.empty((B, Nq, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros((B, L, Hkv, HEAD_DIM), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.zeros((B, L, Hkv, HEAD_DIM), dtype=torch.float32, device=dev)
+    _f32(dq, "dq", (B, Nq, Hq, HEAD_DIM))
+    _f32(dk, "dk", (B, L, Hkv, HEAD_DIM))
+    _f32(dv, "dv", (B, L, Hkv, HEAD_DIM))
+    st = load_library().qsa_sparse_attend_backward(
+        ctypes.byref(shp), _p(q), _p(k), _p(v), _p(lens), _p(sel), _p(n_sel), _p(out), _p(lse),
+        _p(d_out), _p(dq), _p(dk), _p(dv), _stream(dev))
+    _check(st, "qsa_sparse_attend_backward")
+    return dq, dk, dv
+
+
+def index_scores_backward(shp: QsaShape, q_idx, k_cmp, lens, d_scores, dq_idx=None,
+                          dk_cmp=None):
+    """qsa_index_scores_backward; dq_idx and dk_cmp (float32) are added into
+    (zero-filled here when not given).  Returns (dq_idx, dk_cmp)."""
+    B, L, Nq = shp.batch, shp.max_len, shp.n_query
+    dev = q_idx.device
+    _need(q_idx, "q_idx", (B, Nq, IDX_HEADS, IDX_DIM), _BF)
+    _need(k_cmp, "k_cmp", (B, L // BLOCK, IDX_DIM), _BF)
+    _need(lens, "lens", (B,), _I32)
+    _f32(d_scores, "d_scores", (B, Nq, L // BLOCK))
+    if dq_idx is None:
+        dq_idx = torch.zeros((B, Nq, IDX_HEADS, IDX_DIM), dtype=torch.float32, device=dev)
+    if dk_cmp is None:
+        dk_cmp = torch.zeros((B, L // BLOCK, IDX_DIM), dtype=torch.float32, device=dev)
+    _f32(dq_idx, "dq_idx", (B, Nq, IDX_HEADS, IDX_DIM))
+    _f32(dk_cmp, "dk_cmp", (B, L // BLOCK, IDX_DIM))
+    st = load_library().qsa_index_scores_backward(ctypes.byref(shp), _p(q_idx), _p(k_cmp),
+                                                  _p(lens), _p(d_scores), _p(dq_idx),
+                                                  _p(dk_cmp), _stream(dev))
+    _check(st, "qsa_index_scores_backward")
+    return dq_idx, dk_cmp
+
+
+def compress_keys_backward(shp: QsaShape, lens, dk_cmp, dk_idx=None):
+    """qsa_compress_keys_backward; dk_idx (float32) is added into."""
+    B, L = shp.batch, shp.max_len
+    dev = dk_cmp.device
+    _need(lens, "lens", (B,), _I32)
+    _f32(dk_cmp, "dk_cmp", (B, L // BLOCK, IDX_DIM))
+    if dk_idx is None:
+        dk_idx = torch.zeros((B, L, IDX_DIM), dtype=torch.float32, device=dev)
+    _f32(dk_idx, "dk_idx", (B, L, IDX_DIM))
+    st = load_library().qsa_compress_keys_backward(ctypes.byref(shp), _p(lens), _p(dk_cmp),
+                                                   _p(dk_idx), _stream(dev))
+    _check(st, "qsa_compress_keys_backward")
+    return dk_idx
 
 
 class KernelTimer:

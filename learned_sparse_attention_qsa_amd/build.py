@@ -24,6 +24,7 @@ HIP_FLAGS = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-result"]
 SOURCES = ["compress.hip", "expand.hip", "topk.hip", "attend.hip", "ceilings.hip", "noalloc.hip",
+           "backward.hip",
            "api.cpp"]
 # The stream scorer's MFMA results are read by a vector epilogue every tile:
 # the VGPR form of MFMA keeps them out of accumulation registers (no

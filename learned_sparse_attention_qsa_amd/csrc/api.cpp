@@ -401,4 +401,65 @@ qsa_status qsa_teacher_recall(const qsa_shape* shape, const int32_t* lens, const
   return hip_status(qsa::launch_teacher_recall(d, teacher, lens, sel, n_sel, recall, s));
 }
 
+qsa_status qsa_sparse_attend_backward(const qsa_shape* shape, const uint16_t* q,
+                                      const uint16_t* k, const uint16_t* v, const int32_t* lens,
+                                      const int32_t* sel, const int32_t* n_sel,
+                                      const uint16_t* out, const float* lse,
+                                      const uint16_t* d_out, float* dq, float* dk, float* dv,
+                                      void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(sel));
+  QSA_TRY(need_i32(n_sel));
+  QSA_TRY(need(out));
+  QSA_TRY(need_i32(lse));
+  QSA_TRY(need(d_out));
+  QSA_TRY(need(dq));
+  QSA_TRY(need(dk));
+  QSA_TRY(need(dv));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(
+      qsa::launch_sparse_attend_bwd(d, q, k, v, lens, sel, n_sel, out, lse, d_out, dq, dk, dv, s));
+}
+
+qsa_status qsa_index_scores_backward(const qsa_shape* shape, const uint16_t* q_idx,
+                                     const uint16_t* k_cmp, const int32_t* lens,
+                                     const float* d_scores, float* dq_idx, float* dk_cmp,
+                                     void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  QSA_TRY(need(q_idx));
+  QSA_TRY(need(k_cmp));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(d_scores));
+  QSA_TRY(need(dq_idx));
+  QSA_TRY(need(dk_cmp));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_index_scores_bwd(d, q_idx, k_cmp, lens, d_scores, dq_idx, dk_cmp, s));
+}
+
+qsa_status qsa_compress_keys_backward(const qsa_shape* shape, const int32_t* lens,
+                                      const float* dk_cmp, float* dk_idx, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0) return QSA_OK;
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(dk_cmp));
+  QSA_TRY(need(dk_idx));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_compress_bwd(d, dk_cmp, lens, dk_idx, s));
+}
+
 }  // extern "C"

@@ -74,6 +74,18 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
                                const uint16_t* v, const int32_t* lens, uint16_t* out,
                                float* lse, void* ws, hipStream_t s);
 
+// ---- backward.hip
+hipError_t launch_sparse_attend_bwd(const Dims& d, const uint16_t* q, const uint16_t* k,
+                                    const uint16_t* v, const int32_t* lens, const int32_t* sel,
+                                    const int32_t* n_sel, const uint16_t* out, const float* lse,
+                                    const uint16_t* d_out, float* dq, float* dk, float* dv,
+                                    hipStream_t s);
+hipError_t launch_index_scores_bwd(const Dims& d, const uint16_t* q_idx, const uint16_t* k_cmp,
+                                   const int32_t* lens, const float* g_scores, float* dq_idx,
+                                   float* dk_cmp, hipStream_t s);
+hipError_t launch_compress_bwd(const Dims& d, const float* dk_cmp, const int32_t* lens,
+                               float* dk_idx, hipStream_t s);
+
 // Profiling hook: when a caller has attached HIP events (qsa_profile_attach),
 // profile_events hands out the next start/stop pair and every launch carries
 // them in its own dispatch packet, so the recorded interval is the kernel's

@@ -14,4 +14,5 @@ from .qsa_oracle import (  # noqa: F401
     attend, query_positions, qsa_forward, dense_decode,
     block_scores_rows, select_blocks_rows, select_rows,
     block_teacher, selection_recall, needle_survival,
+    attend_backward, block_scores_backward, compress_keys_backward,
 )

@@ -380,3 +380,58 @@ def needle_survival(sel: np.ndarray, needle_blocks) -> float:
     if nb.size == 0:
         return 1.0
     return float(np.isin(nb, np.asarray(sel, dtype=np.int64)).mean())
+
+
+# --------------------------------------------------------------------------
+# Gradients (the indexer and the backbone are trained together)
+# --------------------------------------------------------------------------
+
+def attend_backward(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, d_out: np.ndarray,
+                    scale: float):
+    """Gradient of attend()'s output o with respect to q, the gathered k rows
+    and the gathered v rows, given d_out = dL/do (float64 [Hq][D]).
+
+    The indexer and the model are trained together (page "Qwen's million-token
+    window has a 2,048-token keyhole", section "The indexer is trained, not
+    bolted on"), so the sparse attention needs its backward pass; it is the
+    softmax-attention gradient over the gathered rows only: with p the softmax
+    of z = scale q_h . k_s, dp_s = d_out_h . v_s and ds_s = p_s (dp_s -
+    sum_r p_r dp_r),
+      dq_h = scale sum_s ds_s k_s,  dk_s += scale ds_s q_h,  dv_s += p_s d_out_h
+    (query head h reading KV head floor(h / (Hq / Hkv))).
+    Returns (dq [Hq][D], dk [n][Hkv][D], dv [n][Hkv][D]).
+    """
+    hq, hkv = q.shape[0], k_rows.shape[1]
+    group = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k_rows)
+    dv = np.zeros_like(v_rows)
+    for h in range(hq):
+        g = h // group
+        z = scale * (k_rows[:, g, :] @ q[h])
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        dp = v_rows[:, g, :] @ d_out[h]
+        ds = p * (dp - np.dot(p, dp))
+        dq[h] = scale * (ds @ k_rows[:, g, :])
+        dk[:, g, :] += scale * np.outer(ds, q[h])
+        dv[:, g, :] += np.outer(p, d_out[h])
+    return dq, dk, dv
+
+
+def block_scores_backward(q_idx: np.ndarray, kc: np.ndarray, g: np.ndarray):
+    """Gradient of block_scores() (s_j = sum_h max(0, q_h . kc_j)) given
+    g = dL/ds (float64 [n]): dq_h = sum_j g_j [q_h . kc_j > 0] kc_j and
+    dkc_j = sum_h g_j [q_h . kc_j > 0] q_h (the ReLU's derivative taken as 0
+    at 0).  Returns (dq [4][64], dkc [n][64])."""
+    per_head = kc @ q_idx.T                      # [n][4]
+    w = (per_head > 0.0) * g[:, None]            # [n][4]
+    return w.T @ kc, w @ q_idx
+
+
+def compress_keys_backward(d_kc: np.ndarray) -> np.ndarray:
+    """Gradient of compress_keys()'s sum with respect to the token keys: each
+    of a block's four keys receives the block's gradient (the bf16 rounding
+    is taken as the identity, as it is for the configurations' exact sums).
+    d_kc: float64 [m][64] -> [4m][64]."""
+    return np.repeat(d_kc, BLOCK, axis=0)

@@ -440,3 +440,75 @@ def test_needle_survival_counts_kept_planted_blocks():
     assert O.needle_survival(sel, [40, 41, 42, 43]) == 0.5
     assert O.needle_survival(sel, []) == 1.0
     assert O.needle_survival(sel, [5]) == 1.0
+
+
+# ---------------------------------------------------------------- gradients
+
+def _fd(f, x, eps=1e-6):
+    """Central finite differences of a scalar function of an array."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp, xm = x.copy(), x.copy()
+        xp[i] += eps
+        xm[i] -= eps
+        g[i] = (f(xp) - f(xm)) / (2 * eps)
+    return g
+
+
+def test_attend_backward_finite_differences():
+    rng = np.random.default_rng(80)
+    hq, hkv, n, d = 4, 2, 7, 6
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    v = rng.standard_normal((n, hkv, d))
+    do = rng.standard_normal((hq, d))
+    scale = 0.7
+    dq, dk, dv = O.attend_backward(q, k, v, do, scale)
+    loss = lambda qq, kk, vv: float(np.sum(O.attend(qq, kk, vv, scale)[0] * do))
+    np.testing.assert_allclose(dq, _fd(lambda x: loss(x, k, v), q), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dk, _fd(lambda x: loss(q, x, v), k), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dv, _fd(lambda x: loss(q, k, x), v), rtol=1e-6, atol=1e-8)
+
+
+def test_attend_backward_matches_torch_autograd():
+    rng = np.random.default_rng(81)
+    hq, hkv, n, d = 8, 2, 40, 16
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    v = rng.standard_normal((n, hkv, d))
+    do = rng.standard_normal((hq, d))
+    scale = 0.25
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    kk = tk.repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2)   # [hq][n][d]
+    vv = tv.repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2)
+    p = torch.softmax(scale * torch.einsum("hd,hnd->hn", tq, kk), dim=-1)
+    o = torch.einsum("hn,hnd->hd", p, vv)
+    o.backward(torch.tensor(do))
+    dq, dk, dv = O.attend_backward(q, k, v, do, scale)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_block_scores_backward_finite_differences():
+    rng = np.random.default_rng(82)
+    q = rng.standard_normal((4, 8))
+    kc = rng.standard_normal((11, 8))
+    g = rng.standard_normal(11)
+    dq, dkc = O.block_scores_backward(q, kc, g)
+    loss = lambda qq, kk: float(np.dot(O.block_scores(qq, kk), g))
+    np.testing.assert_allclose(dq, _fd(lambda x: loss(x, kc), q), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dkc, _fd(lambda x: loss(q, x), kc), rtol=1e-6, atol=1e-8)
+
+
+def test_compress_backward_is_the_sum_adjoint():
+    # <compress(k), a> = <k, compress_backward(a)> for any k, a (exact sums)
+    rng = np.random.default_rng(83)
+    k = rng.integers(-8, 9, (40, 64)).astype(np.float64)
+    a = rng.standard_normal((10, 64))
+    kc = O.bf16_bits_to_f64(O.compress_keys(bf16(k), 40))
+    assert np.sum(kc * a) == pytest.approx(np.sum(k * O.compress_keys_backward(a)), rel=1e-12)
