@@ -67,6 +67,10 @@ def parse(argv=None):
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--cold-steps", type=int, default=3)
+    ap.add_argument("--dense-prefill-steps", type=int, default=2)
+    ap.add_argument("--page-size", type=int, default=16,
+                    help="tokens per page of the paged K/V legs")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged K/V legs")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     ap.add_argument("--no-configs", action="store_true", help="skip the other three workloads")
@@ -379,6 +383,145 @@ def dense_leg(args, Q, torch, flush, d):
                                                                      "context")})}
 
 
+def paged_pools(Q, torch, k, v, lens, page, seed):
+    """Page pools [n_pages][page][Hkv][128] holding the contiguous caches k, v
+    under a seeded random page order, and their page table: the layout a
+    paged serving cache leaves after many sequences have come and gone."""
+    B, L, Hkv, D = k.shape
+    max_pages = (L + page - 1) // page
+    need = [(int(n) + page - 1) // page for n in lens]
+    n_pages = max(1, sum(need))
+    g = torch.Generator().manual_seed(seed)
+    ids = torch.randperm(n_pages, generator=g).to(torch.int64)
+    table = torch.zeros((B, max_pages), dtype=torch.int32)
+    k_pool = torch.empty((n_pages, page, Hkv, D), dtype=k.dtype, device=k.device)
+    v_pool = torch.empty_like(k_pool)
+    off = 0
+    for b in range(B):
+        n, full = need[b], int(lens[b]) // page
+        pid = ids[off:off + n]
+        off += n
+        table[b, :n] = pid.to(torch.int32)
+        if full:
+            idx = pid[:full].to(k.device)
+            k_pool[idx] = k[b, :full * page].view(full, page, Hkv, D)
+            v_pool[idx] = v[b, :full * page].view(full, page, Hkv, D)
+        if n > full:  # the last, partial page
+            rest = int(lens[b]) - full * page
+            k_pool[int(pid[full]), :rest] = k[b, full * page:full * page + rest]
+            v_pool[int(pid[full]), :rest] = v[b, full * page:full * page + rest]
+    torch.cuda.synchronize()
+    return k_pool, v_pool, Q.PagedKV(table.to(k.device), page, n_pages)
+
+
+def paged_decode_leg(args, Q, torch, flush, d, qsa_ms, dense_ms):
+    """The decode batch with K/V in page pools: QSA forward and the dense
+    decode comparator, both through the page table (the pages' comparison
+    is against paged GQA)."""
+    ws_ = d["ws"]
+    w = d["w"]
+    shp, dev, lens = ws_.shp, ws_.dev, ws_.lens
+    page = args.page_size
+    k_pool, v_pool, pg = paged_pools(Q, torch, dev["k"], dev["v"], w.lens, page, 77)
+
+    def qsa():
+        Q.forward_paged(shp, dev["q_idx"], dev["k_idx"], ws_.k_cmp, dev["q"], k_pool, v_pool, pg,
+                        lens, first_block=ws_.first, out=ws_.out, lse=ws_.lse, sel=ws_.sel,
+                        n_sel=ws_.n_sel, ws=ws_.ws)
+
+    for _ in range(3):
+        flush()
+        qsa()
+    torch.cuda.synchronize()
+    q_ms, q_k, _ = timed_steps(qsa, min(args.steps, 50), flush, Q, torch)
+    res = {"page_size": page, "n_pages": pg.n_pages,
+           "qsa": {"ms_per_step": sum(q_ms) / len(q_ms), "steps": len(q_ms), "kernels": q_k}}
+    res["qsa"]["vs_contiguous"] = res["qsa"]["ms_per_step"] / qsa_ms
+    if dense_ms is not None:
+        wsp = Q.workspace(shp, Q.OP_DENSE_DECODE)
+        out = torch.empty_like(ws_.out)
+
+        def dense():
+            Q.dense_gqa_decode_paged(shp, dev["q"], k_pool, v_pool, pg, lens, out=out, ws=wsp,
+                                     want_lse=False)
+
+        flush()
+        dense()
+        torch.cuda.synchronize()
+        dn_ms, dn_k, _ = timed_steps(dense, args.dense_steps, flush, Q, torch)
+        ms = sum(dn_ms) / len(dn_ms)
+        kv_bytes = int(sum(int(l) for l in w.lens)) * w.kv_heads * 128 * 2 * 2
+        res["dense"] = {"ms_per_step": ms, "kernels": dn_k, "hbm_gbs": kv_bytes / (ms * 1e-3) / 1e9,
+                        "vs_contiguous": ms / dense_ms}
+        res["qsa_speedup"] = ms / res["qsa"]["ms_per_step"]
+    del k_pool, v_pool, pg
+    torch.cuda.empty_cache()
+    return res
+
+
+def dense_prefill_flops(w, np):
+    """Dense causal attention of the chunk: (t + 1) tokens per query and head,
+    QK^T and PV at 2 x 128 flop each per (head, token)."""
+    tot = 0
+    for b in range(w.batch):
+        t = int(w.lens[b]) - w.n_query + np.arange(w.n_query, dtype=np.int64)
+        tot += int((t + 1).sum())
+    return tot * w.q_heads * 128 * 4
+
+
+def dense_prefill_leg(args, Q, torch, np, flush, ws, w, qsa_ms):
+    """Dense causal GQA over the prefill chunk (the comparator of the pages'
+    prefill speedup), contiguous and paged, and the QSA forward over the same
+    page pools."""
+    shp, dev, lens = ws.shp, ws.dev, ws.lens
+    out = torch.empty_like(ws.out)
+    flops = dense_prefill_flops(w, np)
+    n = args.dense_prefill_steps
+    res = {"flops": flops}
+
+    def record(step):
+        flush()
+        step()
+        torch.cuda.synchronize()
+        ms_, k_, _ = timed_steps(step, n, flush, Q, torch)
+        ms = sum(ms_) / len(ms_)
+        rec = {"ms_per_step": ms, "steps": len(ms_), "kernels": k_}
+        st = k_.get("dense_prefill_kernel")
+        if st:
+            ach = flops / (st["avg_us"] * 1e-6) / 1e12
+            rec["mfma"] = {"kernel": "dense_prefill_kernel", "achieved": ach,
+                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / MFMA_BF16_PEAK_TFLOPS}
+        return rec
+
+    log(f"[bench] {w.name}: dense prefill comparator, contiguous")
+    res["contiguous"] = record(lambda: Q.dense_gqa_prefill(shp, dev["q"], dev["k"], dev["v"], lens,
+                                                           out=out, want_lse=False))
+    res["qsa_speedup"] = res["contiguous"]["ms_per_step"] / qsa_ms
+    if not args.no_paged:
+        log(f"[bench] {w.name}: paged ({args.page_size}-token pages)")
+        k_pool, v_pool, pg = paged_pools(Q, torch, dev["k"], dev["v"], w.lens, args.page_size, 78)
+        res["page_size"] = args.page_size
+        res["paged"] = record(lambda: Q.dense_gqa_prefill(shp, dev["q"], k_pool, v_pool, lens,
+                                                          paged=pg, out=out, want_lse=False))
+
+        def qsa():
+            Q.forward_paged(shp, dev["q_idx"], dev["k_idx"], ws.k_cmp, dev["q"], k_pool, v_pool,
+                            pg, lens, first_block=ws.first, out=ws.out, lse=ws.lse, sel=ws.sel,
+                            n_sel=ws.n_sel, ws=ws.ws)
+
+        flush()
+        qsa()
+        torch.cuda.synchronize()
+        q_ms, q_k, _ = timed_steps(qsa, args.prefill_steps, flush, Q, torch)
+        res["qsa_paged"] = {"ms_per_step": sum(q_ms) / len(q_ms), "steps": len(q_ms),
+                            "kernels": q_k}
+        res["qsa_paged_speedup"] = res["paged"]["ms_per_step"] / res["qsa_paged"]["ms_per_step"]
+        del k_pool, v_pool, pg
+        torch.cuda.empty_cache()
+    return res
+
+
 def prefill_record(w, step_ms, kstats, np):
     idx_flops, attn_flops = prefill_work(w, np)
     ms = sum(step_ms) / len(step_ms)
@@ -427,6 +570,9 @@ def prefill_leg(args, Q, W, torch, np, flush, cfg=3, steps=None):
             hit[i] = np.isin(blocks, sel_h[i, :nsel_h[i]]).mean()
         res["needle_survival"] = {"mean": float(hit.mean()), "min": float(hit.min()),
                                   "spans": len(w.needle_starts[0]), "blocks": int(blocks.size)}
+    if not args.no_dense:
+        res["dense_comparator"] = dense_prefill_leg(args, Q, torch, np, flush, ws, w,
+                                                    res["ms_per_step"])
     del ws
     torch.cuda.empty_cache()
     return res, w
@@ -856,6 +1002,10 @@ def main(argv=None):
         dn = dense_leg(args, Q, torch, flush, d)
         dn["qsa_speedup"] = dn["ms_per_step"] / ms
         line["dense"] = dn
+    if not args.no_paged:
+        log(f"[bench] paged K/V ({args.page_size}-token pages): QSA and the dense comparator")
+        line["paged"] = paged_decode_leg(args, Q, torch, flush, d, ms,
+                                         None if args.no_dense else line["dense"]["ms_per_step"])
     d_light = {k: d[k] for k in ("w", "sel", "n_sel")}
     del d
     torch.cuda.empty_cache()

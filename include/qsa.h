@@ -204,6 +204,61 @@ qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q,
                                 const int32_t* lens, uint16_t* out, float* lse,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Paged K/V (the pages' speed baseline attends over a paged cache, section
+ * "Three speed claims, three different experiments").  The core K and V of
+ * all sequences live in pools of fixed-size pages, [n_pages][page_size][Hkv]
+ * [128] bf16 each; token tok of sequence b is row tok mod page_size of page
+ * page_table[b * max_pages + tok / page_size].  page_size is a power of two
+ * in [1, 2^20]; max_pages * page_size >= Lmax; n_pages * page_size
+ * < 2^31 (pool rows are 32-bit indices); page ids must lie in
+ * [0, n_pages) (an id outside it is clamped: the read stays inside the pool
+ * but returns another page).  Only pages holding tokens < lens[b] are read.
+ * page_table is device memory owned by the caller.  The indexer caches
+ * (k_idx, k_cmp) stay per sequence, as in qsa_forward. */
+typedef struct {
+  const int32_t* page_table; /* [B][max_pages] int32, device */
+  int32_t page_size;         /* tokens per page */
+  int32_t max_pages;         /* page-table entries per sequence */
+  int32_t n_pages;           /* pages in each pool */
+} qsa_paged_kv;
+
+/* qsa_sparse_attend over paged K/V: same selection, math and outputs; k and
+ * v are the page pools.  Workspace: QSA_OP_SPARSE_ATTEND. */
+qsa_status qsa_sparse_attend_paged(const qsa_shape* shape, const uint16_t* q,
+                                   const uint16_t* k_pool, const uint16_t* v_pool,
+                                   const qsa_paged_kv* kv, const int32_t* lens,
+                                   const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* qsa_forward over paged K/V: same arguments and results, K and V read
+ * through the page table.  Workspace: QSA_OP_FORWARD. */
+qsa_status qsa_forward_paged(const qsa_shape* shape, const uint16_t* q_idx,
+                             const uint16_t* k_idx, uint16_t* k_cmp, const int32_t* first_block,
+                             const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const qsa_paged_kv* kv, const int32_t* lens, uint16_t* out,
+                             float* lse, int32_t* sel_out, int32_t* n_sel_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* qsa_dense_gqa_decode over paged K/V (the comparator as the pages run it).
+ * Workspace: QSA_OP_DENSE_DECODE. */
+qsa_status qsa_dense_gqa_decode_paged(const qsa_shape* shape, const uint16_t* q,
+                                      const uint16_t* k_pool, const uint16_t* v_pool,
+                                      const qsa_paged_kv* kv, const int32_t* lens,
+                                      uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/* Comparator for a prefill chunk: dense causal GQA over positions 0..t of
+ * each of the Nq queries (the pages compare a prefill chunk of the attention
+ * module against paged GQA, section "Three speed claims, three different
+ * experiments").  Same math and layouts as qsa_dense_gqa_decode, organised
+ * for many queries: each workgroup stages K/V tiles once for up to 256
+ * (query, head) columns of one KV head.  kv NULL: k and v are the contiguous
+ * caches [B][Lmax][Hkv][128]; otherwise the page pools of *kv.  No
+ * workspace; lse may be NULL. */
+qsa_status qsa_dense_gqa_prefill(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const qsa_paged_kv* kv,
+                                 const int32_t* lens, uint16_t* out, float* lse, void* stream);
+
 /* The indexer's training target: the indexer is trained together with the
  * model and learns from the full-attention distribution (page "Qwen's
  * million-token window has a 2,048-token keyhole", section "The indexer is

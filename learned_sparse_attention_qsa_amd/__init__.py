@@ -47,6 +47,10 @@ EXPORTS = (
     "qsa_forward",
     "qsa_forward_noalloc",
     "qsa_dense_gqa_decode",
+    "qsa_sparse_attend_paged",
+    "qsa_forward_paged",
+    "qsa_dense_gqa_decode_paged",
+    "qsa_dense_gqa_prefill",
     "qsa_block_teacher",
     "qsa_teacher_recall",
     "qsa_sparse_attend_backward",
@@ -71,6 +75,31 @@ class QsaShape(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
     ]
+
+
+class QsaPagedKV(ctypes.Structure):
+    _fields_ = [
+        ("page_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32),
+    ]
+
+
+class PagedKV:
+    """A page table (device int32 [B][max_pages]) over K/V page pools
+    [n_pages][page_size][Hkv][128]; keeps the table tensor alive."""
+
+    def __init__(self, page_table: torch.Tensor, page_size: int, n_pages: int):
+        if page_table.dtype != torch.int32 or page_table.dim() != 2:
+            raise ValueError("page_table must be int32 [B][max_pages]")
+        if not page_table.is_contiguous():
+            raise ValueError("page_table must be contiguous")
+        self.page_table = page_table
+        self.page_size = int(page_size)
+        self.n_pages = int(n_pages)
+        self.c = QsaPagedKV(page_table.data_ptr(), self.page_size, page_table.shape[1],
+                            self.n_pages)
 
 
 class QsaError(RuntimeError):
@@ -104,12 +133,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_dense_gqa_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    pp = ctypes.POINTER(QsaPagedKV)
+    lib.qsa_sparse_attend_paged.argtypes = [sp, vp, vp, vp, pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_forward_paged.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.qsa_dense_gqa_decode_paged.argtypes = [sp, vp, vp, vp, pp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_dense_gqa_prefill.argtypes = [sp, vp, vp, vp, pp, vp, vp, vp, vp]
     lib.qsa_block_teacher.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qsa_teacher_recall.argtypes = [sp, vp, vp, vp, vp, vp, vp]
     lib.qsa_sparse_attend_backward.argtypes = [sp] + [vp] * 13
     lib.qsa_index_scores_backward.argtypes = [sp] + [vp] * 7
     lib.qsa_compress_keys_backward.argtypes = [sp, vp, vp, vp, vp]
-    for name in EXPORTS[2:14]:
+    for name in EXPORTS[2:18]:
         getattr(lib, name).restype = i32
     lib.qsa_profile_attach.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.qsa_profile_attach.restype = i32
@@ -338,6 +373,112 @@ def dense_gqa_decode(shp: QsaShape, q, k, v, lens, out=None, lse=None, ws=None,
     st = load_library().qsa_dense_gqa_decode(ctypes.byref(shp), _p(q), _p(k), _p(v), _p(lens),
                                              _p(out), _p(lse), _p(ws), nb, _stream(dev))
     _check(st, "qsa_dense_gqa_decode")
+    return out, lse
+
+
+def _need_pools(k, v, paged: PagedKV, shp: QsaShape) -> None:
+    pool = (paged.n_pages, paged.page_size, shp.kv_heads, HEAD_DIM)
+    _need(k, "k_pool", pool, _BF)
+    _need(v, "v_pool", pool, _BF)
+    _need(paged.page_table, "page_table", (shp.batch, paged.page_table.shape[1]), _I32)
+
+
+def _attn_outputs(shp, dev, out, lse, want_lse):
+    B, Nq, Hq = shp.batch, shp.n_query, shp.q_heads
+    if out is None:
+        out = torch.empty((B, Nq, Hq, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", (B, Nq, Hq, HEAD_DIM), _BF)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, Nq, Hq), (torch.float32,))
+    return out, lse
+
+
+def sparse_attend_paged(shp: QsaShape, q, k_pool, v_pool, paged: PagedKV, lens, sel, n_sel,
+                        out=None, lse=None, ws=None, want_lse: bool = True):
+    """sparse_attend with K/V read through a page table."""
+    B, Nq, Hq = shp.batch, shp.n_query, shp.q_heads
+    dev = q.device
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    _need_pools(k_pool, v_pool, paged, shp)
+    _need(lens, "lens", (B,), _I32)
+    _need(sel, "sel", (B, Nq, TOPK), _I32)
+    _need(n_sel, "n_sel", (B, Nq), _I32)
+    out, lse = _attn_outputs(shp, dev, out, lse, want_lse)
+    ws, nb = _ws(shp, OP_SPARSE_ATTEND, ws, dev)
+    st = load_library().qsa_sparse_attend_paged(ctypes.byref(shp), _p(q), _p(k_pool),
+                                                _p(v_pool), ctypes.byref(paged.c), _p(lens),
+                                                _p(sel), _p(n_sel), _p(out), _p(lse), _p(ws), nb,
+                                                _stream(dev))
+    _check(st, "qsa_sparse_attend_paged")
+    return out, lse
+
+
+def forward_paged(shp: QsaShape, q_idx, k_idx, k_cmp, q, k_pool, v_pool, paged: PagedKV, lens,
+                  first_block=None, out=None, lse=None, sel=None, n_sel=None, ws=None,
+                  want_lse: bool = True):
+    """forward with the core K/V read through a page table (the indexer caches
+    stay per sequence).  Returns (out, lse, sel, n_sel)."""
+    B, L, Nq, Hq = shp.batch, shp.max_len, shp.n_query, shp.q_heads
+    dev = q.device
+    _need(q_idx, "q_idx", (B, Nq, IDX_HEADS, IDX_DIM), _BF)
+    _need(k_idx, "k_idx", (B, L, IDX_DIM), _BF)
+    _need(k_cmp, "k_cmp", (B, L // BLOCK, IDX_DIM), _BF)
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    _need_pools(k_pool, v_pool, paged, shp)
+    _need(lens, "lens", (B,), _I32)
+    if first_block is not None:
+        _need(first_block, "first_block", (B,), _I32)
+    out, lse = _attn_outputs(shp, dev, out, lse, want_lse)
+    if (sel is None) != (n_sel is None):
+        raise ValueError("give both sel and n_sel, or neither")
+    if sel is not None:
+        _need(sel, "sel", (B, Nq, TOPK), _I32)
+        _need(n_sel, "n_sel", (B, Nq), _I32)
+    ws, nb = _ws(shp, OP_FORWARD, ws, dev)
+    st = load_library().qsa_forward_paged(ctypes.byref(shp), _p(q_idx), _p(k_idx), _p(k_cmp),
+                                          _p(first_block), _p(q), _p(k_pool), _p(v_pool),
+                                          ctypes.byref(paged.c), _p(lens), _p(out), _p(lse),
+                                          _p(sel), _p(n_sel), _p(ws), nb, _stream(dev))
+    _check(st, "qsa_forward_paged")
+    return out, lse, sel, n_sel
+
+
+def dense_gqa_decode_paged(shp: QsaShape, q, k_pool, v_pool, paged: PagedKV, lens, out=None,
+                           lse=None, ws=None, want_lse: bool = True):
+    B, Nq, Hq = shp.batch, shp.n_query, shp.q_heads
+    dev = q.device
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    _need_pools(k_pool, v_pool, paged, shp)
+    _need(lens, "lens", (B,), _I32)
+    out, lse = _attn_outputs(shp, dev, out, lse, want_lse)
+    ws, nb = _ws(shp, OP_DENSE_DECODE, ws, dev)
+    st = load_library().qsa_dense_gqa_decode_paged(ctypes.byref(shp), _p(q), _p(k_pool),
+                                                   _p(v_pool), ctypes.byref(paged.c), _p(lens),
+                                                   _p(out), _p(lse), _p(ws), nb, _stream(dev))
+    _check(st, "qsa_dense_gqa_decode_paged")
+    return out, lse
+
+
+def dense_gqa_prefill(shp: QsaShape, q, k, v, lens, paged: PagedKV | None = None, out=None,
+                      lse=None, want_lse: bool = True):
+    """Dense causal GQA for many queries (a prefill chunk); k and v are the
+    contiguous caches, or the page pools of `paged`."""
+    B, L, Nq, Hq, Hkv = shp.batch, shp.max_len, shp.n_query, shp.q_heads, shp.kv_heads
+    dev = q.device
+    _need(q, "q", (B, Nq, Hq, HEAD_DIM), _BF)
+    if paged is None:
+        _need(k, "k", (B, L, Hkv, HEAD_DIM), _BF)
+        _need(v, "v", (B, L, Hkv, HEAD_DIM), _BF)
+    else:
+        _need_pools(k, v, paged, shp)
+    _need(lens, "lens", (B,), _I32)
+    out, lse = _attn_outputs(shp, dev, out, lse, want_lse)
+    st = load_library().qsa_dense_gqa_prefill(ctypes.byref(shp), _p(q), _p(k), _p(v),
+                                              ctypes.byref(paged.c) if paged else None, _p(lens),
+                                              _p(out), _p(lse), _stream(dev))
+    _check(st, "qsa_dense_gqa_prefill")
     return out, lse
 
 

@@ -175,6 +175,115 @@ qsa_status need_i32(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 3u) == 0 ? QSA_OK : QSA_ERR_ALIGN;
 }
 
+// Host-visible checks of a page descriptor; fills the kernels' form.
+qsa_status check_paged(const Dims& d, const qsa_paged_kv* kv, qsa::Paged* pg) {
+  if (!kv) return QSA_ERR_NULL;
+  QSA_TRY(need_i32(kv->page_table));
+  const int32_t ps = kv->page_size;
+  if (ps < 1 || ps > (1 << 20) || (ps & (ps - 1)) != 0) return QSA_ERR_SHAPE;
+  if (kv->max_pages < 1 || kv->n_pages < 1) return QSA_ERR_SHAPE;
+  if ((int64_t)kv->max_pages * ps < d.Lmax) return QSA_ERR_SHAPE;
+  if ((int64_t)kv->n_pages * ps > INT32_MAX) return QSA_ERR_SHAPE;  // pool rows are int32
+  pg->page_table = kv->page_table;
+  pg->page_shift = __builtin_ctz((unsigned)ps);
+  pg->max_pages = kv->max_pages;
+  pg->n_pages = kv->n_pages;
+  return QSA_OK;
+}
+
+}  // namespace
+
+namespace {
+qsa_status forward_impl(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_idx,
+                        uint16_t* k_cmp, const int32_t* first_block, const uint16_t* q,
+                        const uint16_t* k, const uint16_t* v, const qsa_paged_kv* kv,
+                        const int32_t* lens, uint16_t* out, float* lse, int32_t* sel_out,
+                        int32_t* n_sel_out, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0) return QSA_OK;
+  qsa::Paged pg{};
+  if (kv) QSA_TRY(check_paged(d, kv, &pg));
+  QSA_TRY(need(q_idx));
+  QSA_TRY(need(k_idx));
+  QSA_TRY(need(k_cmp));
+  if (first_block) QSA_TRY(need_i32(first_block));
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(out));
+  if (lse) QSA_TRY(need_i32(lse));
+  if (sel_out) QSA_TRY(need(sel_out));
+  if (n_sel_out) QSA_TRY(need_i32(n_sel_out));
+  if ((sel_out == nullptr) != (n_sel_out == nullptr)) return QSA_ERR_NULL;
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_FORWARD, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  ForwardPtrs p;
+  carve_forward(d, shape->flags, ws, &p);
+  int32_t* sel = sel_out ? sel_out : p.sel;
+  int32_t* n_sel = sel_out ? n_sel_out : p.n_sel;
+  const qsa::TopkPath path = qsa::choose_topk_path(d, shape->flags);
+  // decode-shaped calls compress inside the scoring pass; others first
+  const bool fuse = d.Nq > 0 && qsa::topk_can_fuse_compress(d, path);
+  if (!fuse) QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, s)));
+  if (d.Nq == 0) return QSA_OK;
+  const qsa::CompressFuse cf{k_idx, first_block};
+  QSA_TRY(hip_status(qsa::launch_index_topk(d, path, q_idx, k_cmp, lens, sel, n_sel, p.shared,
+                                            s, fuse ? &cf : nullptr)));
+  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.att.part_o,
+                                              p.att.part_lse, s, kv ? &pg : nullptr));
+}
+
+qsa_status sparse_attend_impl(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const qsa_paged_kv* kv, const int32_t* lens,
+                              const int32_t* sel, const int32_t* n_sel, uint16_t* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  qsa::Paged pg{};
+  if (kv) QSA_TRY(check_paged(d, kv, &pg));
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(sel));
+  QSA_TRY(need_i32(n_sel));
+  QSA_TRY(need(out));
+  if (lse) QSA_TRY(need_i32(lse));
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_SPARSE_ATTEND, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  AttendPtrs p;
+  carve_attend(d, ws, &p);
+  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.part_o,
+                                              p.part_lse, s, kv ? &pg : nullptr));
+}
+
+qsa_status dense_decode_impl(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const qsa_paged_kv* kv, const int32_t* lens,
+                             uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  QSA_TRY(check_shape(shape, &d));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  qsa::Paged pg{};
+  if (kv) QSA_TRY(check_paged(d, kv, &pg));
+  QSA_TRY(need(q));
+  QSA_TRY(need(k));
+  QSA_TRY(need(v));
+  QSA_TRY(need_i32(lens));
+  QSA_TRY(need(out));
+  if (lse) QSA_TRY(need_i32(lse));
+  QSA_TRY(check_ws(d, shape->flags, QSA_OP_DENSE_DECODE, ws, ws_bytes));
+  QSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QSA_TRY(check_lens(d, lens, s));
+  return hip_status(qsa::launch_dense_decode(d, q, k, v, lens, out, lse, ws, s, kv ? &pg : nullptr));
+}
 }  // namespace
 
 extern "C" {
@@ -285,25 +394,8 @@ qsa_status qsa_sparse_attend(const qsa_shape* shape, const uint16_t* q, const ui
                              const uint16_t* v, const int32_t* lens, const int32_t* sel,
                              const int32_t* n_sel, uint16_t* out, float* lse, void* ws,
                              size_t ws_bytes, void* stream) {
-  Dims d;
-  QSA_TRY(check_shape(shape, &d));
-  if (d.B == 0 || d.Nq == 0) return QSA_OK;
-  QSA_TRY(need(q));
-  QSA_TRY(need(k));
-  QSA_TRY(need(v));
-  QSA_TRY(need_i32(lens));
-  QSA_TRY(need(sel));
-  QSA_TRY(need_i32(n_sel));
-  QSA_TRY(need(out));
-  if (lse) QSA_TRY(need_i32(lse));
-  QSA_TRY(check_ws(d, shape->flags, QSA_OP_SPARSE_ATTEND, ws, ws_bytes));
-  QSA_TRY(check_device());
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  QSA_TRY(check_lens(d, lens, s));
-  AttendPtrs p;
-  carve_attend(d, ws, &p);
-  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.part_o,
-                                              p.part_lse, s));
+  return sparse_attend_impl(shape, q, k, v, nullptr, lens, sel, n_sel, out, lse, ws, ws_bytes,
+                            stream);
 }
 
 qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint16_t* k_idx,
@@ -311,59 +403,64 @@ qsa_status qsa_forward(const qsa_shape* shape, const uint16_t* q_idx, const uint
                        const uint16_t* k, const uint16_t* v, const int32_t* lens, uint16_t* out,
                        float* lse, int32_t* sel_out, int32_t* n_sel_out, void* ws,
                        size_t ws_bytes, void* stream) {
+  return forward_impl(shape, q_idx, k_idx, k_cmp, first_block, q, k, v, nullptr, lens, out, lse,
+                      sel_out, n_sel_out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_forward_paged(const qsa_shape* shape, const uint16_t* q_idx,
+                             const uint16_t* k_idx, uint16_t* k_cmp, const int32_t* first_block,
+                             const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const qsa_paged_kv* kv, const int32_t* lens, uint16_t* out,
+                             float* lse, int32_t* sel_out, int32_t* n_sel_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!kv) return QSA_ERR_NULL;
+  return forward_impl(shape, q_idx, k_idx, k_cmp, first_block, q, k_pool, v_pool, kv, lens, out,
+                      lse, sel_out, n_sel_out, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_sparse_attend_paged(const qsa_shape* shape, const uint16_t* q,
+                                   const uint16_t* k_pool, const uint16_t* v_pool,
+                                   const qsa_paged_kv* kv, const int32_t* lens,
+                                   const int32_t* sel, const int32_t* n_sel, uint16_t* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!kv) return QSA_ERR_NULL;
+  return sparse_attend_impl(shape, q, k_pool, v_pool, kv, lens, sel, n_sel, out, lse, ws,
+                            ws_bytes, stream);
+}
+
+qsa_status qsa_dense_gqa_decode_paged(const qsa_shape* shape, const uint16_t* q,
+                                      const uint16_t* k_pool, const uint16_t* v_pool,
+                                      const qsa_paged_kv* kv, const int32_t* lens,
+                                      uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!kv) return QSA_ERR_NULL;
+  return dense_decode_impl(shape, q, k_pool, v_pool, kv, lens, out, lse, ws, ws_bytes, stream);
+}
+
+qsa_status qsa_dense_gqa_prefill(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const qsa_paged_kv* kv, const int32_t* lens,
+                                 uint16_t* out, float* lse, void* stream) {
   Dims d;
   QSA_TRY(check_shape(shape, &d));
-  if (d.B == 0) return QSA_OK;
-  QSA_TRY(need(q_idx));
-  QSA_TRY(need(k_idx));
-  QSA_TRY(need(k_cmp));
-  if (first_block) QSA_TRY(need_i32(first_block));
+  if (d.B == 0 || d.Nq == 0) return QSA_OK;
+  qsa::Paged pg{};
+  if (kv) QSA_TRY(check_paged(d, kv, &pg));
   QSA_TRY(need(q));
   QSA_TRY(need(k));
   QSA_TRY(need(v));
   QSA_TRY(need_i32(lens));
   QSA_TRY(need(out));
   if (lse) QSA_TRY(need_i32(lse));
-  if (sel_out) QSA_TRY(need(sel_out));
-  if (n_sel_out) QSA_TRY(need_i32(n_sel_out));
-  if ((sel_out == nullptr) != (n_sel_out == nullptr)) return QSA_ERR_NULL;
-  QSA_TRY(check_ws(d, shape->flags, QSA_OP_FORWARD, ws, ws_bytes));
   QSA_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   QSA_TRY(check_lens(d, lens, s));
-  ForwardPtrs p;
-  carve_forward(d, shape->flags, ws, &p);
-  int32_t* sel = sel_out ? sel_out : p.sel;
-  int32_t* n_sel = sel_out ? n_sel_out : p.n_sel;
-  const qsa::TopkPath path = qsa::choose_topk_path(d, shape->flags);
-  // decode-shaped calls compress inside the scoring pass; others first
-  const bool fuse = d.Nq > 0 && qsa::topk_can_fuse_compress(d, path);
-  if (!fuse) QSA_TRY(hip_status(qsa::launch_compress(d, k_idx, lens, first_block, k_cmp, s)));
-  if (d.Nq == 0) return QSA_OK;
-  const qsa::CompressFuse cf{k_idx, first_block};
-  QSA_TRY(hip_status(qsa::launch_index_topk(d, path, q_idx, k_cmp, lens, sel, n_sel, p.shared,
-                                            s, fuse ? &cf : nullptr)));
-  return hip_status(qsa::launch_sparse_attend(d, q, k, v, lens, sel, n_sel, out, lse, p.att.part_o,
-                                              p.att.part_lse, s));
+  return hip_status(qsa::launch_dense_prefill(d, q, k, v, lens, out, lse, s, kv ? &pg : nullptr));
 }
 
 qsa_status qsa_dense_gqa_decode(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, uint16_t* out, float* lse,
                                 void* ws, size_t ws_bytes, void* stream) {
-  Dims d;
-  QSA_TRY(check_shape(shape, &d));
-  if (d.B == 0 || d.Nq == 0) return QSA_OK;
-  QSA_TRY(need(q));
-  QSA_TRY(need(k));
-  QSA_TRY(need(v));
-  QSA_TRY(need_i32(lens));
-  QSA_TRY(need(out));
-  if (lse) QSA_TRY(need_i32(lse));
-  QSA_TRY(check_ws(d, shape->flags, QSA_OP_DENSE_DECODE, ws, ws_bytes));
-  QSA_TRY(check_device());
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  QSA_TRY(check_lens(d, lens, s));
-  return hip_status(qsa::launch_dense_decode(d, q, k, v, lens, out, lse, ws, s));
+  return dense_decode_impl(shape, q, k, v, nullptr, lens, out, lse, ws, ws_bytes, stream);
 }
 
 qsa_status qsa_block_teacher(const qsa_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -65,7 +65,24 @@ struct AttnArgs {
   float scale_log2;
   int split_tokens, n_split;
   int tail_last;  // 1: the last split also takes the query's own block
+  // paged K/V (pt != null): token tok of sequence b is row
+  // pt[b * max_pages + tok / page] * page + tok % page of a pool of n_pages
+  // pages of `page` tokens (page = 1 << page_shift)
+  const int32_t* pt;
+  int page_shift, max_pages, n_pages;
 };
+
+// Paged K/V: the pool row of token tok of sequence b (ids clamped into the pool).
+__device__ __forceinline__ int pool_row(const AttnArgs& a, int b, int tok) {
+  const int page = clampi(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
+  return (page << a.page_shift) + (tok & ((1 << a.page_shift) - 1));
+}
+
+// Element offset of token tok's row (all KV heads) of sequence b in K or V.
+__device__ __forceinline__ long long kv_off(const AttnArgs& a, int b, int tok) {
+  if (a.pt == nullptr) return ((long long)b * a.Lmax + tok) * a.Hkv * kHeadDim;
+  return (long long)pool_row(a, b, tok) * a.Hkv * kHeadDim;
+}
 
 // Running softmax state of one wavefront: 16 query columns (one per lane
 // column), 128 output dims as 8 tiles of 16.
@@ -262,7 +279,6 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
     ns = clampi(a.n_sel[row], 0, bt < kTopK ? bt : kTopK);
     ntok = 4 * ns + (t - 4 * bt) + 1;
   }
-  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
   const uint16_t* kbase = a.k + g * kHeadDim;
   const uint16_t* vbase = a.v + g * kHeadDim;
   // With tail_last, the query's own block (tokens 4 bt .. t, known from lens
@@ -274,13 +290,20 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   if (own_tail)
     load_tile(tail, kbase, vbase, 0, [&](int kk) -> long long {
       const int tok = 4 * (t >> 2) + kk;
-      return tok <= t ? (long long)(kv_seq + (size_t)tok * a.Hkv) * kHeadDim : -1;
+      return tok <= t ? kv_off(a, b, tok) : -1;
     });
-  // ids outside [0, bt) are a caller bug: clamped so no access leaves the row
+  // ids outside [0, bt) are a caller bug: clamped so no access leaves the
+  // row.  Paged K/V with pages of 4 tokens or more: a block lies inside one
+  // page, so its id is replaced here, once, by the pool row of its first
+  // token, and the tiles read rows without a table lookup.
+  const bool paged4 = a.pt != nullptr && a.page_shift >= 2;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const int e = tid + kThreads * i;
-    if (e < nsb && kb0 + e < ns) s_sel[e] = clampi(my_sel[i], 0, bt - 1);
+    if (e < nsb && kb0 + e < ns) {
+      const int j = clampi(my_sel[i], 0, bt - 1);
+      s_sel[e] = paged4 ? pool_row(a, b, 4 * j) : j;
+    }
   }
   __syncthreads();
   // the selected tokens of this split (with tail_last the query's own block
@@ -289,8 +312,11 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
                                 : min(ntok, k_begin + a.split_tokens);
   auto row_of = [&](int kk) -> long long {
     if (kk >= k_end) return -1;
-    const int tok = kk < 4 * ns ? 4 * s_sel[(kk >> 2) - kb0] + (kk & 3) : 4 * bt + (kk - 4 * ns);
-    return (long long)(kv_seq + (size_t)tok * a.Hkv) * kHeadDim;
+    if (kk < 4 * ns) {
+      const int e = s_sel[(kk >> 2) - kb0];
+      return paged4 ? ((long long)e + (kk & 3)) * a.Hkv * kHeadDim : kv_off(a, b, 4 * e + (kk & 3));
+    }
+    return kv_off(a, b, 4 * bt + (kk - 4 * ns));
   };
   uint16_t* vt = s_v[wave];
   Run r;
@@ -406,6 +432,11 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
 // 256-byte pieces of one 1 KiB row, so each token's K and V cross the fabric
 // once, as whole rows.  Always writes partials (merged by merge_kernel).
 constexpr int kDenseWaves = 8;
+// kPaged: K/V rows through the page table.  The page ids of a tile's 32
+// tokens (lane x holds token T + x's) are loaded one tile ahead of the
+// tile's own loads, and each lane takes its rows' ids by shuffle, so the
+// table adds no round trip to the tile pipeline.
+template <bool kPaged>
 __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t s_vw[kDenseWaves][kTile * kVStride];
   const int split = blockIdx.x, b = blockIdx.z;
@@ -436,19 +467,42 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   const int t_hi = len - a.Nq + c_last / a.G;
   const int k_begin = split * a.split_tokens;
   const int k_end = min(t_hi + 1, k_begin + a.split_tokens);
-  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
   const uint16_t* kbase = a.k + g * kHeadDim;
   const uint16_t* vbase = a.v + g * kHeadDim;
-  auto row_of = [&](int kk) -> long long {
-    return kk < k_end ? (long long)(kv_seq + (size_t)kk * a.Hkv) * kHeadDim : -1;
+  auto row_of = [&](int kk) -> long long { return kk < k_end ? kv_off(a, b, kk) : -1; };
+  auto page_ids = [&](int T) -> int {
+    const int tok = min(T + (lane & 31), k_end - 1);
+    return clampi(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
+  };
+  auto paged_row = [&](int T, int pe) {
+    return [&, T, pe](int kk) -> long long {
+      const int page = __shfl(pe, (kk - T) & 31);
+      if (kk >= k_end) return -1;
+      return (((long long)page << a.page_shift) + (kk & ((1 << a.page_shift) - 1))) * a.Hkv *
+             kHeadDim;
+    };
   };
   Run r;
   run_init(r);
   KVTile cur, nxt;
-  if (k_begin < k_end) load_tile(cur, kbase, vbase, k_begin, row_of);
+  int pe_nxt = 0;  // page ids of the tile after the one in flight
+  if (k_begin < k_end) {
+    if constexpr (kPaged) {
+      load_tile(cur, kbase, vbase, k_begin, paged_row(k_begin, page_ids(k_begin)));
+      if (k_begin + kTile < k_end) pe_nxt = page_ids(k_begin + kTile);
+    } else {
+      load_tile(cur, kbase, vbase, k_begin, row_of);
+    }
+  }
   for (int k0 = k_begin; k0 < k_end; k0 += kTile) {
     stash_v(s_v, cur);
-    if (k0 + kTile < k_end) load_tile(nxt, kbase, vbase, k0 + kTile, row_of);
+    int pe_after = 0;
+    if constexpr (kPaged) {
+      if (k0 + kTile < k_end) load_tile(nxt, kbase, vbase, k0 + kTile, paged_row(k0 + kTile, pe_nxt));
+      if (k0 + 2 * kTile < k_end) pe_after = page_ids(k0 + 2 * kTile);
+    } else {
+      if (k0 + kTile < k_end) load_tile(nxt, kbase, vbase, k0 + kTile, row_of);
+    }
     float z[8];
     qk_logits(cur, qf, a.scale_log2, z);
 #pragma unroll
@@ -462,6 +516,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
     softmax_pv(r, z, s_v);
     wave_sync_lds();
     cur = nxt;
+    pe_nxt = pe_after;
   }
   float* po = a.part_o + (((row * a.Hq) + h) * a.n_split + split) * kHeadDim;
   float* pl = a.part_lse + ((row * a.Hq) + h) * a.n_split + split;
@@ -509,7 +564,6 @@ __global__ __launch_bounds__(64 * kDenseWaves) void block_teacher_kernel(AttnArg
   const int t_hi = len - a.Nq + c_last / a.G;
   const int k_begin = split * a.split_tokens;  // a multiple of 32
   const int k_end = min(t_hi + 1, k_begin + a.split_tokens);
-  const size_t kv_seq = (size_t)b * a.Lmax * a.Hkv;
   const uint16_t* kbase = a.k + g * kHeadDim;
   const int nbp = a.Lmax >> 2;
   const bool grouped = a.G <= 16 && (16 % a.G) == 0;
@@ -519,8 +573,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void block_teacher_kernel(AttnArg
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kk = k0 + s * 16 + (lane & 15);
-      const uint4* kp = reinterpret_cast<const uint4*>(
-          kbase + (size_t)(kv_seq + (size_t)min(kk, len > 0 ? len - 1 : 0) * a.Hkv) * kHeadDim);
+      const uint4* kp = reinterpret_cast<const uint4*>(kbase + kv_off(a, b, min(kk, len > 0 ? len - 1 : 0)));
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) t.k[s][ks] = kk < k_end ? kp[ks * 4 + (lane >> 4)] : zero_u4();
     }
@@ -552,6 +605,179 @@ __global__ __launch_bounds__(64 * kDenseWaves) void block_teacher_kernel(AttnArg
       }
     }
     cur = nxt;
+  }
+}
+
+// ------------------------------------------------------------------ dense prefill
+// Dense causal GQA over positions 0..t of every query (the comparator of a
+// prefill chunk, contiguous or paged K/V).  Grid (ceil(Nq / QW), Hkv, B),
+// 512 threads: one KV head g and QW = floor(256 / G) consecutive queries,
+// whose (query, head) columns the 8 wavefronts hold 32 apiece (two 16-column
+// MFMA groups sharing every K and V operand).  The workgroup walks tokens
+// 0 .. t of its last query in 64-token tiles staged once in LDS for all its
+// wavefronts: K row-major (the A operand of S^T = K Q^T), V transposed to
+// dims x tokens so that the A operand of O^T += V^T P is two 8-byte reads.
+// The next tile's global loads are issued before the current tile's MFMA
+// work.  Causal masking is per column (tokens after its query).
+constexpr int kPrefWaves = 8;
+constexpr int kPrefTok = 64;
+constexpr int kPrefVtStride = 72;  // elements per transposed-V row (one dim)
+
+// Eight probabilities (finite, >= 0) as an MFMA operand: hardware
+// round-to-nearest-even conversion, pairwise.
+__device__ __forceinline__ bf16x8 pack8_rne(const float* p) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  uint4 u;
+  u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[0], p[1]}, bf16x2));
+  u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[2], p[3]}, bf16x2));
+  u.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[4], p[5]}, bf16x2));
+  u.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[6], p[7]}, bf16x2));
+  return as_bf16x8(u);
+}
+
+__global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs a) {
+  __shared__ __align__(16) uint16_t s_k[kPrefTok * kVStride];
+  __shared__ __align__(16) uint16_t s_vt[kHeadDim * kPrefVtStride];
+  const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int qw = 16 * 2 * kPrefWaves / a.G;  // queries per workgroup
+  const int len = clampi(a.lens[b], 0, a.Lmax);
+  const float c2 = a.scale_log2;
+  bf16x8 qf[2][4];
+  int tq[2];
+  bool cv[2];
+  size_t rh[2];  // (row, head) index of each column group's column
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = wave * 32 + j * 16 + (lane & 15);
+    const int qi = qt * qw + c / a.G;
+    cv[j] = c < qw * a.G && qi < a.Nq;
+    tq[j] = len - a.Nq + qi;
+    rh[j] = ((size_t)b * a.Nq + (cv[j] ? qi : 0)) * a.Hq + g * a.G + c % a.G;
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + rh[j] * kHeadDim);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[j][ks] = as_bf16x8(cv[j] && tq[j] >= 0 ? qp[ks * 4 + (lane >> 4)] : zero_u4());
+  }
+  const int q_last = min(qt * qw + qw - 1, a.Nq - 1);
+  const int t_hi = len - a.Nq + q_last;       // the workgroup's last token
+  const int t_lo = len - a.Nq + qt * qw;      // its first query's last token
+  // this thread's share of a tile: token k0 + lane, 16-byte pieces wave and
+  // wave + 8 of its K and V rows (a token past t_hi loads t_hi's row, which
+  // the masks then ignore)
+  uint4 pk[2], pv[2];
+  auto load = [&](int k0) {
+    const long long off = kv_off(a, b, min(k0 + lane, t_hi)) + (long long)g * kHeadDim;
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k + off);
+    const uint4* vp = reinterpret_cast<const uint4*>(a.v + off);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      pk[p] = kp[wave + 8 * p];
+      pv[p] = vp[wave + 8 * p];
+    }
+  };
+  // running softmax per column group: m in the exp2 domain, l, O^T tiles
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  f32x4 o[2][8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (t_hi >= 0) load(0);
+  for (int k0 = 0; k0 <= t_hi; k0 += kPrefTok) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int piece = wave + 8 * p;
+      *reinterpret_cast<uint4*>(&s_k[lane * kVStride + piece * 8]) = pk[p];
+      const uint32_t w[4] = {pv[p].x, pv[p].y, pv[p].z, pv[p].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        s_vt[(piece * 8 + e) * kPrefVtStride + lane] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    if (k0 + kPrefTok <= t_hi) load(k0 + kPrefTok);
+    // S^T for the 64 tokens: z[j][4 qr + i] is token 16 qr + 4 (lane >> 4) + i
+    float z[2][16];
+#pragma unroll
+    for (int qr = 0; qr < 4; ++qr) {
+      uint4 kf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[ks] = *reinterpret_cast<const uint4*>(
+            &s_k[(qr * 16 + (lane & 15)) * kVStride + ks * 32 + (lane >> 4) * 8]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16(as_bf16x8(kf[ks]), qf[j][ks], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[j][qr * 4 + i] = acc[i];
+      }
+    }
+    if (k0 + kPrefTok - 1 > t_lo) {  // tiles on or past the diagonal: causal mask
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = k0 + (e >> 2) * 16 + (lane >> 4) * 4 + (e & 3);
+          if (!cv[j] || kk > tq[j]) z[j][e] = kNegInf;
+        }
+    }
+    float alpha[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float tmax = z[j][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, z[j][e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m[j], tmax * c2);
+      // a column with every logit masked so far keeps m = -inf
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      alpha[j] = __builtin_amdgcn_exp2f(m[j] - m_use);
+      m[j] = m_new;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        z[j][e] = __builtin_amdgcn_exp2f(fmaf(z[j][e], c2, -m_use));
+        ps += z[j][e];
+      }
+      l[j] = l[j] * alpha[j] + ps;
+    }
+    // the running maximum rarely moves once a few tiles are in: rescale O
+    // only when it did for some column of the wavefront
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f) != 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[j][dt] = o[j][dt] * alpha[j];
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 pf0 = pack8_rne(&z[0][h2 * 8]);
+      const bf16x8 pf1 = pack8_rne(&z[1][h2 * 8]);
+      const uint16_t* base = &s_vt[(lane & 15) * kPrefVtStride + h2 * 32 + 4 * (lane >> 4)];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(base + dt * 16 * kPrefVtStride);
+        const uint2 hi = *reinterpret_cast<const uint2*>(base + dt * 16 * kPrefVtStride + 16);
+        const bf16x8 u = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[0][dt] = mfma16(u, pf0, o[0][dt]);
+        o[1][dt] = mfma16(u, pf1, o[1][dt]);
+      }
+    }
+    __syncthreads();  // the tile is rewritten next
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    Run r;
+    r.m = m[j];
+    r.l = l[j];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) r.o[dt] = o[j][dt];
+    finish(r, cv[j], a.out + rh[j] * kHeadDim, a.lse ? a.lse + rh[j] : nullptr, nullptr, nullptr,
+           false);
   }
 }
 
@@ -736,12 +962,22 @@ AttendLayout attend_layout(const Dims& d) {
   return l;
 }
 
+namespace {
+void set_paging(AttnArgs& a, const Paged* pg) {
+  a.pt = pg ? pg->page_table : nullptr;
+  a.page_shift = pg ? pg->page_shift : 0;
+  a.max_pages = pg ? pg->max_pages : 0;
+  a.n_pages = pg ? pg->n_pages : 0;
+}
+}  // namespace
+
 hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, const int32_t* sel,
                                 const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
-                                float* part_lse, hipStream_t s) {
+                                float* part_lse, hipStream_t s, const Paged* pg) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   AttnArgs a{};
+  set_paging(a, pg);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -845,9 +1081,10 @@ size_t dense_workspace_bytes(const Dims& d) {
 
 hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* lens, uint16_t* out,
-                               float* lse, void* ws, hipStream_t s) {
+                               float* lse, void* ws, hipStream_t s, const Paged* pg) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
   AttnArgs a{};
+  set_paging(a, pg);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -868,12 +1105,40 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
   a.part_lse = c.take<float>(rh * a.n_split);
   const int units = d.Hkv * ((d.Nq * a.G + 15) / 16);
   const int waves = units < kDenseWaves ? units : kDenseWaves;
-  QSA_LAUNCH(dense_decode_kernel,
-             dim3((unsigned)a.n_split, (unsigned)((units + kDenseWaves - 1) / kDenseWaves),
-                  (unsigned)d.B),
-             dim3(64 * (unsigned)waves), 0, s, a);
+  const dim3 grid((unsigned)a.n_split, (unsigned)((units + kDenseWaves - 1) / kDenseWaves),
+                  (unsigned)d.B);
+  if (a.pt)
+    QSA_LAUNCH(dense_decode_kernel<true>, grid, dim3(64 * (unsigned)waves), 0, s, a);
+  else
+    QSA_LAUNCH(dense_decode_kernel<false>, grid, dim3(64 * (unsigned)waves), 0, s, a);
   QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
              a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_prefill(const Dims& d, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const int32_t* lens, uint16_t* out, float* lse,
+                                hipStream_t s, const Paged* pg) {
+  if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  AttnArgs a{};
+  set_paging(a, pg);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lens = lens;
+  a.out = out;
+  a.lse = lse;
+  a.B = d.B;
+  a.Lmax = d.Lmax;
+  a.Nq = d.Nq;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.Hq / d.Hkv;
+  a.scale_log2 = d.scale * kLog2e;
+  const int qw = 16 * 2 * kPrefWaves / a.G;
+  QSA_LAUNCH(dense_prefill_kernel,
+             dim3((unsigned)((d.Nq + qw - 1) / qw), (unsigned)d.Hkv, (unsigned)d.B),
+             dim3(64 * kPrefWaves), 0, s, a);
   return hipGetLastError();
 }
 

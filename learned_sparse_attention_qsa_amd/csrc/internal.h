@@ -50,6 +50,12 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
                              const CompressFuse* fuse = nullptr);
 
 // ---- attend.hip
+// Paged K/V: token tok of sequence b is row page_table[b * max_pages + tok /
+// page] * page + tok % page of a pool of n_pages pages (page = 1 << page_shift).
+struct Paged {
+  const int32_t* page_table;
+  int page_shift, max_pages, n_pages;
+};
 // Scratch of the sparse attention when a query row is split over several
 // workgroups: partial outputs and log-sum-exps.
 struct AttendLayout {
@@ -59,7 +65,7 @@ AttendLayout attend_layout(const Dims& d);
 hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, const int32_t* lens, const int32_t* sel,
                                 const int32_t* n_sel, uint16_t* out, float* lse, float* part_o,
-                                float* part_lse, hipStream_t s);
+                                float* part_lse, hipStream_t s, const Paged* pg = nullptr);
 size_t dense_workspace_bytes(const Dims& d);
 // The indexer's training target (dense attention mass per micro-block, over
 // the heads) and the share of it a selection keeps.
@@ -72,7 +78,10 @@ hipError_t launch_teacher_recall(const Dims& d, const float* teacher, const int3
                                  hipStream_t s);
 hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const int32_t* lens, uint16_t* out,
-                               float* lse, void* ws, hipStream_t s);
+                               float* lse, void* ws, hipStream_t s, const Paged* pg = nullptr);
+hipError_t launch_dense_prefill(const Dims& d, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const int32_t* lens, uint16_t* out, float* lse,
+                                hipStream_t s, const Paged* pg = nullptr);
 
 // ---- backward.hip
 hipError_t launch_sparse_attend_bwd(const Dims& d, const uint16_t* q, const uint16_t* k,

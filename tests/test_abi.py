@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = Q.load_library()
     declared = header_symbols()
-    assert len(declared) == 19
+    assert len(declared) == 23
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -162,3 +162,35 @@ def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_launch():
     bad = Q.shape(1, 6, 1, 8, 1)               # max_len not a multiple of 4
     assert lib.qsa_forward_noalloc(ctypes.byref(bad), *args) == Q.ERR_SHAPE
     assert Q.status_string(Q.ERR_SCRATCH).startswith("shape needs more scratch")
+
+
+def test_paged_descriptor_rejected_before_any_launch():
+    lib = Q.load_library()
+    shp = Q.shape(2, 4096, 4, 8, 1)
+    table = Q.QsaPagedKV(FAKE.value, 16, 256, 600)    # 256 pages of 16 tokens cover 4,096
+    ok = ctypes.byref(table)
+    ws = Q.workspace_bytes(shp, Q.OP_SPARSE_ATTEND)
+
+    def attend(kv):
+        return lib.qsa_sparse_attend_paged(ctypes.byref(shp), FAKE, FAKE, FAKE, kv, FAKE, FAKE,
+                                           FAKE, FAKE, None, FAKE, max(ws, 16), None)
+
+    assert attend(None) == Q.ERR_NULL
+    for ps, mp, npg in ((12, 512, 600), (0, 256, 600), (1 << 21, 1, 1), (16, 255, 600),
+                        (16, 256, 0), (16, 0, 600)):
+        bad = Q.QsaPagedKV(FAKE.value, ps, mp, npg)
+        assert attend(ctypes.byref(bad)) == Q.ERR_SHAPE, (ps, mp, npg)
+    mis = Q.QsaPagedKV(FAKE.value + 2, 16, 256, 600)
+    assert attend(ctypes.byref(mis)) == Q.ERR_ALIGN
+    assert lib.qsa_dense_gqa_decode_paged(ctypes.byref(shp), FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                          None, FAKE, 1 << 30, None) == Q.ERR_NULL
+    assert lib.qsa_forward_paged(ctypes.byref(shp), *([FAKE] * 7), None, *([FAKE] * 5),
+                                 FAKE, 1 << 30, None) == Q.ERR_NULL
+    short = Q.QsaPagedKV(FAKE.value, 64, 63, 600)     # 63 pages of 64 tokens < 4,096
+    assert lib.qsa_dense_gqa_prefill(ctypes.byref(shp), FAKE, FAKE, FAKE, ctypes.byref(short),
+                                     FAKE, FAKE, None, None) == Q.ERR_SHAPE
+    # prefill without a table takes contiguous caches; empty work is a no-op
+    assert lib.qsa_dense_gqa_prefill(ctypes.byref(Q.shape(3, 8, 0, 8, 1)), None, None, None,
+                                     None, None, None, None, None) == Q.OK
+    assert lib.qsa_dense_gqa_prefill(ctypes.byref(shp), None, FAKE, FAKE, ok, FAKE, FAKE,
+                                     None, None) == Q.ERR_NULL
