@@ -636,9 +636,28 @@ __device__ __forceinline__ bf16x8 pack8_rne(const float* p) {
   return as_bf16x8(u);
 }
 
+// Maximum over the four lanes L, L^16, L^32, L^48 (one MFMA output column):
+// the gfx950 row-swap moves, no LDS round trip.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+  x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
+// Position of token tau (0..31 of a 32-token half) in a transposed V row:
+// the eight tokens one lane group g = (tau >> 2) & 3 feeds to the PV MFMA
+// (4g..4g+3 and 16+4g..16+4g+3) are stored contiguously, so the A operand
+// is one 16-byte read.
+__device__ __forceinline__ int vt_pos(int tau) {
+  return (((tau >> 2) & 3) << 3) | ((tau >> 4) << 2) | (tau & 3);
+}
+
 __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs a) {
-  __shared__ __align__(16) uint16_t s_k[kPrefTok * kVStride];
-  __shared__ __align__(16) uint16_t s_vt[kHeadDim * kPrefVtStride];
+  __shared__ __align__(16) uint16_t s_k[2][kPrefTok * kVStride];
+  __shared__ __align__(16) uint16_t s_vt[2][kHeadDim * kPrefVtStride];
   const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int qw = 16 * 2 * kPrefWaves / a.G;  // queries per workgroup
@@ -661,20 +680,66 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
       qf[j][ks] = as_bf16x8(cv[j] && tq[j] >= 0 ? qp[ks * 4 + (lane >> 4)] : zero_u4());
   }
   const int q_last = min(qt * qw + qw - 1, a.Nq - 1);
-  const int t_hi = len - a.Nq + q_last;       // the workgroup's last token
-  const int t_lo = len - a.Nq + qt * qw;      // its first query's last token
-  // this thread's share of a tile: token k0 + lane, 16-byte pieces wave and
-  // wave + 8 of its K and V rows (a token past t_hi loads t_hi's row, which
-  // the masks then ignore)
-  uint4 pk[2], pv[2];
-  auto load = [&](int k0) {
-    const long long off = kv_off(a, b, min(k0 + lane, t_hi)) + (long long)g * kHeadDim;
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k + off);
-    const uint4* vp = reinterpret_cast<const uint4*>(a.v + off);
+  const int t_hi = len - a.Nq + q_last;  // the workgroup's last token
+  const int t_lo = len - a.Nq + qt * qw; // its first query's last token
+  const int n_tiles = t_hi >= 0 ? t_hi / kPrefTok + 1 : 0;
+  // A thread's share of a tile: token 64 i + lane, 16-byte pieces wave and
+  // wave + 8 of its K or V row (a token past t_hi reads t_hi's row, which
+  // the masks then ignore).
+  auto row_ptr = [&](const uint16_t* base, int i) -> const uint4* {
+    const long long off = kv_off(a, b, min(i * kPrefTok + lane, t_hi)) + (long long)g * kHeadDim;
+    return reinterpret_cast<const uint4*>(base + off);
+  };
+  const int vcol = (lane & 32) | vt_pos(lane & 31);  // this thread's token in a V^T row
+  auto stash_k = [&](int buf, uint4 r0, uint4 r1) {
+    *reinterpret_cast<uint4*>(&s_k[buf][lane * kVStride + wave * 8]) = r0;
+    *reinterpret_cast<uint4*>(&s_k[buf][lane * kVStride + (wave + 8) * 8]) = r1;
+  };
+  auto stash_v1 = [&](int buf, int piece, uint4 r) {
+    uint16_t* d = &s_vt[buf][piece * 8 * kPrefVtStride + vcol];
+    d[0 * kPrefVtStride] = (uint16_t)r.x;
+    d[1 * kPrefVtStride] = (uint16_t)(r.x >> 16);
+    d[2 * kPrefVtStride] = (uint16_t)r.y;
+    d[3 * kPrefVtStride] = (uint16_t)(r.y >> 16);
+    d[4 * kPrefVtStride] = (uint16_t)r.z;
+    d[5 * kPrefVtStride] = (uint16_t)(r.z >> 16);
+    d[6 * kPrefVtStride] = (uint16_t)r.w;
+    d[7 * kPrefVtStride] = (uint16_t)(r.w >> 16);
+  };
+  auto stash_v = [&](int buf, uint4 r0, uint4 r1) {
+    stash_v1(buf, wave, r0);
+    stash_v1(buf, wave + 8, r1);
+  };
+  // S^T of tile i from K buffer `buf`: z[j][4 qr + e] is token 64 i + 16 qr +
+  // 4 (lane >> 4) + e of column group j, raw logits, causally masked on or
+  // past the diagonal.
+  auto qk = [&](int buf, int i, float (&z)[2][16]) {
+    const uint16_t* sk = s_k[buf];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      pk[p] = kp[wave + 8 * p];
-      pv[p] = vp[wave + 8 * p];
+    for (int qr = 0; qr < 4; ++qr) {
+      uint4 kf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[ks] = *reinterpret_cast<const uint4*>(
+            &sk[(qr * 16 + (lane & 15)) * kVStride + ks * 32 + (lane >> 4) * 8]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16(as_bf16x8(kf[ks]), qf[j][ks], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[j][qr * 4 + e] = acc[e];
+      }
+    }
+    const int k0 = i * kPrefTok;
+    if (k0 + kPrefTok - 1 > t_lo) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = k0 + (e >> 2) * 16 + (lane >> 4) * 4 + (e & 3);
+          if (!cv[j] || kk > tq[j]) z[j][e] = kNegInf;
+        }
     }
   };
   // running softmax per column group: m in the exp2 domain, l, O^T tiles
@@ -684,54 +749,49 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (t_hi >= 0) load(0);
-  for (int k0 = 0; k0 <= t_hi; k0 += kPrefTok) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int piece = wave + 8 * p;
-      *reinterpret_cast<uint4*>(&s_k[lane * kVStride + piece * 8]) = pk[p];
-      const uint32_t w[4] = {pv[p].x, pv[p].y, pv[p].z, pv[p].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        s_vt[(piece * 8 + e) * kPrefVtStride + lane] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  // Software pipeline over tiles i = 0 .. n_tiles-1, one barrier per tile.
+  // Iteration i computes S of tile i+1 (K buffer (i+1)&1) while it finishes
+  // the softmax and PV of tile i (V buffer i&1), then stores K(i+2) into K
+  // buffer i&1 and V(i+1) into V buffer (i+1)&1, both last read in iteration
+  // i-1, and requests K(i+3) and V(i+2) from memory.
+  float z[2][16], zn[2][16];
+  uint4 rk0 = zero_u4(), rk1 = zero_u4(), rv0 = zero_u4(), rv1 = zero_u4();
+  if (n_tiles > 0) {
+    const uint4* kp = row_ptr(a.k, 0);
+    const uint4* vp = row_ptr(a.v, 0);
+    stash_k(0, kp[wave], kp[wave + 8]);
+    stash_v(0, vp[wave], vp[wave + 8]);
+    if (n_tiles > 1) {
+      const uint4* kp1 = row_ptr(a.k, 1);
+      stash_k(1, kp1[wave], kp1[wave + 8]);
     }
-    __syncthreads();
-    if (k0 + kPrefTok <= t_hi) load(k0 + kPrefTok);
-    // S^T for the 64 tokens: z[j][4 qr + i] is token 16 qr + 4 (lane >> 4) + i
-    float z[2][16];
-#pragma unroll
-    for (int qr = 0; qr < 4; ++qr) {
-      uint4 kf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf[ks] = *reinterpret_cast<const uint4*>(
-            &s_k[(qr * 16 + (lane & 15)) * kVStride + ks * 32 + (lane >> 4) * 8]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16(as_bf16x8(kf[ks]), qf[j][ks], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[j][qr * 4 + i] = acc[i];
-      }
-    }
-    if (k0 + kPrefTok - 1 > t_lo) {  // tiles on or past the diagonal: causal mask
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = k0 + (e >> 2) * 16 + (lane >> 4) * 4 + (e & 3);
-          if (!cv[j] || kk > tq[j]) z[j][e] = kNegInf;
-        }
-    }
+  }
+  // Every path into the loop has the Q fragments in registers: without this
+  // wait the compiler, merging the paths, waits for every load in flight at
+  // the first MFMA of each iteration.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only
+  __syncthreads();
+  if (n_tiles > 0) qk(0, 0, z);
+  if (n_tiles > 2) {
+    const uint4* kp = row_ptr(a.k, 2);
+    rk0 = kp[wave];
+    rk1 = kp[wave + 8];
+  }
+  if (n_tiles > 1) {
+    const uint4* vp = row_ptr(a.v, 1);
+    rv0 = vp[wave];
+    rv1 = vp[wave + 8];
+  }
+  for (int i = 0; i < n_tiles; ++i) {
+    const int cur = i & 1;
+    if (i + 1 < n_tiles) qk(cur ^ 1, i + 1, zn);
     float alpha[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float tmax = z[j][0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, z[j][e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_over_rows(tmax);
       const float m_new = fmaxf(m[j], tmax * c2);
       // a column with every logit masked so far keeps m = -inf
       const float m_use = m_new == kNegInf ? 0.f : m_new;
@@ -753,21 +813,37 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[j][dt] = o[j][dt] * alpha[j];
     }
+    const uint16_t* svt = s_vt[cur];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const bf16x8 pf0 = pack8_rne(&z[0][h2 * 8]);
       const bf16x8 pf1 = pack8_rne(&z[1][h2 * 8]);
-      const uint16_t* base = &s_vt[(lane & 15) * kPrefVtStride + h2 * 32 + 4 * (lane >> 4)];
+      const uint16_t* base = &svt[(lane & 15) * kPrefVtStride + h2 * 32 + 8 * (lane >> 4)];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(base + dt * 16 * kPrefVtStride);
-        const uint2 hi = *reinterpret_cast<const uint2*>(base + dt * 16 * kPrefVtStride + 16);
-        const bf16x8 u = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16x8 u =
+            as_bf16x8(*reinterpret_cast<const uint4*>(base + dt * 16 * kPrefVtStride));
         o[0][dt] = mfma16(u, pf0, o[0][dt]);
         o[1][dt] = mfma16(u, pf1, o[1][dt]);
       }
     }
-    __syncthreads();  // the tile is rewritten next
+    if (i + 2 < n_tiles) stash_k(cur, rk0, rk1);
+    if (i + 1 < n_tiles) stash_v(cur ^ 1, rv0, rv1);
+    if (i + 3 < n_tiles) {
+      const uint4* kp = row_ptr(a.k, i + 3);
+      rk0 = kp[wave];
+      rk1 = kp[wave + 8];
+    }
+    if (i + 2 < n_tiles) {
+      const uint4* vp = row_ptr(a.v, i + 2);
+      rv0 = vp[wave];
+      rv1 = vp[wave + 8];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) z[j][e] = zn[j][e];
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
