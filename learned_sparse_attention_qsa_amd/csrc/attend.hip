@@ -41,13 +41,28 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* p) {
+// Eight probabilities (finite, >= 0) as an MFMA operand: hardware
+// round-to-nearest-even conversion, pairwise.
+__device__ __forceinline__ bf16x8 pack8_rne(const float* p) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   uint4 u;
-  u.x = f32_to_bf16(p[0]) | (f32_to_bf16(p[1]) << 16);
-  u.y = f32_to_bf16(p[2]) | (f32_to_bf16(p[3]) << 16);
-  u.z = f32_to_bf16(p[4]) | (f32_to_bf16(p[5]) << 16);
-  u.w = f32_to_bf16(p[6]) | (f32_to_bf16(p[7]) << 16);
+  u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[0], p[1]}, bf16x2));
+  u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[2], p[3]}, bf16x2));
+  u.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[4], p[5]}, bf16x2));
+  u.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[6], p[7]}, bf16x2));
   return as_bf16x8(u);
+}
+
+// Maximum over the four lanes L, L^16, L^32, L^48 (one MFMA output column):
+// the gfx950 row-swap moves, no LDS round trip.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+  x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
 struct AttnArgs {
@@ -106,22 +121,21 @@ __device__ __forceinline__ void softmax_pv(Run& r, float* z, const uint16_t* vt)
   float tmax = z[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_over_rows(tmax);
   const float m_new = fmaxf(r.m, tmax);
   // A column with every logit masked so far keeps m = -inf; guard the exp2.
   const float m_use = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = exp2f(r.m - m_use);
+  const float alpha = __builtin_amdgcn_exp2f(r.m - m_use);
   float p[8];
   float ps = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(z[e] - m_use);
+    p[e] = __builtin_amdgcn_exp2f(z[e] - m_use);
     ps += p[e];
   }
   r.l = r.l * alpha + ps;
   r.m = m_new;
-  const bf16x8 pf = pack8(p);
+  const bf16x8 pf = pack8_rne(p);
   const int g = lane >> 4;
   const int dl = lane & 15;
 #pragma unroll
@@ -623,29 +637,6 @@ constexpr int kPrefWaves = 8;
 constexpr int kPrefTok = 64;
 constexpr int kPrefVtStride = 72;  // elements per transposed-V row (one dim)
 
-// Eight probabilities (finite, >= 0) as an MFMA operand: hardware
-// round-to-nearest-even conversion, pairwise.
-__device__ __forceinline__ bf16x8 pack8_rne(const float* p) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  uint4 u;
-  u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[0], p[1]}, bf16x2));
-  u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[2], p[3]}, bf16x2));
-  u.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[4], p[5]}, bf16x2));
-  u.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p[6], p[7]}, bf16x2));
-  return as_bf16x8(u);
-}
-
-// Maximum over the four lanes L, L^16, L^32, L^48 (one MFMA output column):
-// the gfx950 row-swap moves, no LDS round trip.
-__device__ __forceinline__ float max_over_rows(float x) {
-  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-  x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-}
 
 // Position of token tau (0..31 of a 32-token half) in a transposed V row:
 // the eight tokens one lane group g = (tau >> 2) & 3 feeds to the PV MFMA
