@@ -549,6 +549,50 @@ def prefill_record(w, step_ms, kstats, np):
     return res
 
 
+def prefill_gather_ceiling(Q, torch, flush, ws, w, ak, reps=3):
+    """The prefill attention against the rate at which this part gathers the
+    same bytes: every query's selected micro-blocks and its own block, 4 KiB
+    of K and 4 KiB of V each (the 4 consecutive token rows of all KV heads),
+    read by the plain gather probe in the selection's own order: the bound
+    for any kernel that fetches each query's rows once.  Also how often a
+    block is chosen (the reuse a block-major kernel could exploit)."""
+    B, Nq = w.batch, w.n_query
+    sel = ws.sel.to(torch.int64)
+    pos = ws.lens.to(torch.int64).view(B, 1) - Nq + torch.arange(Nq, device="cuda").view(1, Nq)
+    own = (pos // 4).view(B, Nq, 1)
+    seq_blocks = w.max_len // 4
+    blk = torch.cat([sel, own], dim=2)
+    blk = torch.where(blk < 0, own, blk)  # (rows with fewer than 512 blocks re-read their own)
+    idx = (blk + torch.arange(B, device="cuda").view(B, 1, 1) * seq_blocks).reshape(-1).contiguous()
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    best = None
+    for wgs in (2048, 8192):
+        def probe():
+            Q.ceil_gather(ws.dev["k"], idx, 4096, wgs, sink)
+            Q.ceil_gather(ws.dev["v"], idx, 4096, wgs, sink)
+        probe()
+        totals = []
+        for _ in range(reps):
+            flush()
+            timer = Q.KernelTimer(max_launches=4)
+            torch.cuda.synchronize()
+            with timer:
+                probe()
+            totals.append(sum(ms for _, ms in timer.records()) * 1000.0)
+        us = min(totals)
+        if best is None or us < best[0]:
+            best = (us, wgs)
+    nbytes = idx.numel() * 4096 * 2
+    uniq = int(torch.unique(idx).numel())
+    return {"probe_us": best[0], "workgroups": best[1], "bytes": nbytes,
+            "unique_blocks": uniq, "mean_queries_per_block": idx.numel() / max(uniq, 1),
+            "probe_gbs": nbytes / (best[0] * 1e-6) / 1e9,
+            "attention_us": ak["avg_us"], "attention_over_probe": ak["avg_us"] / best[0],
+            "note": "qsa_ceil_gather over the step's own selection (K then V, 4 KiB blocks); "
+                    "the attention also computes, and fetches whole blocks only where the "
+                    "selection has them"}
+
+
 def prefill_leg(args, Q, W, torch, np, flush, cfg=3, steps=None):
     w = W.make(cfg)
     log(f"[bench] {w.name}: inputs ready")
@@ -570,6 +614,9 @@ def prefill_leg(args, Q, W, torch, np, flush, cfg=3, steps=None):
             hit[i] = np.isin(blocks, sel_h[i, :nsel_h[i]]).mean()
         res["needle_survival"] = {"mean": float(hit.mean()), "min": float(hit.min()),
                                   "spans": len(w.needle_starts[0]), "blocks": int(blocks.size)}
+    ak = res["kernels"].get("sparse_attend_kernel")
+    if ak:
+        res["attention_gather_ceiling"] = prefill_gather_ceiling(Q, torch, flush, ws, w, ak)
     if not args.no_dense:
         res["dense_comparator"] = dense_prefill_leg(args, Q, torch, np, flush, ws, w,
                                                     res["ms_per_step"])

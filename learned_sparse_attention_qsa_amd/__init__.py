@@ -19,7 +19,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libqsa.so")
+# QSA_LIBRARY selects another build of the same library (the sanitized one)
+LIB_PATH = os.environ.get("QSA_LIBRARY") or os.path.join(_HERE, "lib", "libqsa.so")
 
 IDX_HEADS = 4
 IDX_DIM = 64

@@ -3,6 +3,9 @@
     python -m learned_sparse_attention_qsa_amd.build        # or build()
 
 Outputs learned_sparse_attention_qsa_amd/lib/libqsa.so.  Every call rebuilds.
+build_sanitized() builds lib/libqsa_san.so, the same library with its host
+code instrumented by AddressSanitizer and UndefinedBehaviorSanitizer (device
+code unchanged), for the CPU tests of the C ABI's argument checking.
 """
 from __future__ import annotations
 
@@ -17,6 +20,11 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(LIBDIR, "libqsa.so")
+SAN_LIB = os.path.join(LIBDIR, "libqsa_san.so")
+SAN_OBJDIR = os.path.join(PKG, "_build", "san")
+# host-side sanitizers only: each flag behind -Xarch_host
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -39,11 +47,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, san: bool = False) -> str:
+    obj = os.path.join(SAN_OBJDIR if san else OBJDIR, os.path.basename(src) + ".o")
+    extra = SAN_FLAGS if san else []
+    cmd = [_hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [_hipcc(), "-O2", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc(), "-O2" if not san else "-O1", f"--offload-arch={ARCH}", "-fPIC",
+               "-std=c++17", *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -64,6 +75,40 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(SAN_OBJDIR, exist_ok=True)
+    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, san=True), SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libsan",
+           *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (to preload into a
+    process that loads libqsa_san.so)."""
+    hip_bin = os.path.dirname(os.path.realpath(_hipcc()))
+    for cxx in (os.path.join(hip_bin, "..", "llvm", "bin", "clang++"),
+                "/opt/rocm/llvm/bin/clang++", "clang++"):
+        try:
+            r = subprocess.run([cxx, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                               capture_output=True, text=True)
+        except OSError:
+            continue
+        path = r.stdout.strip()
+        if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+            return path
+    raise RuntimeError("AddressSanitizer runtime not found")
 
 
 if __name__ == "__main__":
