@@ -326,6 +326,20 @@ qsa_status qsa_index_scores_backward(const qsa_shape* shape, const uint16_t* q_i
 qsa_status qsa_compress_keys_backward(const qsa_shape* shape, const int32_t* lens,
                                       const float* dk_cmp, float* dk_idx, void* stream);
 
+/* Debug builds (the library compiled with QSA_DEBUG, lib/libqsa_debug.so),
+ * for finding caller bugs (not part of the method).  Every kernel clamps
+ * caller-supplied values that index memory or bound a loop (lens outside
+ * [Nq, Lmax], a selected block outside [0, bt), n_sel outside
+ * [0, min(bt, 512)], a page id outside the pool, first_block past the
+ * completed blocks) so that no access leaves its buffer; a debug build also
+ * counts each value a guard caught.  qsa_debug_build returns 1 in such a
+ * build, 0 otherwise.  qsa_debug_guard_hits waits for the current device to
+ * finish its work, then stores the count since the previous call (clearing
+ * it); in other builds it stores 0.  Not for use while kernels run on other
+ * streams of the device. */
+int32_t qsa_debug_build(void);
+qsa_status qsa_debug_guard_hits(uint64_t* hits);
+
 /* Kernel timing hook, for benchmarks and profilers (not part of the method).
  * qsa_profile_attach hands the library n_events caller-created hipEvent_t
  * handles (created with timing enabled, owned by the caller).  From then on,

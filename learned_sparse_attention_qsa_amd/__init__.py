@@ -57,6 +57,8 @@ EXPORTS = (
     "qsa_sparse_attend_backward",
     "qsa_index_scores_backward",
     "qsa_compress_keys_backward",
+    "qsa_debug_build",
+    "qsa_debug_guard_hits",
     "qsa_profile_attach",
     "qsa_profile_detach",
     "qsa_profile_kernel_name",
@@ -147,6 +149,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_compress_keys_backward.argtypes = [sp, vp, vp, vp, vp]
     for name in EXPORTS[2:18]:
         getattr(lib, name).restype = i32
+    lib.qsa_debug_build.argtypes = []
+    lib.qsa_debug_build.restype = i32
+    lib.qsa_debug_guard_hits.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    lib.qsa_debug_guard_hits.restype = i32
     lib.qsa_profile_attach.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.qsa_profile_attach.restype = i32
     lib.qsa_profile_detach.argtypes = []
@@ -481,6 +487,19 @@ def dense_gqa_prefill(shp: QsaShape, q, k, v, lens, paged: PagedKV | None = None
                                               _p(out), _p(lse), _stream(dev))
     _check(st, "qsa_dense_gqa_prefill")
     return out, lse
+
+
+def debug_build() -> bool:
+    """True when the loaded library was built with QSA_DEBUG."""
+    return bool(load_library().qsa_debug_build())
+
+
+def debug_guard_hits() -> int:
+    """Caller-supplied values the kernels' guards caught since the previous
+    call (debug builds; 0 otherwise).  Waits for the device."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().qsa_debug_guard_hits(ctypes.byref(n)), "qsa_debug_guard_hits")
+    return int(n.value)
 
 
 def ceil_stream_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor) -> None:

@@ -6,6 +6,8 @@ Outputs learned_sparse_attention_qsa_amd/lib/libqsa.so.  Every call rebuilds.
 build_sanitized() builds lib/libqsa_san.so, the same library with its host
 code instrumented by AddressSanitizer and UndefinedBehaviorSanitizer (device
 code unchanged), for the CPU tests of the C ABI's argument checking.
+build_debug() builds lib/libqsa_debug.so with QSA_DEBUG: the kernels' guards
+on caller-supplied values also count what they catch (qsa_debug_guard_hits).
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(LIBDIR, "libqsa.so")
 SAN_LIB = os.path.join(LIBDIR, "libqsa_san.so")
 SAN_OBJDIR = os.path.join(PKG, "_build", "san")
+DEBUG_LIB = os.path.join(LIBDIR, "libqsa_debug.so")
+DEBUG_OBJDIR = os.path.join(PKG, "_build", "debug")
 # host-side sanitizers only: each flag behind -Xarch_host
 SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
@@ -47,9 +51,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, san: bool = False) -> str:
-    obj = os.path.join(SAN_OBJDIR if san else OBJDIR, os.path.basename(src) + ".o")
-    extra = SAN_FLAGS if san else []
+def _compile(src: str, san: bool = False, debug: bool = False) -> str:
+    objdir = SAN_OBJDIR if san else (DEBUG_OBJDIR if debug else OBJDIR)
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    extra = SAN_FLAGS if san else (["-DQSA_DEBUG"] if debug else [])
     cmd = [_hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
            "-o", obj]
     if src.endswith(".cpp"):
@@ -92,6 +97,22 @@ def build_sanitized(verbose: bool = False) -> str:
     if verbose:
         print(f"built {SAN_LIB}")
     return SAN_LIB
+
+
+def build_debug(verbose: bool = False) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(DEBUG_OBJDIR, exist_ok=True)
+    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, debug=True), SOURCES))
+    tmp = DEBUG_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DEBUG_LIB)
+    if verbose:
+        print(f"built {DEBUG_LIB}")
+    return DEBUG_LIB
 
 
 def sanitizer_runtime() -> str:

@@ -33,6 +33,19 @@ bool profile_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   return true;
 }
 void profile_commit() { ++t_count; }
+
+#ifdef QSA_DEBUG
+// Guard counters of the source files (debug builds register one per file).
+namespace {
+std::vector<hipError_t (*)(unsigned int*)>& guard_counters() {
+  static std::vector<hipError_t (*)(unsigned int*)> v;
+  return v;
+}
+}  // namespace
+void register_guard_counter(hipError_t (*read_and_clear)(unsigned int*)) {
+  guard_counters().push_back(read_and_clear);
+}
+#endif
 }  // namespace qsa
 
 namespace {
@@ -301,6 +314,29 @@ int32_t qsa_profile_detach(void) {
   t_events = nullptr;
   t_cap = 0;
   return n;
+}
+
+int32_t qsa_debug_build(void) {
+#ifdef QSA_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+qsa_status qsa_debug_guard_hits(uint64_t* hits) {
+  if (!hits) return QSA_ERR_NULL;
+  *hits = 0;
+#ifdef QSA_DEBUG
+  QSA_TRY(check_device());
+  if (hipDeviceSynchronize() != hipSuccess) return QSA_ERR_HIP;
+  for (auto read_and_clear : qsa::guard_counters()) {
+    unsigned int v = 0;
+    if (read_and_clear(&v) != hipSuccess) return QSA_ERR_HIP;
+    *hits += v;
+  }
+#endif
+  return QSA_OK;
 }
 
 const char* qsa_profile_kernel_name(int32_t i) {

@@ -89,7 +89,7 @@ struct AttnArgs {
 
 // Paged K/V: the pool row of token tok of sequence b (ids clamped into the pool).
 __device__ __forceinline__ int pool_row(const AttnArgs& a, int b, int tok) {
-  const int page = clampi(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
+  const int page = guard(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
   return (page << a.page_shift) + (tok & ((1 << a.page_shift) - 1));
 }
 
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   const int q = unit / (a.Hkv * hchunks);
   const int g = (unit / hchunks) % a.Hkv, hc = unit % hchunks;
   const size_t row = (size_t)b * a.Nq + q;
-  const int len = clampi(a.lens[b], 0, a.Lmax);
+  const int len = guard_len(a.lens[b], a.Nq, a.Lmax);
   const int t = len - a.Nq + q;
   const int k_begin = split * a.split_tokens;
   // This split's slice of the selection, loaded before n_sel is known (the
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   int ns = 0, ntok = 0, bt = 0;
   if (t >= 0) {
     bt = t >> 2;
-    ns = clampi(a.n_sel[row], 0, bt < kTopK ? bt : kTopK);
+    ns = guard(a.n_sel[row], 0, bt < kTopK ? bt : kTopK);
     ntok = 4 * ns + (t - 4 * bt) + 1;
   }
   const uint16_t* kbase = a.k + g * kHeadDim;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   for (int i = 0; i < kSelPer; ++i) {
     const int e = tid + kThreads * i;
     if (e < nsb && kb0 + e < ns) {
-      const int j = clampi(my_sel[i], 0, bt - 1);
+      const int j = guard(my_sel[i], 0, bt - 1);
       s_sel[e] = paged4 ? pool_row(a, b, 4 * j) : j;
     }
   }
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   const int g = u / cchunks, cc = u % cchunks;
   uint16_t* s_v = s_vw[wave];
   const int lane = lane_id();
-  const int len = clampi(a.lens[b], 0, a.Lmax);
+  const int len = guard_len(a.lens[b], a.Nq, a.Lmax);
   const int col = lane & 15;
   const int c = cc * 16 + col;  // (query, head) column
   const bool col_valid = c < a.Nq * a.G;
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   auto row_of = [&](int kk) -> long long { return kk < k_end ? kv_off(a, b, kk) : -1; };
   auto page_ids = [&](int T) -> int {
     const int tok = min(T + (lane & 31), k_end - 1);
-    return clampi(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
+    return guard(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
   };
   auto paged_row = [&](int T, int pe) {
     return [&, T, pe](int kk) -> long long {
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void block_teacher_kernel(AttnArg
   if (u >= a.Hkv * cchunks) return;  // (no workgroup barrier below)
   const int g = u / cchunks, cc = u % cchunks;
   const int lane = lane_id();
-  const int len = clampi(a.lens[b], 0, a.Lmax);
+  const int len = guard_len(a.lens[b], a.Nq, a.Lmax);
   const int col = lane & 15;
   const int c = cc * 16 + col;  // (query, head) column
   const bool col_valid = c < a.Nq * a.G;
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
   const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int qw = 16 * 2 * kPrefWaves / a.G;  // queries per workgroup
-  const int len = clampi(a.lens[b], 0, a.Lmax);
+  const int len = guard_len(a.lens[b], a.Nq, a.Lmax);
   const float c2 = a.scale_log2;
   bf16x8 qf[2][4];
   int tq[2];
@@ -865,14 +865,14 @@ __global__ __launch_bounds__(256) void teacher_recall_kernel(const float* __rest
   __shared__ float wsum[4];
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const size_t row = (size_t)b * Nq + q;
-  const int t = clampi(lens[b], 0, Lmax) - Nq + q;
+  const int t = guard_len(lens[b], Nq, Lmax) - Nq + q;
   const int nbp = Lmax >> 2;
   float acc = 0.f;
   if (t >= 0) {
     const int bt = t >> 2;
-    const int ns = clampi(n_sel[row], 0, min(bt, kTopK));
+    const int ns = guard(n_sel[row], 0, min(bt, kTopK));
     const float* tr = teacher + row * nbp;
-    for (int i = tid; i < ns; i += blockDim.x) acc += tr[clampi(sel[row * kTopK + i], 0, bt - 1)];
+    for (int i = tid; i < ns; i += blockDim.x) acc += tr[guard(sel[row * kTopK + i], 0, bt - 1)];
     if (tid == 0) acc += tr[bt];
   }
 #pragma unroll

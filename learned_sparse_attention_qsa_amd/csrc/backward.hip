@@ -50,12 +50,12 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
   const int g = blockIdx.y / hchunks, hc = blockIdx.y % hchunks;
   const int h0 = g * G + hc * kBwdHeads, nh = min(kBwdHeads, G - hc * kBwdHeads);
   const size_t row = (size_t)b * Nq + qi;
-  const int len = clampi(lens[b], 0, Lmax);
+  const int len = guard_len(lens[b], Nq, Lmax);
   const int t = len - Nq + qi;
   int ns = 0, ntok = 0, bt = 0;
   if (t >= 0) {
     bt = t >> 2;
-    ns = clampi(n_sel[row], 0, min(bt, kTopK));
+    ns = guard(n_sel[row], 0, min(bt, kTopK));
     ntok = 4 * ns + (t - 4 * bt) + 1;
   }
   // the heads' q, dO, D = dO . O and lse (exp2 domain)
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
     s_q[h][d] = bf(q[off]);
     s_do[h][d] = bf(d_out[off]);
   }
-  for (int i = tid; i < ns; i += kBwdThreads) s_sel[i] = clampi(sel[row * kTopK + i], 0, bt - 1);
+  for (int i = tid; i < ns; i += kBwdThreads) s_sel[i] = guard(sel[row * kTopK + i], 0, bt - 1);
   if (tid < kBwdHeads * 16) {
     // 16 lanes per head: partial dot products of dO and O
     const int h = tid >> 4, part = tid & 15;
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kBwdThreads) void index_scores_bwd_kernel(
   __shared__ float s_dq[kIbwdQ][kIdxHeads][kIdxDim];
   const int slice = blockIdx.x, q0 = blockIdx.y * kIbwdQ, b = blockIdx.z, tid = threadIdx.x;
   const int nq = min(kIbwdQ, Nq - q0);
-  const int len = clampi(lens[b], 0, Lmax);
+  const int len = guard_len(lens[b], Nq, Lmax);
   const int nbp = Lmax >> 2;
   for (int i = tid; i < kIbwdQ * kIdxHeads * kIdxDim; i += kBwdThreads) {
     const int qq = i / (kIdxHeads * kIdxDim), rem = i % (kIdxHeads * kIdxDim);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(const float* __restri
                                                            const int32_t* __restrict__ lens,
                                                            float* __restrict__ dk_idx, int Lmax) {
   const int b = blockIdx.y;
-  const int nb = clampi(lens[b], 0, Lmax) >> 2;
+  const int nb = guard(lens[b], 0, Lmax) >> 2;
   const size_t n = (size_t)nb * 4 * kIdxDim;
   const float* src = dk_cmp + (size_t)b * (Lmax >> 2) * kIdxDim;
   float* dst = dk_idx + (size_t)b * Lmax * kIdxDim;

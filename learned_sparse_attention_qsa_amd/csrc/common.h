@@ -73,6 +73,49 @@ __device__ __forceinline__ uint4 compress_chunk(const uint4* rows) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// ---- guards on caller-supplied values
+// A length outside [Nq, Lmax], a selected block outside [0, bt), a selection
+// count other than min(bt, 512), a page id outside the pool or a first block
+// past the completed ones is a caller bug.  Kernels clamp such values so that
+// no access leaves its buffer.  Builds with QSA_DEBUG also count every value
+// a guard caught, in a device counter per source file that the library's
+// qsa_debug_guard_hits() collects and clears.
+#ifdef QSA_DEBUG
+namespace {
+__device__ unsigned int g_guard_hits;
+}
+__device__ __forceinline__ void guard_hit() { atomicAdd(&g_guard_hits, 1u); }
+void register_guard_counter(hipError_t (*read_and_clear)(unsigned int*));
+namespace {
+hipError_t read_and_clear_guard_hits(unsigned int* out) {
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_guard_hits), sizeof(unsigned int));
+  if (e != hipSuccess) return e;
+  const unsigned int zero = 0u;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_guard_hits), &zero, sizeof(unsigned int));
+}
+const bool g_guard_registered = (register_guard_counter(&read_and_clear_guard_hits), true);
+}  // namespace
+#else
+__device__ __forceinline__ void guard_hit() {}
+#endif
+
+// x clamped to [lo, hi]; a value outside is a caught caller bug.
+__device__ __forceinline__ int guard(int x, int lo, int hi) {
+  const int c = clampi(x, lo, hi);
+#ifdef QSA_DEBUG
+  if (c != x) guard_hit();
+#endif
+  return c;
+}
+
+// A sequence length: clamped to [0, Lmax]; outside [Nq, Lmax] is caught.
+__device__ __forceinline__ int guard_len(int x, int Nq, int Lmax) {
+#ifdef QSA_DEBUG
+  if (x < Nq || x > Lmax) guard_hit();
+#endif
+  return clampi(x, 0, Lmax);
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

@@ -22,9 +22,9 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint16_t* __restric
                                                        const int32_t* __restrict__ first_block,
                                                        uint16_t* __restrict__ k_cmp, int Lmax) {
   const int b = blockIdx.y;
-  const int len = clampi(lens[b], 0, Lmax);
+  const int len = guard(lens[b], 0, Lmax);
   const int nb = len >> 2;
-  const int fb = first_block ? clampi(first_block[b], 0, nb) : 0;
+  const int fb = first_block ? guard(first_block[b], 0, nb) : 0;
   const size_t nbp = (size_t)(Lmax >> 2);
   const uint4* src = reinterpret_cast<const uint4*>(k_idx + (size_t)b * Lmax * kIdxDim);
   uint4* dst = reinterpret_cast<uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);

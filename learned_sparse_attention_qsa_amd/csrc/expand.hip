@@ -24,11 +24,11 @@ __global__ __launch_bounds__(128) void expand_kernel(const int32_t* __restrict__
   const int q = blockIdx.x;
   const int b = blockIdx.y;
   const size_t row = (size_t)b * Nq + q;
-  const int t = clampi(lens[b], 0, Lmax) - Nq + q;
+  const int t = guard_len(lens[b], Nq, Lmax) - Nq + q;
   int ns = 0, nt = 0, bt = 0;
   if (t >= 0) {
     bt = t >> 2;
-    ns = clampi(n_sel[row], 0, bt < kTopK ? bt : kTopK);
+    ns = guard(n_sel[row], 0, bt < kTopK ? bt : kTopK);
     nt = 4 * ns + (t - 4 * bt) + 1;
   }
   int4* out = reinterpret_cast<int4*>(tok + row * kMaxTok);
@@ -36,7 +36,11 @@ __global__ __launch_bounds__(128) void expand_kernel(const int32_t* __restrict__
   for (int g = threadIdx.x; g < kMaxTok / 4; g += blockDim.x) {
     int4 w;
     if (g < ns) {
-      const int base = 4 * srow[g];
+      const int id = srow[g];  // (ids outside [0, bt) are expanded as given)
+#ifdef QSA_DEBUG
+      if (id < 0 || id >= bt) guard_hit();
+#endif
+      const int base = 4 * id;
       w = make_int4(base, base + 1, base + 2, base + 3);
     } else {
       int e[4];

@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int tps = blockDim.x / nsub;
   const int seg = tid / tps, sub = tid % tps;
   const uint32_t n_seg_raw = seg < nsub ? cand_cnt[row * nsub + seg] : 0u;
-  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
+  const int t = query_t(guard_len(lens[b], Nq, Lmax), Nq, q);
   int32_t* srow = sel + row * kTopK;
   if (write_trivial(t, srow, n_sel + row)) return;
   const int bt = t >> 2;
@@ -549,14 +549,14 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ k_idx,
                                                           const int32_t* __restrict__ first_block) {
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
-  const int len = clampi(lens[b], 0, Lmax);
+  const int len = guard_len(lens[b], Nq, Lmax);
   const int nbp = Lmax >> 2;
   const int t_last = query_t(len, Nq, min(q0 + 3, Nq - 1));
   const int j_begin = slice * kTableSlice;
   const int j_end = min(j_begin + kTableSlice, t_last >= 0 ? (t_last >> 2) : 0);
   if (k_idx != nullptr) {
     const int nb = len >> 2;
-    const int fb = first_block ? clampi(first_block[b], 0, nb) : 0;
+    const int fb = first_block ? guard(first_block[b], 0, nb) : 0;
     const long long c0 = (long long)max(fb, j_begin) * 8;
     const long long c1 = (long long)min(nb, j_begin + kTableSlice) * 8;
     if (c0 < c1) {  // (uniform over the workgroup)
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
     s_mm[0] = 0xffffffffu;
     s_mm[1] = 0u;
   }
-  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
+  const int t = query_t(guard_len(lens[b], Nq, Lmax), Nq, q);
   int32_t* srow = sel + (size_t)row * kTopK;
   if (write_trivial(t, srow, n_sel + row)) return;
   const int bt = t >> 2;
@@ -1471,7 +1471,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   // (wavefront-uniform, so that the scan's loop control stays scalar)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / kPar, par = wave % kPar;
-  const int len = clampi(lens[b], 0, Lmax);
+  const int len = guard_len(lens[b], Nq, Lmax);
   const int nbp = Lmax >> 2;
   const int gq0 = qbase + grp * 32;  // first query of the group
   const int t_last = query_t(len, Nq, min(gq0 + 31, Nq - 1));
@@ -1736,7 +1736,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_filter_kernel(
   if (tid < 4) s_cnt[tid] = 0u;
 
   // the group's queries ascend in position: its first and last valid one
-  const int len = clampi(lens[b], 0, Lmax);
+  const int len = guard_len(lens[b], Nq, Lmax);
   const int nb = len >> 2;
   const int t_first = query_t(len, Nq, q0);
   const int t_last = query_t(len, Nq, min(q0 + 3, Nq - 1));
@@ -1748,7 +1748,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_filter_kernel(
   const int j_end = min(j_begin + slice_blocks, bt_g);
   const bool active = j_begin < j_end;  // (uniform)
   int fb = nb;  // blocks from fb on are not in the cache yet
-  if (k_idx != nullptr) fb = first_block ? clampi(first_block[b], 0, nb) : 0;
+  if (k_idx != nullptr) fb = first_block ? guard(first_block[b], 0, nb) : 0;
   // blocks not yet in the cache, compressed here: in the prefetched batches
   // (then written to the cache) and among the samples
   auto fix_new = [&](uint4 (&bv)[kScanU][2], int bi) {
@@ -1914,7 +1914,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_select_kernel(
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = lane_id();
   const int wave = tid >> 6;
   const size_t row = (size_t)b * Nq + q;
-  const int t = query_t(clampi(lens[b], 0, Lmax), Nq, q);
+  const int t = query_t(guard_len(lens[b], Nq, Lmax), Nq, q);
   int32_t* srow = sel + row * kTopK;
   if (write_trivial(t, srow, n_sel + row)) return;
   const int bt = t >> 2;

@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = Q.load_library()
     declared = header_symbols()
-    assert len(declared) == 23
+    assert len(declared) == 25
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -194,3 +194,19 @@ def test_paged_descriptor_rejected_before_any_launch():
                                      None, None, None, None, None) == Q.OK
     assert lib.qsa_dense_gqa_prefill(ctypes.byref(shp), None, FAKE, FAKE, ok, FAKE, FAKE,
                                      None, None) == Q.ERR_NULL
+
+
+def test_debug_entry_points_without_a_device():
+    from learned_sparse_attention_qsa_amd import build as B
+    lib = Q.load_library()
+    assert lib.qsa_debug_build() == 0
+    n = ctypes.c_uint64(7)
+    assert lib.qsa_debug_guard_hits(ctypes.byref(n)) == Q.OK and n.value == 0
+    assert lib.qsa_debug_guard_hits(None) == Q.ERR_NULL
+    if not os.path.exists(B.DEBUG_LIB):
+        B.build_debug()
+    dbg = ctypes.CDLL(B.DEBUG_LIB)
+    dbg.qsa_debug_build.restype = ctypes.c_int32
+    dbg.qsa_debug_guard_hits.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    assert dbg.qsa_debug_build() == 1
+    assert dbg.qsa_debug_guard_hits(None) == Q.ERR_NULL
