@@ -484,13 +484,15 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   const uint16_t* kbase = a.k + g * kHeadDim;
   const uint16_t* vbase = a.v + g * kHeadDim;
   auto row_of = [&](int kk) -> long long { return kk < k_end ? kv_off(a, b, kk) : -1; };
+  // (the id is checked where it is used, so that nothing waits for the
+  // load early)
   auto page_ids = [&](int T) -> int {
     const int tok = min(T + (lane & 31), k_end - 1);
-    return guard(a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)], 0, a.n_pages - 1);
+    return a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)];
   };
   auto paged_row = [&](int T, int pe) {
     return [&, T, pe](int kk) -> long long {
-      const int page = __shfl(pe, (kk - T) & 31);
+      const int page = guard(__shfl(pe, (kk - T) & 31), 0, a.n_pages - 1);
       if (kk >= k_end) return -1;
       return (((long long)page << a.page_shift) + (kk & ((1 << a.page_shift) - 1))) * a.Hkv *
              kHeadDim;
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
   if (k_begin < k_end) {
     if constexpr (kPaged) {
       load_tile(cur, kbase, vbase, k_begin, paged_row(k_begin, page_ids(k_begin)));
-      if (k_begin + kTile < k_end) pe_nxt = page_ids(k_begin + kTile);
+      pe_nxt = page_ids(k_begin + kTile);
     } else {
       load_tile(cur, kbase, vbase, k_begin, row_of);
     }
@@ -513,7 +515,9 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense_decode_kernel(AttnArgs
     int pe_after = 0;
     if constexpr (kPaged) {
       if (k0 + kTile < k_end) load_tile(nxt, kbase, vbase, k0 + kTile, paged_row(k0 + kTile, pe_nxt));
-      if (k0 + 2 * kTile < k_end) pe_after = page_ids(k0 + 2 * kTile);
+      // (unconditional: past the end it reads the last token's id; a
+      // conditional load would be waited for at the iteration's end)
+      pe_after = page_ids(k0 + 2 * kTile);
     } else {
       if (k0 + kTile < k_end) load_tile(nxt, kbase, vbase, k0 + kTile, row_of);
     }
@@ -646,6 +650,12 @@ __device__ __forceinline__ int vt_pos(int tau) {
   return (((tau >> 2) & 3) << 3) | ((tau >> 4) << 2) | (tau & 3);
 }
 
+// kPaged: K/V through the page table.  The page ids of the rows an
+// iteration requests at its end are loaded at its start, so the table read
+// completes under the iteration's MFMA work; a page id carried from one
+// iteration to the next would instead make the compiler wait, at the loop's
+// back edge, for every load issued before it (the row prefetches too).
+template <bool kPaged>
 __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t s_k[2][kPrefTok * kVStride];
   __shared__ __align__(16) uint16_t s_vt[2][kHeadDim * kPrefVtStride];
@@ -678,9 +688,24 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
   // wave + 8 of its K or V row (a token past t_hi reads t_hi's row, which
   // the masks then ignore).
   auto row_ptr = [&](const uint16_t* base, int i) -> const uint4* {
-    const long long off = kv_off(a, b, min(i * kPrefTok + lane, t_hi)) + (long long)g * kHeadDim;
-    return reinterpret_cast<const uint4*>(base + off);
+    const int tok = min(i * kPrefTok + lane, t_hi);
+    const long long row = kPaged ? (long long)pool_row(a, b, tok) : (long long)b * a.Lmax + tok;
+    return reinterpret_cast<const uint4*>(base + row * a.Hkv * kHeadDim + (long long)g * kHeadDim);
   };
+  // paged: the page id of this thread's token of tile i (a load, checked
+  // only where it is used, so that nothing waits for it early), and the row
+  // of that token given its page id
+  auto page_of = [&](int i) -> int {
+    const int tok = min(i * kPrefTok + lane, t_hi);
+    return a.pt[(size_t)b * a.max_pages + (tok >> a.page_shift)];
+  };
+  auto row_in = [&](const uint16_t* base, int i, int page) -> const uint4* {
+    const int tok = min(i * kPrefTok + lane, t_hi);
+    page = guard(page, 0, a.n_pages - 1);
+    const long long r = ((long long)page << a.page_shift) + (tok & ((1 << a.page_shift) - 1));
+    return reinterpret_cast<const uint4*>(base + r * a.Hkv * kHeadDim + (long long)g * kHeadDim);
+  };
+
   const int vcol = (lane & 32) | vt_pos(lane & 31);  // this thread's token in a V^T row
   auto stash_k = [&](int buf, uint4 r0, uint4 r1) {
     *reinterpret_cast<uint4*>(&s_k[buf][lane * kVStride + wave * 8]) = r0;
@@ -750,31 +775,34 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
   if (n_tiles > 0) {
     const uint4* kp = row_ptr(a.k, 0);
     const uint4* vp = row_ptr(a.v, 0);
+    const uint4* kp1 = row_ptr(a.k, 1);
     stash_k(0, kp[wave], kp[wave + 8]);
     stash_v(0, vp[wave], vp[wave + 8]);
-    if (n_tiles > 1) {
-      const uint4* kp1 = row_ptr(a.k, 1);
-      stash_k(1, kp1[wave], kp1[wave + 8]);
-    }
+    stash_k(1, kp1[wave], kp1[wave + 8]);
   }
   // Every path into the loop has the Q fragments in registers: without this
   // wait the compiler, merging the paths, waits for every load in flight at
   // the first MFMA of each iteration.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only
   __syncthreads();
-  if (n_tiles > 0) qk(0, 0, z);
-  if (n_tiles > 2) {
+  if (n_tiles > 0) {
+    qk(0, 0, z);
     const uint4* kp = row_ptr(a.k, 2);
+    const uint4* vp = row_ptr(a.v, 1);
     rk0 = kp[wave];
     rk1 = kp[wave + 8];
-  }
-  if (n_tiles > 1) {
-    const uint4* vp = row_ptr(a.v, 1);
     rv0 = vp[wave];
     rv1 = vp[wave + 8];
   }
   for (int i = 0; i < n_tiles; ++i) {
     const int cur = i & 1;
+    // paged: ids of the rows requested at the end of this iteration (a tile
+    // past the last reads the last token's id, unused)
+    int pg_k = 0, pg_v = 0;
+    if (kPaged) {
+      pg_k = page_of(i + 3);
+      pg_v = page_of(i + 2);
+    }
     if (i + 1 < n_tiles) qk(cur ^ 1, i + 1, zn);
     float alpha[2];
 #pragma unroll
@@ -818,15 +846,17 @@ __global__ __launch_bounds__(64 * kPrefWaves) void dense_prefill_kernel(AttnArgs
         o[1][dt] = mfma16(u, pf1, o[1][dt]);
       }
     }
-    if (i + 2 < n_tiles) stash_k(cur, rk0, rk1);
-    if (i + 1 < n_tiles) stash_v(cur ^ 1, rv0, rv1);
-    if (i + 3 < n_tiles) {
-      const uint4* kp = row_ptr(a.k, i + 3);
+    // Stores and loads are unconditional: tiles past the last read the last
+    // token's rows and fill buffers no later iteration reads.  (Conditional
+    // ones make the compiler's wait counts conservative at the merges, down
+    // to waiting for every load in flight.)
+    stash_k(cur, rk0, rk1);
+    stash_v(cur ^ 1, rv0, rv1);
+    {
+      const uint4* kp = kPaged ? row_in(a.k, i + 3, pg_k) : row_ptr(a.k, i + 3);
       rk0 = kp[wave];
       rk1 = kp[wave + 8];
-    }
-    if (i + 2 < n_tiles) {
-      const uint4* vp = row_ptr(a.v, i + 2);
+      const uint4* vp = kPaged ? row_in(a.v, i + 2, pg_v) : row_ptr(a.v, i + 2);
       rv0 = vp[wave];
       rv1 = vp[wave + 8];
     }
@@ -1203,9 +1233,11 @@ hipError_t launch_dense_prefill(const Dims& d, const uint16_t* q, const uint16_t
   a.G = d.Hq / d.Hkv;
   a.scale_log2 = d.scale * kLog2e;
   const int qw = 16 * 2 * kPrefWaves / a.G;
-  QSA_LAUNCH(dense_prefill_kernel,
-             dim3((unsigned)((d.Nq + qw - 1) / qw), (unsigned)d.Hkv, (unsigned)d.B),
-             dim3(64 * kPrefWaves), 0, s, a);
+  const dim3 grid((unsigned)((d.Nq + qw - 1) / qw), (unsigned)d.Hkv, (unsigned)d.B);
+  if (a.pt)
+    QSA_LAUNCH(dense_prefill_kernel<true>, grid, dim3(64 * kPrefWaves), 0, s, a);
+  else
+    QSA_LAUNCH(dense_prefill_kernel<false>, grid, dim3(64 * kPrefWaves), 0, s, a);
   return hipGetLastError();
 }
 
