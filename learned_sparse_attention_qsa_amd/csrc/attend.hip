@@ -375,12 +375,16 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();  // every wavefront is done with its V tile: reuse s_v
-  float* O = reinterpret_cast<float*>(&s_v[0][0]);  // [kWaves][16][128]
+  // [kWaves][16][kOStride]: a column's 128 floats padded to 132 so that the
+  // 16 columns' float4 stores of one wavefront hit distinct banks
+  constexpr int kOStride = kHeadDim + 4;
+  static_assert(kOStride * 16 * 4 <= kTile * kVStride * 2, "merge scratch fits the V tiles");
+  float* O = reinterpret_cast<float*>(&s_v[0][0]);
   {
     const int gq = lane >> 4;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(O + (wave * 16 + col) * kHeadDim + dt * 16 + gq * 4) =
+      *reinterpret_cast<float4*>(O + (wave * 16 + col) * kOStride + dt * 16 + gq * 4) =
           make_float4(r.o[dt][0], r.o[dt][1], r.o[dt][2], r.o[dt][3]);
     if (lane < 16) {
       s_m[wave][lane] = r.m;
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_attend_kernel(AttnArgs a) 
 #pragma unroll
     for (int j = 0; j < kWpu; ++j) {
       const int w = uu + kUnits * j;
-      o += s_f[w][c] * O[(w * 16 + c) * kHeadDim + d];
+      o += s_f[w][c] * O[(w * 16 + c) * kOStride + d];
     }
     o *= s_inv[uu][c];
     const size_t rh = row * a.Hq + head0(uu) + c;
