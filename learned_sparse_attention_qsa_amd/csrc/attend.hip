@@ -919,58 +919,37 @@ __global__ __launch_bounds__(256) void teacher_recall_kernel(const float* __rest
 // ------------------------------------------------------------------ merge
 // Grid (Hq, Nq, B), 128 threads (one per output dim).  Combines the n_split
 // partial (o, lse) pairs of one (query, head): o = sum_s e^(lse_s - M) o_s /
-// sum_s e^(lse_s - M).  Loads go out 32 splits at a time so that their
-// latencies overlap.
+// sum_s e^(lse_s - M).  Up to kChunk partials: every load goes out at once,
+// unconditionally (slots past n_split re-read the last partial and weigh 0),
+// so they share one round trip; more partials are walked kChunk at a time.
+template <int kChunk>
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse, int Nq, int Hq,
                                                     int n_split) {
-  constexpr int kChunk = 32;
   const int h = blockIdx.x, q = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const size_t rh = ((size_t)b * Nq + q) * Hq + h;
   const float* pl = part_lse + rh * n_split;
   const float* po = part_o + rh * n_split * kHeadDim + d;
   float M = kNegInf;
-  float acc = 0.f, sw = 0.f;
-  if (n_split <= kChunk) {
-    // every partial in one round of loads
-    float w[kChunk], v[kChunk];
+  for (int s0 = 0; s0 < n_split; s0 += kChunk) {
 #pragma unroll
-    for (int s = 0; s < kChunk; ++s) {
-      const bool ok = s < n_split;
-      w[s] = ok ? pl[s] : kNegInf;
-      v[s] = ok ? po[(size_t)s * kHeadDim] : 0.f;
-    }
-#pragma unroll
-    for (int s = 0; s < kChunk; ++s) M = fmaxf(M, w[s]);
-    if (M != kNegInf) {
-#pragma unroll
-      for (int s = 0; s < kChunk; ++s) {
-        const float e = w[s] == kNegInf ? 0.f : __expf(w[s] - M);
-        sw += e;
-        acc += e * v[s];
-      }
-    }
-  } else {
-    for (int s0 = 0; s0 < n_split; s0 += kChunk) {
-#pragma unroll
-      for (int s = 0; s < kChunk; ++s)
-        if (s0 + s < n_split) M = fmaxf(M, pl[s0 + s]);
-    }
+    for (int s = 0; s < kChunk; ++s) M = fmaxf(M, pl[min(s0 + s, n_split - 1)]);
   }
-  if (n_split > kChunk && M != kNegInf) {
+  float acc = 0.f, sw = 0.f;
+  if (M != kNegInf) {
     for (int s0 = 0; s0 < n_split; s0 += kChunk) {
       float w[kChunk], v[kChunk];
 #pragma unroll
       for (int s = 0; s < kChunk; ++s) {
-        const bool ok = s0 + s < n_split;
-        w[s] = ok ? pl[s0 + s] : kNegInf;
-        v[s] = ok ? po[(size_t)(s0 + s) * kHeadDim] : 0.f;
+        const int si = min(s0 + s, n_split - 1);
+        w[s] = pl[si];
+        v[s] = po[(size_t)si * kHeadDim];
       }
 #pragma unroll
       for (int s = 0; s < kChunk; ++s) {
-        const float e = w[s] == kNegInf ? 0.f : __expf(w[s] - M);
+        const float e = (s0 + s < n_split && w[s] != kNegInf) ? __expf(w[s] - M) : 0.f;
         sw += e;
         acc += e * v[s];
       }
@@ -979,6 +958,21 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   const float o = sw > 0.f ? acc / sw : 0.f;
   out[rh * kHeadDim + d] = (uint16_t)f32_to_bf16(o);
   if (lse && d == 0) lse[rh] = sw > 0.f ? M + __logf(sw) : kNegInf;
+}
+
+hipError_t launch_merge(const float* part_o, const float* part_lse, uint16_t* out, float* lse,
+                        const Dims& d, int n_split, hipStream_t s) {
+  const dim3 grid((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B);
+  if (n_split <= 4)
+    QSA_LAUNCH(merge_kernel<4>, grid, dim3(128), 0, s, part_o, part_lse, out, lse, d.Nq, d.Hq,
+               n_split);
+  else if (n_split <= 8)
+    QSA_LAUNCH(merge_kernel<8>, grid, dim3(128), 0, s, part_o, part_lse, out, lse, d.Nq, d.Hq,
+               n_split);
+  else
+    QSA_LAUNCH(merge_kernel<16>, grid, dim3(128), 0, s, part_o, part_lse, out, lse, d.Nq, d.Hq,
+               n_split);
+  return hipGetLastError();
 }
 
 int sparse_units(const Dims& d) {
@@ -1113,9 +1107,7 @@ hipError_t launch_sparse_attend(const Dims& d, const uint16_t* q, const uint16_t
   else
     QSA_LAUNCH_AS("sparse_attend_kernel<true>", (sparse_attend_kernel<true, 4, 1>), grid,
                   dim3(256), 0, s, a);
-  if (a.n_split > 1)
-    QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
-               part_o, part_lse, out, lse, d.Nq, d.Hq, a.n_split);
+  if (a.n_split > 1) return launch_merge(part_o, part_lse, out, lse, d, a.n_split, s);
   return hipGetLastError();
 }
 
@@ -1212,9 +1204,7 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
     QSA_LAUNCH(dense_decode_kernel<true>, grid, dim3(64 * (unsigned)waves), 0, s, a);
   else
     QSA_LAUNCH(dense_decode_kernel<false>, grid, dim3(64 * (unsigned)waves), 0, s, a);
-  QSA_LAUNCH(merge_kernel, dim3((unsigned)d.Hq, (unsigned)d.Nq, (unsigned)d.B), dim3(128), 0, s,
-             a.part_o, a.part_lse, out, lse, d.Nq, d.Hq, a.n_split);
-  return hipGetLastError();
+  return launch_merge(a.part_o, a.part_lse, out, lse, d, a.n_split, s);
 }
 
 hipError_t launch_dense_prefill(const Dims& d, const uint16_t* q, const uint16_t* k,
