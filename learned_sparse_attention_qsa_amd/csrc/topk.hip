@@ -593,17 +593,15 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
   for (int batch = 0; batch < 2; ++batch) {
     const int jt = j_begin + wave * (2 * U * 16) + batch * (U * 16);
     if (jt >= j_end) break;
+    // Unconditional loads (a block past the slice re-reads the slice's last
+    // one; its score is masked below): with per-lane conditions the
+    // compiler's wait before the first MFMA covers nearly the whole batch.
     uint4 bv[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jt + u * 16 + r;
-      if (j < j_end) {
-        bv[u][0] = kb[(size_t)j * 8 + kc];
-        bv[u][1] = kb[(size_t)j * 8 + 4 + kc];
-      } else {
-        bv[u][0] = zero_u4();
-        bv[u][1] = zero_u4();
-      }
+      const int j = min(jt + u * 16 + r, j_end - 1);
+      bv[u][0] = kb[(size_t)j * 8 + kc];
+      bv[u][1] = kb[(size_t)j * 8 + 4 + kc];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
