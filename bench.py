@@ -306,10 +306,17 @@ def decode_leg(args, Q, W, torch, np, flush):
     nsel_h = ws.n_sel.cpu().numpy()
     kcmp, attn, qidx = decode_bytes(w, sel_h, nsel_h, np)
     # cold: the whole compressed-key cache rebuilt inside the call
-    log(f"[bench] decode cold: {args.cold_steps} steps with a full compressed-key rebuild")
-    cold_ms, cold_k, _ = timed_steps(lambda: ws.step(cold=True), args.cold_steps, flush, Q, torch)
-    ws.step()  # leave the steady-state cache and selection behind
-    torch.cuda.synchronize()
+    cold = None
+    if args.cold_steps > 0:
+        log(f"[bench] decode cold: {args.cold_steps} steps with a full compressed-key rebuild")
+        cold_ms, cold_k, _ = timed_steps(lambda: ws.step(cold=True), args.cold_steps, flush, Q,
+                                         torch)
+        ws.step()  # leave the steady-state cache and selection behind
+        torch.cuda.synchronize()
+        cold = {"ms_per_step": sum(cold_ms) / len(cold_ms), "steps": len(cold_ms),
+                "kernels": cold_k,
+                "note": "every block of the 1M-token contexts compressed inside the call "
+                        "(k_idx 512 MiB read, k_cmp 128 MiB written), then the step"}
     # selection quality: the share of the dense attention mass (pooled per
     # micro-block, the indexer's training target) that the selection keeps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -352,11 +359,7 @@ def decode_leg(args, Q, W, torch, np, flush):
     return dict(w=w, ws=ws, step_ms=step_ms, kstats=kstats, wall=wall, sel=sel_h, n_sel=nsel_h,
                 quality=quality, backward=backward,
                 algo=decode_algo(kcmp, attn, qidx, w.batch), kcmp_bytes=kcmp, attn_bytes=attn,
-                qidx_bytes=qidx,
-                cold={"ms_per_step": sum(cold_ms) / len(cold_ms), "steps": len(cold_ms),
-                      "kernels": cold_k,
-                      "note": "every block of the 1M-token contexts compressed inside the call "
-                              "(k_idx 512 MiB read, k_cmp 128 MiB written), then the step"})
+                qidx_bytes=qidx, cold=cold)
 
 
 def dense_leg(args, Q, torch, flush, d):

@@ -58,3 +58,34 @@ def padded_tok(res, B, Nq):
         tok[b, i, :t.shape[0]] = t
         n_tok[b, i] = t.shape[0]
     return tok, n_tok
+
+
+def paged_pools_dev(k, v, lens, page, seed):
+    """Page pools [n_pages][page][Hkv][128] holding the device caches k, v
+    ([B][L][Hkv][128]) under a seeded random page order, and their page
+    table (a Q.PagedKV)."""
+    import learned_sparse_attention_qsa_amd as Q
+    B, L, Hkv, D = k.shape
+    max_pages = (L + page - 1) // page
+    need = [(int(n) + page - 1) // page for n in lens]
+    n_pages = max(1, sum(need))
+    g = torch.Generator().manual_seed(seed)
+    ids = torch.randperm(n_pages, generator=g)
+    table = torch.zeros((B, max_pages), dtype=torch.int32)
+    k_pool = torch.empty((n_pages, page, Hkv, D), dtype=k.dtype, device=k.device)
+    v_pool = torch.empty_like(k_pool)
+    off = 0
+    for b in range(B):
+        n, full = need[b], int(lens[b]) // page
+        pid = ids[off:off + n]
+        off += n
+        table[b, :n] = pid.to(torch.int32)
+        if full:
+            idx = pid[:full].to(k.device)
+            k_pool[idx] = k[b, :full * page].view(full, page, Hkv, D)
+            v_pool[idx] = v[b, :full * page].view(full, page, Hkv, D)
+        if n > full:
+            rest = int(lens[b]) - full * page
+            k_pool[int(pid[full]), :rest] = k[b, full * page:full * page + rest]
+            v_pool[int(pid[full]), :rest] = v[b, full * page:full * page + rest]
+    return k_pool, v_pool, Q.PagedKV(table.to(k.device), page, n_pages)

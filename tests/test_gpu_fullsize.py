@@ -7,7 +7,11 @@ and the call compresses only the new ones):
     rows, outputs of sampled rows;
   * the 1M last-chunk prefill: the selection of every one of the 16,384
     rows, outputs of sampled rows;
-  * the dense 1M comparator: one row of every sequence.
+  * the dense 1M comparator: one row of every sequence;
+  * paged K/V at the bench's shapes (16-token pages in a shuffled pool): the
+    1M decode forward and dense decode, and the 1M-chunk dense prefill, bit
+    for bit against the contiguous results; the dense prefill also against
+    the oracle on sampled rows.
 
 Selections bit for bit (the oracle's row-batched scorer and selector);
 outputs to max-abs <= 2e-2 and rel-L2 <= 1e-2 against the float64 oracle."""
@@ -21,7 +25,7 @@ import torch
 import learned_sparse_attention_qsa_amd as Q
 import oracle as O
 import workloads as W
-from gpu_util import check_close, dev_bf16, dev_i32, host_f64_from_bf16
+from gpu_util import check_close, dev_bf16, dev_i32, host_f64_from_bf16, paged_pools_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -137,3 +141,58 @@ def test_dense_decode_1m_one_row_per_sequence():
     check_close(np.stack([got[b, i] for b, i in rows]), np.stack([ref[r][0] for r in rows]))
     for b, i in rows:
         np.testing.assert_allclose(lse_h[b, i], ref[(b, i)][1], atol=2e-2, rtol=0)
+
+
+def test_paged_decode_1m_matches_contiguous():
+    say("paged decode 1M: inputs")
+    w = W.make(4)
+    shp = Q.shape(w.batch, w.max_len, w.n_query, w.q_heads, w.kv_heads)
+    prev = (w.lens - w.n_query).astype(np.int32)
+    first = dev_i32((prev // 4).astype(np.int32))
+    t = {n: dev_bf16(getattr(w, n)) for n in ("q_idx", "k_idx", "q", "k", "v")}
+    lens = dev_i32(w.lens)
+    k_cmp = torch.zeros((w.batch, w.max_len // 4, 64), dtype=torch.bfloat16, device="cuda")
+    Q.compress_keys(shp, t["k_idx"], dev_i32(prev), k_cmp)
+    k_cmp2 = k_cmp.clone()
+    say("paged decode 1M: pools")
+    k_pool, v_pool, pg = paged_pools_dev(t["k"], t["v"], w.lens, 16, 41)
+    say("paged decode 1M: forward, contiguous and paged")
+    o1, l1, s1, n1 = Q.forward(shp, t["q_idx"], t["k_idx"], k_cmp, t["q"], t["k"], t["v"], lens,
+                               first_block=first,
+                               sel=torch.empty((w.batch, w.n_query, 512), dtype=torch.int32,
+                                               device="cuda"),
+                               n_sel=torch.empty((w.batch, w.n_query), dtype=torch.int32,
+                                                 device="cuda"))
+    o2, l2, s2, n2 = Q.forward_paged(shp, t["q_idx"], t["k_idx"], k_cmp2, t["q"], k_pool, v_pool,
+                                     pg, lens, first_block=first,
+                                     sel=torch.empty_like(s1), n_sel=torch.empty_like(n1))
+    say("paged decode 1M: dense comparator, contiguous and paged")
+    d1, dl1 = Q.dense_gqa_decode(shp, t["q"], t["k"], t["v"], lens)
+    d2, dl2 = Q.dense_gqa_decode_paged(shp, t["q"], k_pool, v_pool, pg, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(n1, n2) and torch.equal(k_cmp, k_cmp2)
+    for a, b in ((o1, o2), (l1, l2), (d1, d2), (dl1, dl2)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_dense_prefill_1m_chunk():
+    say("dense prefill 1M: inputs")
+    w = W.make(3)
+    shp = Q.shape(w.batch, w.max_len, w.n_query, w.q_heads, w.kv_heads)
+    q, k, v, lens = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), dev_i32(w.lens)
+    say("dense prefill 1M: contiguous")
+    o1, l1 = Q.dense_gqa_prefill(shp, q, k, v, lens)
+    say("dense prefill 1M: paged")
+    k_pool, v_pool, pg = paged_pools_dev(k, v, w.lens, 16, 42)
+    o2, l2 = Q.dense_gqa_prefill(shp, q, k_pool, v_pool, lens, paged=pg)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    got = host_f64_from_bf16(o1)
+    lse_h = l1.cpu().numpy()
+    rows = [(0, 0), (0, 8191), (0, w.n_query - 1)]
+    say("dense prefill 1M: oracle on", rows)
+    ref = O.dense_decode(w.q, w.k, w.v, w.lens, w.n_query, queries=rows)
+    check_close(np.stack([got[r] for r in rows]), np.stack([ref[r][0] for r in rows]))
+    for r in rows:
+        np.testing.assert_allclose(lse_h[r], ref[r][1], atol=2e-2, rtol=0)
