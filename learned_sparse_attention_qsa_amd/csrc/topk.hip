@@ -1162,26 +1162,52 @@ __device__ __forceinline__ void stream_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// B fragments of column tile c (MFMA B layout: lane -> block 32c + lane&31,
-// dims 16 ks + 8 (lane>>5)), through a buffer resource that spans the
-// tile's blocks below bt_g: the blocks at or past bt_g read as zeros (their
-// scores are masked).  The tile's address is scalar work; the lane offset
-// (voff bytes) is fixed.
+// The stream scorer reads the compressed keys in fragment order: a copy in
+// which column tile c (32 blocks) is 4 KiB laid out as [k-step ks][lane l],
+// 16 bytes each, lane l holding block 32c + (l & 31), dims 16 ks + 8 (l >> 5)
+// .. + 8 -- the 32x32x16 MFMA's B operand.  A wavefront's fragment load then
+// reads 1 KiB of consecutive bytes (8 cache lines) where the row-major cache
+// needs 32 lines, which kept the texture path busy 92 % of the scan.
+// frag_order_kernel writes the copy: one thread per 16-byte chunk of the
+// sequence's blocks below its last query's own block.
+constexpr int kFragTile = kColTile * 8;  // 16-byte chunks per column tile
+__global__ __launch_bounds__(256) void frag_order_kernel(const uint4* __restrict__ src,
+                                                         uint4* __restrict__ dst,
+                                                         const int32_t* __restrict__ lens,
+                                                         int Lmax, int Nq, int ncol_pad) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;  // chunk index in the sequence
+  const int j = i >> 3, d8 = i & 7;
+  const int len = guard_len(lens[b], Nq, Lmax);
+  const int nb = len > 0 ? ((len - 1) >> 2) : 0;  // blocks below the last query's own block
+  if (j >= nb) return;
+  const int nbp = Lmax >> 2;
+  const uint4 v = src[(size_t)b * nbp * 8 + i];
+  const int c = j >> 5, r = j & 31, ks = d8 >> 1, half = d8 & 1;
+  dst[((size_t)b * ncol_pad + c) * kFragTile + ks * 64 + half * 32 + r] = v;
+}
+
+// B fragments of column tile c from the fragment-ordered copy (kb: the
+// sequence's first tile), through a buffer resource over the tile: lanes of
+// blocks at or past bt_g get an offset past its end and read zeros (their
+// scores are masked).  The tile's address is scalar work; voff is the
+// lane's byte offset within a k-step (lane x 16).
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw 32-bit buffer, no swizzle
 __device__ __forceinline__ void load_cols(const uint4* kb, int c, int bt_g, uint32_t voff,
                                           uint4 (&bv)[4]) {
   // (every operand is wavefront-uniform; readfirstlane lets the compiler
   // keep the descriptor in scalar registers, with no waterfall loop; the
-  // 32-byte steps go in the scalar offset)
+  // 1 KiB k-steps go in the scalar offset)
   const int valid = __builtin_amdgcn_readfirstlane(min(max(bt_g - c * kColTile, 0), kColTile));
-  const uint64_t a = reinterpret_cast<uint64_t>(kb + (size_t)c * kColTile * 8);
+  const uint64_t a = reinterpret_cast<uint64_t>(kb + (size_t)c * kFragTile);
   const uint64_t au = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(au), (short)0, valid * kIdxDim * 2, (int)kBufferConfig);
+      reinterpret_cast<void*>(au), (short)0, kFragTile * 16, (int)kBufferConfig);
+  const uint32_t vo = (int)(lane_id() & 31) < valid ? voff : 0x40000000u;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    bv[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 32 * ks, 0));
+    bv[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, 1024 * ks, 0));
 }
 
 // MFMAs of half kHalf (row tiles 2 kHalf, 2 kHalf + 1) against one column tile.
@@ -1452,7 +1478,7 @@ __device__ __forceinline__ int query_bound(const Stream& st, int q, bool fits) {
 // Grid (ceil(Nq/64), B); 4 wavefronts: two per group of 32 queries, one per
 // column-tile parity.
 __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
-                                                           const uint16_t* __restrict__ k_cmp,
+                                                           const uint4* __restrict__ k_frag,
                                                            const int32_t* __restrict__ lens,
                                                            uint64_t* __restrict__ lists,
                                                            uint32_t* __restrict__ list_cnt,
@@ -1481,7 +1507,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   const int ns = __builtin_amdgcn_readfirstlane(
       ncol > kSampleStep * par ? (ncol - 1 - kSampleStep * par) / kSampleStride + 1 : 0);
   const int nf = __builtin_amdgcn_readfirstlane(ncol > par ? (ncol - 1 - par) / kPar + 1 : 0);
-  const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
+  const uint4* kb = k_frag + (size_t)b * ((nbp + kColTile - 1) / kColTile) * kFragTile;
   for (int i = tid; i < kStreamQ * kHistWords; i += blockDim.x) (&s_h[0][0])[i] = 0u;
   if (tid < kStreamQ) {
     s_mx[tid] = 0u;
@@ -1494,7 +1520,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const u
   st.cnt = &s_cnt[grp * 32];
   st.rec = s_rec[wave];
   st.tau = &s_tau[grp * 32];
-  st.voff = (uint32_t)(((lane & 31) * 8 + (lane >> 5)) * 16);
+  st.voff = (uint32_t)(lane * 16);
   // Stationary A fragments: 4 row tiles x 4 k-steps.  Row (lane & 31) of row
   // tile rt is query gq0 + rt*8 + row/4, head row%4; k chunk lane >> 5.
   bf16x8 A[4][4];
@@ -2235,6 +2261,7 @@ struct StreamWs {
   uint64_t* lists;
   uint32_t* cnt;
   int32_t* tau;
+  uint4* frag;  // [B][column tiles][kFragTile] fragment-ordered compressed keys
 };
 TableWs carve_table(const Dims& d, void* ws, size_t* total) {
   Carve c{static_cast<char*>(ws), 0};
@@ -2266,6 +2293,7 @@ StreamWs carve_stream(const Dims& d, void* ws, size_t* total) {
   w.lists = c.take<uint64_t>(rows * kListCap);
   w.cnt = c.take<uint32_t>(rows);
   w.tau = c.take<int32_t>(rows);
+  w.frag = c.take<uint4>((size_t)d.B * ((d.Lmax / 4 + kColTile - 1) / kColTile) * kFragTile);
   if (total) *total = c.off;
   return w;
 }
@@ -2333,9 +2361,14 @@ hipError_t launch_index_topk(const Dims& d, TopkPath path, const uint16_t* q_idx
                d.Nq, g.slice_blocks, g.n_slices);
   } else {
     StreamWs w = carve_stream(d, ws, nullptr);
+    const int nbp = d.Lmax / 4;
+    const int ncol_pad = (nbp + kColTile - 1) / kColTile;
+    QSA_LAUNCH(frag_order_kernel, dim3((unsigned)(((size_t)nbp * 8 + 255) / 256), (unsigned)d.B),
+               dim3(256), 0, s, reinterpret_cast<const uint4*>(k_cmp), w.frag, lens, d.Lmax,
+               d.Nq, ncol_pad);
     const dim3 grid((unsigned)((d.Nq + kStreamQ - 1) / kStreamQ), (unsigned)d.B);
-    QSA_LAUNCH(score_stream_kernel, grid, dim3(64 * kStreamWaves), 0, s, q_idx, k_cmp, lens, w.lists, w.cnt,
-               w.tau, d.Lmax, d.Nq);
+    QSA_LAUNCH(score_stream_kernel, grid, dim3(64 * kStreamWaves), 0, s, q_idx,
+               (const uint4*)w.frag, lens, w.lists, w.cnt, w.tau, d.Lmax, d.Nq);
     QSA_LAUNCH(select_kernel<true>, grid_q, dim3(256), 0, s, w.lists, w.cnt, 1, kListCap,
                (const int32_t*)w.tau, (const uint32_t*)nullptr, 0, q_idx, k_cmp, lens, sel, n_sel,
                d.Lmax, d.Nq);
