@@ -1188,26 +1188,31 @@ __global__ __launch_bounds__(256) void frag_order_kernel(const uint4* __restrict
 }
 
 // B fragments of column tile c from the fragment-ordered copy (kb: the
-// sequence's first tile), through a buffer resource over the tile: lanes of
-// blocks at or past bt_g get an offset past its end and read zeros (their
-// scores are masked).  The tile's address is scalar work; voff is the
-// lane's byte offset within a k-step (lane x 16).
+// sequence's first tile), through a buffer resource over the tile.  A tile
+// with no block below bt_g (the prefetch past the last one) gets a resource
+// of size 0 and reads zeros; a partial tile is read whole: it lies inside the
+// copy, and a column of the MFMA's B operand only reaches the scores of its
+// own block, which are masked for blocks at or past bt_g whatever the bytes
+// held there.  The masking is scalar work, so the lane offset voff (lane x
+// 16 within a k-step) stays one loop-invariant register: rewriting an
+// address register per tile made the compiler wait for the loads in flight
+// that used it.
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw 32-bit buffer, no swizzle
 __device__ __forceinline__ void load_cols(const uint4* kb, int c, int bt_g, uint32_t voff,
                                           uint4 (&bv)[4]) {
   // (every operand is wavefront-uniform; readfirstlane lets the compiler
   // keep the descriptor in scalar registers, with no waterfall loop; the
   // 1 KiB k-steps go in the scalar offset)
-  const int valid = __builtin_amdgcn_readfirstlane(min(max(bt_g - c * kColTile, 0), kColTile));
+  const int nrec = __builtin_amdgcn_readfirstlane(c * kColTile < bt_g ? kFragTile * 16 : 0);
   const uint64_t a = reinterpret_cast<uint64_t>(kb + (size_t)c * kFragTile);
   const uint64_t au = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(au), (short)0, kFragTile * 16, (int)kBufferConfig);
-  const uint32_t vo = (int)(lane_id() & 31) < valid ? voff : 0x40000000u;
+      reinterpret_cast<void*>(au), (short)0, nrec, (int)kBufferConfig);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    bv[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, 1024 * ks, 0));
+    bv[ks] =
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 1024 * ks, 0));
 }
 
 // MFMAs of half kHalf (row tiles 2 kHalf, 2 kHalf + 1) against one column tile.
@@ -1326,7 +1331,7 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
   if (hit) {
     const int at = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    uint4* rp = st.rec + 3 * at;
+    uint4* rp = st.rec + __umul24((uint32_t)at, 3u);  // (a full-rate multiply)
     rp[0] = make_uint4(__float_as_uint(sc[0]), __float_as_uint(sc[1]), __float_as_uint(sc[2]),
                        __float_as_uint(sc[3]));
     rp[1] = make_uint4(__float_as_uint(sc[4]), __float_as_uint(sc[5]), __float_as_uint(sc[6]),
@@ -1475,8 +1480,8 @@ __device__ __forceinline__ int query_bound(const Stream& st, int q, bool fits) {
   return (max(0, (int)(st.mx[q] >> kSampleShift) - kSampleBase) + m) << kSampleShift;  // bin edge
 }
 
-// Grid (ceil(Nq/64), B); 4 wavefronts: two per group of 32 queries, one per
-// column-tile parity.
+// Grid (ceil(Nq/64), B); kStreamWaves = 8 wavefronts: kPar = 4 per group of
+// 32 queries, one per column-tile parity.
 __global__ __launch_bounds__(64 * kStreamWaves) void score_stream_kernel(const uint16_t* __restrict__ q_idx,
                                                            const uint4* __restrict__ k_frag,
                                                            const int32_t* __restrict__ lens,
