@@ -155,18 +155,19 @@ def timed_steps(step, n, flush, Q, torch):
     return step_ms, kernel_stats(timer.records(), nk), wall
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload=None):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE per dispatch,
     each scaled by what the same counter reads for a 1 GiB copy).  None when
-    there is no such record or the kernel's source changed since it was
+    there is no such record, when it was taken on another workload than
+    `workload` (if given), or when the kernel's source changed since it was
     taken (the record keeps the source file's SHA-256)."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     try:
         with open(os.path.join(here, "profiles", "traffic.json")) as f:
             rec = json.load(f).get(kernel)
-        if rec is None:
+        if rec is None or (workload is not None and rec.get("workload") != workload):
             return None
         with open(os.path.join(here, rec["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
@@ -177,10 +178,11 @@ def measured_traffic(kernel):
         return None
 
 
-def roofline_of(kstats, algo):
+def roofline_of(kstats, algo, workload=None):
     """Roofline record of the dominant kernel (largest time per step) of a
     leg.  algo: base kernel name -> (bound, work per step, unit of work,
-    description); "hbm" work is bytes, "mfma" work is flop."""
+    description); "hbm" work is bytes, "mfma" work is flop.  `traffic` comes
+    from the counters taken on `workload` only."""
     if not kstats:
         return None
     name, st = max(kstats.items(), key=lambda kv: kv[1]["avg_us"] * kv[1]["launches_per_step"])
@@ -195,7 +197,7 @@ def roofline_of(kstats, algo):
     else:
         ach, peak, unit = per_launch / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     return {"bound": bound, "kernel": name, "achieved": ach, "peak": peak, "unit": unit,
-            "frac": ach / peak, "traffic": measured_traffic(name),
+            "frac": ach / peak, "traffic": measured_traffic(name, workload),
             "algorithmic_" + ("bytes" if bound == "hbm" else "flop"): per_launch,
             "work_is": what}
 
@@ -383,7 +385,7 @@ def dense_leg(args, Q, torch, flush, d):
             "hbm_gbs": kv_bytes / (ms * 1e-3) / 1e9, "kv_bytes": kv_bytes,
             "roofline": roofline_of(kstats, {"dense_decode_kernel": ("hbm", kv_bytes,
                                                                      "every K and V row of the "
-                                                                     "context")})}
+                                                                     "context")}, w.name)}
 
 
 def paged_pools(Q, torch, k, v, lens, page, seed):
@@ -537,7 +539,7 @@ def prefill_record(w, step_ms, kstats, np):
         res["indexer_mfma"] = {"kernel": "score_stream_kernel", "achieved": ach,
                                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                               "traffic": measured_traffic("score_stream_kernel")}
+                               "traffic": measured_traffic("score_stream_kernel", w.name)}
     ak = kstats.get("sparse_attend_kernel")
     if ak:
         ach = attn_flops / (ak["avg_us"] * 1e-6) / 1e12
@@ -548,7 +550,7 @@ def prefill_record(w, step_ms, kstats, np):
                                  "unique_kv_bytes": kv_unique,
                                  "unique_kv_hbm_frac": kv_unique / (ak["avg_us"] * 1e-6) / 1e9
                                  / HBM_PEAK_GBS,
-                                 "traffic": measured_traffic("sparse_attend_kernel")}
+                                 "traffic": measured_traffic("sparse_attend_kernel", w.name)}
     return res
 
 
@@ -656,7 +658,8 @@ def other_configs(Q, W, torch, np, flush):
                    "step_hbm": {"algorithmic_bytes": step_bytes,
                                 "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
                                 "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-                   "roofline": roofline_of(kstats, decode_algo(kcmp, attn, qidx, w.batch))}
+                   "roofline": roofline_of(kstats, decode_algo(kcmp, attn, qidx, w.batch),
+                                           w.name)}
             if cfg == 0:
                 rec["note"] = ("64 queries over a 4,096-token context: too small to load the "
                                "part, so launch and round-trip latencies dominate")
@@ -1041,7 +1044,7 @@ def main(argv=None):
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
                      "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": roofline_of(d["kstats"], d["algo"]),
+        "roofline": roofline_of(d["kstats"], d["algo"], w.name),
         "kernels": d["kstats"],
         "cold": d["cold"],
         "selection_quality": d["quality"],

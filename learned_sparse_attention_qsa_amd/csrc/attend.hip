@@ -932,27 +932,33 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   const size_t rh = ((size_t)b * Nq + q) * Hq + h;
   const float* pl = part_lse + rh * n_split;
   const float* po = part_o + rh * n_split * kHeadDim + d;
-  float M = kNegInf;
+  // A chunk's lse values and outputs are requested together (one memory
+  // round trip per chunk, one in all for n_split <= kChunk); a later chunk
+  // with a larger maximum rescales the sums so far.
+  float M = kNegInf, acc = 0.f, sw = 0.f;
   for (int s0 = 0; s0 < n_split; s0 += kChunk) {
+    float w[kChunk], v[kChunk];
 #pragma unroll
-    for (int s = 0; s < kChunk; ++s) M = fmaxf(M, pl[min(s0 + s, n_split - 1)]);
-  }
-  float acc = 0.f, sw = 0.f;
-  if (M != kNegInf) {
-    for (int s0 = 0; s0 < n_split; s0 += kChunk) {
-      float w[kChunk], v[kChunk];
+    for (int s = 0; s < kChunk; ++s) {
+      const int si = min(s0 + s, n_split - 1);
+      w[s] = pl[si];
+      v[s] = po[(size_t)si * kHeadDim];
+    }
+    float Mc = M;
 #pragma unroll
-      for (int s = 0; s < kChunk; ++s) {
-        const int si = min(s0 + s, n_split - 1);
-        w[s] = pl[si];
-        v[s] = po[(size_t)si * kHeadDim];
-      }
+    for (int s = 0; s < kChunk; ++s) Mc = fmaxf(Mc, w[s]);
+    if (Mc == kNegInf) continue;  // nothing attended so far
+    if (Mc > M) {
+      const float r = __expf(M - Mc);  // 0 while M is -inf
+      acc *= r;
+      sw *= r;
+      M = Mc;
+    }
 #pragma unroll
-      for (int s = 0; s < kChunk; ++s) {
-        const float e = (s0 + s < n_split && w[s] != kNegInf) ? __expf(w[s] - M) : 0.f;
-        sw += e;
-        acc += e * v[s];
-      }
+    for (int s = 0; s < kChunk; ++s) {
+      const float e = (s0 + s < n_split && w[s] != kNegInf) ? __expf(w[s] - M) : 0.f;
+      sw += e;
+      acc += e * v[s];
     }
   }
   const float o = sw > 0.f ? acc / sw : 0.f;

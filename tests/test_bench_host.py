@@ -33,14 +33,17 @@ def test_traffic_record_follows_the_source(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("kernel v1\n")
     (tmp_path / "profiles").mkdir()
-    rec = {"k": {"source": "k.hip",
+    rec = {"k": {"source": "k.hip", "workload": "w1",
                  "source_sha256": hashlib.sha256(b"kernel v1\n").hexdigest(),
                  "fetch_kib_per_launch": 100.0, "fetch_scale": 2.0,
                  "write_kib_per_launch": 10.0, "write_scale": 1.0}}
     (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "__file__", str(tmp_path / "bench.py"))
     assert bench.measured_traffic("k") == (100.0 * 2.0 + 10.0) * 1024.0
+    assert bench.measured_traffic("k", "w1") == (100.0 * 2.0 + 10.0) * 1024.0
     assert bench.measured_traffic("other") is None
+    # counters taken on another workload say nothing about this one
+    assert bench.measured_traffic("k", "w2") is None
     src.write_text("kernel v2\n")  # the kernel changed since the counters were taken
     assert bench.measured_traffic("k") is None
 
