@@ -1316,7 +1316,10 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
   const int lane = lane_id();
   const int j = col * kColTile + (lane & 31);
   float sc[8];
-  bool hit = false;
+  // the mask of lanes to record, as the OR of the comparisons' own lane
+  // masks (scalar work), and the branch taken on it directly: no per-lane
+  // flag is materialised in a vector register
+  uint64_t m = 0;
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -1325,13 +1328,13 @@ __device__ __forceinline__ int filter_epilogue(Stream& st, const f32x16 (&acc)[2
       float v = relu_sum_test(acc[r][4 * c], acc[r][4 * c + 1], acc[r][4 * c + 2], acc[r][4 * c + 3]);
       if (!kFull) v = slot_valid(st, rt, c, j) ? v : kNegInf;
       sc[r * 4 + c] = v;
-      hit = hit | (v > st.tau_l[rt][c]);
+      m |= __builtin_amdgcn_ballot_w64(v > st.tau_l[rt][c]);
     }
-  const uint64_t m = __ballot(hit);
-  if (hit) {
-    const int at = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    uint4* rp = st.rec + __umul24((uint32_t)at, 3u);  // (a full-rate multiply)
+  if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+    const uint32_t at =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    // (the queue's end is scalar; a full-rate 24-bit multiply for the lane's place)
+    uint4* rp = (st.rec + 3 * qn) + __umul24(at, 3u);
     rp[0] = make_uint4(__float_as_uint(sc[0]), __float_as_uint(sc[1]), __float_as_uint(sc[2]),
                        __float_as_uint(sc[3]));
     rp[1] = make_uint4(__float_as_uint(sc[4]), __float_as_uint(sc[5]), __float_as_uint(sc[6]),
