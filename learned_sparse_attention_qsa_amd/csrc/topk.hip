@@ -1677,7 +1677,7 @@ constexpr int kScanU = 4;              // 16-block tiles per wavefront batch
 constexpr int kScanCandCap = 8192;     // candidates a select workgroup holds in LDS
 constexpr int kScanMaxSlices = 2048;   // slices a select workgroup can walk
 constexpr int kScanMaxSliceBlocks = 8192;
-constexpr int kScanBitmapBlocks = 262144;  // rows up to this many blocks rank by bitmaps
+constexpr int kScanBmWords = kScanMaxSliceBlocks / 32;  // a slice's bitmap, 32-bit words
 
 // One wavefront: the lower edge (as float bits) of the bin, 64 per octave,
 // holding the k-th largest of the 16 values each lane holds (non-negative
@@ -1721,6 +1721,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_filter_kernel(
   __shared__ uint32_t s_hist[4][256];
   __shared__ uint32_t s_cnt[4];
   __shared__ uint32_t s_tau[4];
+  __shared__ __align__(8) uint32_t s_bm[4][kScanBmWords];  // candidates of the slice, per query
+  __shared__ uint32_t s_bmpre[4][kScanBmWords];
+  __shared__ uint32_t s_bmsum[kScanWaves];
   const int slice = blockIdx.x, q0 = blockIdx.y * 4, b = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1878,18 +1881,54 @@ __global__ __launch_bounds__(kScanThreads) void scan_filter_kernel(
       if (bi + 3 < nbatch) load_fix(bB, bi + 3);
     }
   }
-  __syncthreads();
-  // 4. the group's segments of this slice (an empty one when nothing was scanned)
+  // 4. the group's segments of this slice (an empty one when nothing was
+  // scanned), each in ascending block order: a candidate's place is the
+  // number of the query's candidates below it in the slice, counted on a
+  // bitmap of the slice's blocks (the appends above come in no fixed order).
+  // A row's segments in slice order then list its candidates ascending.
+  // Overflowed segments are left unordered: their rows take the exact path.
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (q0 + q >= Nq) break;
+  for (int i = tid; i < 4 * kScanBmWords; i += kScanThreads) (&s_bm[0][0])[i] = 0u;
+  __syncthreads();
+  const int q = tid >> 7, qt = tid & 127;  // 128 threads per query
+  const uint32_t n = s_cnt[q];
+  const bool ordered = n <= (uint32_t)kScanSegCap;  // (uniform per query)
+  if (ordered)
+    for (uint32_t i = qt; i < n; i += 128) {
+      const uint32_t o = key_block(s_seg[q][i]) - (uint32_t)j_begin;
+      atomicOr(&s_bm[q][o >> 5], 1u << (o & 31));
+    }
+  __syncthreads();
+  {
+    // exclusive prefix of the word popcounts, two words per thread
+    const uint2 w = reinterpret_cast<const uint2*>(s_bm[q])[qt];
+    const uint32_t c0 = (uint32_t)__popc(w.x), own = c0 + (uint32_t)__popc(w.y);
+    const uint32_t incl = wave_incl_sum(own);
+    if (lane == 63) s_bmsum[tid >> 6] = incl;
+    __syncthreads();
+    const uint32_t below = (tid & 64) ? s_bmsum[(tid >> 6) - 1] : 0u;  // other wavefront of q
+    const uint32_t ex = below + incl - own;
+    s_bmpre[q][2 * qt] = ex;
+    s_bmpre[q][2 * qt + 1] = ex + c0;
+  }
+  __syncthreads();
+  if (q0 + q < Nq) {
     const size_t sidx = ((size_t)b * Nq + q0 + q) * n_slices + slice;
-    const uint32_t n = s_cnt[q];
-    if (tid == 0) seg_cnt[sidx] = n;
+    if (qt == 0) seg_cnt[sidx] = n;
     const uint32_t nk = min(n, (uint32_t)kScanSegCap);
-    for (uint32_t i = tid; i < nk; i += kScanThreads) seg[sidx * kScanSegCap + i] = s_seg[q][i];
+    for (uint32_t i = qt; i < nk; i += 128) {
+      const uint64_t key = s_seg[q][i];
+      uint32_t at = i;
+      if (ordered) {
+        const uint32_t o = key_block(key) - (uint32_t)j_begin;
+        at = s_bmpre[q][o >> 5] + (uint32_t)__popc(s_bm[q][o >> 5] & ((1u << (o & 31)) - 1u));
+      }
+      seg[sidx * kScanSegCap + at] = key;
+    }
   }
 }
+static_assert(kScanThreads == 4 * 128 && kScanBmWords == 2 * 128,
+              "segment order: 128 threads and 256 bitmap words per query");
 
 // Block-wide exclusive prefix sum of one value per thread (512 threads) and
 // the total; s_red: kScanWaves words.  Ends past a barrier.
@@ -1917,11 +1956,10 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* s_red, 
 //    holds several score values it is narrowed by histograms of its score
 //    bits, 11 at a time, until one value v remains (usually at once): the
 //    winners are the scores above v and the lowest-id candidates scoring v;
-//  * the order: winners and ties at v are marked in two bitmaps over the
-//    row's blocks; a prefix popcount over the tie bitmap keeps the first
-//    (lowest-id) ties needed, and one over the merged bitmap writes the ids
-//    in ascending order.  Rows of more than kScanBitmapBlocks blocks rank
-//    each winner by counting the winners below it instead.
+//  * the order: the list is already ascending in block id (each segment is
+//    ordered by the filter, and the segments follow the slices), so a prefix
+//    count of the ties keeps the first (lowest-id) ones needed and a prefix
+//    count of the kept entries writes them in list order: no sort.
 // Rows with too few candidates (tau above the 512th best score), an
 // overflowed segment or more candidates than the LDS list holds take the
 // exact whole-row path.
@@ -1931,31 +1969,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_select_kernel(
     const int32_t* __restrict__ lens, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
     int Lmax, int Nq, int slice_blocks, int n_slices) {
   __shared__ __align__(16) uint64_t keys[kScanCandCap];
-  // winners, ties; word w at w + w / 16 (so that the 16 consecutive words a
-  // thread owns start in different banks)
-  __shared__ __align__(16) uint32_t bm[2 * (kScanBitmapBlocks / 32) * 17 / 16];
   __shared__ uint32_t s_pre[kScanMaxSlices + 1];
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t s_red[2 * kScanWaves];
   __shared__ uint32_t bcast[8];
-  __shared__ int32_t outb[kTopK];
-  __shared__ uint32_t outn;
   __shared__ uint32_t s_bad;
   __shared__ uint32_t s_mm[4];
   __shared__ float qf[kIdxHeads * kIdxDim];
   const int q = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = lane_id();
   const int wave = tid >> 6;
   const size_t row = (size_t)b * Nq + q;
+  const uint32_t* cnt = seg_cnt + row * n_slices;
+  const uint64_t* rseg = seg + row * n_slices * (size_t)kScanSegCap;
   const int t = query_t(guard_len(lens[b], Nq, Lmax), Nq, q);
   int32_t* srow = sel + row * kTopK;
   if (write_trivial(t, srow, n_sel + row)) return;
   const int bt = t >> 2;
   const int n_used = min(n_slices, (bt + slice_blocks - 1) / slice_blocks);  // (<= kScanMaxSlices)
-  const uint32_t* cnt = seg_cnt + row * n_slices;
-  const uint64_t* rseg = seg + row * n_slices * (size_t)kScanSegCap;
   if (tid == 0) {
     s_bad = 0u;
-    outn = 0u;
     s_mm[0] = 0xffffffffu;
     s_mm[1] = 0u;
     s_mm[2] = 0xffffffffu;
@@ -2131,90 +2163,42 @@ __global__ __launch_bounds__(kScanThreads) void scan_select_kernel(
   const uint32_t v = blo;
   auto is_win = [&](uint64_t key) -> bool { return (uint32_t)(key >> 32) > v; };
   auto is_tie = [&](uint64_t key) -> bool { return (uint32_t)(key >> 32) == v; };
-  if (bt <= kScanBitmapBlocks) {
-    // ---- bitmaps over the row's blocks: winners (words [0, W)) and ties
-    // (words [W, 2W)); thread t owns words [t cw, t cw + cw) of each
-    const int W = (bt + 31) >> 5;
-    const int cw = (W + kScanThreads - 1) / kScanThreads;  // <= 16
-    auto P = [](int w) { return w + (w >> 4); };           // padded place of word w
-    for (int i = tid; i < P(2 * W); i += kScanThreads) bm[i] = 0u;
-    __syncthreads();
-    for (uint32_t e = tid; e < total; e += kScanThreads) {
+  // ---- the winners in list order, which is ascending block order (each
+  // segment is ordered and the segments follow the slices): thread t walks
+  // the run [t per, t per + per) of the list; a prefix count of the ties
+  // keeps the first `need` of them (the lowest ids), a prefix count of the
+  // kept entries places them
+  const uint32_t per = (total + kScanThreads - 1) / kScanThreads;  // <= kScanCandCap / 512
+  const uint32_t e0 = min(total, (uint32_t)tid * per), e1 = min(total, e0 + per);
+  uint32_t ntie = 0;
+  for (uint32_t e = e0; e < e1; ++e) ntie += is_tie(keys[e]) ? 1u : 0u;
+  uint32_t tot;
+  const uint32_t tie0 = block_excl_sum(ntie, s_red, tot);
+  uint32_t nkeep = 0;
+  {
+    uint32_t tr = tie0;
+    for (uint32_t e = e0; e < e1; ++e) {
       const uint64_t key = keys[e];
-      const int j = (int)key_block(key);
-      if (is_win(key)) atomicOr(&bm[P(j >> 5)], 1u << (j & 31));
-      else if (is_tie(key)) atomicOr(&bm[P(W + (j >> 5))], 1u << (j & 31));
+      const bool tie = is_tie(key);
+      nkeep += (is_win(key) || (tie && tr < need)) ? 1u : 0u;
+      tr += tie ? 1u : 0u;
     }
-    __syncthreads();
-    const int w0 = tid * cw, n_own = max(0, min(W, w0 + cw) - w0);
-    uint32_t tw[16], ww[16];
-    uint32_t ntie = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool in = i < n_own;
-      tw[i] = in ? bm[P(W + w0 + i)] : 0u;
-      ww[i] = in ? bm[P(w0 + i)] : 0u;
-      ntie += (uint32_t)__popc(tw[i]);
-    }
-    uint32_t tot;
-    uint32_t tie_before = block_excl_sum(ntie, s_red, tot);
-    // keep the first `need` ties (lowest ids) and merge them into the winners
-    uint32_t nwin = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t t2 = tw[i];
-      while (t2 != 0u && tie_before < need) {
-        const uint32_t bit = t2 & (0u - t2);
-        ww[i] |= bit;
-        ++tie_before;
-        t2 ^= bit;
-      }
-      nwin += (uint32_t)__popc(ww[i]);
-    }
-    uint32_t pos = block_excl_sum(nwin, s_red, tot);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t x = ww[i];
-      while (x != 0u) {
-        const int bit = __ffs((int)x) - 1;
-        if (pos < (uint32_t)kTopK) srow[pos] = (int32_t)(32 * (w0 + i) + bit);
+  }
+  uint32_t pos = block_excl_sum(nkeep, s_red, tot);
+  {
+    uint32_t tr = tie0;
+    for (uint32_t e = e0; e < e1; ++e) {
+      const uint64_t key = keys[e];
+      const bool tie = is_tie(key);
+      if (is_win(key) || (tie && tr < need)) {
+        if (pos < (uint32_t)kTopK) srow[pos] = (int32_t)key_block(key);
         ++pos;
-        x &= x - 1u;
       }
+      tr += tie ? 1u : 0u;
     }
-  } else {
-    // ---- long rows: the winners, then the ties with fewer than `need`
-    // lower-id ties (by counting), each placed by the number of winners below
-    __syncthreads();
-    for (uint32_t e = tid; e < total; e += kScanThreads) {
-      const uint64_t key = keys[e];
-      bool take = is_win(key);
-      if (!take && is_tie(key)) {
-        const uint32_t j = key_block(key);
-        uint32_t below = 0;
-        for (uint32_t i = 0; i < total; ++i) {
-          const uint64_t k2 = keys[i];
-          below += (is_tie(k2) && key_block(k2) < j) ? 1u : 0u;
-        }
-        take = below < need;
-      }
-      if (take) outb[atomicAdd(&outn, 1u)] = (int32_t)key_block(key);
-    }
-    __syncthreads();
-    const int32_t my = outb[tid];
-    uint32_t rank = 0;
-    const int4* o4 = reinterpret_cast<const int4*>(outb);
-#pragma unroll 8
-    for (int i = 0; i < kTopK / 4; ++i) {
-      const int4 o = o4[i];
-      rank += (uint32_t)(o.x < my) + (uint32_t)(o.y < my) + (uint32_t)(o.z < my) +
-              (uint32_t)(o.w < my);
-    }
-    srow[rank] = my;
   }
   if (tid == 0) n_sel[row] = kTopK;
 }
-static_assert(kScanThreads == kTopK, "the long-row order gives each winner one thread");
 
 
 }  // namespace
@@ -2244,9 +2228,9 @@ bool scan_fits(const Dims& d) { return d.Nq <= 64 && scan_geom(d).n_slices <= kS
 
 // Automatic choice: decode-shaped calls (at most 64 queries per sequence)
 // take the table engine while its score table fits 512 MiB (at a 1M-token
-// context, batch 4 x 4: 70 us per step against 76 us for the scan engine,
-// whose sampled bound costs more latency at the start of its pass than the
-// table's write and read-back), longer contexts the scan engine, whose
+// context, batch 4 x 4: 67.5 us per step against 70.0 us for the scan
+// engine, whose sampled bound costs more latency at the start of its pass
+// than the table's write and read-back), longer contexts the scan engine, whose
 // workspace grows with the slices instead of the context; prefill-shaped
 // calls the stream engine.
 TopkPath choose_topk_path(const Dims& d, uint32_t flags) {
