@@ -2,7 +2,8 @@
 (the compressed-key cache already holds every block before the call's queries
 and the call compresses only the new ones):
 
-  * the 1M-context decode: every query row, selection and output;
+  * the 1M-context decode: every query row, selection and output, with the
+    automatic top-k engine (table) and with the scan engine;
   * the 256K last-chunk prefill: the selection of every one of the 16,384
     rows, outputs of sampled rows;
   * the 1M last-chunk prefill: the selection of every one of the 16,384
@@ -43,11 +44,12 @@ def host_threads():
     return max(1, min(16, n))
 
 
-def run_forward(w):
+def run_forward(w, flags=0):
     """qsa_forward in the steady state bench.py times: the cache holds the
     blocks of the tokens before the queries, the call compresses from the
-    first block those tokens leave incomplete."""
-    shp = Q.shape(w.batch, w.max_len, w.n_query, w.q_heads, w.kv_heads)
+    first block those tokens leave incomplete.  flags: the top-k engine (0:
+    the automatic choice)."""
+    shp = Q.shape(w.batch, w.max_len, w.n_query, w.q_heads, w.kv_heads, flags=flags)
     prev = (w.lens - w.n_query).astype(np.int32)
     first = (prev // 4).astype(np.int32)
     k_idx = dev_bf16(w.k_idx)
@@ -93,11 +95,14 @@ def sample_rows(w, n, seed):
     return [(0, i) for i in sorted(picks)]
 
 
-def test_decode_1m_every_row():
-    say("decode 1M: inputs")
+@pytest.mark.parametrize("flags", [0, Q.FLAG_TOPK_SCAN], ids=["auto", "scan"])
+def test_decode_1m_every_row(flags):
+    # the automatic choice is the table engine; the scan engine (the one for
+    # contexts whose score table would not fit) at the same shape
+    say(f"decode 1M: inputs (flags {flags})")
     w = W.make(4)
     say("decode 1M: forward")
-    got = run_forward(w)
+    got = run_forward(w, flags)
     say("decode 1M: oracle")
     compare_outputs(w, got, [(b, i) for b in range(w.batch) for i in range(w.n_query)])
 
