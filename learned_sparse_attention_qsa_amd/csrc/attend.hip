@@ -8,9 +8,11 @@
 // three different experiments").  Query head h reads KV head floor(h/G).
 //
 // Layout of the work.  A wavefront owns one KV head and up to 16 query heads
-// of that group (the sparse kernel: the heads of one query; the dense kernel:
-// 32 (query, head) rows of one sequence, all queries sharing the K/V stream).
-// It walks the tokens in tiles of 32:
+// of that group (the sparse kernel: the heads of one query; the dense decode
+// kernel: 16 (query, head) columns of one sequence, the workgroup's
+// wavefronts sharing the K/V stream; the dense prefill kernel, which stages
+// 64-token K/V tiles in LDS, is described at its definition).  It walks the
+// tokens in tiles of 32:
 //   * S^T = K Q^T with MFMA 16x16x32: K rows are gathered straight from HBM
 //     into the A operand (each lane loads 16 contiguous bytes of one row),
 //     the stationary Q fragment is the B operand;
@@ -19,7 +21,10 @@
 //   * O^T += V^T P with MFMA: P already sits in the B-operand layout, V goes
 //     through a per-wavefront LDS tile and is read back transposed.
 // Long token ranges are split across workgroups; partial (o, lse) pairs are
-// merged by merge_kernel.
+// merged by merge_kernel.  Paged K/V: the same kernels read token rows
+// through a page table (pool row = table[b][t / page] * page +
+// t mod page).  The file also holds the indexer's training target (dense
+// attention mass pooled per micro-block) and the recall of a selection.
 #include "common.h"
 #include "internal.h"
 

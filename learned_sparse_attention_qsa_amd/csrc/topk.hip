@@ -12,7 +12,7 @@
 // values) and the complemented id makes every key of a query distinct, with
 // equal scores preferring lower ids.  The selection is the 512 largest keys.
 //
-// Two engines, with bit-identical results:
+// Three engines, with bit-identical results:
 //
 //  TABLE (few queries, decode-shaped): one streaming pass scores every block
 //  with MFMA (16x16x32, 4 queries x 4 heads per tile) and writes the fp32
@@ -27,19 +27,25 @@
 //  bare k_cmp scan: the score table (4 B per query per block) written once.
 //
 //  STREAM (many queries, prefill-shaped): a workgroup holds 64 queries x 4
-//  heads stationary in registers and streams the compressed keys straight
-//  into registers in tiles of 32 blocks, MFMA 32x32x16.  A first pass over
-//  1/32 of the tiles sets each query's bound tau (the lower bin edge of its
-//  40th best sample score); the second pass keeps the blocks scoring
-//  strictly above tau (about 1,400 per query).  If at least 512 blocks pass, no block at or
-//  below tau can be in the top 512; the select kernel checks this.  No
-//  score table is written.
+//  heads stationary in registers and streams a fragment-ordered copy of the
+//  compressed keys straight into registers in tiles of 32 blocks, MFMA
+//  32x32x16.  A first pass over 1/32 of the tiles sets each query's bound
+//  tau (the lower bin edge of its 40th best sample score); the second pass
+//  keeps the blocks scoring strictly above tau (about 1,400 per query).  If
+//  at least 512 blocks pass, no block at or below tau can be in the top 512;
+//  the select kernel checks this, finds the 512th key by an LDS radix select
+//  and sorts the winners' ids.  No score table is written.
 //
-// The stream engine finishes with a select kernel (an LDS radix select of the
-// 512th key, then a sort of the winners' ids).  Rows whose candidates cannot be
-// trusted or held (an overflow, too few candidates, or very many equal
-// scores) are finished by an exact fallback that recomputes or re-reads the
-// whole row.
+//  SCAN (few queries at contexts whose score table would not fit): every
+//  workgroup bounds its queries from the same 1,024 sample blocks of the
+//  sequence, streams its slice with MFMA 16x16x32 and keeps the blocks
+//  reaching the bound in a per-slice segment, written in ascending block
+//  order; one workgroup per row then finds the exact top 512 in the
+//  concatenated segments, already ascending, with no sort.
+//
+// Rows whose candidates cannot be trusted or held (an overflow, too few
+// candidates, or very many equal scores) are finished by an exact fallback
+// that recomputes or re-reads the whole row.
 
 #include "common.h"
 #include "internal.h"
