@@ -54,7 +54,6 @@ namespace qsa {
 namespace {
 
 constexpr int kHistBins = 2048;    // histogram bins of the table engine's pick
-constexpr int kTableSlice = 1024;  // blocks per scoring workgroup (table engine)
 constexpr int kGroup = 16;         // blocks per group maximum (table engine)
 constexpr int kSelCap = 4096;      // candidates a select workgroup holds in LDS (a stream list)
 constexpr int kHistW = 256;        // stream engine: sample-histogram bins per query
@@ -533,9 +532,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 }
 
 // ------------------------------------------------------------------ TABLE
-// Grid (ceil(Lmax/4 / kTableSlice), ceil(Nq/4), B), 256 threads.  Wavefront w
-// scores blocks [j_begin + 256 w, + 256) in two batches of eight 16-block
-// tiles.  MFMA 16x16x32: A = 16 rows (query r/4, head r%4), B = 16 blocks;
+// Grid (ceil(Lmax/4 / (4 kSpan)), ceil(Nq/4), B), 256 threads: a slice of
+// 4 kSpan blocks per workgroup, the span chosen so that the grid fills the
+// chip (256 at long contexts, shorter below).  Wavefront w scores blocks
+// [j_begin + kSpan w, + kSpan) in batches of up to eight 16-block tiles.
+// MFMA 16x16x32: A = 16 rows (query r/4, head r%4), B = 16 blocks;
 // the lane (r, kc) receives block r of the tile for query q0 + kc, all four
 // heads.  A tile is also one group: its maximum over the 16 lanes of a query
 // goes to gmax.
@@ -545,6 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 // each workgroup writes those of its slice to k_cmp before scoring them
 // (the vector L1 is shared by the workgroup's wavefronts, so a barrier
 // orders the writes before the reads).
+template <int kSpan>
 __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __restrict__ q_idx,
                                                           uint16_t* __restrict__ k_cmp,
                                                           const int32_t* __restrict__ lens,
@@ -558,13 +560,14 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
   const int len = guard_len(lens[b], Nq, Lmax);
   const int nbp = Lmax >> 2;
   const int t_last = query_t(len, Nq, min(q0 + 3, Nq - 1));
-  const int j_begin = slice * kTableSlice;
-  const int j_end = min(j_begin + kTableSlice, t_last >= 0 ? (t_last >> 2) : 0);
+  constexpr int kSlice = 4 * kSpan;
+  const int j_begin = slice * kSlice;
+  const int j_end = min(j_begin + kSlice, t_last >= 0 ? (t_last >> 2) : 0);
   if (k_idx != nullptr) {
     const int nb = len >> 2;
     const int fb = first_block ? guard(first_block[b], 0, nb) : 0;
     const long long c0 = (long long)max(fb, j_begin) * 8;
-    const long long c1 = (long long)min(nb, j_begin + kTableSlice) * 8;
+    const long long c1 = (long long)min(nb, j_begin + kSlice) * 8;
     if (c0 < c1) {  // (uniform over the workgroup)
       const uint4* src = reinterpret_cast<const uint4*>(k_idx + (size_t)b * Lmax * kIdxDim);
       uint4* dst = reinterpret_cast<uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
@@ -594,10 +597,12 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
   uint32_t* grow = gmax + orow * gstride;
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
 
-  constexpr int U = 8;
+  constexpr int U = kSpan >= 128 ? 8 : kSpan / 16;  // tiles per batch
+  constexpr int kBatches = kSpan / (16 * U);
+  static_assert(kBatches * U * 16 == kSpan, "whole batches per wavefront");
 #pragma unroll 1
-  for (int batch = 0; batch < 2; ++batch) {
-    const int jt = j_begin + wave * (2 * U * 16) + batch * (U * 16);
+  for (int batch = 0; batch < kBatches; ++batch) {
+    const int jt = j_begin + wave * kSpan + batch * (U * 16);
     if (jt >= j_end) break;
     // Unconditional loads (a block past the slice re-reads the slice's last
     // one; its score is masked below): with per-lane conditions the
@@ -2315,10 +2320,20 @@ hipError_t launch_table_score(const Dims& d, const uint16_t* q_idx, uint16_t* k_
   if (fuse && !topk_can_fuse_compress(d, TopkPath::kTable)) return hipErrorInvalidValue;
   TableWs w = carve_table(d, ws, nullptr);
   const unsigned qg = (unsigned)((d.Nq + 3) / 4);
-  const dim3 grid((unsigned)((d.Lmax / 4 + kTableSlice - 1) / kTableSlice), qg, (unsigned)d.B);
-  QSA_LAUNCH(score_table_kernel, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores,
-             table_stride(d), w.gmax, group_stride(d), d.Lmax, d.Nq,
-             fuse ? fuse->k_idx : nullptr, fuse ? fuse->first_block : nullptr);
+  // the longest span (256 blocks per wavefront) that still gives about two
+  // workgroups per compute unit
+  const long long nbp = d.Lmax / 4, rows = (long long)qg * d.B;
+  int span = 256;
+  while (span > 64 && ((nbp + 4 * span - 1) / (4 * span)) * rows < 512) span /= 2;
+  const dim3 grid((unsigned)((nbp + 4 * span - 1) / (4 * span)), qg, (unsigned)d.B);
+#define QSA_TABLE_SCORE(S)                                                                    \
+  QSA_LAUNCH(score_table_kernel<S>, grid, dim3(256), 0, s, q_idx, k_cmp, lens, w.scores,     \
+             table_stride(d), w.gmax, group_stride(d), d.Lmax, d.Nq,                        \
+             fuse ? fuse->k_idx : nullptr, fuse ? fuse->first_block : nullptr)
+  if (span == 256) QSA_TABLE_SCORE(256);
+  else if (span == 128) QSA_TABLE_SCORE(128);
+  else QSA_TABLE_SCORE(64);
+#undef QSA_TABLE_SCORE
   return hipGetLastError();
 }
 

@@ -481,7 +481,8 @@ def test_kernel_timer_records_every_launch():
     known = ("compress_kernel", "score_table_kernel", "table_pick_kernel", "sparse_attend_kernel",
              "merge_kernel")
     assert all(n.startswith(known) for n in names), names
-    assert names.index("score_table_kernel") < names.index("table_pick_kernel"), names
+    base = [n.split("<")[0] for n in names]  # template instances under their base name
+    assert base.index("score_table_kernel") < base.index("table_pick_kernel"), names
     assert any(n.startswith("sparse_attend_kernel") for n in names), names
     assert all(ms > 0.0 for _, ms in recs), recs
     assert torch.equal(out0, out1)
