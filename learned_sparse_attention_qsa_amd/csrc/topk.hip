@@ -657,8 +657,10 @@ __global__ __launch_bounds__(256) void score_table_kernel(const uint16_t* __rest
 //     the score bits, 11 at a time, do.
 //  5. output: blocks above the cutoff, plus the lowest-index blocks at the
 //     cutoff score, compacted in list order, which is ascending.
-// A row whose candidate groups or blocks exceed the LDS lists (many equal
-// scores) is finished by the exact whole-row select.
+// Rows of at most kPickCand blocks skip steps 2 and 3: every block is a
+// candidate, read straight from the table.  A row whose candidate groups or
+// blocks exceed the LDS lists (many equal scores) is finished by the exact
+// whole-row select.
 constexpr int kPickThreads = 1024;
 constexpr int kPickWaves = kPickThreads / 64;  // 16: one lane of a 16-lane row each
 constexpr int kPickGroups = 2048;  // candidate groups a row keeps in LDS
@@ -834,6 +836,18 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
   const int G = (bt + kGroup - 1) / kGroup;
   const int nchunks = (G + 16 * kPickThreads - 1) / (16 * kPickThreads);
   const uint32_t* trow = scores + (size_t)row * tstride;
+  // Rows of at most kPickCand blocks: every block is a candidate, read
+  // straight from the table (two per thread, requested now) instead of
+  // through the candidate groups; the bound below stays 0 for them.
+  const bool small = bt <= kPickCand;  // (uniform)
+  uint32_t sm[2] = {0u, 0u};
+  if (small) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * tid + e;
+      sm[e] = i < bt ? trow[i] : 0u;
+    }
+  }
 
   // ---- 1. bound: bv, a value that at least 512 group maxima reach
   uint32_t m1 = 0;
@@ -918,7 +932,7 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
 
   // ---- 2. candidate groups, ascending
   uint32_t ng = 0;
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = 0; c < (small ? 0 : nchunks); ++c) {
     uint32_t x[16];
     const uint32_t vm = pick_chunk(g4, n4, G, c, first, x);
     uint32_t keep = 0;
@@ -944,8 +958,8 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
   __syncthreads();
 
   // ---- 3. candidate blocks of those groups, ascending
-  uint32_t n = 0;
-  if (ng <= (uint32_t)kPickGroups) {
+  uint32_t n = small ? (uint32_t)bt : 0u;
+  if (!small && ng <= (uint32_t)kPickGroups) {
     const int rounds = (int)((ng + kPickThreads / 4 - 1) / (kPickThreads / 4));
     const int quarter = tid & 3;
     uint4 v[kPickRounds];
@@ -1021,8 +1035,8 @@ __global__ __launch_bounds__(kPickThreads) void table_pick_kernel(
   for (int e = 0; e < 2; ++e) {
     const uint32_t i = 2u * (uint32_t)tid + e;
     mv[e] = i < n;
-    mb[e] = mv[e] ? cbits[i] : 0u;
-    mj[e] = mv[e] ? cj[i] : 0u;
+    mb[e] = mv[e] ? (small ? sm[e] : cbits[i]) : 0u;
+    mj[e] = mv[e] ? (small ? i : cj[i]) : 0u;
   }
   // the candidates' scale: [bv, rowmax]
   const float lo4 = __uint_as_float(bv);
