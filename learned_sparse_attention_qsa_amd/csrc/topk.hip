@@ -250,40 +250,6 @@ __device__ __forceinline__ void wave_suffix_bin4(uint32_t c0, uint32_t c1, uint3
   suffix = cum;
 }
 
-// One wavefront, a kHistBins-bin histogram h (LDS or global): the highest bin
-// whose suffix count reaches k, and that suffix count.
-__device__ __forceinline__ void wave_suffix_bin_2048(const uint32_t* h, uint32_t k, int& bin,
-                                                     uint32_t& suffix) {
-  const int lane = lane_id();
-  // lane holds bins [32*lane, 32*lane+32); rotated order keeps LDS reads
-  // conflict-free
-  uint32_t mine = 0;
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) mine += h[32 * lane + ((i + lane) & 31)];
-  uint32_t S = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(S, off);
-    if (lane + off < 64) S += o;
-  }
-  const uint64_t m = __ballot(S >= k);
-  const int L = 63 - __clzll((long long)m);
-  const uint32_t above = __shfl(S, L) - __shfl(mine, L);
-  // lanes 0..31 take one bin of lane L's range each; suffix within it
-  const int i = lane & 31;
-  uint32_t c = lane < 32 ? h[32 * L + i] : 0u;
-  uint32_t T = c;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const uint32_t o = __shfl_down(T, off);
-    if (i + off < 32) T += o;
-  }
-  const uint64_t m2 = __ballot(lane < 32 && above + T >= k);
-  const int I = 63 - __clzll((long long)m2);
-  bin = 32 * L + I;
-  suffix = above + __shfl(T, I);
-}
-
 // ------------------------------------------------------------------ select
 // Exact top-512 of one query straight from its whole row.  Slow path for
 // rows whose candidate list does not fit the fast path (very many equal or
