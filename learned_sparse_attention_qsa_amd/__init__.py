@@ -13,7 +13,6 @@ int32 for lens / sel / tok.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -668,6 +667,3 @@ class KernelTimer:
         return [(name, self.events[2 * i].elapsed_time(self.events[2 * i + 1]))
                 for i, name in enumerate(self._names)]
 
-
-def default_scale() -> float:
-    return 1.0 / math.sqrt(HEAD_DIM)
