@@ -196,10 +196,16 @@ def roofline_of(kstats, algo, workload=None):
         ach, peak, unit = per_launch / sec / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         ach, peak, unit = per_launch / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    return {"bound": bound, "kernel": name, "achieved": ach, "peak": peak, "unit": unit,
-            "frac": ach / peak, "traffic": measured_traffic(name, workload),
-            "algorithmic_" + ("bytes" if bound == "hbm" else "flop"): per_launch,
-            "work_is": what}
+    traffic = measured_traffic(name, workload)
+    rec = {"bound": bound, "kernel": name, "achieved": ach, "peak": peak, "unit": unit,
+           "frac": ach / peak, "traffic": traffic,
+           "algorithmic_" + ("bytes" if bound == "hbm" else "flop"): per_launch,
+           "work_is": what}
+    if traffic is not None:
+        # the counted HBM bytes per launch over this run's duration
+        rec["traffic_gbs"] = traffic / sec / 1e9
+        rec["traffic_frac_of_hbm_peak"] = traffic / sec / 1e9 / HBM_PEAK_GBS
+    return rec
 
 
 def pct(xs, p):
@@ -551,6 +557,11 @@ def prefill_record(w, step_ms, kstats, np):
                                  "unique_kv_hbm_frac": kv_unique / (ak["avg_us"] * 1e-6) / 1e9
                                  / HBM_PEAK_GBS,
                                  "traffic": measured_traffic("sparse_attend_kernel", w.name)}
+        tr = res["attention_mfma"]["traffic"]
+        if tr is not None:
+            # the gathered rows the counters saw leave the L2, over this run's duration
+            res["attention_mfma"]["traffic_frac_of_hbm_peak"] = (
+                tr / (ak["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS)
     return res
 
 

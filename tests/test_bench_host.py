@@ -68,6 +68,9 @@ def test_roofline_of_recorded_template_names():
     assert r["kernel"] == "sparse_attend_kernel"
     assert r["achieved"] == pytest.approx(100e6 / 20e-6 / 1e9)
     assert r["frac"] == pytest.approx(r["achieved"] / bench.HBM_PEAK_GBS)
+    # no counter record for this workload: no traffic and no rate from it
+    assert bench.roofline_of(st, algo, "no-such-workload")["traffic"] is None
+    assert "traffic_gbs" not in bench.roofline_of(st, algo, "no-such-workload")
 
 
 def test_prefill_record_emits_attention_and_indexer_fractions():
