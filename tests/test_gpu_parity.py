@@ -434,6 +434,43 @@ def test_forward_incremental_decode_steps():
         check_close(np.stack([got[b, i] for b, i in keys]), np.stack([res["out"][k] for k in keys]))
 
 
+@pytest.mark.parametrize("nq", [1, 2, 3])
+@pytest.mark.parametrize("flags", [0, Q.FLAG_TOPK_SCAN], ids=["auto", "scan"])
+def test_forward_decode_odd_query_counts(nq, flags):
+    # decode steps of 1-3 query positions (a partial group of 4 in the scan
+    # kernels, whose spare rows repeat the last query), in the steady state
+    # (the cache holds every block before the step, the call compresses only
+    # the new ones); lengths of every residue mod 4, one under the 2,052-token
+    # dense range and a 4-token context
+    say(f"forward decode nq={nq} flags={flags}")
+    lens = np.array([70003, 33334, 131075, 2050, 4 + nq], np.int32)
+    w = W.make_custom(60 + nq, list(lens), nq, 16, 2)
+    shp = shape_of(w, flags)
+    k_idx = dev_bf16(w.k_idx)
+    k_cmp = torch.zeros((w.batch, w.max_len // 4, 64), dtype=torch.bfloat16, device="cuda")
+    prev = lens - nq
+    Q.compress_keys(shp, k_idx, dev_i32(prev), k_cmp)
+    out, lse, sel, n_sel = Q.forward(
+        shp, dev_bf16(w.q_idx), k_idx, k_cmp, dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+        dev_i32(lens), first_block=dev_i32((prev // 4).astype(np.int32)),
+        sel=torch.empty((w.batch, nq, 512), dtype=torch.int32, device="cuda"),
+        n_sel=torch.empty((w.batch, nq), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, lens, nq)
+    want_sel, want_n = padded_sel(res, w.batch, nq, lens)
+    np.testing.assert_array_equal(n_sel.cpu().numpy(), want_n)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
+    kc = host_u16(k_cmp)
+    for b in range(w.batch):
+        np.testing.assert_array_equal(kc[b, :lens[b] // 4], res["kc"][b])
+    got = host_f64_from_bf16(out)
+    keys = sorted(res["out"].keys())
+    check_close(np.stack([got[b, i] for b, i in keys]), np.stack([res["out"][k] for k in keys]))
+    lse_h = lse.cpu().numpy()
+    for k in keys:
+        np.testing.assert_allclose(lse_h[k], res["lse"][k], atol=2e-2, rtol=0, err_msg=str(k))
+
+
 # ------------------------------------------------------------------ dense comparator
 
 @pytest.mark.parametrize("nq", [6, 9])  # 3 and 5 chunks of 16 (query, head) columns per KV head
