@@ -1,7 +1,7 @@
-"""Paged K/V: the QSA forward, the sparse attention and the dense decode
-comparator read K and V through a page table over shuffled page pools, and
-must give bit-identical results to the contiguous caches (only the
-addressing differs).  Pool rows past a sequence's length, the pages its
+"""Paged K/V: the QSA forward (decode- and prefill-shaped), the sparse
+attention and the dense decode comparator read K and V through a page table
+over shuffled page pools, and must give bit-identical results to the
+contiguous caches (only the addressing differs).  Pool rows past a sequence's length, the pages its
 table does not need and the pool's spare pages hold NaN, so a read of
 anything outside the valid tokens would show.  The dense prefill comparator
 (contiguous and paged) is checked against the float64 oracle on sampled
@@ -89,6 +89,41 @@ def test_paged_forward_and_attend_match_contiguous(page):
     # and the paged result is the oracle's on a few rows
     rows = [(0, 0), (1, Nq - 1), (2, 2)]
     res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, Nq, queries=rows)
+    got = host_f64_from_bf16(o2)
+    check_close(np.stack([got[r] for r in rows]), np.stack([res["out"][r] for r in rows]))
+
+
+@pytest.mark.parametrize("page", [2, 4, 64])
+def test_paged_prefill_forward_matches_contiguous(page):
+    # a prefill-shaped call (300 queries x 4 KV heads fill the chip without
+    # splits): the stream top-k engine and the attention workgroups that hold
+    # all four KV heads of a query, reading the pools through the table
+    nq = 300
+    w = W.make_custom(1700 + page, [20003, 9001], nq, 32, 4)
+    say(f"paged prefill forward: page {page}, lens {list(w.lens)}")
+    B, L = w.batch, w.max_len
+    shp = Q.shape(B, L, nq, 32, 4)
+    t = {n: dev_bf16(getattr(w, n)) for n in ("q_idx", "k_idx", "q", "k", "v")}
+    lens = dev_i32(w.lens)
+    k_pool, v_pool, pg = make_pool(w.k, w.v, w.lens, page, 1800 + page)
+    kc1 = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
+    kc2 = torch.zeros_like(kc1)
+    def sel_bufs():
+        return (torch.empty((B, nq, 512), dtype=torch.int32, device="cuda"),
+                torch.empty((B, nq), dtype=torch.int32, device="cuda"))
+
+    s1, n1 = sel_bufs()
+    s2, n2 = sel_bufs()
+    o1, l1, _, _ = Q.forward(shp, t["q_idx"], t["k_idx"], kc1, t["q"], t["k"], t["v"], lens,
+                             sel=s1, n_sel=n1)
+    o2, l2, _, _ = Q.forward_paged(shp, t["q_idx"], t["k_idx"], kc2, t["q"], k_pool, v_pool, pg,
+                                   lens, sel=s2, n_sel=n2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(n1, n2)
+    np.testing.assert_array_equal(bits(o2), bits(o1))
+    np.testing.assert_array_equal(bits(l2), bits(l1))
+    rows = [(0, 0), (0, nq - 1), (1, 7), (1, nq - 1)]
+    res = O.qsa_forward(w.q_idx, w.k_idx, w.q, w.k, w.v, w.lens, nq, queries=rows)
     got = host_f64_from_bf16(o2)
     check_close(np.stack([got[r] for r in rows]), np.stack([res["out"][r] for r in rows]))
 
