@@ -471,6 +471,28 @@ def test_forward_decode_odd_query_counts(nq, flags):
         np.testing.assert_allclose(lse_h[k], res["lse"][k], atol=2e-2, rtol=0, err_msg=str(k))
 
 
+def test_host_lens_check(monkeypatch):
+    # QSA_CHECK=1: the library reads lens back before launching anything and
+    # rejects a sequence shorter than its query count or longer than the
+    # cache; without it the call trusts lens (the caller's contract)
+    say("QSA_CHECK")
+    w = W.make_custom(70, [3000, 2500], 4, 16, 2)
+    shp = shape_of(w)
+    args = (dev_bf16(w.q_idx), dev_bf16(w.k_idx), gpu_kcmp(w), dev_bf16(w.q), dev_bf16(w.k),
+            dev_bf16(w.v))
+    monkeypatch.setenv("QSA_CHECK", "1")
+    out, _ = Q.forward(shp, *args, dev_i32(w.lens))[:2]  # valid: runs
+    torch.cuda.synchronize()
+    for bad in ([3000, 3], [3000, w.max_len + 4]):
+        with pytest.raises(Q.QsaError) as err:
+            Q.forward(shp, *args, dev_i32(np.array(bad, np.int32)))
+        assert err.value.status == Q.ERR_SHAPE
+    monkeypatch.delenv("QSA_CHECK")
+    out2, _ = Q.forward(shp, *args, dev_i32(w.lens))[:2]
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
 # ------------------------------------------------------------------ dense comparator
 
 @pytest.mark.parametrize("nq", [6, 9])  # 3 and 5 chunks of 16 (query, head) columns per KV head
