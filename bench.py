@@ -349,19 +349,35 @@ def decode_leg(args, Q, W, torch, np, flush):
     dv = torch.zeros_like(dk)
     dq_idx = torch.zeros(ws.dev["q_idx"].shape, dtype=torch.float32, device="cuda")
     dk_cmp = torch.zeros(ws.k_cmp.shape, dtype=torch.float32, device="cuda")
+    def run_backward():
+        Q.sparse_attend_backward(ws.shp, ws.dev["q"], ws.dev["k"], ws.dev["v"], ws.lens, ws.sel,
+                                 ws.n_sel, ws.out, ws.lse, d_out, dk=dk, dv=dv)
+        ev[1].record()
+        Q.index_scores_backward(ws.shp, ws.dev["q_idx"], ws.k_cmp, ws.lens, d_s, dq_idx=dq_idx,
+                                dk_cmp=dk_cmp)
+
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ev[0].record()
-    Q.sparse_attend_backward(ws.shp, ws.dev["q"], ws.dev["k"], ws.dev["v"], ws.lens, ws.sel,
-                             ws.n_sel, ws.out, ws.lse, d_out, dk=dk, dv=dv)
-    ev[1].record()
-    Q.index_scores_backward(ws.shp, ws.dev["q_idx"], ws.k_cmp, ws.lens, d_s, dq_idx=dq_idx,
-                            dk_cmp=dk_cmp)
-    ev[2].record()
-    torch.cuda.synchronize()
-    backward = {"attend_backward_us": 1000 * ev[0].elapsed_time(ev[1]),
-                "index_scores_backward_us": 1000 * ev[1].elapsed_time(ev[2]),
-                "note": "one call each on the decode batch, caches warm; float32 vector math, "
-                        "dk/dv and dk_cmp added atomically"}
+    run_backward()  # first launches (code object loading) untimed
+    reps = 3
+    t_att = t_idx = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        run_backward()
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_att += ev[0].elapsed_time(ev[1])
+        t_idx += ev[1].elapsed_time(ev[2])
+    # the indexer backward's algorithmic HBM bytes: each candidate block's
+    # compressed key (128 B) and its Nq gradient entries read, its float32
+    # dk_cmp row read and written (2 x 256 B), dq_idx read and written once
+    nblk = sum((int(n) - 1) // 4 for n in w.lens)
+    idx_bytes = nblk * (128 + 4 * w.n_query + 512) + 2 * w.batch * w.n_query * 4 * 64 * 4
+    backward = {"attend_backward_us": 1000 * t_att / reps,
+                "index_scores_backward_us": 1000 * t_idx / reps,
+                "index_scores_backward_gbs": idx_bytes / (t_idx / reps * 1e-3) / 1e9,
+                "note": f"mean of {reps} calls each on the decode batch after one untimed call, "
+                        "caches warm; the gradients accumulate into the same buffers; "
+                        "dk/dv added atomically, dk_cmp read, added and written back"}
     del d_out, d_s, dk, dv, dq_idx, dk_cmp
     torch.cuda.empty_cache()
     return dict(w=w, ws=ws, step_ms=step_ms, kstats=kstats, wall=wall, sel=sel_h, n_sel=nsel_h,

@@ -161,75 +161,209 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
   }
 }
 
-// Grid (n_slices, ceil(Nq / 16), B), 256 threads: the blocks of one slice
-// against up to 16 queries of one sequence.  Thread per block: the four
-// heads' dot products, the gradient's mask, dkc of the block (registers,
-// added to dk_cmp at the end) and dq (LDS, added to dq_idx at the end).
-constexpr int kIbwdQ = 16;
-__global__ __launch_bounds__(kBwdThreads) void index_scores_bwd_kernel(
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Grid (n_slices, ceil(Nq / kQ), B), 256 threads (four wavefronts): the
+// blocks of one slice against up to kQ queries of one sequence.  Each
+// wavefront takes 64-block tiles of the slice in turn:
+//  1. block side, on the matrix cores: the products q_h . kc_j of the kQ x 4
+//     (query, head) rows and the tile's blocks, 16 x 16 per pair of
+//     16x16x32 bf16 MFMA steps (bf16 inputs, float32 sums).  A lane then
+//     holds the four heads of one query for one block and keeps
+//     w = g (product > 0 and the block a candidate of the query) or 0;
+//     the w rows and the tile's keys go to the wavefront's LDS;
+//  2. dimension side, float32 FMA: a lane owns kDL = 16 / kQ consecutive
+//     dimensions of every (64 / kDL)-th block; per block j it sums
+//     w_j,r q_r,d over the rows r into dkc_j,d, added to dk_cmp as one
+//     row (a plain read-add-write when this workgroup is the row's only
+//     writer, atomic adds otherwise), and adds w_j,r kc_j,d to its dq_r,d
+//     registers.
+// The lanes' dq are summed in LDS and added to dq_idx at the end.
+template <int kQ>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kQ <= 4 ? 2 : 1)))
+void index_scores_bwd_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp,
     const int32_t* __restrict__ lens, const float* __restrict__ g_scores,
     float* __restrict__ dq_idx, float* __restrict__ dk_cmp, int Lmax, int Nq, int slice_blocks) {
-  __shared__ float s_q[kIbwdQ][kIdxHeads][kIdxDim];
-  __shared__ float s_dq[kIbwdQ][kIdxHeads][kIdxDim];
-  const int slice = blockIdx.x, q0 = blockIdx.y * kIbwdQ, b = blockIdx.z, tid = threadIdx.x;
-  const int nq = min(kIbwdQ, Nq - q0);
+  constexpr int kR = kQ * kIdxHeads;   // (query, head) rows
+  constexpr int kMT = kR / 16;         // 16-row MFMA tiles
+  constexpr int kDL = 16 / kQ;         // dimensions per lane on the dimension side
+  constexpr int kG = kIdxDim / kDL;    // lanes per block on the dimension side
+  constexpr int kKRow = 9;             // LDS key row: 64 bf16 + 16 bytes of stagger, in uint4
+  constexpr int kWRow = kR / 4;        // LDS w row, in float4
+  constexpr int kWaves = kBwdThreads / 64;
+  __shared__ uint4 s_k[kWaves][64 * kKRow];
+  __shared__ f32x4 s_w[kWaves][64 * kWRow];
+  __shared__ float s_dq[kR * kIdxDim];
+  const int slice = blockIdx.x, q0 = blockIdx.y * kQ, b = blockIdx.z, tid = threadIdx.x;
+  const int nq = min(kQ, Nq - q0);
   const int len = guard_len(lens[b], Nq, Lmax);
   const int nbp = Lmax >> 2;
-  for (int i = tid; i < kIbwdQ * kIdxHeads * kIdxDim; i += kBwdThreads) {
-    const int qq = i / (kIdxHeads * kIdxDim), rem = i % (kIdxHeads * kIdxDim);
-    (&s_q[0][0][0])[i] =
-        qq < nq ? bf(q_idx[((size_t)b * Nq + q0 + qq) * kIdxHeads * kIdxDim + rem]) : 0.f;
-    (&s_dq[0][0][0])[i] = 0.f;
-  }
-  __syncthreads();
   const int t_last = len - Nq + q0 + nq - 1;
-  const int bt_max = t_last >= 0 ? (t_last >> 2) : 0;
-  const int j0 = slice * slice_blocks, j1 = min(j0 + slice_blocks, bt_max);
-  for (int j = j0 + tid; j < j1; j += kBwdThreads) {
-    float kc[kIdxDim];
-    const uint4* kr = reinterpret_cast<const uint4*>(k_cmp + ((size_t)b * nbp + j) * kIdxDim);
+  const int j0 = slice * slice_blocks, j1 = min(j0 + slice_blocks, t_last >> 2);
+  if (j1 <= j0) return;  // (uniform over the workgroup)
+  for (int i = tid; i < kR * kIdxDim; i += kBwdThreads) s_dq[i] = 0.f;
+
+  const int lane = lane_id(), wave = tid >> 6;
+  const int r = lane & 15, kc = lane >> 4;
+  // block side: A fragments (row 16 mt + r = query 4 mt + r / 4, head r % 4,
+  // dimensions 8 kc.. and 32 + 8 kc..) and this lane's query 4 mt + kc
+  bf16x8 qa[kMT][2];
+  int lim[kMT];
+  const size_t qrow0 = (size_t)b * Nq + q0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 u = kr[c];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int mt = 0; mt < kMT; ++mt) {
+    const int qq = 4 * mt + (r >> 2);
+    uint4 u0 = zero_u4(), u1 = zero_u4();
+    if (qq < nq) {
+      const uint4* p =
+          reinterpret_cast<const uint4*>(q_idx + ((qrow0 + qq) * kIdxHeads + (r & 3)) * kIdxDim);
+      u0 = p[kc];
+      u1 = p[4 + kc];
+    }
+    qa[mt][0] = as_bf16x8(u0);
+    qa[mt][1] = as_bf16x8(u1);
+    const int qw = 4 * mt + kc;
+    lim[mt] = qw < nq ? min((len - Nq + q0 + qw) >> 2, j1) : 0;
+  }
+  // dimension side: this lane's dimensions d0.. of every row
+  const int d0 = (lane % kG) * kDL, js = lane / kG;
+  float qv[kR][kDL], dq[kR][kDL];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kc[8 * c + 2 * e] = bf16_lo(w[e]);
-        kc[8 * c + 2 * e + 1] = bf16_hi(w[e]);
+  for (int rr = 0; rr < kR; ++rr)
+#pragma unroll
+    for (int e = 0; e < kDL; ++e) {
+      qv[rr][e] = rr / kIdxHeads < nq ? bf(q_idx[(qrow0 * kIdxHeads + rr) * kIdxDim + d0 + e]) : 0.f;
+      dq[rr][e] = 0.f;
+    }
+  __syncthreads();
+
+  const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
+  const float* gb = g_scores + qrow0 * nbp;
+  float* dkb = dk_cmp + (size_t)b * nbp * kIdxDim;
+  const bool sole = gridDim.y == 1;
+  uint4* sk = s_k[wave];
+  f32x4* sw = s_w[wave];
+  const int ntiles = (j1 - j0 + 63) >> 6;
+  // the tile's keys and g values, loaded one tile ahead
+  uint4 bv[4][2];
+  float gv[kMT][4];
+  auto load_tile = [&](int jt) {
+    // Unconditional key loads: a block past the slice re-reads its last one
+    // and gets w = 0.
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int j = min(jt + nt * 16 + r, j1 - 1);
+      bv[nt][0] = kb[(size_t)j * 8 + kc];
+      bv[nt][1] = kb[(size_t)j * 8 + 4 + kc];
+    }
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int j = jt + nt * 16 + r;
+        gv[mt][nt] = j < lim[mt] ? gb[(size_t)(4 * mt + kc) * nbp + j] : 0.f;
+      }
+  };
+  if (wave < ntiles) load_tile(j0 + wave * 64);
+#pragma unroll 1
+  for (int tile = wave; tile < ntiles; tile += kWaves) {
+    const int jt = j0 + tile * 64;
+    wave_sync_lds();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      sk[(nt * 16 + r) * kKRow + kc] = bv[nt][0];
+      sk[(nt * 16 + r) * kKRow + 4 + kc] = bv[nt][1];
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(qa[mt][0], as_bf16x8(bv[nt][0]), acc);
+        acc = mfma16(qa[mt][1], as_bf16x8(bv[nt][1]), acc);
+        const float g = gv[mt][nt];
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = acc[i] > 0.f ? g : 0.f;
+        sw[(nt * 16 + r) * kWRow + 4 * mt + kc] = w;
       }
     }
-    float dkc[kIdxDim];
+    wave_sync_lds();
+    if (tile + kWaves < ntiles) load_tile(jt + kWaves * 64);
+    const uint16_t* skh = reinterpret_cast<const uint16_t*>(sk);
+    // Dimension side.  With a sole writer, the dk_cmp values of a row are
+    // read two rows ahead of its add.
+    auto fetch = [&](int jl, float (&v)[kDL]) {
+      const int j = jt + jl;
 #pragma unroll
-    for (int d = 0; d < kIdxDim; ++d) dkc[d] = 0.f;
-    for (int qq = 0; qq < nq; ++qq) {
-      const int t = len - Nq + q0 + qq;
-      if (t < 0 || j >= (t >> 2)) continue;  // not a candidate of this query
-      const float gj = g_scores[((size_t)b * Nq + q0 + qq) * nbp + j];
-      if (gj == 0.f) continue;
+      for (int e = 0; e < kDL; ++e) v[e] = 0.f;
+      if (sole && j < j1) {
+        const float* src = dkb + (size_t)j * kIdxDim + d0;
 #pragma unroll
-      for (int h = 0; h < kIdxHeads; ++h) {
-        float dot = 0.f;
+        for (int e = 0; e < kDL; ++e) v[e] = src[e];
+      }
+    };
+    auto row = [&](int jl, const float (&cur)[kDL]) {
+      const int j = jt + jl;
+      float kv[kDL], dk[kDL];
 #pragma unroll
-        for (int d = 0; d < kIdxDim; ++d) dot = fmaf(s_q[qq][h][d], kc[d], dot);
-        if (dot > 0.f) {
+      for (int e = 0; e < kDL; ++e) {
+        kv[e] = bf(skh[jl * kKRow * 8 + d0 + e]);
+        dk[e] = 0.f;
+      }
 #pragma unroll
-          for (int d = 0; d < kIdxDim; ++d) {
-            dkc[d] = fmaf(gj, s_q[qq][h][d], dkc[d]);
-            atomicAdd(&s_dq[qq][h][d], gj * kc[d]);
+      for (int c = 0; c < kWRow; ++c) {
+        const f32x4 w4 = sw[jl * kWRow + c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < kDL; ++e) {
+            dq[4 * c + i][e] = fmaf(w4[i], kv[e], dq[4 * c + i][e]);
+            dk[e] = fmaf(w4[i], qv[4 * c + i][e], dk[e]);
           }
+      }
+      if (j < j1) {
+        float* dst = dkb + (size_t)j * kIdxDim + d0;
+        if (sole) {
+#pragma unroll
+          for (int e = 0; e < kDL; ++e) dst[e] = cur[e] + dk[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < kDL; ++e)
+            if (dk[e] != 0.f) atomicAdd(&dst[e], dk[e]);
         }
       }
-    }
-    float* dst = dk_cmp + ((size_t)b * nbp + j) * kIdxDim;
+    };
+    constexpr int kRows = 64 / kDL;  // rows per lane per tile (even)
+    float pre0[kDL], pre1[kDL], cur[kDL];
+    fetch(js, pre0);
+    fetch(kDL + js, pre1);
+#pragma unroll 1
+    for (int jj = 0; jj < kRows; jj += 2) {
 #pragma unroll
-    for (int d = 0; d < kIdxDim; ++d)
-      if (dkc[d] != 0.f) atomicAdd(&dst[d], dkc[d]);
+      for (int e = 0; e < kDL; ++e) cur[e] = pre0[e];
+      if (jj + 2 < kRows) fetch((jj + 2) * kDL + js, pre0);
+      row(jj * kDL + js, cur);
+#pragma unroll
+      for (int e = 0; e < kDL; ++e) cur[e] = pre1[e];
+      if (jj + 3 < kRows) fetch((jj + 3) * kDL + js, pre1);
+      row((jj + 1) * kDL + js, cur);
+    }
   }
+#pragma unroll
+  for (int rr = 0; rr < kR; ++rr)
+#pragma unroll
+    for (int e = 0; e < kDL; ++e)
+      if (dq[rr][e] != 0.f) atomicAdd(&s_dq[rr * kIdxDim + d0 + e], dq[rr][e]);
   __syncthreads();
+  float* dqb = dq_idx + qrow0 * kIdxHeads * kIdxDim;
   for (int i = tid; i < nq * kIdxHeads * kIdxDim; i += kBwdThreads) {
-    const float x = (&s_dq[0][0][0])[i];
-    if (x != 0.f) atomicAdd(&dq_idx[((size_t)b * Nq + q0) * kIdxHeads * kIdxDim + i], x);
+    const float x = s_dq[i];
+    if (x != 0.f) atomicAdd(&dqb[i], x);
   }
 }
 
@@ -272,10 +406,17 @@ hipError_t launch_index_scores_bwd(const Dims& d, const uint16_t* q_idx, const u
   const int nbp = d.Lmax / 4;
   const int slice = 1024;
   const unsigned n_slices = (unsigned)((nbp + slice - 1) / slice);
-  QSA_LAUNCH(index_scores_bwd_kernel,
-             dim3(n_slices, (unsigned)((d.Nq + kIbwdQ - 1) / kIbwdQ), (unsigned)d.B),
-             dim3(kBwdThreads), 0, s, q_idx, k_cmp, lens, g_scores, dq_idx, dk_cmp, d.Lmax, d.Nq,
-             slice);
+#define QSA_IBWD(KQ)                                                                           \
+  QSA_LAUNCH(index_scores_bwd_kernel<KQ>,                                                      \
+             dim3(n_slices, (unsigned)((d.Nq + (KQ)-1) / (KQ)), (unsigned)d.B), dim3(kBwdThreads), \
+             0, s, q_idx, k_cmp, lens, g_scores, dq_idx, dk_cmp, d.Lmax, d.Nq, slice)
+  if (d.Nq <= 4)
+    QSA_IBWD(4);
+  else if (d.Nq <= 8)
+    QSA_IBWD(8);
+  else
+    QSA_IBWD(16);
+#undef QSA_IBWD
   return hipGetLastError();
 }
 

@@ -72,9 +72,13 @@ def test_sparse_attend_backward(hq, hkv):
     assert (dk[~touched] == 0).all() and (dv[~touched] == 0).all()
 
 
-def test_index_scores_and_compress_backward():
-    w = W.make_custom(910, [9000, 40001], 6, 8, 1, parts=("index",))
-    say(f"indexer backward: lens {list(w.lens)}")
+# 1 and 4 queries: one workgroup per block slice of a sequence (the dk_cmp rows
+# read, added and written back); 6: the eight-query layout; 20: sixteen-query
+# workgroups, two per slice (atomic adds to dk_cmp), the second one partial.
+@pytest.mark.parametrize("n_query", [1, 4, 6, 20])
+def test_index_scores_and_compress_backward(n_query):
+    w = W.make_custom(910, [9000, 40001], n_query, 8, 1, parts=("index",))
+    say(f"indexer backward: lens {list(w.lens)} n_query {n_query}")
     B, L, Nq = w.batch, w.max_len, w.n_query
     shp = Q.shape(B, L, Nq, 8, 1)
     lens = dev_i32(w.lens)
@@ -82,11 +86,18 @@ def test_index_scores_and_compress_backward():
     Q.compress_keys(shp, dev_bf16(w.k_idx), lens, k_cmp)
     rng = np.random.default_rng(911)
     g = O.bf16_bits_to_f64(bf16_bits(rng.standard_normal((B, Nq, L // 4)).astype(np.float32)))
+    # the gradients are added to what the buffers hold
+    base_dq = rng.integers(-4, 5, (B, Nq, 4, 64)).astype(np.float32)
+    base_dkc = rng.integers(-4, 5, (B, L // 4, 64)).astype(np.float32)
     dq_idx, dk_cmp = Q.index_scores_backward(shp, dev_bf16(w.q_idx), k_cmp, lens,
-                                             torch.from_numpy(g.astype(np.float32)).cuda())
+                                             torch.from_numpy(g.astype(np.float32)).cuda(),
+                                             dq_idx=torch.from_numpy(base_dq).cuda(),
+                                             dk_cmp=torch.from_numpy(base_dkc).cuda())
+    dk_cmp -= torch.from_numpy(base_dkc).cuda()
     dk_idx = Q.compress_keys_backward(shp, lens, dk_cmp)
     torch.cuda.synchronize()
-    dq_idx, dk_cmp_h, dk_idx = dq_idx.cpu().numpy(), dk_cmp.cpu().numpy(), dk_idx.cpu().numpy()
+    dq_idx = dq_idx.cpu().numpy() - base_dq
+    dk_cmp_h, dk_idx = dk_cmp.cpu().numpy(), dk_idx.cpu().numpy()
     want_dq = np.zeros(dq_idx.shape)
     want_dkc = np.zeros(dk_cmp_h.shape)
     for b in range(B):
