@@ -13,8 +13,11 @@
 //      dq_h = sum_j g_j [q_h . kc_j > 0] kc_j,  dkc_j = sum_h g_j [q_h . kc_j > 0] q_h;
 //  * compression (a sum of four keys): every key of a block receives the
 //    block's gradient.
-// Float32 arithmetic throughout (plain vector math; the forward pass's MFMA
-// tiles are not reused here).
+// The products q . k, dO . v and q_h . kc_j run on the matrix cores (bf16
+// inputs, exact products, float32 sums); every gradient sum is float32 vector
+// FMA.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -23,143 +26,9 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 64;    // tokens per step
-constexpr int kBwdHeads = 16;   // query heads per workgroup (one chunk of a group)
 constexpr float kLog2eB = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-// Grid (Nq, Hkv * hchunks, B), 256 threads: one query row, one KV head g and
-// up to 16 of its query heads.
-__global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ n_sel, const uint16_t* __restrict__ out,
-    const float* __restrict__ lse, const uint16_t* __restrict__ d_out, float* __restrict__ dq,
-    float* __restrict__ dk, float* __restrict__ dv, int Lmax, int Nq, int Hq, int Hkv,
-    float scale) {
-  __shared__ float s_q[kBwdHeads][kHeadDim];
-  __shared__ float s_do[kBwdHeads][kHeadDim];
-  __shared__ float s_D[kBwdHeads], s_lse2[kBwdHeads];
-  __shared__ int32_t s_sel[kTopK];
-  __shared__ __align__(16) uint16_t s_k[kBwdTile][kHeadDim];
-  __shared__ __align__(16) uint16_t s_v[kBwdTile][kHeadDim];
-  __shared__ float s_p[kBwdTile][kBwdHeads], s_ds[kBwdTile][kBwdHeads];
-  __shared__ int32_t s_tok[kBwdTile];
-  const int qi = blockIdx.x, b = blockIdx.z, tid = threadIdx.x;
-  const int G = Hq / Hkv, hchunks = (G + kBwdHeads - 1) / kBwdHeads;
-  const int g = blockIdx.y / hchunks, hc = blockIdx.y % hchunks;
-  const int h0 = g * G + hc * kBwdHeads, nh = min(kBwdHeads, G - hc * kBwdHeads);
-  const size_t row = (size_t)b * Nq + qi;
-  const int len = guard_len(lens[b], Nq, Lmax);
-  const int t = len - Nq + qi;
-  int ns = 0, ntok = 0, bt = 0;
-  if (t >= 0) {
-    bt = t >> 2;
-    ns = guard(n_sel[row], 0, min(bt, kTopK));
-    ntok = 4 * ns + (t - 4 * bt) + 1;
-  }
-  // the heads' q, dO, D = dO . O and lse (exp2 domain)
-  for (int i = tid; i < nh * kHeadDim; i += kBwdThreads) {
-    const int h = i >> 7, d = i & 127;
-    const size_t off = (row * Hq + h0 + h) * kHeadDim + d;
-    s_q[h][d] = bf(q[off]);
-    s_do[h][d] = bf(d_out[off]);
-  }
-  for (int i = tid; i < ns; i += kBwdThreads) s_sel[i] = guard(sel[row * kTopK + i], 0, bt - 1);
-  if (tid < kBwdHeads * 16) {
-    // 16 lanes per head: partial dot products of dO and O
-    const int h = tid >> 4, part = tid & 15;
-    float acc = 0.f;
-    if (h < nh) {
-      const size_t off = (row * Hq + h0 + h) * kHeadDim;
-      for (int d = part; d < kHeadDim; d += 16) acc += bf(d_out[off + d]) * bf(out[off + d]);
-    }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (part == 0 && h < nh) {
-      s_D[h] = acc;
-      s_lse2[h] = lse[row * Hq + h0 + h] * kLog2eB;
-    }
-  }
-  __syncthreads();
-  const float sl2 = scale * kLog2eB;
-  // dq accumulators: thread (d = tid & 127, half = tid >> 7) holds heads half, half + 2, ...
-  const int dd = tid & 127, half = tid >> 7;
-  float acc_dq[kBwdHeads / 2];
-#pragma unroll
-  for (int i = 0; i < kBwdHeads / 2; ++i) acc_dq[i] = 0.f;
-  const size_t kv_seq = (size_t)b * Lmax * Hkv;
-  for (int k0 = 0; k0 < ntok; k0 += kBwdTile) {
-    // the tile's token ids and K/V rows of head g
-    if (tid < kBwdTile) {
-      const int kk = k0 + tid;
-      int tok = -1;
-      if (kk < ntok) tok = kk < 4 * ns ? 4 * s_sel[kk >> 2] + (kk & 3) : 4 * bt + (kk - 4 * ns);
-      s_tok[tid] = tok;
-    }
-    __syncthreads();
-    for (int i = tid; i < kBwdTile * 16; i += kBwdThreads) {
-      const int r = i >> 4, c = i & 15;  // row, 16-byte chunk
-      const int tok = s_tok[r];
-      uint4 kv = zero_u4(), vv = zero_u4();
-      if (tok >= 0) {
-        const size_t off = (kv_seq + (size_t)tok * Hkv + g) * kHeadDim;
-        kv = reinterpret_cast<const uint4*>(k + off)[c];
-        vv = reinterpret_cast<const uint4*>(v + off)[c];
-      }
-      reinterpret_cast<uint4*>(&s_k[r][0])[c] = kv;
-      reinterpret_cast<uint4*>(&s_v[r][0])[c] = vv;
-    }
-    __syncthreads();
-    // p and ds of (token, head) pairs: thread -> token tid & 63, heads (tid >> 6) + 4 i
-    {
-      const int r = tid & 63, hb = tid >> 6;
-      const bool live = s_tok[r] >= 0;
-      for (int h = hb; h < kBwdHeads; h += 4) {
-        float z = 0.f, dp = 0.f;
-        if (h < nh && live) {
-#pragma unroll 8
-          for (int d = 0; d < kHeadDim; ++d) {
-            z = fmaf(s_q[h][d], bf(s_k[r][d]), z);
-            dp = fmaf(s_do[h][d], bf(s_v[r][d]), dp);
-          }
-        }
-        const float p = (h < nh && live) ? exp2f(z * sl2 - s_lse2[h]) : 0.f;
-        s_p[r][h] = p;
-        s_ds[r][h] = (h < nh && live) ? p * (dp - s_D[h]) : 0.f;
-      }
-    }
-    __syncthreads();
-    // dq: thread (dd, half) over the tile's tokens
-#pragma unroll
-    for (int i = 0; i < kBwdHeads / 2; ++i) {
-      const int h = half + 2 * i;
-      if (h >= nh) continue;
-      float a = 0.f;
-      for (int r = 0; r < kBwdTile; ++r) a = fmaf(s_ds[r][h], bf(s_k[r][dd]), a);
-      acc_dq[i] += a;
-    }
-    // dk, dv of the tile's tokens: thread (dd, half) over 32 tokens each
-    for (int r = half * 32; r < half * 32 + 32; ++r) {
-      const int tok = s_tok[r];
-      if (tok < 0) continue;
-      float ak = 0.f, av = 0.f;
-      for (int h = 0; h < nh; ++h) {
-        ak = fmaf(s_ds[r][h], s_q[h][dd], ak);
-        av = fmaf(s_p[r][h], s_do[h][dd], av);
-      }
-      const size_t off = (kv_seq + (size_t)tok * Hkv + g) * kHeadDim + dd;
-      atomicAdd(&dk[off], scale * ak);
-      atomicAdd(&dv[off], av);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < kBwdHeads / 2; ++i) {
-    const int h = half + 2 * i;
-    if (h < nh) dq[(row * Hq + h0 + h) * kHeadDim + dd] = scale * acc_dq[i];
-  }
-}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -167,6 +36,224 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Grid (Nq * kChunks, Hkv * hchunks, B), 256 threads: one chunk of up to
+// 256 entries of one query's token list, one KV head g and up to kH of its
+// query heads (rows of the 16-row MFMA tiles past the group's heads are
+// zero).  Per 64-token tile:
+//  1. wavefront w, tokens 16 w .. 16 w + 15, on the matrix cores: the logits
+//     z = q_h . k_s and dp_s = dO_h . v_s of the 16 x 16 (head, token) pairs
+//     in four 16x16x32 bf16 steps each (bf16 inputs, float32 sums); a lane
+//     holds four heads of one token and forms p = exp(scale z - lse) and
+//     ds = p (dp - D_h), stored in LDS with the tile's keys and token ids;
+//  2. float32 FMA: a thread owns kDT = 32 / kH dimensions, 128 / kDT
+//     apart, and every (256 kDT / 128)-th token of the tile and adds ds k
+//     into its dq registers and scale sum_h ds q_h, sum_h p dO_h into dk,
+//     dv (atomic adds, as a token can be read by several queries and head
+//     chunks; the lanes of one add cover whole 128-byte lines).
+// dq is summed over the workgroup in LDS and added to dq, which a fill kernel
+// clears first (the chunks of one query add into the same rows).
+constexpr int kAbChunk = 256;                                  // token list entries per workgroup
+constexpr int kAbChunks = (kMaxTok + kAbChunk - 1) / kAbChunk;  // chunks per query
+constexpr int kAbKRow = kHeadDim / 8 + 1;                      // LDS key row in uint4 (staggered)
+
+template <int kH>
+__global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ n_sel, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, const uint16_t* __restrict__ d_out, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dv, int Lmax, int Nq, int Hq, int Hkv,
+    float scale) {
+  constexpr int kDT = 32 / kH;                   // dimensions per thread, step 2
+  constexpr int kTPT = kHeadDim / kDT;           // threads per token
+  constexpr int kTG = kBwdThreads / kTPT;        // token groups
+  __shared__ uint4 s_k[kBwdTile * kAbKRow];
+  __shared__ f32x4 s_p[kBwdTile * kH / 4], s_ds[kBwdTile * kH / 4];
+  __shared__ int32_t s_tok[kBwdTile];
+  __shared__ int32_t s_sel[kAbChunk / kBlock];
+  __shared__ float s_D[16], s_lse2[16];
+  __shared__ float s_dq[kH * kHeadDim];
+  const int qi = blockIdx.x / kAbChunks, chunk = blockIdx.x % kAbChunks;
+  const int b = blockIdx.z, tid = threadIdx.x;
+  const int G = Hq / Hkv, hchunks = (G + kH - 1) / kH;
+  const int g = blockIdx.y / hchunks, hc = blockIdx.y % hchunks;
+  const int h0 = g * G + hc * kH, nh = min(kH, G - hc * kH);
+  const size_t row = (size_t)b * Nq + qi;
+  const int len = guard_len(lens[b], Nq, Lmax);
+  const int t = len - Nq + qi;
+  const int bt = t >> 2;
+  const int ns = guard(n_sel[row], 0, min(bt, kTopK));
+  const int ntok = 4 * ns + (t - 4 * bt) + 1;
+  const int c0 = chunk * kAbChunk, c1 = min(c0 + kAbChunk, ntok);
+  if (c0 >= c1) return;  // (uniform over the workgroup)
+  for (int i = tid; i < kAbChunk / kBlock; i += kBwdThreads) {
+    const int j = (c0 >> 2) + i;
+    s_sel[i] = j < ns ? guard(sel[row * kTopK + j], 0, bt - 1) : 0;
+  }
+  for (int i = tid; i < kH * kHeadDim; i += kBwdThreads) s_dq[i] = 0.f;
+  // Loads below are unconditional (rows clamped to the chunk's heads, values
+  // masked after), so that each group of them costs one memory round trip.
+  {
+    // 16 lanes per head, eight dimensions each: partial dot products of dO and O
+    const int h = tid >> 4, part = tid & 15;
+    const size_t off = (row * Hq + h0 + min(h, nh - 1)) * kHeadDim + 8 * part;
+    const uint4 a = *reinterpret_cast<const uint4*>(d_out + off);
+    const uint4 o = *reinterpret_cast<const uint4*>(out + off);
+    const float l2 = lse[row * Hq + h0 + min(h, nh - 1)] * kLog2eB;
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_lo(aw[i]), bf16_lo(ow[i]), acc);
+      acc = fmaf(bf16_hi(aw[i]), bf16_hi(ow[i]), acc);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (part == 0) {
+      s_D[h] = h < nh ? acc : 0.f;
+      s_lse2[h] = h < nh ? l2 : 0.f;
+    }
+  }
+  const int lane = lane_id(), wave = tid >> 6;
+  const int r = lane & 15, kc = lane >> 4;
+  // A fragments: head r, dimensions 32 ks + 8 kc ..
+  bf16x8 qa[4], da[4];
+  {
+    const uint4* pq = reinterpret_cast<const uint4*>(q + (row * Hq + h0 + min(r, nh - 1)) * kHeadDim);
+    const uint4* pd =
+        reinterpret_cast<const uint4*>(d_out + (row * Hq + h0 + min(r, nh - 1)) * kHeadDim);
+    uint4 uq[4], ud[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uq[ks] = pq[4 * ks + kc];
+      ud[ks] = pd[4 * ks + kc];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qa[ks] = as_bf16x8(r < nh ? uq[ks] : zero_u4());
+      da[ks] = as_bf16x8(r < nh ? ud[ks] : zero_u4());
+    }
+  }
+  // FMA side: this thread's dimensions d0 + e kTPT (e < kDT) and token group
+  const int d0 = tid % kTPT, tg = tid / kTPT;
+  float qr[kH][kDT], dr[kH][kDT], acc_dq[kH][kDT];
+  {
+    uint16_t uq[kH][kDT], ud[kH][kDT];
+#pragma unroll
+    for (int h = 0; h < kH; ++h)
+#pragma unroll
+      for (int e = 0; e < kDT; ++e) {
+        const size_t off = (row * Hq + h0 + min(h, nh - 1)) * kHeadDim + d0 + e * kTPT;
+        uq[h][e] = q[off];
+        ud[h][e] = d_out[off];
+      }
+#pragma unroll
+    for (int h = 0; h < kH; ++h)
+#pragma unroll
+      for (int e = 0; e < kDT; ++e) {
+        qr[h][e] = h < nh ? bf(uq[h][e]) : 0.f;
+        dr[h][e] = h < nh ? bf(ud[h][e]) : 0.f;
+        acc_dq[h][e] = 0.f;
+      }
+  }
+  __syncthreads();
+  float Dl[4], L2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Dl[i] = s_D[4 * kc + i];
+    L2[i] = s_lse2[4 * kc + i];
+  }
+  const float sl2 = scale * kLog2eB;
+  const size_t kv_seq = (size_t)b * Lmax * Hkv;
+  const uint4* k4 = reinterpret_cast<const uint4*>(k);
+  const uint4* v4 = reinterpret_cast<const uint4*>(v);
+  const uint16_t* skh = reinterpret_cast<const uint16_t*>(s_k);
+  const float* spf = reinterpret_cast<const float*>(s_p);
+  const float* sdf = reinterpret_cast<const float*>(s_ds);
+  for (int k0 = c0; k0 < c1; k0 += kBwdTile) {
+    {
+      const int rl = wave * 16 + r;  // the lane's token in the tile
+      const int kk = k0 + rl;
+      const bool live = kk < c1;
+      // a dead slot reads the own block's first token (ds = p = 0 there)
+      const int tok = !live ? 4 * bt
+                      : kk < 4 * ns ? 4 * s_sel[(kk - c0) >> 2] + (kk & 3)
+                                    : 4 * bt + (kk - 4 * ns);
+      const size_t rb = (kv_seq + (size_t)tok * Hkv + g) * (kHeadDim / 8);
+      uint4 kb[4], vb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kb[ks] = k4[rb + 4 * ks + kc];
+        vb[ks] = v4[rb + 4 * ks + kc];
+      }
+      f32x4 z = {0.f, 0.f, 0.f, 0.f}, dp = z;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        z = mfma16(qa[ks], as_bf16x8(kb[ks]), z);
+        dp = mfma16(da[ks], as_bf16x8(vb[ks]), dp);
+        s_k[rl * kAbKRow + 4 * ks + kc] = kb[ks];
+      }
+      if (4 * kc < kH) {
+        f32x4 pv, dsv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool on = live && 4 * kc + i < nh;
+          const float p = on ? exp2f(z[i] * sl2 - L2[i]) : 0.f;
+          pv[i] = p;
+          dsv[i] = on ? p * (dp[i] - Dl[i]) : 0.f;
+        }
+        s_p[rl * (kH / 4) + kc] = pv;
+        s_ds[rl * (kH / 4) + kc] = dsv;
+      }
+      if (kc == 0) s_tok[rl] = live ? tok : -1;
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int rl = tg; rl < kBwdTile; rl += kTG) {
+      const int tok = s_tok[rl];
+      if (tok < 0) continue;
+      float kv[kDT], ak[kDT], av[kDT];
+#pragma unroll
+      for (int e = 0; e < kDT; ++e) {
+        kv[e] = bf(skh[rl * kAbKRow * 8 + d0 + e * kTPT]);
+        ak[e] = 0.f;
+        av[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < kH; ++h) {
+        const float ds = sdf[rl * kH + h], p = spf[rl * kH + h];
+#pragma unroll
+        for (int e = 0; e < kDT; ++e) {
+          acc_dq[h][e] = fmaf(ds, kv[e], acc_dq[h][e]);
+          ak[e] = fmaf(ds, qr[h][e], ak[e]);
+          av[e] = fmaf(p, dr[h][e], av[e]);
+        }
+      }
+      const size_t off = (kv_seq + (size_t)tok * Hkv + g) * kHeadDim + d0;
+#pragma unroll
+      for (int e = 0; e < kDT; ++e) {
+        atomicAdd(&dk[off + e * kTPT], scale * ak[e]);
+        atomicAdd(&dv[off + e * kTPT], av[e]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < kH; ++h)
+#pragma unroll
+    for (int e = 0; e < kDT; ++e)
+      if (h < nh) atomicAdd(&s_dq[h * kHeadDim + d0 + e * kTPT], acc_dq[h][e]);
+  __syncthreads();
+  for (int i = tid; i < nh * kHeadDim; i += kBwdThreads)
+    atomicAdd(&dq[(row * Hq + h0) * kHeadDim + i], scale * s_dq[i]);
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
 }
 
 // Grid (n_slices, ceil(Nq / kQ), B), 256 threads (four wavefronts): the
@@ -217,31 +304,37 @@ void index_scores_bwd_kernel(
   bf16x8 qa[kMT][2];
   int lim[kMT];
   const size_t qrow0 = (size_t)b * Nq + q0;
+  // (unconditional loads, rows clamped to the workgroup's queries and
+  // masked after: one memory round trip for all of them)
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
     const int qq = 4 * mt + (r >> 2);
-    uint4 u0 = zero_u4(), u1 = zero_u4();
-    if (qq < nq) {
-      const uint4* p =
-          reinterpret_cast<const uint4*>(q_idx + ((qrow0 + qq) * kIdxHeads + (r & 3)) * kIdxDim);
-      u0 = p[kc];
-      u1 = p[4 + kc];
-    }
-    qa[mt][0] = as_bf16x8(u0);
-    qa[mt][1] = as_bf16x8(u1);
+    const uint4* p = reinterpret_cast<const uint4*>(
+        q_idx + ((qrow0 + min(qq, nq - 1)) * kIdxHeads + (r & 3)) * kIdxDim);
+    const uint4 u0 = p[kc], u1 = p[4 + kc];
+    qa[mt][0] = as_bf16x8(qq < nq ? u0 : zero_u4());
+    qa[mt][1] = as_bf16x8(qq < nq ? u1 : zero_u4());
     const int qw = 4 * mt + kc;
     lim[mt] = qw < nq ? min((len - Nq + q0 + qw) >> 2, j1) : 0;
   }
   // dimension side: this lane's dimensions d0.. of every row
   const int d0 = (lane % kG) * kDL, js = lane / kG;
   float qv[kR][kDL], dq[kR][kDL];
+  {
+    uint16_t uq[kR][kDL];
 #pragma unroll
-  for (int rr = 0; rr < kR; ++rr)
+    for (int rr = 0; rr < kR; ++rr)
 #pragma unroll
-    for (int e = 0; e < kDL; ++e) {
-      qv[rr][e] = rr / kIdxHeads < nq ? bf(q_idx[(qrow0 * kIdxHeads + rr) * kIdxDim + d0 + e]) : 0.f;
-      dq[rr][e] = 0.f;
-    }
+      for (int e = 0; e < kDL; ++e)
+        uq[rr][e] = q_idx[(qrow0 * kIdxHeads + min(rr, kIdxHeads * nq - 1)) * kIdxDim + d0 + e];
+#pragma unroll
+    for (int rr = 0; rr < kR; ++rr)
+#pragma unroll
+      for (int e = 0; e < kDL; ++e) {
+        qv[rr][e] = rr / kIdxHeads < nq ? bf(uq[rr][e]) : 0.f;
+        dq[rr][e] = 0.f;
+      }
+  }
   __syncthreads();
 
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
@@ -391,11 +484,21 @@ hipError_t launch_sparse_attend_bwd(const Dims& d, const uint16_t* q, const uint
                                     const uint16_t* d_out, float* dq, float* dk, float* dv,
                                     hipStream_t s) {
   if (d.B == 0 || d.Nq == 0) return hipSuccess;
+  const size_t nq_el = (size_t)d.B * d.Nq * d.Hq * kHeadDim;
+  QSA_LAUNCH(zero_f32_kernel, dim3((unsigned)std::min<size_t>((nq_el + 255) / 256, 1024)),
+             dim3(256), 0, s, dq, nq_el);
   const int G = d.Hq / d.Hkv;
-  const int hchunks = (G + kBwdHeads - 1) / kBwdHeads;
-  QSA_LAUNCH(sparse_attend_bwd_kernel, dim3((unsigned)d.Nq, (unsigned)(d.Hkv * hchunks), (unsigned)d.B),
-             dim3(kBwdThreads), 0, s, q, k, v, lens, sel, n_sel, out, lse, d_out, dq, dk, dv,
-             d.Lmax, d.Nq, d.Hq, d.Hkv, d.scale);
+  const dim3 block(kBwdThreads);
+  if (G <= 8) {
+    const dim3 grid((unsigned)(d.Nq * kAbChunks), (unsigned)d.Hkv, (unsigned)d.B);
+    QSA_LAUNCH(sparse_attend_bwd_kernel<8>, grid, block, 0, s, q, k, v, lens, sel, n_sel, out,
+               lse, d_out, dq, dk, dv, d.Lmax, d.Nq, d.Hq, d.Hkv, d.scale);
+  } else {
+    const dim3 grid((unsigned)(d.Nq * kAbChunks), (unsigned)(d.Hkv * ((G + 15) / 16)),
+                    (unsigned)d.B);
+    QSA_LAUNCH(sparse_attend_bwd_kernel<16>, grid, block, 0, s, q, k, v, lens, sel, n_sel, out,
+               lse, d_out, dq, dk, dv, d.Lmax, d.Nq, d.Hq, d.Hkv, d.scale);
+  }
   return hipGetLastError();
 }
 
