@@ -256,21 +256,48 @@ __global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
     p[i] = 0.f;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// bf16 bits of x rounded to nearest even (finite x).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x = hi + mid + lo, each part a bf16 rounded to nearest even from what the
+// previous parts leave (each subtraction is exact); the three parts carry 24
+// significant bits, so their products with a bf16 value, summed in float32,
+// match float32 arithmetic on x.
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_rne_bits(x);
+  const float r1 = x - __uint_as_float(hi << 16);
+  mid = bf16_rne_bits(r1);
+  lo = bf16_rne_bits(r1 - __uint_as_float(mid << 16));
+}
+
 // Grid (n_slices, ceil(Nq / kQ), B), 256 threads (four wavefronts): the
 // blocks of one slice against up to kQ queries of one sequence.  Each
 // wavefront takes 64-block tiles of the slice in turn:
-//  1. block side, on the matrix cores: the products q_h . kc_j of the kQ x 4
-//     (query, head) rows and the tile's blocks, 16 x 16 per pair of
-//     16x16x32 bf16 MFMA steps (bf16 inputs, float32 sums).  A lane then
-//     holds the four heads of one query for one block and keeps
-//     w = g (product > 0 and the block a candidate of the query) or 0;
-//     the w rows and the tile's keys go to the wavefront's LDS;
-//  2. dimension side, float32 FMA: a lane owns kDL = 16 / kQ consecutive
-//     dimensions of every (64 / kDL)-th block; per block j it sums
-//     w_j,r q_r,d over the rows r into dkc_j,d, added to dk_cmp as one
-//     row (a plain read-add-write when this workgroup is the row's only
-//     writer, atomic adds otherwise), and adds w_j,r kc_j,d to its dq_r,d
-//     registers.
+//  1. on the matrix cores: the products q_r . kc_j of the kQ x 4 (query,
+//     head) rows r and the tile's blocks, 16 x 16 per pair of 16x16x32 bf16
+//     MFMA steps.  A lane then holds four heads of one query for one block
+//     and keeps w = g (product > 0 and the block a candidate of the query)
+//     or 0; that is the A fragment layout of a 16x16x16 step with blocks as
+//     rows, so dkc_j,d = sum_r w_j,r q_r,d follows from three such steps per
+//     16 rows r (w split into three bf16 parts; q is bf16) with no exchange
+//     between lanes.  The B fragments give lane column c the dimension
+//     4 c + n of column tile n, so a lane ends with four consecutive
+//     dimensions of four blocks, added to dk_cmp 16 bytes at a time (a
+//     read-add-write, the old values read one tile ahead, when this
+//     workgroup is the rows' only writer; atomic adds otherwise).  The w
+//     rows and the tile's keys go to the wavefront's LDS;
+//  2. float32 FMA: a lane owns kDL = 16 / kQ consecutive dimensions of
+//     every (64 / kDL)-th block of the tile and adds w_j,r kc_j,d to its
+//     dq_r,d registers.
 // The lanes' dq are summed in LDS and added to dq_idx at the end.
 template <int kQ>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kQ <= 4 ? 2 : 1)))
@@ -280,8 +307,8 @@ void index_scores_bwd_kernel(
     float* __restrict__ dq_idx, float* __restrict__ dk_cmp, int Lmax, int Nq, int slice_blocks) {
   constexpr int kR = kQ * kIdxHeads;   // (query, head) rows
   constexpr int kMT = kR / 16;         // 16-row MFMA tiles
-  constexpr int kDL = 16 / kQ;         // dimensions per lane on the dimension side
-  constexpr int kG = kIdxDim / kDL;    // lanes per block on the dimension side
+  constexpr int kDL = 16 / kQ;         // dimensions per lane in the dq sums
+  constexpr int kG = kIdxDim / kDL;    // lanes per block in the dq sums
   constexpr int kKRow = 9;             // LDS key row: 64 bf16 + 16 bytes of stagger, in uint4
   constexpr int kWRow = kR / 4;        // LDS w row, in float4
   constexpr int kWaves = kBwdThreads / 64;
@@ -299,13 +326,15 @@ void index_scores_bwd_kernel(
 
   const int lane = lane_id(), wave = tid >> 6;
   const int r = lane & 15, kc = lane >> 4;
-  // block side: A fragments (row 16 mt + r = query 4 mt + r / 4, head r % 4,
-  // dimensions 8 kc.. and 32 + 8 kc..) and this lane's query 4 mt + kc
-  bf16x8 qa[kMT][2];
-  int lim[kMT];
   const size_t qrow0 = (size_t)b * Nq + q0;
   // (unconditional loads, rows clamped to the workgroup's queries and
   // masked after: one memory round trip for all of them)
+  // products: A fragments (row 16 mt + r = query 4 mt + r / 4, head r % 4,
+  // dimensions 8 kc.. and 32 + 8 kc..) and this lane's query 4 mt + kc;
+  // dk_cmp: B fragments (rows 16 mt + 4 kc + i, dimension 4 r + n)
+  bf16x8 qa[kMT][2];
+  s16x4 qb[kMT][4];
+  int lim[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
     const int qq = 4 * mt + (r >> 2);
@@ -316,25 +345,28 @@ void index_scores_bwd_kernel(
     qa[mt][1] = as_bf16x8(qq < nq ? u1 : zero_u4());
     const int qw = 4 * mt + kc;
     lim[mt] = qw < nq ? min((len - Nq + q0 + qw) >> 2, j1) : 0;
+    uint2 qd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      qd[i] = *reinterpret_cast<const uint2*>(
+          q_idx + (qrow0 * kIdxHeads + min(16 * mt + 4 * kc + i, kIdxHeads * nq - 1)) * kIdxDim +
+          4 * r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool on = (16 * mt + 4 * kc + i) / kIdxHeads < nq;
+      qb[mt][0][i] = on ? (short)(qd[i].x & 0xffffu) : (short)0;
+      qb[mt][1][i] = on ? (short)(qd[i].x >> 16) : (short)0;
+      qb[mt][2][i] = on ? (short)(qd[i].y & 0xffffu) : (short)0;
+      qb[mt][3][i] = on ? (short)(qd[i].y >> 16) : (short)0;
+    }
   }
-  // dimension side: this lane's dimensions d0.. of every row
+  // dq sums: this lane's dimensions d0.. of every row
   const int d0 = (lane % kG) * kDL, js = lane / kG;
-  float qv[kR][kDL], dq[kR][kDL];
-  {
-    uint16_t uq[kR][kDL];
+  float dq[kR][kDL];
 #pragma unroll
-    for (int rr = 0; rr < kR; ++rr)
+  for (int rr = 0; rr < kR; ++rr)
 #pragma unroll
-      for (int e = 0; e < kDL; ++e)
-        uq[rr][e] = q_idx[(qrow0 * kIdxHeads + min(rr, kIdxHeads * nq - 1)) * kIdxDim + d0 + e];
-#pragma unroll
-    for (int rr = 0; rr < kR; ++rr)
-#pragma unroll
-      for (int e = 0; e < kDL; ++e) {
-        qv[rr][e] = rr / kIdxHeads < nq ? bf(uq[rr][e]) : 0.f;
-        dq[rr][e] = 0.f;
-      }
-  }
+    for (int e = 0; e < kDL; ++e) dq[rr][e] = 0.f;
   __syncthreads();
 
   const uint4* kb = reinterpret_cast<const uint4*>(k_cmp + (size_t)b * nbp * kIdxDim);
@@ -344,12 +376,14 @@ void index_scores_bwd_kernel(
   uint4* sk = s_k[wave];
   f32x4* sw = s_w[wave];
   const int ntiles = (j1 - j0 + 63) >> 6;
-  // the tile's keys and g values, loaded one tile ahead
+  // the tile's keys, g values and (sole writer) dk_cmp values, loaded one
+  // tile ahead
   uint4 bv[4][2];
   float gv[kMT][4];
+  f32x4 old[4][4];
   auto load_tile = [&](int jt) {
-    // Unconditional key loads: a block past the slice re-reads its last one
-    // and gets w = 0.
+    // Unconditional loads: a block past the slice re-reads its last one and
+    // gets w = 0 (and no add).
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int j = min(jt + nt * 16 + r, j1 - 1);
@@ -363,6 +397,15 @@ void index_scores_bwd_kernel(
         const int j = jt + nt * 16 + r;
         gv[mt][nt] = j < lim[mt] ? gb[(size_t)(4 * mt + kc) * nbp + j] : 0.f;
       }
+    if (sole) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = min(jt + nt * 16 + 4 * kc + i, j1 - 1);
+          old[nt][i] = *reinterpret_cast<const f32x4*>(dkb + (size_t)j * kIdxDim + 4 * r);
+        }
+    }
   };
   if (wave < ntiles) load_tile(j0 + wave * 64);
 #pragma unroll 1
@@ -373,6 +416,9 @@ void index_scores_bwd_kernel(
     for (int nt = 0; nt < 4; ++nt) {
       sk[(nt * 16 + r) * kKRow + kc] = bv[nt][0];
       sk[(nt * 16 + r) * kKRow + 4 + kc] = bv[nt][1];
+      f32x4 dk[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -380,71 +426,60 @@ void index_scores_bwd_kernel(
         acc = mfma16(qa[mt][1], as_bf16x8(bv[nt][1]), acc);
         const float g = gv[mt][nt];
         f32x4 w;
+        s16x4 wh, wm, wl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = acc[i] > 0.f ? g : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          w[i] = acc[i] > 0.f ? g : 0.f;
+          uint32_t h, m, l;
+          split3_bf16(w[i], h, m, l);
+          wh[i] = (short)h;
+          wm[i] = (short)m;
+          wl[i] = (short)l;
+        }
         sw[(nt * 16 + r) * kWRow + 4 * mt + kc] = w;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          dk[n] = mfma16k16(wh, qb[mt][n], dk[n]);
+          dk[n] = mfma16k16(wm, qb[mt][n], dk[n]);
+          dk[n] = mfma16k16(wl, qb[mt][n], dk[n]);
+        }
+      }
+      // dk[n][i]: block jt + 16 nt + 4 kc + i, dimension 4 r + n
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = jt + nt * 16 + 4 * kc + i;
+        if (j < j1) {
+          float* dst = dkb + (size_t)j * kIdxDim + 4 * r;
+          if (sole) {
+            f32x4 o = old[nt][i];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) o[n] += dk[n][i];
+            *reinterpret_cast<f32x4*>(dst) = o;
+          } else {
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              if (dk[n][i] != 0.f) atomicAdd(&dst[n], dk[n][i]);
+          }
+        }
       }
     }
     wave_sync_lds();
     if (tile + kWaves < ntiles) load_tile(jt + kWaves * 64);
     const uint16_t* skh = reinterpret_cast<const uint16_t*>(sk);
-    // Dimension side.  With a sole writer, the dk_cmp values of a row are
-    // read two rows ahead of its add.
-    auto fetch = [&](int jl, float (&v)[kDL]) {
-      const int j = jt + jl;
+#pragma unroll 2
+    for (int jj = 0; jj < 64 / kDL; ++jj) {
+      const int jl = jj * kDL + js;
+      float kv[kDL];
 #pragma unroll
-      for (int e = 0; e < kDL; ++e) v[e] = 0.f;
-      if (sole && j < j1) {
-        const float* src = dkb + (size_t)j * kIdxDim + d0;
-#pragma unroll
-        for (int e = 0; e < kDL; ++e) v[e] = src[e];
-      }
-    };
-    auto row = [&](int jl, const float (&cur)[kDL]) {
-      const int j = jt + jl;
-      float kv[kDL], dk[kDL];
-#pragma unroll
-      for (int e = 0; e < kDL; ++e) {
-        kv[e] = bf(skh[jl * kKRow * 8 + d0 + e]);
-        dk[e] = 0.f;
-      }
+      for (int e = 0; e < kDL; ++e) kv[e] = bf(skh[jl * kKRow * 8 + d0 + e]);
 #pragma unroll
       for (int c = 0; c < kWRow; ++c) {
         const f32x4 w4 = sw[jl * kWRow + c];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < kDL; ++e) {
-            dq[4 * c + i][e] = fmaf(w4[i], kv[e], dq[4 * c + i][e]);
-            dk[e] = fmaf(w4[i], qv[4 * c + i][e], dk[e]);
-          }
+          for (int e = 0; e < kDL; ++e) dq[4 * c + i][e] = fmaf(w4[i], kv[e], dq[4 * c + i][e]);
       }
-      if (j < j1) {
-        float* dst = dkb + (size_t)j * kIdxDim + d0;
-        if (sole) {
-#pragma unroll
-          for (int e = 0; e < kDL; ++e) dst[e] = cur[e] + dk[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < kDL; ++e)
-            if (dk[e] != 0.f) atomicAdd(&dst[e], dk[e]);
-        }
-      }
-    };
-    constexpr int kRows = 64 / kDL;  // rows per lane per tile (even)
-    float pre0[kDL], pre1[kDL], cur[kDL];
-    fetch(js, pre0);
-    fetch(kDL + js, pre1);
-#pragma unroll 1
-    for (int jj = 0; jj < kRows; jj += 2) {
-#pragma unroll
-      for (int e = 0; e < kDL; ++e) cur[e] = pre0[e];
-      if (jj + 2 < kRows) fetch((jj + 2) * kDL + js, pre0);
-      row(jj * kDL + js, cur);
-#pragma unroll
-      for (int e = 0; e < kDL; ++e) cur[e] = pre1[e];
-      if (jj + 3 < kRows) fetch((jj + 3) * kDL + js, pre1);
-      row((jj + 1) * kDL + js, cur);
     }
   }
 #pragma unroll
