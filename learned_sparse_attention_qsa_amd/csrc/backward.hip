@@ -52,8 +52,8 @@ __device__ __forceinline__ void wave_sync_lds() {
 //     into its dq registers and scale sum_h ds q_h, sum_h p dO_h into dk,
 //     dv (atomic adds, as a token can be read by several queries and head
 //     chunks; the lanes of one add cover whole 128-byte lines).
-// dq is summed over the workgroup in LDS and added to dq, which a fill kernel
-// clears first (the chunks of one query add into the same rows).
+// dq is summed over the workgroup (shuffles, then LDS) and added to dq, which
+// a fill kernel clears first (the chunks of one query add into the same rows).
 constexpr int kAbChunk = 256;                                  // token list entries per workgroup
 constexpr int kAbChunks = (kMaxTok + kAbChunk - 1) / kAbChunk;  // chunks per query
 constexpr int kAbKRow = kHeadDim / 8 + 1;                      // LDS key row in uint4 (staggered)
@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
   __shared__ int32_t s_tok[kBwdTile];
   __shared__ int32_t s_sel[kAbChunk / kBlock];
   __shared__ float s_D[16], s_lse2[16];
-  __shared__ float s_dq[kH * kHeadDim];
+  __shared__ float s_part[kBwdThreads / 64][kH * kHeadDim];
+  __shared__ uint4 s_qd[2 * kH * kHeadDim / 8];
   const int qi = blockIdx.x / kAbChunks, chunk = blockIdx.x % kAbChunks;
   const int b = blockIdx.z, tid = threadIdx.x;
   const int G = Hq / Hkv, hchunks = (G + kH - 1) / kH;
@@ -92,7 +93,6 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
     const int j = (c0 >> 2) + i;
     s_sel[i] = j < ns ? guard(sel[row * kTopK + j], 0, bt - 1) : 0;
   }
-  for (int i = tid; i < kH * kHeadDim; i += kBwdThreads) s_dq[i] = 0.f;
   // Loads below are unconditional (rows clamped to the chunk's heads, values
   // masked after), so that each group of them costs one memory round trip.
   {
@@ -138,27 +138,27 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
   }
   // FMA side: this thread's dimensions d0 + e kTPT (e < kDT) and token group
   const int d0 = tid % kTPT, tg = tid / kTPT;
+  // the chunk's q and dO rows, staged in LDS for the FMA side
+  for (int i = tid; i < 2 * kH * (kHeadDim / 8); i += kBwdThreads) {
+    const int src = i / (kH * (kHeadDim / 8)), rem = i % (kH * (kHeadDim / 8));
+    const int h = rem / (kHeadDim / 8), c = rem % (kHeadDim / 8);
+    const uint16_t* p = (src ? d_out : q) + (row * Hq + h0 + min(h, nh - 1)) * kHeadDim;
+    s_qd[i] = reinterpret_cast<const uint4*>(p)[c];
+  }
+  __syncthreads();
   float qr[kH][kDT], dr[kH][kDT], acc_dq[kH][kDT];
   {
-    uint16_t uq[kH][kDT], ud[kH][kDT];
+    const uint16_t* sq = reinterpret_cast<const uint16_t*>(s_qd);
 #pragma unroll
     for (int h = 0; h < kH; ++h)
 #pragma unroll
       for (int e = 0; e < kDT; ++e) {
-        const size_t off = (row * Hq + h0 + min(h, nh - 1)) * kHeadDim + d0 + e * kTPT;
-        uq[h][e] = q[off];
-        ud[h][e] = d_out[off];
-      }
-#pragma unroll
-    for (int h = 0; h < kH; ++h)
-#pragma unroll
-      for (int e = 0; e < kDT; ++e) {
-        qr[h][e] = h < nh ? bf(uq[h][e]) : 0.f;
-        dr[h][e] = h < nh ? bf(ud[h][e]) : 0.f;
+        const int off = h * kHeadDim + d0 + e * kTPT;
+        qr[h][e] = h < nh ? bf(sq[off]) : 0.f;
+        dr[h][e] = h < nh ? bf(sq[kH * kHeadDim + off]) : 0.f;
         acc_dq[h][e] = 0.f;
       }
   }
-  __syncthreads();
   float Dl[4], L2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -240,14 +240,31 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
     }
     __syncthreads();
   }
+  // dq: the lanes of a wavefront that share dimensions summed by shuffles,
+  // each wavefront's sums stored in its own LDS region, the regions summed
+  // by the workgroup (LDS atomic adds from lanes that share an address cost
+  // far more)
+  constexpr int kLPW = 64 / kTPT;  // token groups per wavefront
 #pragma unroll
   for (int h = 0; h < kH; ++h)
 #pragma unroll
     for (int e = 0; e < kDT; ++e)
-      if (h < nh) atomicAdd(&s_dq[h * kHeadDim + d0 + e * kTPT], acc_dq[h][e]);
+#pragma unroll
+      for (int m = kTPT; m < 64; m <<= 1) acc_dq[h][e] += __shfl_xor(acc_dq[h][e], m);
+  const int gw = lane / kTPT;
+#pragma unroll
+  for (int h = 0; h < kH; ++h)
+    if (h % kLPW == gw) {
+#pragma unroll
+      for (int e = 0; e < kDT; ++e) s_part[wave][h * kHeadDim + d0 + e * kTPT] = acc_dq[h][e];
+    }
   __syncthreads();
-  for (int i = tid; i < nh * kHeadDim; i += kBwdThreads)
-    atomicAdd(&dq[(row * Hq + h0) * kHeadDim + i], scale * s_dq[i]);
+  for (int i = tid; i < nh * kHeadDim; i += kBwdThreads) {
+    float x = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBwdThreads / 64; ++w) x += s_part[w][i];
+    atomicAdd(&dq[(row * Hq + h0) * kHeadDim + i], scale * x);
+  }
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
@@ -298,7 +315,7 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
 //  2. float32 FMA: a lane owns kDL = 16 / kQ consecutive dimensions of
 //     every (64 / kDL)-th block of the tile and adds w_j,r kc_j,d to its
 //     dq_r,d registers.
-// The lanes' dq are summed in LDS and added to dq_idx at the end.
+// The lanes' dq are summed (shuffles, then LDS) and added to dq_idx at the end.
 template <int kQ>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kQ <= 4 ? 2 : 1)))
 void index_scores_bwd_kernel(
@@ -314,7 +331,6 @@ void index_scores_bwd_kernel(
   constexpr int kWaves = kBwdThreads / 64;
   __shared__ uint4 s_k[kWaves][64 * kKRow];
   __shared__ f32x4 s_w[kWaves][64 * kWRow];
-  __shared__ float s_dq[kR * kIdxDim];
   const int slice = blockIdx.x, q0 = blockIdx.y * kQ, b = blockIdx.z, tid = threadIdx.x;
   const int nq = min(kQ, Nq - q0);
   const int len = guard_len(lens[b], Nq, Lmax);
@@ -322,7 +338,6 @@ void index_scores_bwd_kernel(
   const int t_last = len - Nq + q0 + nq - 1;
   const int j0 = slice * slice_blocks, j1 = min(j0 + slice_blocks, t_last >> 2);
   if (j1 <= j0) return;  // (uniform over the workgroup)
-  for (int i = tid; i < kR * kIdxDim; i += kBwdThreads) s_dq[i] = 0.f;
 
   const int lane = lane_id(), wave = tid >> 6;
   const int r = lane & 15, kc = lane >> 4;
@@ -482,15 +497,31 @@ void index_scores_bwd_kernel(
       }
     }
   }
+  // dq: the kDL lanes of a dimension group summed by shuffles, each
+  // wavefront's sums stored in its own LDS region (its w rows are done with),
+  // the four regions summed by the workgroup.  (LDS atomic adds from lanes
+  // that share an address cost far more than this.)
 #pragma unroll
   for (int rr = 0; rr < kR; ++rr)
 #pragma unroll
     for (int e = 0; e < kDL; ++e)
-      if (dq[rr][e] != 0.f) atomicAdd(&s_dq[rr * kIdxDim + d0 + e], dq[rr][e]);
+#pragma unroll
+      for (int m = kG; m < 64; m <<= 1) dq[rr][e] += __shfl_xor(dq[rr][e], m);
+  float* part = reinterpret_cast<float*>(sw);  // kR x 64 floats
+  wave_sync_lds();
+#pragma unroll
+  for (int rr = 0; rr < kR; ++rr)
+    if (js == rr % kDL) {
+#pragma unroll
+      for (int e = 0; e < kDL; ++e) part[rr * kIdxDim + d0 + e] = dq[rr][e];
+    }
   __syncthreads();
   float* dqb = dq_idx + qrow0 * kIdxHeads * kIdxDim;
+  const float* parts = reinterpret_cast<const float*>(&s_w[0][0]);
   for (int i = tid; i < nq * kIdxHeads * kIdxDim; i += kBwdThreads) {
-    const float x = s_dq[i];
+    float x = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) x += parts[w * kR * kIdxDim + i];
     if (x != 0.f) atomicAdd(&dqb[i], x);
   }
 }
