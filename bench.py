@@ -868,9 +868,20 @@ def ceilings(Q, torch, flush, reps=10):
         out[f"gather_{name}"] = {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
     del kv
     torch.cuda.empty_cache()
+    # LDS atomic adds: cycles per wavefront instruction on one SIMD (2,048
+    # workgroups of four wavefronts, 256 adds each, over 1,024 SIMDs at 2.4 GHz)
+    wgs, iters = 2048, 256
+    lsink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    for f32 in (False, True):
+        for share in (1, 4, 64):
+            us = run(lambda: Q.ceil_lds_atomic(f32, share, wgs, iters, lsink))
+            cyc = us * 1e-6 * 2.4e9 / (wgs * 4 * iters / 1024)
+            out[f"lds_atomic_{'f32' if f32 else 'u32'}_share{share}"] = {
+                "us": us, "cycles_per_wave_instruction": cyc}
     out["note"] = ("kernel durations from dispatch-carried HIP events, median of "
                    f"{reps}, each after a 1 GiB flush; head_row_256B reads one KV head's "
-                   "piece of each token (a quarter of the bytes of the others)")
+                   "piece of each token (a quarter of the bytes of the others); lds_atomic: "
+                   "share = lanes of a wavefront on one LDS address")
     return out
 
 

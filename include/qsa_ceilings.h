@@ -39,6 +39,17 @@ qsa_status qsa_ceil_stream_read(const void* buf, size_t bytes, int32_t workgroup
 qsa_status qsa_ceil_gather(const void* base, const int64_t* row_index, int64_t n_rows,
                            int32_t row_bytes, int32_t workgroups, uint32_t* sink, void* stream);
 
+/* LDS atomic adds (a cost the kernels' reductions are designed around, not a
+ * memory ceiling): `workgroups` (1 .. 2^20) workgroups of 256 threads each
+ * issue `iters` (1 .. 4096) atomic adds of 1 to a 4 KiB LDS array, 32-bit
+ * integer (f32 = 0) or float32 (f32 = 1), with `share` (1, 2, 4, 16 or 64)
+ * consecutive lanes of a wavefront on one address and the address groups of
+ * a wavefront distinct.  Stores one word of the result to sink[blockIdx]
+ * only in a practically impossible case; sink must hold `workgroups` words
+ * (QSA_ERR_SHAPE for other arguments). */
+qsa_status qsa_ceil_lds_atomic(int32_t f32, int32_t share, int32_t workgroups, int32_t iters,
+                               uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

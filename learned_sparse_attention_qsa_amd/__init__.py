@@ -64,6 +64,7 @@ EXPORTS = (
     # include/qsa_ceilings.h: memory-system ceilings for benchmarks
     "qsa_ceil_stream_read",
     "qsa_ceil_gather",
+    "qsa_ceil_lds_atomic",
 )
 
 
@@ -162,6 +163,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_ceil_stream_read.restype = i32
     lib.qsa_ceil_gather.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp, vp]
     lib.qsa_ceil_gather.restype = i32
+    lib.qsa_ceil_lds_atomic.argtypes = [i32, i32, i32, i32, vp, vp]
+    lib.qsa_ceil_lds_atomic.restype = i32
     _lib = lib
     return lib
 
@@ -524,6 +527,16 @@ def ceil_gather(base: torch.Tensor, row_index: torch.Tensor, row_bytes: int, wor
         raise ValueError("a gathered piece lies outside base")
     _check(load_library().qsa_ceil_gather(_p(base), _p(row_index), n, row_bytes, workgroups,
                                           _p(sink), _stream(base.device)), "qsa_ceil_gather")
+
+
+def ceil_lds_atomic(f32: bool, share: int, workgroups: int, iters: int,
+                    sink: torch.Tensor) -> None:
+    """LDS atomic adds with `share` lanes per address (qsa_ceil_lds_atomic);
+    sink holds at least `workgroups` words."""
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 4 * workgroups:
+        raise ValueError("sink must be a GPU tensor of at least `workgroups` words")
+    _check(load_library().qsa_ceil_lds_atomic(int(f32), share, workgroups, iters, _p(sink),
+                                              _stream(sink.device)), "qsa_ceil_lds_atomic")
 
 
 def block_teacher(shp: QsaShape, q, k, v, lens, teacher=None, ws=None):

@@ -4,7 +4,8 @@
 // pieces the sparse attention reads (one KV head's 256-byte K or V row, one
 // token's 1 KiB row of all four KV heads, one micro-block's 4 KiB of four
 // consecutive token rows).  The kernels only read; each folds what it read
-// into one word so the loads cannot be dropped.
+// into one word so the loads cannot be dropped.  A last probe times LDS
+// atomic adds by how many lanes share an address, 32-bit integer and float32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,6 +67,20 @@ __global__ __launch_bounds__(256) void ceil_gather_kernel(const uint4* __restric
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Every thread adds 1 iters times to the LDS word of its address group
+// (lane / share, rotated by 64 words per step), 32-bit integer or float32.
+template <typename T>
+__global__ __launch_bounds__(256) void ceil_lds_atomic_kernel(int share, int iters,
+                                                              uint32_t* __restrict__ sink) {
+  __shared__ T h[1024];
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) h[i] = (T)0;
+  __syncthreads();
+  const int a = ((int)threadIdx.x >> 6) * 64 + ((int)threadIdx.x & 63) / share;
+  for (int i = 0; i < iters; ++i) atomicAdd(&h[(a + i * 64) & 1023], (T)1);
+  __syncthreads();
+  if (threadIdx.x == 0 && h[0] == (T)-1) sink[blockIdx.x] = 1u;  // practically never
+}
+
 }  // namespace
 }  // namespace qsa
 
@@ -95,6 +110,23 @@ qsa_status qsa_ceil_gather(const void* base, const int64_t* row_index, int64_t n
   QSA_LAUNCH(qsa::ceil_gather_kernel, dim3((unsigned)workgroups), dim3(256), 0,
              static_cast<hipStream_t>(stream), static_cast<const uint4*>(base), row_index, n_rows,
              row_bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+qsa_status qsa_ceil_lds_atomic(int32_t f32, int32_t share, int32_t workgroups, int32_t iters,
+                               uint32_t* sink, void* stream) {
+  if (!sink) return QSA_ERR_NULL;
+  if ((f32 != 0 && f32 != 1) || (share != 1 && share != 2 && share != 4 && share != 16 &&
+                                 share != 64) ||
+      workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > 4096)
+    return QSA_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (f32)
+    QSA_LAUNCH(qsa::ceil_lds_atomic_kernel<float>, dim3((unsigned)workgroups), dim3(256), 0, s,
+               share, iters, sink);
+  else
+    QSA_LAUNCH(qsa::ceil_lds_atomic_kernel<uint32_t>, dim3((unsigned)workgroups), dim3(256), 0, s,
+               share, iters, sink);
   return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_HIP;
 }
 

@@ -25,7 +25,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = Q.load_library()
     declared = header_symbols()
-    assert len(declared) == 25
+    assert len(declared) == 26
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -148,6 +148,12 @@ def test_ceiling_probes_reject_bad_arguments():
     assert lib.qsa_ceil_gather(FAKE, FAKE, -1, 256, 4, sink, None) == Q.ERR_SHAPE
     assert lib.qsa_ceil_gather(FAKE, None, 10, 256, 4, sink, None) == Q.ERR_NULL
     assert lib.qsa_ceil_gather(FAKE, FAKE, 0, 256, 4, sink, None) == Q.OK
+    assert lib.qsa_ceil_lds_atomic(0, 1, 4, 16, None, None) == Q.ERR_NULL
+    assert lib.qsa_ceil_lds_atomic(2, 1, 4, 16, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_lds_atomic(0, 3, 4, 16, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_lds_atomic(1, 64, 0, 16, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_lds_atomic(1, 64, 4, 0, sink, None) == Q.ERR_SHAPE
+    assert lib.qsa_ceil_lds_atomic(1, 64, 4, 4097, sink, None) == Q.ERR_SHAPE
 
 
 def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_launch():
