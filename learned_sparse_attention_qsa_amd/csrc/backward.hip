@@ -172,22 +172,27 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
   const uint16_t* skh = reinterpret_cast<const uint16_t*>(s_k);
   const float* spf = reinterpret_cast<const float*>(s_p);
   const float* sdf = reinterpret_cast<const float*>(s_ds);
+  // the lane's token of a tile and its K and V pieces, loaded one tile ahead
+  const int rl = wave * 16 + r;
+  int tok = 0;
+  uint4 kb[4], vb[4];
+  auto load_kv = [&](int k0) {
+    const int kk = k0 + rl;
+    // a dead slot reads the own block's first token (ds = p = 0 there)
+    tok = kk >= c1 ? 4 * bt
+          : kk < 4 * ns ? 4 * s_sel[(kk - c0) >> 2] + (kk & 3)
+                        : 4 * bt + (kk - 4 * ns);
+    const size_t rb = (kv_seq + (size_t)tok * Hkv + g) * (kHeadDim / 8);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kb[ks] = k4[rb + 4 * ks + kc];
+      vb[ks] = v4[rb + 4 * ks + kc];
+    }
+  };
+  load_kv(c0);
   for (int k0 = c0; k0 < c1; k0 += kBwdTile) {
     {
-      const int rl = wave * 16 + r;  // the lane's token in the tile
-      const int kk = k0 + rl;
-      const bool live = kk < c1;
-      // a dead slot reads the own block's first token (ds = p = 0 there)
-      const int tok = !live ? 4 * bt
-                      : kk < 4 * ns ? 4 * s_sel[(kk - c0) >> 2] + (kk & 3)
-                                    : 4 * bt + (kk - 4 * ns);
-      const size_t rb = (kv_seq + (size_t)tok * Hkv + g) * (kHeadDim / 8);
-      uint4 kb[4], vb[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        kb[ks] = k4[rb + 4 * ks + kc];
-        vb[ks] = v4[rb + 4 * ks + kc];
-      }
+      const bool live = k0 + rl < c1;
       f32x4 z = {0.f, 0.f, 0.f, 0.f}, dp = z;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -210,20 +215,21 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
       if (kc == 0) s_tok[rl] = live ? tok : -1;
     }
     __syncthreads();
+    if (k0 + kBwdTile < c1) load_kv(k0 + kBwdTile);
 #pragma unroll 2
-    for (int rl = tg; rl < kBwdTile; rl += kTG) {
-      const int tok = s_tok[rl];
-      if (tok < 0) continue;
+    for (int jr = tg; jr < kBwdTile; jr += kTG) {
+      const int tk = s_tok[jr];
+      if (tk < 0) continue;
       float kv[kDT], ak[kDT], av[kDT];
 #pragma unroll
       for (int e = 0; e < kDT; ++e) {
-        kv[e] = bf(skh[rl * kAbKRow * 8 + d0 + e * kTPT]);
+        kv[e] = bf(skh[jr * kAbKRow * 8 + d0 + e * kTPT]);
         ak[e] = 0.f;
         av[e] = 0.f;
       }
 #pragma unroll
       for (int h = 0; h < kH; ++h) {
-        const float ds = sdf[rl * kH + h], p = spf[rl * kH + h];
+        const float ds = sdf[jr * kH + h], p = spf[jr * kH + h];
 #pragma unroll
         for (int e = 0; e < kDT; ++e) {
           acc_dq[h][e] = fmaf(ds, kv[e], acc_dq[h][e]);
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
           av[e] = fmaf(p, dr[h][e], av[e]);
         }
       }
-      const size_t off = (kv_seq + (size_t)tok * Hkv + g) * kHeadDim + d0;
+      const size_t off = (kv_seq + (size_t)tk * Hkv + g) * kHeadDim + d0;
 #pragma unroll
       for (int e = 0; e < kDT; ++e) {
         atomicAdd(&dk[off + e * kTPT], scale * ak[e]);
