@@ -38,7 +38,7 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Grid (Nq * kChunks, Hkv * hchunks, B), 256 threads: one chunk of up to
+// Grid (Nq * kAbChunks, Hkv * hchunks, B), 256 threads: one chunk of up to
 // 256 entries of one query's token list, one KV head g and up to kH of its
 // query heads (rows of the 16-row MFMA tiles past the group's heads are
 // zero).  Per 64-token tile:
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kBwdThreads) void sparse_attend_bwd_kernel(
     const float* __restrict__ lse, const uint16_t* __restrict__ d_out, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, int Lmax, int Nq, int Hq, int Hkv,
     float scale) {
-  constexpr int kDT = 32 / kH;                   // dimensions per thread, step 2
+  constexpr int kDT = 32 / kH;                   // dimensions per thread in the FMA phase
   constexpr int kTPT = kHeadDim / kDT;           // threads per token
   constexpr int kTG = kBwdThreads / kTPT;        // token groups
   __shared__ uint4 s_k[kBwdTile * kAbKRow];
