@@ -9,6 +9,8 @@ and the call compresses only the new ones):
   * the 1M last-chunk prefill: the selection of every one of the 16,384
     rows, outputs of sampled rows;
   * the dense 1M comparator: one row of every sequence;
+  * the backward passes on the 1M decode batch: every row's dq, dk and dv on
+    every token read (zero elsewhere), the indexer gradients of all blocks;
   * paged K/V at the bench's shapes (16-token pages in a shuffled pool): the
     1M decode forward and dense decode, and the 1M-chunk dense prefill, bit
     for bit against the contiguous results; the dense prefill also against
@@ -34,6 +36,13 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def bf16_bits_np(x):
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(
+        np.uint16)
 
 
 def host_threads():
@@ -105,6 +114,73 @@ def test_decode_1m_every_row(flags):
     got = run_forward(w, flags)
     say("decode 1M: oracle")
     compare_outputs(w, got, [(b, i) for b in range(w.batch) for i in range(w.n_query)])
+
+
+def test_backward_1m_decode():
+    # the backward passes on the batch and in the launch configuration bench.py
+    # times them: every query row's dq; dk and dv on every token any query
+    # read, and zero elsewhere; the indexer gradients over all 1M blocks
+    say("backward 1M: inputs")
+    w = W.make(4)
+    B, L, Nq, Hq, Hkv = w.batch, w.max_len, w.n_query, w.q_heads, w.kv_heads
+    shp = Q.shape(B, L, Nq, Hq, Hkv)
+    prev = (w.lens - Nq).astype(np.int32)
+    lens = dev_i32(w.lens)
+    k_idx = dev_bf16(w.k_idx)
+    k_cmp = torch.zeros((B, L // 4, 64), dtype=torch.bfloat16, device="cuda")
+    Q.compress_keys(shp, k_idx, dev_i32(prev), k_cmp)
+    q, k, v, q_idx = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), dev_bf16(w.q_idx)
+    sel = torch.empty((B, Nq, 512), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((B, Nq), dtype=torch.int32, device="cuda")
+    say("backward 1M: forward and backward")
+    out, lse, _, _ = Q.forward(shp, q_idx, k_idx, k_cmp, q, k, v, lens,
+                               first_block=dev_i32(prev // 4), sel=sel, n_sel=n_sel)
+    rng = np.random.default_rng(4243)
+    d_out_bits = bf16_bits_np(rng.standard_normal((B, Nq, Hq, 128)).astype(np.float32))
+    g = rng.standard_normal((B, Nq, L // 4)).astype(np.float32)
+    dq, dk, dv = Q.sparse_attend_backward(shp, q, k, v, lens, sel, n_sel, out, lse,
+                                          dev_bf16(d_out_bits))
+    dq_idx, dk_cmp = Q.index_scores_backward(shp, q_idx, k_cmp, lens, torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    say("backward 1M: oracle")
+    res = O.qsa_forward(w.q_idx, w.k_idx, None, None, None, w.lens, Nq)
+    want_dq = np.zeros((B, Nq, Hq, 128))
+    want_dq_idx = np.zeros((B, Nq, 4, 64))
+    dq_h, dq_idx_h = dq.cpu().numpy(), dq_idx.cpu().numpy()
+    for b in range(B):
+        toks = [res["tok"][(b, i)] for i in range(Nq)]
+        union = np.unique(np.concatenate(toks))
+        pos = {int(t): n for n, t in enumerate(union)}
+        kr = O.bf16_bits_to_f64(w.k[b, union])
+        vr = O.bf16_bits_to_f64(w.v[b, union])
+        want_dk = np.zeros(kr.shape)
+        want_dv = np.zeros(vr.shape)
+        kc = O.bf16_bits_to_f64(res["kc"][b])
+        want_dkc = np.zeros((L // 4, 64))
+        for i in range(Nq):
+            rows = np.array([pos[int(t)] for t in toks[i]])
+            gq, gk, gv = O.attend_backward(O.bf16_bits_to_f64(w.q[b, i]), kr[rows], vr[rows],
+                                           O.bf16_bits_to_f64(d_out_bits[b, i]), w.scale)
+            want_dq[b, i] = gq
+            np.add.at(want_dk, rows, gk)
+            np.add.at(want_dv, rows, gv)
+            bt = (int(w.lens[b]) - Nq + i) // 4
+            gi, gkc = O.block_scores_backward(O.bf16_bits_to_f64(w.q_idx[b, i]), kc[:bt],
+                                              g[b, i, :bt].astype(np.float64))
+            want_dq_idx[b, i] = gi
+            want_dkc[:bt] += gkc
+        ut = torch.from_numpy(union).cuda()
+        check_close(dk[b].index_select(0, ut).cpu().numpy(), want_dk)
+        check_close(dv[b].index_select(0, ut).cpu().numpy(), want_dv)
+        # no other row was touched
+        nz = (dk[b] != 0).any(-1).any(-1) | (dv[b] != 0).any(-1).any(-1)
+        assert int(nz.sum()) <= union.size and not bool(nz.index_fill(0, ut, False).any())
+        got_dkc = dk_cmp[b].cpu().numpy()
+        rel = np.linalg.norm(got_dkc - want_dkc) / np.linalg.norm(want_dkc)
+        assert rel <= 1e-5, f"dk_cmp of sequence {b}: rel-L2 {rel:.2e}"
+    check_close(dq_h, want_dq)
+    rel = np.linalg.norm(dq_idx_h - want_dq_idx) / np.linalg.norm(want_dq_idx)
+    assert rel <= 1e-5, f"dq_idx: rel-L2 {rel:.2e}"
 
 
 def test_prefill_256k_every_row_selection():
