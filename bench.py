@@ -352,31 +352,43 @@ def decode_leg(args, Q, W, torch, np, flush):
     def run_backward():
         Q.sparse_attend_backward(ws.shp, ws.dev["q"], ws.dev["k"], ws.dev["v"], ws.lens, ws.sel,
                                  ws.n_sel, ws.out, ws.lse, d_out, dk=dk, dv=dv)
-        ev[1].record()
         Q.index_scores_backward(ws.shp, ws.dev["q_idx"], ws.k_cmp, ws.lens, d_s, dq_idx=dq_idx,
                                 dk_cmp=dk_cmp)
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     run_backward()  # first launches (code object loading) untimed
+    torch.cuda.synchronize()
+    # kernel durations from the HIP events each dispatch carries (the
+    # attention backward is a fill of dq and the gradient kernel)
     reps = 3
+    timer = Q.KernelTimer(max_launches=4 * reps)
+    with timer:
+        for _ in range(reps):
+            run_backward()
     t_att = t_idx = 0.0
-    for _ in range(reps):
-        ev[0].record()
-        run_backward()
-        ev[2].record()
-        torch.cuda.synchronize()
-        t_att += ev[0].elapsed_time(ev[1])
-        t_idx += ev[1].elapsed_time(ev[2])
+    for name, ms in timer.records():
+        if name.startswith("index_scores_bwd_kernel"):
+            t_idx += ms
+        else:
+            t_att += ms
     # the indexer backward's algorithmic HBM bytes: each candidate block's
     # compressed key (128 B) and its Nq gradient entries read, its float32
     # dk_cmp row read and written (2 x 256 B), dq_idx read and written once
     nblk = sum((int(n) - 1) // 4 for n in w.lens)
     idx_bytes = nblk * (128 + 4 * w.n_query + 512) + 2 * w.batch * w.n_query * 4 * 64 * 4
+    # the attention backward's algorithmic bytes: per (query, KV head) and
+    # token of its list, the K and V pieces read (2 x 256 B bf16) and the
+    # float32 dk and dv pieces read and written by the adds (2 x 2 x 512 B);
+    # q, dO, O and dq are small beside them
+    ntok = sum(4 * int(nsel_h[b, i]) + (int(w.lens[b]) - w.n_query + i) % 4 + 1
+               for b in range(w.batch) for i in range(w.n_query))
+    att_bytes = ntok * w.kv_heads * (2 * 256 + 4 * 512)
     backward = {"attend_backward_us": 1000 * t_att / reps,
+                "attend_backward_gbs": att_bytes / (t_att / reps * 1e-3) / 1e9,
                 "index_scores_backward_us": 1000 * t_idx / reps,
                 "index_scores_backward_gbs": idx_bytes / (t_idx / reps * 1e-3) / 1e9,
-                "note": f"mean of {reps} calls each on the decode batch after one untimed call, "
-                        "caches warm; the gradients accumulate into the same buffers; "
+                "note": f"kernel time per call, mean of {reps} calls each on the decode batch "
+                        "after one untimed call, caches warm (the attention backward: its dq fill "
+                        "and gradient kernels); the gradients accumulate into the same buffers; "
                         "dk/dv added atomically, dk_cmp read, added and written back"}
     del d_out, d_s, dk, dv, dq_idx, dk_cmp
     torch.cuda.empty_cache()
