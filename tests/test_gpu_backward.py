@@ -31,11 +31,19 @@ def bf16_bits(x):
     return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
 
 
+LONG = [6001, 2100, 30002]
+SHORT = [5, 7, 70, 1030]
+
+
 # 8 query heads per KV head and fewer: one eight-head chunk per group; 20
-# per KV head: a sixteen-head chunk and a partial one of four
-@pytest.mark.parametrize("hq,hkv", [(16, 2), (32, 4), (8, 8), (40, 2)])
-def test_sparse_attend_backward(hq, hkv):
-    w = W.make_custom(900 + hq, [6001, 2100, 30002], 5, hq, hkv)
+# per KV head: a sixteen-head chunk and a partial one of four.  Short
+# contexts: rows with no completed block before them (only their own block's
+# 1 to 4 tokens), with fewer than 512 blocks, and a token list of one chunk.
+@pytest.mark.parametrize("hq,hkv,lens", [(16, 2, LONG), (32, 4, LONG), (8, 8, LONG), (40, 2, LONG),
+                                         (32, 4, SHORT)], ids=["16-2", "32-4", "8-8", "40-2",
+                                                               "32-4-short"])
+def test_sparse_attend_backward(hq, hkv, lens):
+    w = W.make_custom(900 + hq, lens, 5, hq, hkv)
     say(f"attention backward: lens {list(w.lens)}, {hq}/{hkv} heads")
     shp = Q.shape(w.batch, w.max_len, w.n_query, hq, hkv)
     t = {n: dev_bf16(getattr(w, n)) for n in ("q_idx", "k_idx", "q", "k", "v")}
@@ -79,9 +87,13 @@ def test_sparse_attend_backward(hq, hkv):
 # 1 and 4 queries: one workgroup per block slice of a sequence (the dk_cmp rows
 # read, added and written back); 6: the eight-query layout; 20: sixteen-query
 # workgroups, two per slice (atomic adds to dk_cmp), the second one partial.
-@pytest.mark.parametrize("n_query", [1, 4, 6, 20])
-def test_index_scores_and_compress_backward(n_query):
-    w = W.make_custom(910, [9000, 40001], n_query, 8, 1, parts=("index",))
+# Short contexts: rows with no candidate block, and slices cut short.
+@pytest.mark.parametrize("n_query,lens", [(1, [9000, 40001]), (4, [9000, 40001]),
+                                          (6, [9000, 40001]), (20, [9000, 40001]),
+                                          (5, SHORT), (20, [24, 23, 300])],
+                         ids=["1", "4", "6", "20", "5-short", "20-short"])
+def test_index_scores_and_compress_backward(n_query, lens):
+    w = W.make_custom(910, lens, n_query, 8, 1, parts=("index",))
     say(f"indexer backward: lens {list(w.lens)} n_query {n_query}")
     B, L, Nq = w.batch, w.max_len, w.n_query
     shp = Q.shape(B, L, Nq, 8, 1)
