@@ -112,6 +112,8 @@ __device__ __forceinline__ int guard(int x, int lo, int hi) {
 __device__ __forceinline__ int guard_len(int x, int Nq, int Lmax) {
 #ifdef QSA_DEBUG
   if (x < Nq || x > Lmax) guard_hit();
+#else
+  (void)Nq;
 #endif
   return clampi(x, 0, Lmax);
 }
