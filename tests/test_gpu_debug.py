@@ -3,7 +3,7 @@ caller-supplied values count what they catch.  Valid calls give the release
 build's results bit for bit and no hits; a selection with ids outside
 [0, bt) and counts above min(bt, 512), or a page table with ids outside the
 pool, is clamped as in the release build (every access stays in its buffer)
-and counted."""
+and counted, in the forward kernels and in the attention backward."""
 import sys
 
 import numpy as np
@@ -102,3 +102,23 @@ def test_out_of_range_page_id_is_clamped_and_counted(debug_library):
                                       dev_i32(w.lens))
     assert Q.debug_guard_hits() > 0
     assert torch.isfinite(out.float()).all()
+
+
+def test_backward_over_out_of_range_selection_is_clamped_and_counted(debug_library):
+    w = W.make_custom(1703, [9001, 3002], 6, 16, 2)
+    shp, t, lens, out, lse, sel, n_sel = run_forward(w)
+    assert Q.debug_guard_hits() == 0
+    bad = sel.clone()
+    bad[0, 0, 3] = 1 << 20          # past the row's blocks
+    bad[1, 2, 0] = -5               # negative
+    bad_n = n_sel.clone()
+    bad_n[1, 5] = 700               # more than 512
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1703)
+    d_out = torch.randn(out.shape, generator=g, device="cuda").to(torch.bfloat16)
+    say("attention backward over a corrupted selection")
+    dq, dk, dv = Q.sparse_attend_backward(shp, t["q"], t["k"], t["v"], lens, bad, bad_n, out,
+                                          lse, d_out)
+    hits = Q.debug_guard_hits()
+    assert hits >= 3, hits
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
