@@ -319,8 +319,8 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
 //     workgroup is the rows' only writer; atomic adds otherwise).  The w
 //     rows and the tile's keys go to the wavefront's LDS;
 //  2. float32 FMA: a lane owns kDL = 16 / kQ consecutive dimensions of
-//     every (64 / kDL)-th block of the tile and adds w_j,r kc_j,d to its
-//     dq_r,d registers.
+//     every kDL-th block of the tile (from its lane group's offset) and adds
+//     w_j,r kc_j,d to its dq_r,d registers.
 // The lanes' dq are summed (shuffles, then LDS) and added to dq_idx at the end.
 template <int kQ>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kQ <= 4 ? 2 : 1)))
